@@ -1,0 +1,170 @@
+"""fp64 CPU oracle of the Gated DeltaNet layer (ctypes wrapper over gdn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does, and
+this package imports nothing from it.  It shares no code with the HIP path.
+
+Every array handed to the C oracle is converted here to float64.  bf16 inputs
+arrive as ``numpy.uint16`` bit patterns and are widened exactly (a bf16 value
+is the top half of an IEEE float32).
+
+What each function computes, and the page passages it follows, is documented
+in ``gdn_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gdn_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+             "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.orc_prelude.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P, P]
+    lib.orc_recurrent.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, I, I]
+    lib.orc_chunked.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P, P, I, I]
+    lib.orc_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P]
+    for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step):
+        f.restype = I
+    _lib = lib
+    return lib
+
+
+def f64(a) -> np.ndarray:
+    """Widen an input array to contiguous float64 (uint16 arrays are bf16 bits)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _cu(cu_seqlens, T):
+    if cu_seqlens is None:
+        return None, 1
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be a non-decreasing int32 vector from 0 to T")
+    return cu, cu.size - 1
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise RuntimeError(f"oracle {name} failed with code {rc}")
+
+
+def prelude(x, w, cu_seqlens=None, *, H_qk, H_v, dk, dv, eps=1e-6):
+    """Causal conv (width 4) -> SiLU -> L2 norm of q, k.  Returns fp64 (q, k, v)."""
+    x = f64(x)
+    w = f64(w)
+    T, Craw = x.shape
+    if Craw != 2 * H_qk * dk + H_v * dv or w.shape != (Craw, 4):
+        raise ValueError("prelude shape mismatch")
+    cu, N = _cu(cu_seqlens, T)
+    q = np.zeros((T, H_qk, dk))
+    k = np.zeros((T, H_qk, dk))
+    v = np.zeros((T, H_v, dv))
+    rc = _load().orc_prelude(_ptr(x), _ptr(w), _ptr(cu), N, T, H_qk, H_v, dk, dv, eps,
+                             _ptr(q), _ptr(k), _ptr(v))
+    _check(rc, "prelude")
+    return q, k, v
+
+
+def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens):
+    q, k, v, g, beta = (f64(a) for a in (q, k, v, g, beta))
+    T, H_qk, dk = q.shape
+    _, H_v, dv = v.shape
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, H_v) or beta.shape != (T, H_v):
+        raise ValueError("prefill shape mismatch")
+    cu, N = _cu(cu_seqlens, T)
+    S0 = None if initial_state is None else f64(initial_state)
+    if S0 is not None and S0.shape != (N, H_v, dv, dk):
+        raise ValueError("initial_state shape mismatch")
+    return q, k, v, g, beta, S0, cu, N, T, H_qk, H_v, dk, dv
+
+
+def recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, heads=None):
+    """Token-by-token gated delta rule.  Returns fp64 (o [T,H_v,dv], S [N,H_v,dv,dk]).
+
+    ``heads`` = (h_lo, h_hi) restricts the work to those V-heads; the other
+    entries of the results are zero.
+    """
+    q, k, v, g, beta, S0, cu, N, T, H_qk, H_v, dk, dv = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens)
+    h_lo, h_hi = (0, H_v) if heads is None else heads
+    o = np.zeros((T, H_v, dv))
+    S = np.zeros((N, H_v, dv, dk))
+    rc = _load().orc_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                               _ptr(cu), N, T, H_qk, H_v, dk, dv, float(scale), _ptr(o),
+                               _ptr(S), h_lo, h_hi)
+    _check(rc, "recurrent")
+    return o, S
+
+
+def chunked(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, chunk=64,
+            heads=None):
+    """Chunked (WY/UT) form of the same recurrence; same results up to rounding."""
+    q, k, v, g, beta, S0, cu, N, T, H_qk, H_v, dk, dv = _prefill_args(
+        q, k, v, g, beta, initial_state, cu_seqlens)
+    h_lo, h_hi = (0, H_v) if heads is None else heads
+    o = np.zeros((T, H_v, dv))
+    S = np.zeros((N, H_v, dv, dk))
+    rc = _load().orc_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                             _ptr(cu), N, T, H_qk, H_v, dk, dv, float(scale), int(chunk),
+                             _ptr(o), _ptr(S), h_lo, h_hi)
+    _check(rc, "chunked")
+    return o, S
+
+
+def decode_step(q, k, v, g, beta, pool, slot_idx, scale=1.0):
+    """One token per sequence on pool[slot_idx[b]].  Returns (o, new pool) in fp64.
+
+    The input pool is not modified; the returned pool is a float64 copy with the
+    addressed slots advanced by one token.
+    """
+    q, k, v, g, beta = (f64(a) for a in (q, k, v, g, beta))
+    B, H_qk, dk = q.shape
+    _, H_v, dv = v.shape
+    pool = f64(pool).copy()
+    P = pool.shape[0]
+    if pool.shape != (P, H_v, dv, dk) or g.shape != (B, H_v) or beta.shape != (B, H_v):
+        raise ValueError("decode shape mismatch")
+    slots = np.ascontiguousarray(slot_idx, dtype=np.int32)
+    if slots.shape != (B,):
+        raise ValueError("slot_idx shape mismatch")
+    o = np.zeros((B, H_v, dv))
+    rc = _load().orc_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(pool),
+                                 _ptr(slots), B, P, H_qk, H_v, dk, dv, float(scale), _ptr(o))
+    _check(rc, "decode_step")
+    return o, pool
