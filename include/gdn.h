@@ -1,0 +1,147 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet layer library (libgdn.so).
+ *
+ * The layer keeps, per (sequence, V-head), a d_v x d_k fp32 state S and for each
+ * token applies the gated delta rule
+ *     S_t = a_t * S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t (scale * q_t)
+ * with decay a_t = exp(g_t) and write strength b_t.
+ *
+ * Pages cited (title, site):
+ *   [Dissect] "从参数竞赛到效率革命：拆解 Qwen3.8-27B 的稠密架构与长上下文混合注意力"
+ *             (www.2kiu.com): sec. 2.1 gives the layer shape (16 QK heads, 48 V heads,
+ *             key and value head dim 128, short conv of width 4, the conv1d.weight,
+ *             A_log and dt_bias weights) and the fp32 state dtype; sec. 2.2 gives the
+ *             delta-rule update (the a_t = 1 case of the formula above) and its
+ *             erase-then-write meaning.
+ *   [OOM]     "Qwen3.8-27B 混合线性注意力到底解决了什么" (www.mhpn.cn): sec. 1.2 gives a
+ *             per-token step taking (q_t, k_t, v_t, S_prev, two gates) and returning
+ *             (o_t, S_t) -- the argument set of gdn_decode_step.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are HIP device pointers (or host-coherent memory
+ *     the device can address); the caller allocates and owns every buffer.  The
+ *     library never allocates, frees or retains a caller buffer.
+ *   - All arrays are dense, row-major, with the listed shapes.  bf16 arrays hold
+ *     IEEE bfloat16 bit patterns (uint16); outputs are rounded to nearest even.
+ *   - A state is [d_v][d_k] fp32 with d_k contiguous (the v k^T orientation of
+ *     [Dissect sec. 2.2]).  V-head h reads QK head h / (H_v / H_qk).
+ *   - The decay gate is passed as its logarithm g (a = exp(g)), fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; nothing synchronises unless the
+ *     environment variable GDN_DEBUG=1 is set, in which case each call waits for
+ *     its kernels and reports device-side failures.
+ *   - Return value: GDN_OK (0) or a negative gdn_status.  On failure nothing has
+ *     been enqueued (argument errors are detected on the host before any launch)
+ *     except for GDN_ERR_HIP, which reports a failing launch.  The text of the
+ *     last failure on the calling thread is returned by gdn_last_error().
+ *   - Only d_k = d_v = 128 is built; other head sizes return GDN_ERR_UNSUPPORTED.
+ *   - Array contents are not inspected on the host (that would need a sync):
+ *     cu_seqlens must be non-decreasing from 0 to T, slot ids distinct and in
+ *     [0, P).  With GDN_DEBUG=1 these preconditions are checked on the device.
+ *   - Thread safety: calls may be made concurrently from several threads; the
+ *     library keeps no mutable state except the per-thread error text.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = -1, /* NULL required pointer, bad size, H_v % H_qk != 0, ... */
+    GDN_ERR_UNSUPPORTED = -2, /* head size or dtype not built */
+    GDN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    GDN_ERR_HIP = -4,         /* a HIP launch/runtime call failed (text in gdn_last_error) */
+    GDN_ERR_DEVICE_CHECK = -5 /* GDN_DEBUG=1 only: a device-side precondition failed */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* ABI version of the loaded library (GDN_ABI_VERSION at build time). */
+int gdn_abi_version(void);
+
+/* Text describing the last failing call on this thread ("" if none). The string
+ * is owned by the library and valid until the next call on the same thread. */
+const char *gdn_last_error(void);
+
+/*
+ * gdn_conv_prelude -- short causal depthwise conv (width 4), SiLU, then split
+ * into q, k, v and L2-normalise every q and k head.  [Dissect sec. 2.1]: the
+ * conv kernel width 4 and the per-layer conv1d weight.
+ *
+ *   x_raw      device bf16 [T][C_raw], C_raw = 2*H_qk*d_k + H_v*d_v, channels
+ *              ordered [q heads | k heads | v heads], each head's channels contiguous
+ *   conv_w     device bf16 [C_raw][4]; tap 3 multiplies the current token, tap 0
+ *              the token three steps back; no bias
+ *   cu_seqlens device int32 [N+1] packed sequence offsets, or NULL for a single
+ *              sequence (then N must be 1).  Conv taps before each sequence's first
+ *              token read zero.
+ *   l2_eps     q = y / sqrt(sum(y^2) + l2_eps) per head (same for k)
+ *   q, k       device bf16 [T][H_qk][d_k] outputs;  v  device bf16 [T][H_v][d_v]
+ * Outputs must not alias inputs.  T = 0 is a no-op.
+ */
+int gdn_conv_prelude(const void *x_raw, const void *conv_w, const int32_t *cu_seqlens, int N,
+                     int T, int H_qk, int H_v, int d_k, int d_v, float l2_eps, void *q, void *k,
+                     void *v, void *stream);
+
+/*
+ * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill needs for
+ * the given sizes and io dtype (host-only; no device call).  It bounds the
+ * number of 64-token chunks by ceil(T/64) + N, so it holds for any cu_seqlens.
+ */
+size_t gdn_prefill_workspace_size(int io_dtype, int N, int T, int H_qk, int H_v, int d_k,
+                                  int d_v);
+
+/*
+ * gdn_prefill -- run the recurrence over packed sequences ([Dissect sec. 2.2],
+ * gated by a_t = exp(g_t)), returning every o_t and each sequence's final state.
+ *
+ *   io_dtype       GDN_BF16: q, k, v, o are bf16; computed by the chunked (64-token)
+ *                  kernels with bf16 matrix-core products and an fp32 state.
+ *                  GDN_F32:  q, k, v, o are fp32; computed token by token in fp32.
+ *   q, k           device [T][H_qk][d_k];  v  device [T][H_v][d_v]
+ *   g, beta        device fp32 [T][H_v]: log decay (<= 0) and write strength
+ *   initial_state  device fp32 [N][H_v][d_v][d_k], or NULL for zero states
+ *   final_state    device fp32 [N][H_v][d_v][d_k] output, or NULL to skip it.
+ *                  May alias initial_state exactly (in-place hand-off).
+ *   cu_seqlens     device int32 [N+1], or NULL for one sequence of T tokens (N = 1)
+ *   scale          multiplies q (1.0 in the layer as described on the pages)
+ *   o              device [T][H_v][d_v] output (io dtype); must not alias inputs
+ *   workspace      device scratch of at least gdn_prefill_workspace_size(...) bytes
+ *                  (may be NULL when that size is 0); contents on entry are ignored
+ */
+int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const float *g,
+                const float *beta, const float *initial_state, float *final_state,
+                const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_decode_step -- one token for each of B sequences whose states live in a
+ * slot pool; each addressed state is read once and overwritten in place.
+ * [OOM sec. 1.2] per-token step (q, k, v, S_prev, gates) -> (o, S); the update
+ * is the gated delta rule above, and o uses the updated state.
+ *
+ *   q, k        device bf16 [B][H_qk][d_k];  v  device bf16 [B][H_v][d_v]
+ *   g, beta     device fp32 [B][H_v]
+ *   state_pool  device fp32 [P][H_v][d_v][d_k]; slots not named in slot_idx are
+ *               neither read nor written
+ *   slot_idx    device int32 [B], distinct values in [0, P)
+ *   o           device bf16 [B][H_v][d_v] output
+ * B = 0 is a no-op.
+ */
+int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, float *state_pool, const int32_t *slot_idx, int B, int P,
+                    int H_qk, int H_v, int d_k, int d_v, float scale, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

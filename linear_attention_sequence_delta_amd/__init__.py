@@ -1,0 +1,244 @@
+"""MI355X (gfx950) Gated DeltaNet layer: thin Python binding over libgdn.so.
+
+The functions here carry the names of the C entry points in include/gdn.h and
+only marshal arguments: they check devices, dtypes and shapes of torch tensors,
+allocate outputs with torch, and pass raw device pointers plus the current HIP
+stream to the library.  Every step of the layer runs in the library's kernels;
+there is no Python or CPU fallback -- if libgdn.so is missing or cannot be
+loaded, every call raises.
+
+Build the library with ``python -m linear_attention_sequence_delta_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARG = -1
+GDN_ERR_UNSUPPORTED = -2
+GDN_ERR_WORKSPACE = -3
+GDN_ERR_HIP = -4
+GDN_ERR_DEVICE_CHECK = -5
+GDN_F32 = 0
+GDN_BF16 = 1
+
+EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
+           "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step")
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    def __init__(self, code: int, fn: str, msg: str):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn.so with argument types set (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m linear_attention_sequence_delta_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.gdn_abi_version.argtypes = []
+    L.gdn_abi_version.restype = I
+    L.gdn_last_error.argtypes = []
+    L.gdn_last_error.restype = ctypes.c_char_p
+    L.gdn_conv_prelude.argtypes = [P, P, P, I, I, I, I, I, I, F, P, P, P, P]
+    L.gdn_conv_prelude.restype = I
+    L.gdn_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    L.gdn_prefill_workspace_size.restype = Z
+    L.gdn_prefill.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
+    L.gdn_prefill.restype = I
+    L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
+    L.gdn_decode_step.restype = I
+    _lib = L
+    return L
+
+
+def _check(rc: int, fn: str):
+    if rc != GDN_OK:
+        raise GDNError(rc, fn, lib().gdn_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _device_of(t):
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device (torch 'cuda')")
+    return t.device
+
+
+def gdn_abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def gdn_conv_prelude(x, conv_w, cu_seqlens=None, *, H_qk: int = 16, H_v: int = 48,
+                     d_k: int = 128, d_v: int = 128, l2_eps: float = 1e-6,
+                     out: Optional[Tuple] = None):
+    """Causal conv (width 4) + SiLU + q/k L2 norm.  x: bf16 [T, C_raw]; conv_w:
+    bf16 [C_raw, 4]; cu_seqlens: int32 [N+1] or None.  Returns bf16 (q, k, v)."""
+    torch = _torch()
+    dev = _device_of(x)
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, dev, 2)
+    T = x.shape[0]
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    if out is None:
+        q = torch.empty((T, H_qk, d_k), dtype=torch.bfloat16, device=dev)
+        k = torch.empty((T, H_qk, d_k), dtype=torch.bfloat16, device=dev)
+        v = torch.empty((T, H_v, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        q, k, v = out
+        for name, t, shp in (("q", q, (T, H_qk, d_k)), ("k", k, (T, H_qk, d_k)),
+                             ("v", v, (T, H_v, d_v))):
+            _need(t, name, torch.bfloat16, dev)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} must have shape {shp}")
+    if x.shape[1] != 2 * H_qk * d_k + H_v * d_v or tuple(conv_w.shape) != (x.shape[1], 4):
+        raise ValueError("x / conv_w shapes do not match the head configuration")
+    rc = lib().gdn_conv_prelude(_ptr(x), _ptr(conv_w), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k,
+                                d_v, float(l2_eps), _ptr(q), _ptr(k), _ptr(v), _stream(dev))
+    _check(rc, "gdn_conv_prelude")
+    return q, k, v
+
+
+def gdn_prefill_workspace_size(io_dtype: int, N: int, T: int, H_qk: int, H_v: int,
+                               d_k: int = 128, d_v: int = 128) -> int:
+    return int(lib().gdn_prefill_workspace_size(io_dtype, N, T, H_qk, H_v, d_k, d_v))
+
+
+def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale: float = 1.0,
+                final_state=True, o=None, workspace=None):
+    """Prefill over packed sequences.  q, k: [T, H_qk, 128]; v: [T, H_v, 128], all
+    bf16 (chunked matrix-core path) or all fp32 (token-by-token fp32 path); g,
+    beta: fp32 [T, H_v]; initial_state: fp32 [N, H_v, 128, 128] or None.
+
+    final_state: True (allocate and return it), False/None (skip it), or an fp32
+    tensor to write (may be ``initial_state`` itself for an in-place hand-off).
+    Returns (o, final_state or None)."""
+    torch = _torch()
+    dev = _device_of(q)
+    if q.dtype == torch.bfloat16:
+        io, io_t = GDN_BF16, torch.bfloat16
+    elif q.dtype == torch.float32:
+        io, io_t = GDN_F32, torch.float32
+    else:
+        raise ValueError("q must be bfloat16 or float32")
+    _need(q, "q", io_t, dev, 3)
+    _need(k, "k", io_t, dev, 3)
+    _need(v, "v", io_t, dev, 3)
+    T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if tuple(k.shape) != (T, H_qk, d_k) or v.shape[0] != T:
+        raise ValueError("q, k, v shapes disagree")
+    _need(g, "g", torch.float32, dev, 2)
+    _need(beta, "beta", torch.float32, dev, 2)
+    if tuple(g.shape) != (T, H_v) or tuple(beta.shape) != (T, H_v):
+        raise ValueError("g and beta must be [T, H_v]")
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    sshape = (N, H_v, d_v, d_k)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev, 4)
+        if tuple(initial_state.shape) != sshape:
+            raise ValueError(f"initial_state must be {sshape}")
+    if final_state is True:
+        fs = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif final_state is None or final_state is False:
+        fs = None
+    else:
+        fs = final_state
+        _need(fs, "final_state", torch.float32, dev, 4)
+        if tuple(fs.shape) != sshape:
+            raise ValueError(f"final_state must be {sshape}")
+    if o is None:
+        o = torch.empty((T, H_v, d_v), dtype=io_t, device=dev)
+    else:
+        _need(o, "o", io_t, dev, 3)
+        if tuple(o.shape) != (T, H_v, d_v):
+            raise ValueError("o must be [T, H_v, d_v]")
+    ws_need = gdn_prefill_workspace_size(io, N, T, H_qk, H_v, d_k, d_v)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_prefill(io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(initial_state), _ptr(fs), _ptr(cu_seqlens), N, T, H_qk, H_v,
+                           d_k, d_v, float(scale), _ptr(o), _ptr(workspace), ws_bytes,
+                           _stream(dev))
+    _check(rc, "gdn_prefill")
+    return o, fs
+
+
+def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.0, o=None):
+    """One token per sequence; states in state_pool[slot_idx[b]] advance in place.
+    q, k: bf16 [B, H_qk, 128]; v: bf16 [B, H_v, 128]; g, beta: fp32 [B, H_v];
+    state_pool: fp32 [P, H_v, 128, 128]; slot_idx: int32 [B].  Returns o (bf16)."""
+    torch = _torch()
+    dev = _device_of(q)
+    for name, t, nd in (("q", q, 3), ("k", k, 3), ("v", v, 3)):
+        _need(t, name, torch.bfloat16, dev, nd)
+    B, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    _need(g, "g", torch.float32, dev, 2)
+    _need(beta, "beta", torch.float32, dev, 2)
+    _need(state_pool, "state_pool", torch.float32, dev, 4)
+    _need(slot_idx, "slot_idx", torch.int32, dev, 1)
+    P = state_pool.shape[0]
+    if (tuple(k.shape) != (B, H_qk, d_k) or v.shape[0] != B or tuple(g.shape) != (B, H_v)
+            or tuple(beta.shape) != (B, H_v) or tuple(state_pool.shape[1:]) != (H_v, d_v, d_k)
+            or slot_idx.numel() != B):
+        raise ValueError("decode shapes disagree")
+    if o is None:
+        o = torch.empty((B, H_v, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(o, "o", torch.bfloat16, dev, 3)
+    rc = lib().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                               _ptr(slot_idx), B, P, H_qk, H_v, d_k, d_v, float(scale), _ptr(o),
+                               _stream(dev))
+    _check(rc, "gdn_decode_step")
+    return o
+
+
+__all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
+           "gdn_prefill_workspace_size", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

@@ -1,0 +1,203 @@
+// gdn_abi.cpp -- the extern "C" entry points declared in include/gdn.h:
+// host-side argument validation, error reporting and kernel dispatch.
+// No HIP call is made before every host-side check has passed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return GDN_OK;
+}
+
+bool debug_mode() {
+    static const bool on = [] {
+        const char *e = std::getenv("GDN_DEBUG");
+        return e && e[0] && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Report a launch error, and in debug mode wait for the stream and report
+// asynchronous faults too.
+int finish(hipError_t e, hipStream_t s, const char *what) {
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (debug_mode()) {
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    return ok();
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+int check_heads(int H_qk, int H_v, int d_k, int d_v) {
+    if (H_qk < 1 || H_v < 1) return fail(GDN_ERR_INVALID_ARG, "head counts must be >= 1 (H_qk=%d, H_v=%d)", H_qk, H_v);
+    if (H_v % H_qk != 0) return fail(GDN_ERR_INVALID_ARG, "H_v (%d) must be a multiple of H_qk (%d)", H_v, H_qk);
+    if (d_k != gdn::kD || d_v != gdn::kD)
+        return fail(GDN_ERR_UNSUPPORTED, "only d_k = d_v = 128 is built (got d_k=%d, d_v=%d)", d_k, d_v);
+    if ((long long)H_v * gdn::kD > (1LL << 24) || (long long)H_qk * gdn::kD > (1LL << 24))
+        return fail(GDN_ERR_INVALID_ARG, "head count too large");
+    return GDN_OK;
+}
+
+int check_seqs(const int32_t *cu_seqlens, int N, int T) {
+    if (T < 0) return fail(GDN_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (N < 1) return fail(GDN_ERR_INVALID_ARG, "N must be >= 1 (got %d)", N);
+    if (!cu_seqlens && N != 1)
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens is NULL but N = %d (must be 1)", N);
+    return GDN_OK;
+}
+
+int device_check_cu(const int32_t *cu_seqlens, int N, int T, hipStream_t s) {
+    if (!debug_mode() || !cu_seqlens) return GDN_OK;
+    int bad = 0;
+    hipError_t e = gdn::debug_check_cu_seqlens(cu_seqlens, N, T, s, &bad);
+    if (e != hipSuccess) return hip_fail(e, "cu_seqlens check");
+    if (bad) return fail(GDN_ERR_DEVICE_CHECK, "cu_seqlens is not non-decreasing from 0 to T=%d", T);
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+int gdn_conv_prelude(const void *x_raw, const void *conv_w, const int32_t *cu_seqlens, int N,
+                     int T, int H_qk, int H_v, int d_k, int d_v, float l2_eps, void *q, void *k,
+                     void *v, void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
+    if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps))
+        return fail(GDN_ERR_INVALID_ARG, "l2_eps must be finite and >= 0");
+    if (T == 0) return ok();
+    if (!x_raw || !conv_w || !q || !k || !v)
+        return fail(GDN_ERR_INVALID_ARG, "x_raw, conv_w, q, k and v must be non-NULL");
+    const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
+    const size_t nx = (size_t)T * craw * 2, nq = (size_t)T * H_qk * gdn::kD * 2,
+                 nv = (size_t)T * H_v * gdn::kD * 2;
+    if (overlaps(q, nq, x_raw, nx) || overlaps(k, nq, x_raw, nx) || overlaps(v, nv, x_raw, nx) ||
+        overlaps(q, nq, k, nq) || overlaps(q, nq, v, nv) || overlaps(k, nq, v, nv))
+        return fail(GDN_ERR_INVALID_ARG, "prelude outputs must not overlap each other or x_raw");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
+    hipError_t e = gdn::launch_conv_prelude(x_raw, conv_w, cu_seqlens, N, T, H_qk, H_v, l2_eps,
+                                            q, k, v, s);
+    return finish(e, s, "gdn_conv_prelude launch");
+}
+
+size_t gdn_prefill_workspace_size(int io_dtype, int N, int T, int H_qk, int H_v, int d_k,
+                                  int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (io_dtype != GDN_BF16 || N < 1 || T < 1 || H_qk < 1 || H_v < 1) return 0;
+    return gdn::chunked_workspace_bytes(N, T, H_qk, H_v);
+}
+
+int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const float *g,
+                const float *beta, const float *initial_state, float *final_state,
+                const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "io_dtype must be GDN_F32 or GDN_BF16 (got %d)", io_dtype);
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    const size_t esz = io_dtype == GDN_F32 ? 4 : 2;
+    const size_t nqk = (size_t)T * H_qk * gdn::kD * esz, nv = (size_t)T * H_v * gdn::kD * esz;
+    const size_t ng = (size_t)T * H_v * 4, ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o must be non-NULL");
+    if (overlaps(o, nv, q, nqk) || overlaps(o, nv, k, nqk) || overlaps(o, nv, v, nv) ||
+        overlaps(o, nv, g, ng) || overlaps(o, nv, beta, ng) || overlaps(o, nv, initial_state, ns) ||
+        overlaps(o, nv, final_state, ns))
+        return fail(GDN_ERR_INVALID_ARG, "o must not overlap any input or state");
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, ns, initial_state, ns))
+        return fail(GDN_ERR_INVALID_ARG, "final_state must equal initial_state or not overlap it");
+    if (final_state && (overlaps(final_state, ns, q, nqk) || overlaps(final_state, ns, k, nqk) ||
+                        overlaps(final_state, ns, v, nv) || overlaps(final_state, ns, g, ng) ||
+                        overlaps(final_state, ns, beta, ng)))
+        return fail(GDN_ERR_INVALID_ARG, "final_state must not overlap q, k, v, g or beta");
+    const size_t need = gdn_prefill_workspace_size(io_dtype, N, T, H_qk, H_v, d_k, d_v);
+    if (ws_bytes < need || (need > 0 && !workspace))
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (need > 0 && (overlaps(workspace, need, o, nv) || overlaps(workspace, need, q, nqk) ||
+                     overlaps(workspace, need, k, nqk) || overlaps(workspace, need, v, nv) ||
+                     overlaps(workspace, need, final_state, ns) ||
+                     overlaps(workspace, need, initial_state, ns)))
+        return fail(GDN_ERR_INVALID_ARG, "workspace must not overlap inputs or outputs");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
+    hipError_t e;
+    if (io_dtype == GDN_F32)
+        e = gdn::launch_recurrent_prefill(gdn::kIoF32, q, k, v, g, beta, initial_state,
+                                          final_state, cu_seqlens, N, T, H_qk, H_v, scale, o, s);
+    else
+        e = gdn::launch_chunked_prefill(q, k, v, g, beta, initial_state, final_state, cu_seqlens,
+                                        N, T, H_qk, H_v, scale, o, workspace, s);
+    return finish(e, s, "gdn_prefill launch");
+}
+
+int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, float *state_pool, const int32_t *slot_idx, int B, int P,
+                    int H_qk, int H_v, int d_k, int d_v, float scale, void *o, void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if (B < 0) return fail(GDN_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (P < 1) return fail(GDN_ERR_INVALID_ARG, "P must be >= 1 (got %d)", P);
+    if (B > P) return fail(GDN_ERR_INVALID_ARG, "B (%d) distinct slots cannot fit a pool of P=%d", B, P);
+    if ((long long)B * H_v > 0x7FFFFFFFLL) return fail(GDN_ERR_INVALID_ARG, "B * H_v too large");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (B == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !state_pool || !slot_idx || !o)
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta, state_pool, slot_idx and o must be non-NULL");
+    const size_t npool = (size_t)P * H_v * gdn::kD * gdn::kD * 4, no = (size_t)B * H_v * gdn::kD * 2;
+    if (overlaps(o, no, state_pool, npool) || overlaps(o, no, q, (size_t)B * H_qk * gdn::kD * 2) ||
+        overlaps(o, no, k, (size_t)B * H_qk * gdn::kD * 2) || overlaps(o, no, v, no))
+        return fail(GDN_ERR_INVALID_ARG, "o must not overlap inputs or the state pool");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        int bad = 0;
+        hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
+        if (e != hipSuccess) return hip_fail(e, "slot_idx check");
+        if (bad) return fail(GDN_ERR_DEVICE_CHECK, "slot_idx has ids outside [0, %d) or repeated ids", P);
+    }
+    hipError_t e = gdn::launch_decode_step(q, k, v, g, beta, state_pool, slot_idx, B, H_qk, H_v,
+                                           scale, o, s);
+    return finish(e, s, "gdn_decode_step launch");
+}
+
+}  // extern "C"

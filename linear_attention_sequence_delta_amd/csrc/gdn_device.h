@@ -1,0 +1,57 @@
+// gdn_device.h -- device helpers shared by the gfx950 kernels of libgdn.
+// Internal header: not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+// Sum over each aligned group of 16 lanes (one DPP row); every lane of the row
+// receives the row's total.  quad_perm(1,0,3,2), quad_perm(2,3,0,1),
+// row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
+// Load 4 consecutive values (bf16 bits or fp32) as fp32.
+__device__ __forceinline__ void load4(const uint16_t *p, float *d) {
+    uint2 u = *reinterpret_cast<const uint2 *>(p);
+    d[0] = __uint_as_float(u.x << 16);
+    d[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    d[2] = __uint_as_float(u.y << 16);
+    d[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const float *p, float *d) {
+    float4 u = *reinterpret_cast<const float4 *>(p);
+    d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
+}
+__device__ __forceinline__ float load1(const uint16_t *p) { return bf2f(*p); }
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+__device__ __forceinline__ void store1(uint16_t *p, float x) { *p = f2bf(x); }
+__device__ __forceinline__ void store1(float *p, float x) { *p = x; }
+
+}  // namespace gdn

@@ -1,0 +1,43 @@
+// gdn_internal.h -- launchers shared between the kernel files and the C ABI.
+// Internal header: not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kD = 128;       // d_k = d_v built
+constexpr int kChunk = 64;    // prefill chunk length
+constexpr int kIoF32 = 0;
+constexpr int kIoBF16 = 1;
+
+hipError_t launch_conv_prelude(const void *x, const void *w, const int32_t *cu_seqlens, int N,
+                               int T, int H_qk, int H_v, float eps, void *q, void *k, void *v,
+                               hipStream_t stream);
+
+hipError_t launch_decode_step(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *pool, const int32_t *slot_idx, int B,
+                              int H_qk, int H_v, float scale, void *o, hipStream_t stream);
+
+hipError_t launch_recurrent_prefill(int io_dtype, const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta, const float *S0,
+                                    float *S_final, const int32_t *cu_seqlens, int N, int T,
+                                    int H_qk, int H_v, float scale, void *o, hipStream_t stream);
+
+// Chunked bf16 prefill (64-token chunks, bf16 matrix-core products).
+size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v);
+hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *S0, float *S_final,
+                                  const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
+                                  float scale, void *o, void *workspace, hipStream_t stream);
+
+// Device-side precondition checks (GDN_DEBUG=1): launch a one-workgroup scan,
+// wait for the stream, and return the violation bits in *result (0 = ok).
+hipError_t debug_check_cu_seqlens(const int32_t *cu_seqlens, int N, int T, hipStream_t stream,
+                                  int *result);
+hipError_t debug_check_slots(const int32_t *slot_idx, int B, int P, hipStream_t stream,
+                             int *result);
+
+}  // namespace gdn

@@ -1,0 +1,163 @@
+// gdn_prelude.hip -- fused short causal conv (width 4) + SiLU + q/k L2 norm.
+//
+// "从参数竞赛到效率革命：拆解 Qwen3.8-27B 的稠密架构与长上下文混合注意力", sec. 2.1:
+// each linear-attention layer has a depthwise conv of width 4 (conv1d.weight)
+// over its projected q/k/v channels.  Per channel c and token t of a sequence
+// starting at s0:
+//   xc[t, c] = sum_{j=0..3} w[c, j] * x[t - 3 + j, c]   (terms with t-3+j < s0 are 0)
+//   y = xc * sigmoid(xc)
+// then q and k heads are scaled by 1 / sqrt(sum y^2 + eps); v passes through.
+//
+// HBM-bound (20 KiB read + 20 KiB written per token at the standard shape), so
+// the kernel reads every raw value once, in 256-byte rows: a group of 16 lanes
+// owns one 128-channel head block (8 channels = 16 bytes per lane) and walks a
+// run of kRun tokens, keeping the last four inputs in registers.  The head's
+// sum of squares reduces inside the 16-lane DPP row.  Four groups of a wave take
+// four neighbouring head blocks, so each wave reads 1 KiB contiguous per token.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kRun = 32;          // tokens walked by one lane group
+constexpr int kGroupsPerBlock = 16;
+
+__device__ __forceinline__ void unpack8(uint4 u, float *d) {
+    d[0] = __uint_as_float(u.x << 16); d[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    d[2] = __uint_as_float(u.y << 16); d[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    d[4] = __uint_as_float(u.z << 16); d[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    d[6] = __uint_as_float(u.w << 16); d[7] = __uint_as_float(u.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+__global__ __launch_bounds__(256) void conv_prelude_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+    const int32_t *__restrict__ cu_seqlens, int N, int T, int H_qk, int H_v, float eps,
+    uint16_t *__restrict__ q, uint16_t *__restrict__ k, uint16_t *__restrict__ v) {
+    const int lane = threadIdx.x & 63;
+    const int c16 = lane & 15;
+    const int grp = threadIdx.x >> 4;                  // 0..15
+    const int n_blocks = 2 * H_qk + H_v;               // 128-channel head blocks
+    const int cb = blockIdx.y * kGroupsPerBlock + grp;
+    if (cb >= n_blocks) return;
+    const int t0 = blockIdx.x * kRun;
+    const int t1 = min(T, t0 + kRun);
+    const int C = n_blocks * kD;
+    const int ch0 = cb * kD + c16 * 8;                 // first of this lane's 8 channels
+
+    float wt[4][8];
+    {
+        const uint4 *wp = reinterpret_cast<const uint4 *>(w + (size_t)ch0 * 4);
+        float tmp[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack8(wp[i], tmp + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wt[j][e] = tmp[e * 4 + j];
+    }
+
+    // Sequence containing t0: largest n with cu[n] <= t0 (skipping empty ones).
+    int n = 0, s0 = 0, s1 = T;
+    if (cu_seqlens) {
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu_seqlens[mid] <= t0) lo = mid; else hi = mid - 1;
+        }
+        n = lo;
+        s0 = cu_seqlens[n];
+        s1 = cu_seqlens[n + 1];
+    }
+
+    float win[3][8];                                   // x[t-3], x[t-2], x[t-1]
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int src = t0 - 3 + j;
+        if (src >= s0 && src >= 0) {
+            unpack8(*reinterpret_cast<const uint4 *>(x + (size_t)src * C + ch0), win[j]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+        }
+    }
+
+    uint16_t *dst;
+    int dst_stride;
+    if (cb < H_qk) {
+        dst = q + (size_t)cb * kD + c16 * 8;
+        dst_stride = H_qk * kD;
+    } else if (cb < 2 * H_qk) {
+        dst = k + (size_t)(cb - H_qk) * kD + c16 * 8;
+        dst_stride = H_qk * kD;
+    } else {
+        dst = v + (size_t)(cb - 2 * H_qk) * kD + c16 * 8;
+        dst_stride = H_v * kD;
+    }
+    const bool normalise = cb < 2 * H_qk;
+
+    uint4 nxt = make_uint4(0, 0, 0, 0);
+    if (t0 < t1) nxt = *reinterpret_cast<const uint4 *>(x + (size_t)t0 * C + ch0);
+    for (int t = t0; t < t1; ++t) {
+        float cur[8];
+        unpack8(nxt, cur);
+        if (t + 1 < t1) nxt = *reinterpret_cast<const uint4 *>(x + (size_t)(t + 1) * C + ch0);
+        if (cu_seqlens && t >= s1) {                   // a new sequence starts at t
+            while (n + 1 < N && cu_seqlens[n + 1] <= t) ++n;
+            s1 = cu_seqlens[n + 1];
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+        }
+        float y[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = wt[3][e] * cur[e];
+            acc += wt[2][e] * win[2][e];
+            acc += wt[1][e] * win[1][e];
+            acc += wt[0][e] * win[0][e];
+            y[e] = silu(acc);
+            ss += y[e] * y[e];
+        }
+        if (normalise) {
+            const float r = rsqrtf(row16_sum(ss) + eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= r;
+        }
+        uint4 out;
+        out.x = pack_bf2(y[0], y[1]);
+        out.y = pack_bf2(y[2], y[3]);
+        out.z = pack_bf2(y[4], y[5]);
+        out.w = pack_bf2(y[6], y[7]);
+        *reinterpret_cast<uint4 *>(dst + (size_t)t * dst_stride) = out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            win[0][e] = win[1][e];
+            win[1][e] = win[2][e];
+            win[2][e] = cur[e];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv_prelude(const void *x, const void *w, const int32_t *cu_seqlens, int N,
+                               int T, int H_qk, int H_v, float eps, void *q, void *k, void *v,
+                               hipStream_t stream) {
+    const int n_blocks = 2 * H_qk + H_v;
+    dim3 grid((T + kRun - 1) / kRun, (n_blocks + kGroupsPerBlock - 1) / kGroupsPerBlock);
+    hipLaunchKernelGGL(conv_prelude_kernel, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w),
+                       cu_seqlens, N, T, H_qk, H_v, eps, static_cast<uint16_t *>(q),
+                       static_cast<uint16_t *>(k), static_cast<uint16_t *>(v));
+    return hipGetLastError();
+}
+
+}  // namespace gdn

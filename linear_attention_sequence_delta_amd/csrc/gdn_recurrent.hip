@@ -1,0 +1,216 @@
+// gdn_recurrent.hip -- state-in-registers kernels of the gated delta rule:
+//   * the decode step over a state-slot pool (one token per sequence), and
+//   * the token-by-token prefill used for fp32 io.
+//
+// Update per token and state row i (S is d_v x d_k, row i = S[i, :]):
+//   a_i = S_i . k,   c_i = S_i . q,   d_i = beta (v_i - alpha a_i)
+//   S_i <- alpha S_i + d_i k,        o_i = alpha c_i + d_i (k . q)
+// which is S <- alpha S (I - beta k k^T) + beta v k^T followed by o = S q
+// ("从参数竞赛到效率革命：拆解 Qwen3.8-27B 的稠密架构与长上下文混合注意力", sec. 2.2,
+// gated by alpha = exp(g)); both dot products use the old row, so each state
+// row is read once and written once.
+//
+// Thread layout (256 threads = 4 waves own one 128 x 128 state): lane groups of
+// 16 share a row; lane c of a group holds columns 4c..4c+3 and 64+4c..64+4c+3,
+// so one row is two contiguous 256-byte segments and its dot products reduce
+// inside one 16-lane DPP row.  Thread (wave w, group r) owns rows
+// 32w + 4j + r for j = 0..7: 64 fp32 state values per thread, all loaded before
+// any arithmetic so that 64 KiB per workgroup are in flight at once.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+struct RowMap {
+    int wave, c16, r4;
+    __device__ RowMap() {
+        const int lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        c16 = lane & 15;
+        r4 = lane >> 4;
+    }
+    __device__ int row(int j) const { return wave * 32 + j * 4 + r4; }
+    __device__ int col(int half) const { return half * 64 + c16 * 4; }
+};
+
+template <typename T>
+__device__ __forceinline__ void load_vec8(const T *base, const RowMap &m, float *d) {
+    load4(base + m.col(0), d);
+    load4(base + m.col(1), d + 4);
+}
+
+// One token applied to the 8 rows this thread owns.  s[j][0..7] holds row
+// m.row(j), columns (m.col(0)+0..3, m.col(1)+0..3).  vr[j] = v[m.row(j)].
+// Returns, in lanes with c16 < 8, o of row m.row(c16).
+__device__ __forceinline__ float delta_rows(float (&s)[8][8], const float *kk, const float *qq,
+                                            const float *vr, float alpha, float beta,
+                                            const RowMap &m) {
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kq += kk[e] * qq[e];
+    kq = row16_sum(kq);
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a += s[j][e] * kk[e];
+            c += s[j][e] * qq[e];
+        }
+        a = row16_sum(a);
+        c = row16_sum(c);
+        const float d = beta * (vr[j] - alpha * a);
+        const float oj = alpha * c + d * kq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[j][e] = alpha * s[j][e] + d * kk[e];
+        mine = (m.c16 == j) ? oj : mine;
+    }
+    return mine;
+}
+
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ pool,
+    const int32_t *__restrict__ slot_idx, int H_qk, int H_v, float scale,
+    uint16_t *__restrict__ o) {
+    const RowMap m;
+    const int b = blockIdx.x / H_v;
+    const int h = blockIdx.x - b * H_v;
+    const int hq = h / (H_v / H_qk);
+    const int slot = slot_idx[b];
+    float *S = pool + ((size_t)slot * H_v + h) * (kD * kD);
+
+    float s[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        load4(S + m.row(j) * kD + m.col(0), s[j]);
+        load4(S + m.row(j) * kD + m.col(1), s[j] + 4);
+    }
+    float kk[8], qq[8], vr[8];
+    load_vec8(k + ((size_t)b * H_qk + hq) * kD, m, kk);
+    load_vec8(q + ((size_t)b * H_qk + hq) * kD, m, qq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qq[e] *= scale;
+    const uint16_t *vb = v + ((size_t)b * H_v + h) * kD;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = bf2f(vb[m.row(j)]);
+    const float alpha = expf(g[(size_t)b * H_v + h]);
+    const float bt = beta[(size_t)b * H_v + h];
+
+    const float mine = delta_rows(s, kk, qq, vr, alpha, bt, m);
+
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(0)) =
+            make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(1)) =
+            make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
+    }
+    if (m.c16 < 8) o[((size_t)b * H_v + h) * kD + m.wave * 32 + m.c16 * 4 + m.r4] = f2bf(mine);
+}
+
+// Token-by-token prefill: one workgroup per (sequence, V-head) carries the
+// state through the sequence in registers.  The next token's inputs are
+// loaded before the current token's arithmetic.
+template <typename IO>
+__global__ __launch_bounds__(256) void recurrent_prefill_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta,
+    const float *initial_state, float *final_state, const int32_t *__restrict__ cu_seqlens,
+    int T, int H_qk, int H_v, float scale, IO *__restrict__ o) {
+    const RowMap m;
+    const int n = blockIdx.x / H_v;
+    const int h = blockIdx.x - n * H_v;
+    const int hq = h / (H_v / H_qk);
+    const int s0 = cu_seqlens ? cu_seqlens[n] : 0;
+    const int s1 = cu_seqlens ? cu_seqlens[n + 1] : T;
+    const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
+
+    float s[8][8];
+    if (initial_state) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            load4(initial_state + st_off + m.row(j) * kD + m.col(0), s[j]);
+            load4(initial_state + st_off + m.row(j) * kD + m.col(1), s[j] + 4);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
+    }
+
+    float kk[8], qq[8], vr[8], gt = 0.f, bt = 0.f;
+    auto fetch = [&](int t, float *kd, float *qd, float *vd, float &gd, float &bd) {
+        load_vec8(k + ((size_t)t * H_qk + hq) * kD, m, kd);
+        load_vec8(q + ((size_t)t * H_qk + hq) * kD, m, qd);
+        const IO *vb = v + ((size_t)t * H_v + h) * kD;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vd[j] = load1(vb + m.row(j));
+        gd = g[(size_t)t * H_v + h];
+        bd = beta[(size_t)t * H_v + h];
+    };
+    if (s0 < s1) fetch(s0, kk, qq, vr, gt, bt);
+    for (int t = s0; t < s1; ++t) {
+        float kn[8], qn[8], vn[8], gn = 0.f, bn = 0.f;
+        if (t + 1 < s1) fetch(t + 1, kn, qn, vn, gn, bn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qq[e] *= scale;
+        const float mine = delta_rows(s, kk, qq, vr, expf(gt), bt, m);
+        if (m.c16 < 8) store1(o + ((size_t)t * H_v + h) * kD + m.wave * 32 + m.c16 * 4 + m.r4, mine);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kk[e] = kn[e];
+            qq[e] = qn[e];
+            vr[e] = vn[e];
+        }
+        gt = gn;
+        bt = bn;
+    }
+    if (final_state) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            *reinterpret_cast<float4 *>(final_state + st_off + m.row(j) * kD + m.col(0)) =
+                make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+            *reinterpret_cast<float4 *>(final_state + st_off + m.row(j) * kD + m.col(1)) =
+                make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *pool, const int32_t *slot_idx, int B,
+                              int H_qk, int H_v, float scale, void *o, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_step_kernel, dim3(B * H_v), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), g, beta, pool, slot_idx, H_qk, H_v,
+                       scale, static_cast<uint16_t *>(o));
+    return hipGetLastError();
+}
+
+hipError_t launch_recurrent_prefill(int io_dtype, const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta, const float *S0,
+                                    float *S_final, const int32_t *cu_seqlens, int N, int T,
+                                    int H_qk, int H_v, float scale, void *o,
+                                    hipStream_t stream) {
+    if (io_dtype == kIoF32) {
+        hipLaunchKernelGGL(recurrent_prefill_kernel<float>, dim3(N * H_v), dim3(256), 0, stream,
+                           static_cast<const float *>(q), static_cast<const float *>(k),
+                           static_cast<const float *>(v), g, beta, S0, S_final, cu_seqlens, T,
+                           H_qk, H_v, scale, static_cast<float *>(o));
+    } else {
+        hipLaunchKernelGGL(recurrent_prefill_kernel<uint16_t>, dim3(N * H_v), dim3(256), 0,
+                           stream, static_cast<const uint16_t *>(q),
+                           static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v), g,
+                           beta, S0, S_final, cu_seqlens, T, H_qk, H_v, scale,
+                           static_cast<uint16_t *>(o));
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn

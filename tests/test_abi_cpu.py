@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every entry point include/gdn.h declares,
+and rejects bad arguments on the host before any device call (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_delta_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    L = gdn.lib()
+    decl = _declared()
+    assert decl == sorted(gdn.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+    assert gdn.gdn_abi_version() == 1
+
+
+def _prefill(L, **kw):
+    a = dict(io=1, q=1, k=2, v=3, g=4, beta=5, S0=None, Sf=None, cu=None, N=1, T=64, H_qk=16,
+             H_v=48, d_k=128, d_v=128, scale=1.0, o=0x100000, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.gdn_prefill(a["io"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["Sf"],
+                         a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"],
+                         a["scale"], a["o"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_k=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(d_v=256), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(io=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(H_v=47), gdn.GDN_ERR_INVALID_ARG),
+    (dict(H_qk=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=1), gdn.GDN_ERR_INVALID_ARG),                    # o overlaps q
+])
+def test_prefill_rejects_bad_arguments(kw, code):
+    L = gdn.lib()
+    assert _prefill(L, **kw) == code
+    assert L.gdn_last_error().decode()
+
+
+def test_prefill_workspace_checked():
+    L = gdn.lib()
+    need = gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, 4096, 16, 48)
+    if need == 0:
+        pytest.skip("bf16 prefill needs no workspace in this build")
+    big = 1 << 40
+    assert _prefill(L, T=4096, o=big, ws=None, ws_bytes=0) == gdn.GDN_ERR_WORKSPACE
+    assert _prefill(L, T=4096, o=big, ws=2 * big, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert "workspace" in L.gdn_last_error().decode()
+
+
+def test_final_state_partial_alias_rejected():
+    L = gdn.lib()
+    big = 1 << 40
+    ns = 48 * 128 * 128 * 4
+    ws = gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, 64, 16, 48)
+    rc = _prefill(L, o=big, S0=2 * big, Sf=2 * big + 4096, ws=3 * big, ws_bytes=ws)
+    assert rc == gdn.GDN_ERR_INVALID_ARG
+    assert ns > 4096
+
+
+def test_decode_rejects_bad_arguments():
+    L = gdn.lib()
+    args = [1, 2, 3, 4, 5, 0x100000000, 6, 4, 8, 16, 48, 128, 128, 1.0, 0x10000000000, None]
+    assert L.gdn_decode_step(*args[:11], 64, 128, 1.0, args[14], None) == gdn.GDN_ERR_UNSUPPORTED
+    assert L.gdn_decode_step(*args[:7], 9, 8, *args[9:]) == gdn.GDN_ERR_INVALID_ARG   # B > P
+    assert L.gdn_decode_step(*args[:7], 4, 0, *args[9:]) == gdn.GDN_ERR_INVALID_ARG   # P = 0
+    bad = list(args)
+    bad[6] = None
+    assert L.gdn_decode_step(*bad) == gdn.GDN_ERR_INVALID_ARG                      # slot_idx NULL
+    zero = list(args)
+    zero[7] = 0
+    assert L.gdn_decode_step(*zero) == gdn.GDN_OK                                  # B = 0: no-op
+
+
+def test_prelude_rejects_bad_arguments():
+    L = gdn.lib()
+    base = [1, 2, None, 1, 10, 16, 48, 128, 128, 1e-6, 0x100000000, 0x200000000, 0x300000000, None]
+    a = list(base); a[4] = 0
+    assert L.gdn_conv_prelude(*a) == gdn.GDN_OK                                     # T = 0: no-op
+    a = list(base); a[3] = 3
+    assert L.gdn_conv_prelude(*a) == gdn.GDN_ERR_INVALID_ARG                        # N != 1, no cu
+    a = list(base); a[9] = -1.0
+    assert L.gdn_conv_prelude(*a) == gdn.GDN_ERR_INVALID_ARG
+    a = list(base); a[7] = 96
+    assert L.gdn_conv_prelude(*a) == gdn.GDN_ERR_UNSUPPORTED
+    a = list(base); a[0] = None
+    assert L.gdn_conv_prelude(*a) == gdn.GDN_ERR_INVALID_ARG
