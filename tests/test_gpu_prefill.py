@@ -69,7 +69,9 @@ def test_bf16_varlen_mid_chunk_boundaries():
 
 def test_bf16_split_handoff():
     """A prefill split at token s with the final state handed over equals the
-    unsplit run (bitwise when s is a multiple of the chunk length)."""
+    unsplit run to the bf16 bar (the chunked kernels form the first chunk's
+    K S^T directly but later chunks through the chunk-to-chunk lookahead, so
+    even chunk-aligned splits round differently)."""
     p = synth.direct_prefill(4300, T=700, init_state=True)
     o, S = _prefill(p)
     for s in (512, 333):
@@ -80,11 +82,8 @@ def test_bf16_split_handoff():
                           g=p.g[s:], beta=p.beta[s:], q=p.q[s:], k=p.k[s:], v=p.v[s:],
                           S0=Sa.astype(np.float32))
         ob, Sb = _prefill(b)
-        if s % 64 == 0:
-            assert np.array_equal(np.concatenate([oa, ob]), o) and np.array_equal(Sb, S)
-        else:
-            assert_close(np.concatenate([oa, ob]), o, TOL_BF16, "o split")
-            assert_close(Sb, S, TOL_BF16, "S split")
+        assert_close(np.concatenate([oa, ob]), o, TOL_BF16, f"o split at {s}")
+        assert_close(Sb, S, TOL_BF16, f"S split at {s}")
 
 
 def test_bf16_deterministic_and_inplace_state():
