@@ -1,0 +1,254 @@
+"""Benchmark of the Gated DeltaNet layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the layer's prefill path over one batch of synthetic
+input: the conv/SiLU/L2 prelude on raw bf16 projections followed by the
+chunked prefill (plan, prep and scan kernels), for one sequence of 32768
+tokens with 16 QK heads, 48 V heads and d_k = d_v = 128.  `value` is prefill
+tokens/s over the K timed steps.  The decode side of the metric (one decode
+step for 256 sequences over a 256-slot state pool) is timed in the same run
+and reported under "decode".  Every input is generated and resident in HBM
+before the timed regions start; timing uses HIP events on the stream the
+kernels run on.  The fp64 oracle is timed on the host's cores over a bounded
+sample of the same workload and reported as "cpu_baseline".
+
+`--copy-calibration BYTES` runs a plain device copy of BYTES bytes instead: the
+reference run for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+T_PREFILL = 32768
+B_DECODE = 256
+H_QK, H_V, D = 16, 48, 128
+CHUNK = 64
+
+# Algorithmic work (no materialised per-chunk state counted):
+# prefill flops per token per V-head: three dense C x d x d products (K S^T,
+# Q S^T, the state update: 6 d^2) plus five C x C x d triangular products
+# counted at their useful half (K K^T, Q K^T, T applied to K and V, P U: 5 C d).
+PREFILL_FLOP_PER_TOKEN = H_V * (6 * D * D + 5 * CHUNK * D)
+# prelude bytes per token: raw projections in + q, k, v out (bf16)
+PRELUDE_BYTES_PER_TOKEN = 2 * 2 * (2 * H_QK * D + H_V * D)
+# decode bytes per sequence: each (sequence, V-head) state read and written
+# once in fp32, plus q, k, v, o in bf16 and g, beta in fp32
+DECODE_BYTES_PER_SEQ = (H_V * (2 * D * D * 4 + 2 * D * 2 + 2 * 4) + 2 * H_QK * D * 2)
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T32768.txt")
+CHUNKED_SRC = os.path.join(ROOT, "linear_attention_sequence_delta_amd", "csrc", "gdn_chunked.hip")
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_bytes():
+    """HBM bytes per prefill launch from the committed counter summary, or
+    None when it is missing or the kernels changed since it was taken."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+        if kv.get("source_sha256_16") != _sha(CHUNKED_SRC):
+            return None
+        return float(kv["hbm_bytes_per_prefill"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def run_gpu(steps, warmup):
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---------------- prefill workload (inputs resident before timing)
+    p = synth.workload_prefill_32k(T_PREFILL)
+    x, w = to_dev(p.x), to_dev(p.w)
+    g, beta = to_dev(p.g), to_dev(p.beta)
+    q = torch.empty((p.T, H_QK, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((1, H_V, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, p.T, H_QK, H_V),
+                     dtype=torch.uint8, device=dev)
+
+    def prelude():
+        gdn.gdn_conv_prelude(x, w, None, H_qk=H_QK, H_v=H_V, out=(q, k, v))
+
+    def prefill():
+        gdn.gdn_prefill(q, k, v, g, beta, None, None, final_state=fs, o=o, workspace=ws)
+
+    for _ in range(warmup):
+        prelude()
+        prefill()
+    torch.cuda.synchronize()
+    ev = [(_events(torch), _events(torch)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for (a0, a1), (b0, b1) in ev:
+        a0.record()
+        prelude()
+        a1.record()
+        b0.record()
+        prefill()
+        b1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_us = sum(a0.elapsed_time(a1) for (a0, a1), _ in ev) / steps * 1e3
+    pf_us = sum(b0.elapsed_time(b1) for _, (b0, b1) in ev) / steps * 1e3
+    step_ms = wall / steps * 1e3
+
+    # ---------------- decode workload: B = 256 over rotating 256-slot pools
+    d = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
+    pools = [to_dev(d.pool) for _ in range(2)]     # 768 MiB each, larger than the on-die cache
+    dq, dk, dv_, dg, db = (to_dev(a) for a in (d.q, d.k, d.v, d.g, d.beta))
+    slots = to_dev(d.slot_idx)
+    od = torch.empty((B_DECODE, H_V, D), dtype=torch.bfloat16, device=dev)
+    dsteps = max(steps * 4, 8)
+    for i in range(max(warmup, 2)):
+        gdn.gdn_decode_step(dq, dk, dv_, dg, db, pools[i % 2], slots, o=od)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for i in range(dsteps):
+        gdn.gdn_decode_step(dq, dk, dv_, dg, db, pools[i % 2], slots, o=od)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) / dsteps * 1e3
+
+    return dict(pre_us=pre_us, pf_us=pf_us, step_ms=step_ms, dec_us=dec_us)
+
+
+def cpu_baseline(T_sample=T_PREFILL):
+    """The fp64 oracle (prelude + token recurrence) on the first T_sample tokens
+    (by default all of them) of the same prefill workload, all 48 V-heads."""
+    import oracle
+    import synth
+    oracle._load()
+    p = synth.workload_prefill_32k(T_PREFILL)
+    x = p.x[:T_sample]
+    t0 = time.perf_counter()
+    qo, ko, vo = oracle.prelude(x, p.w, None, H_qk=H_QK, H_v=H_V, dk=D, dv=D)
+    oracle.recurrent(qo, ko, vo, p.g[:T_sample], p.beta[:T_sample])
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return {"value": T_sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 prelude + token-by-token recurrence over {T_sample} of the "
+                      f"{T_PREFILL} prefill tokens, all {H_V} V-heads ({dt:.1f} s; the prelude "
+                      f"loop is single-threaded, the recurrence uses OpenMP over heads)"}
+
+
+def copy_calibration(nbytes):
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "note": "each copy reads and writes copy_bytes"}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer shards by "
+              "sequence and head with no exchange, so the per-GPU figure is the one-GPU run.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    import linear_attention_sequence_delta_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_sequence_delta_amd import build as _b
+        _b.build()
+
+    r = run_gpu(args.steps, args.warmup)
+    T = T_PREFILL
+    step_us = r["pre_us"] + r["pf_us"]
+    flops = PREFILL_FLOP_PER_TOKEN * T
+    achieved_tflops = flops / (r["pf_us"] * 1e-6) / 1e12
+    traffic = _traffic_bytes()
+    pre_bytes = PRELUDE_BYTES_PER_TOKEN * T
+    dec_bytes = DECODE_BYTES_PER_SEQ * B_DECODE
+    out = {
+        "metric": "GDN layer tokens/s (prefill T=32K; decode B=256) + % of MFMA/HBM roofline",
+        "value": T / (step_us * 1e-6),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_us / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic, seeded: raw projections N(0,1) bf16, conv weights N(0,0.5) bf16, "
+                "gates from A_log, dt_bias ~ U(-1,1) and a, b ~ N(0,1)",
+        "config": {"workload": "prefill of one 32768-token sequence from raw bf16 projections "
+                               "(conv prelude + chunked prefill), 16 QK / 48 V heads, d=128, "
+                               "chunk 64, fp32 state",
+                   "T": T, "H_qk": H_QK, "H_v": H_V, "d_k": D, "d_v": D, "chunk": CHUNK},
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "gdn_prefill (plan + prep + scan kernels)",
+                     "algorithmic_flop_per_launch": flops},
+        "phases_us": {"prelude": r["pre_us"], "prefill": r["pf_us"],
+                      "wall_per_step": r["step_ms"] * 1e3},
+        "prelude_roofline": {"bound": "hbm", "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
+                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": pre_bytes / (r["pre_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+        "decode": {"value": B_DECODE / (r["dec_us"] * 1e-6), "unit": "tokens/s",
+                   "us_per_step": r["dec_us"],
+                   "workload": "one decode step of 256 sequences, 16 QK / 48 V heads, fp32 "
+                               "states in a 256-slot pool (pools rotated, 768 MiB each)",
+                   "roofline": {"bound": "hbm",
+                                "achieved": dec_bytes / (r["dec_us"] * 1e-6) / 1e9,
+                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
