@@ -104,7 +104,8 @@ size_t gdn_prefill_workspace_size(int io_dtype, int N, int T, int H_qk, int H_v,
  * gated by a_t = exp(g_t)), returning every o_t and each sequence's final state.
  *
  *   io_dtype       GDN_BF16: q, k, v, o are bf16; computed by the chunked (64-token)
- *                  kernels with bf16 matrix-core products and an fp32 state.
+ *                  kernels with bf16 matrix-core products and an fp32 state
+ *                  (at most 8 V-heads per QK head, else GDN_ERR_UNSUPPORTED).
  *                  GDN_F32:  q, k, v, o are fp32; computed token by token in fp32.
  *   q, k           device [T][H_qk][d_k];  v  device [T][H_v][d_v]
  *   g, beta        device fp32 [T][H_v]: log decay (<= 0) and write strength

@@ -135,6 +135,9 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
     if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (io_dtype == GDN_BF16 && H_v / H_qk > gdn::kMaxPrepGroup)
+        return fail(GDN_ERR_UNSUPPORTED, "bf16 prefill supports at most %d V-heads per QK head (got %d)",
+                    gdn::kMaxPrepGroup, H_v / H_qk);
     const size_t esz = io_dtype == GDN_F32 ? 4 : 2;
     const size_t nqk = (size_t)T * H_qk * gdn::kD * esz, nv = (size_t)T * H_v * gdn::kD * esz;
     const size_t ng = (size_t)T * H_v * 4, ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;

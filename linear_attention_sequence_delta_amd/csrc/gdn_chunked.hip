@@ -16,21 +16,21 @@
 //
 // Three kernels:
 //   plan  -- one workgroup: chunk offsets of every packed sequence.
-//   prep  -- fully parallel, one wave per (chunk, V-head): K K^T and Q K^T on
-//            bf16 MFMA, the gated A, its unit-lower-triangular inverse (fp32
+//   prep  -- fully parallel, one wave per (chunk, QK head): K K^T and Q K^T on
+//            bf16 MFMA (once, kept in registers); per V-head of the group the
+//            gated A, its unit-lower-triangular inverse (fp32
 //            substitution on the 16 x 16 diagonal blocks, bf16 MFMA for the
 //            off-diagonal blocks), T', P and G, written to the workspace
-//            (16.25 KiB per chunk and V-head), and K^T of the chunk plus
-//            K_next K^T (24 KiB per chunk and QK head).
+//            (16.25 KiB per chunk and V-head).
 //   scan  -- sequential over the chunks of one (sequence, V-head, 32-column slab
 //            of d_v).  Four state waves split the 64 chunk rows (X = K S^T, R, U)
-//            and the 128 d_k columns of the fp32 state (S' update), using a one
-//            chunk lookahead for X so that a chunk costs two barriers; four output
-//            waves on the same SIMDs form O from the LDS copies of S and U, off
-//            the recurrence's critical path.  The slab state never leaves the chip
+//            and the 128 d_k columns of the fp32 state (S' update, K^T built by
+//            an LDS transpose of the K rows they hold); four output waves on the
+//            same SIMDs form O from the LDS copies of S and U, off the
+//            recurrence's critical path.  The slab state never leaves the chip
 //            between chunks: fp32 in MFMA accumulators, plus a bf16 copy in LDS
-//            that feeds the next chunk's products.  Inputs are prefetched one
-//            chunk ahead into two alternating register sets.
+//            that feeds the next chunk's products.  Inputs are prefetched two
+//            chunks ahead into three rotating register sets.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -128,40 +128,40 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 // Workspace record of one (chunk, V-head): T' and P as bf16 64 x 64 row-major,
 // then the chunk's cumulative log decay G as 64 fp32.
 constexpr int kRecElems = 2 * kTileElems + 2 * kChunk;   // in bf16 units (16640 bytes)
-// Record of one (chunk, QK head): K^T as bf16 [128 d_k][64 chunk rows], then
-// M = K_next K^T as bf16 [64][64] (rows: the next chunk of the same sequence;
-// zero for a sequence's last chunk).  24 KiB.
-constexpr int kKtElems = kD * kChunk;
-constexpr int kQkRecElems = kKtElems + kTileElems;
 
-// One wave per (chunk, V-head).  The K and Q rows of the chunk are loaded
+// One wave per (chunk, QK head).  The K and Q rows of the chunk are loaded
 // straight into MFMA operand registers: the A operand of a 16-row block and
 // the B operand of K^T for the same block are the same fragment (row c of the
-// block, 8 consecutive d_k), so K K^T and Q K^T need no LDS staging.
+// block, 8 consecutive d_k), so K K^T and Q K^T need no LDS staging.  They are
+// formed once and kept in registers for all V-heads of the QK head.
 __global__ __launch_bounds__(64) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    uint16_t *__restrict__ ws, uint16_t *__restrict__ ws_kt) {
+    uint16_t *__restrict__ ws) {
     __shared__ __attribute__((aligned(16))) float sA[kChunk * kAP];
     __shared__ __attribute__((aligned(16))) uint16_t sO[kChunk * kRP];
     __shared__ float sG[kChunk];
     __shared__ float sBt[kChunk];
 
-    const int gc = blockIdx.x, h = blockIdx.y;
+    const int gc = blockIdx.x, hq = blockIdx.y;
     if (gc >= chunk_base[N]) return;
-    const int hq = h / (H_v / H_qk);
+    const int group = H_v / H_qk;
     const int n = seq_of_chunk(chunk_base, N, gc);
     const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
     const int c0 = s0 + kChunk * (gc - chunk_base[n]);
     const int L = min(kChunk, s1 - c0);
     const int lane = threadIdx.x, g4 = lane >> 4, c = lane & 15;
 
-    // gates of the chunk (zero past the end)
-    const size_t grow = (size_t)(c0 + min(lane, L - 1)) * H_v + h;
-    const float graw = g[grow], braw = beta[grow];
-    const float gl = lane < L ? graw : 0.f;
-    const float bl = lane < L ? braw : 0.f;
+    // gates of every V-head of the group (zero past the end), loaded up front
+    constexpr int kMaxGroup = kMaxPrepGroup;
+    float graw[kMaxGroup], braw[kMaxGroup];
+    const size_t grow = (size_t)(c0 + min(lane, L - 1)) * H_v + (size_t)hq * group;
+#pragma unroll
+    for (int vv = 0; vv < kMaxGroup; ++vv) {
+        graw[vv] = vv < group ? g[grow + vv] : 0.f;
+        braw[vv] = vv < group ? beta[grow + vv] : 0.f;
+    }
 
     // K and Q fragments: block I, k-step s -> row 16 I + c, d_k 32 s + 8 g4 .. +7
     uint4 kf[4][4], qf[4][4];
@@ -176,9 +176,6 @@ __global__ __launch_bounds__(64) void prep_kernel(
             qf[I][s] = *reinterpret_cast<const uint4 *>(qc + off + 32 * s);
         }
     }
-    const float G = wave_scan(gl);
-    sG[lane] = G;
-    sBt[lane] = bl;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const bool ok = 16 * I + c < L;
@@ -188,201 +185,165 @@ __global__ __launch_bounds__(64) void prep_kernel(
             if (!ok) qf[I][s] = make_uint4(0, 0, 0, 0);
         }
     }
-    wave_lds_sync();
 
-    // Per QK head (written by its first V-head): K^T of the chunk and
-    // M = K_next K^T, both staged through sO for coalesced stores.
-    if (h % (H_v / H_qk) == 0) {
-        uint16_t *kt = ws_kt + ((size_t)gc * H_qk + hq) * kQkRecElems;
+    // K K^T and Q K^T, lower 16 x 16 tiles (J <= I), kept in registers
+    f32x4 kk[4][4], qk[4][4];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            // lane (g4, c) holds K[16 I + c][32 s + 8 g4 + i]; keep d_k in [64 half, 64 half + 64)
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        sO[(32 * s2 + 8 * g4 + i) * kRP + 16 * I + c] = elem(kf[I][2 * half + s2], i);
-            wave_lds_sync();
-#pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
-                const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
-                *reinterpret_cast<uint4 *>(kt + (64 * half + row) * kChunk + col0) =
-                    *reinterpret_cast<const uint4 *>(sO + row * kRP + col0);
-            }
-            wave_lds_sync();
-        }
-        // next chunk of the same sequence, if any
-        const bool has_next = gc + 1 < chunk_base[n + 1];
-        const int Ln = has_next ? min(kChunk, s1 - (c0 + kChunk)) : 0;
-        const uint16_t *kn = k + (size_t)(c0 + kChunk) * H_qk * kD;
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            uint4 nf[4];
-            const bool ok = 16 * I + c < Ln;
-            const int off = (min(16 * I + c, max(Ln - 1, 0)) * H_qk + hq) * kD + 8 * g4;
+        for (int J = 0; J <= I; ++J) {
+            kk[I][J] = f32x4{0.f, 0.f, 0.f, 0.f};
+            qk[I][J] = kk[I][J];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                nf[s] = make_uint4(0, 0, 0, 0);
-                if (has_next) nf[s] = *reinterpret_cast<const uint4 *>(kn + off + 32 * s);
-                if (!ok) nf[s] = make_uint4(0, 0, 0, 0);
+                kk[I][J] = mfma32(kf[I][s], kf[J][s], kk[I][J]);
+                qk[I][J] = mfma32(qf[I][s], kf[J][s], qk[I][J]);
+            }
+        }
+
+#pragma unroll
+    for (int vv = 0; vv < kMaxGroup; ++vv) {
+        if (vv >= group) break;
+        const int h = hq * group + vv;
+        const float gl = lane < L ? graw[vv] : 0.f;
+        const float bl = lane < L ? braw[vv] : 0.f;
+        const float G = wave_scan(gl);
+        sG[lane] = G;
+        sBt[lane] = bl;
+        wave_lds_sync();
+
+        // gated K K^T -> A (fp32, lower tiles), gated Q K^T -> P (bf16, all tiles)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            float Gr[4], br[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Gr[j] = sG[16 * I + 4 * g4 + j];
+                br[j] = sBt[16 * I + 4 * g4 + j];
             }
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                f32x4 m = {0.f, 0.f, 0.f, 0.f};
+                const int col = 16 * J + c;
+                if (J > I) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) m = mfma32(nf[s], kf[J][s], m);
+                    for (int j = 0; j < 4; ++j) sO[(16 * I + 4 * g4 + j) * kRP + col] = 0;
+                    continue;
+                }
+                const float Gi = sG[col];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sO[(16 * I + 4 * g4 + j) * kRP + 16 * J + c] = f2bf(m[j]);
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 16 * I + 4 * g4 + j;
+                    const float e = __expf(Gr[j] - Gi);
+                    sA[row * kAP + col] = col < row ? br[j] * e * kk[I][J][j] : 0.f;
+                    sO[row * kRP + col] = f2bf(col <= row ? scale * e * qk[I][J][j] : 0.f);
+                }
             }
         }
         wave_lds_sync();
+
+        uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
+        // P rows out (coalesced 16-byte stores) and G
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
             const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
-            *reinterpret_cast<uint4 *>(kt + kKtElems + row * kChunk + col0) =
+            *reinterpret_cast<uint4 *>(rec + kTileElems + row * kChunk + col0) =
                 *reinterpret_cast<const uint4 *>(sO + row * kRP + col0);
         }
-        wave_lds_sync();
-    }
+        reinterpret_cast<float *>(rec + 2 * kTileElems)[lane] = G;
 
-    // Gated K K^T -> A (fp32, lower tiles) and gated Q K^T -> P (bf16, all tiles)
+        float *A = sA;
+        // Diagonal 16 x 16 blocks: lane (b, c) solves column c of block b by
+        // forward substitution, T_bb = (I + A_bb)^{-1}, in fp32.
+        {
+            const int b = g4;
+            float tc[16];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        float Gr[4], br[4];
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == c) ? 1.f : 0.f;
+                const float *Ar = A + (16 * b + r) * kAP + 16 * b;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            Gr[j] = sG[16 * I + 4 * g4 + j];
-            br[j] = sBt[16 * I + 4 * g4 + j];
+                for (int i = 0; i < r; ++i) acc -= Ar[i] * tc[i];
+                tc[r] = acc;
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) A[(16 * b + r) * kAP + 16 * b + c] = tc[r];
         }
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            const int col = 16 * J + c;
-            if (J > I) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sO[(16 * I + 4 * g4 + j) * kRP + col] = 0;
-                continue;
-            }
-            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                kk = mfma32(kf[I][s], kf[J][s], kk);
-                qk = mfma32(qf[I][s], kf[J][s], qk);
-            }
-            const float Gi = sG[col];
+        wave_lds_sync();
+
+        // 16 x 16 x 16 MFMA operands from the fp32 block matrix: rows of block
+        // (I, J) as an A operand, columns of block (I, J) as a B operand.
+        auto rowop = [&](int I, int J) {
+            const float *p = A + (16 * I + c) * kAP + 16 * J + 4 * g4;
+            return to_bf4(p[0], p[1], p[2], p[3]);
+        };
+        auto colop = [&](int I, int J) {
+            const float *p = A + (16 * I + 4 * g4) * kAP + 16 * J + c;
+            return to_bf4(p[0], p[kAP], p[2 * kAP], p[3 * kAP]);
+        };
+        auto accop = [](f32x4 x) { return to_bf4(x[0], x[1], x[2], x[3]); };
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+        // Off-diagonal blocks of A are read before any is overwritten by T.
+        const s16x4 a10 = rowop(1, 0), a21 = rowop(2, 1), a32 = rowop(3, 2);
+        const s16x4 a20 = rowop(2, 0), a30 = rowop(3, 0), a31 = rowop(3, 1);
+
+        // Blocks one below the diagonal: T_{I,I-1} = -T_II A_{I,I-1} T_{I-1,I-1}
+        {
+            const f32x4 y1 = mfma16(a10, colop(0, 0), z4);
+            const f32x4 y2 = mfma16(a21, colop(1, 1), z4);
+            const f32x4 y3 = mfma16(a32, colop(2, 2), z4);
+            const f32x4 t10 = -mfma16(rowop(1, 1), accop(y1), z4);
+            const f32x4 t21 = -mfma16(rowop(2, 2), accop(y2), z4);
+            const f32x4 t32 = -mfma16(rowop(3, 3), accop(y3), z4);
+            wave_lds_sync();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = 16 * I + 4 * g4 + j;
-                const float e = __expf(Gr[j] - Gi);
-                sA[row * kAP + col] = col < row ? br[j] * e * kk[j] : 0.f;
-                sO[row * kRP + col] = f2bf(col <= row ? scale * e * qk[j] : 0.f);
+                A[(16 + 4 * g4 + j) * kAP + c] = t10[j];
+                A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21[j];
+                A[(48 + 4 * g4 + j) * kAP + 32 + c] = t32[j];
             }
         }
-    }
-    wave_lds_sync();
+        wave_lds_sync();
 
-    uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
-    // P rows out (coalesced 16-byte stores) and G
+        // Lower-left 32 x 32 block: T_[23][01] = -T_[23] A_[23][01] T_[01]
+        {
+            const f32x4 x20 = mfma16(a21, colop(1, 0), mfma16(a20, colop(0, 0), z4));
+            const f32x4 x21 = mfma16(a21, colop(1, 1), z4);
+            const f32x4 x30 = mfma16(a31, colop(1, 0), mfma16(a30, colop(0, 0), z4));
+            const f32x4 x31 = mfma16(a31, colop(1, 1), z4);
+            const s16x4 t22 = rowop(2, 2), t32r = rowop(3, 2), t33 = rowop(3, 3);
+            const f32x4 t20 = -mfma16(t22, accop(x20), z4);
+            const f32x4 t21b = -mfma16(t22, accop(x21), z4);
+            const f32x4 t30 = -mfma16(t33, accop(x30), mfma16(t32r, accop(x20), z4));
+            const f32x4 t31 = -mfma16(t33, accop(x31), mfma16(t32r, accop(x21), z4));
+            wave_lds_sync();
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-        const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
-        *reinterpret_cast<uint4 *>(rec + kTileElems + row * kChunk + col0) =
-            *reinterpret_cast<const uint4 *>(sO + row * kRP + col0);
-    }
-    reinterpret_cast<float *>(rec + 2 * kTileElems)[lane] = G;
-
-    float *A = sA;
-    // Diagonal 16 x 16 blocks: lane (b, c) solves column c of block b by
-    // forward substitution, T_bb = (I + A_bb)^{-1}, in fp32.
-    {
-        const int b = g4;
-        float tc[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == c) ? 1.f : 0.f;
-            const float *Ar = A + (16 * b + r) * kAP + 16 * b;
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= Ar[i] * tc[i];
-            tc[r] = acc;
+            for (int j = 0; j < 4; ++j) {
+                A[(32 + 4 * g4 + j) * kAP + c] = t20[j];
+                A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21b[j];
+                A[(48 + 4 * g4 + j) * kAP + c] = t30[j];
+                A[(48 + 4 * g4 + j) * kAP + 16 + c] = t31[j];
+            }
         }
         wave_lds_sync();
+
+        // T' = T diag(b) (upper blocks zero), bf16 rows, coalesced 16-byte stores
 #pragma unroll
-        for (int r = 0; r < 16; ++r) A[(16 * b + r) * kAP + 16 * b + c] = tc[r];
-    }
-    wave_lds_sync();
-
-    // 16 x 16 x 16 MFMA operands from the fp32 block matrix: rows of block
-    // (I, J) as an A operand, columns of block (I, J) as a B operand.
-    auto rowop = [&](int I, int J) {
-        const float *p = A + (16 * I + c) * kAP + 16 * J + 4 * g4;
-        return to_bf4(p[0], p[1], p[2], p[3]);
-    };
-    auto colop = [&](int I, int J) {
-        const float *p = A + (16 * I + 4 * g4) * kAP + 16 * J + c;
-        return to_bf4(p[0], p[kAP], p[2 * kAP], p[3 * kAP]);
-    };
-    auto accop = [](f32x4 x) { return to_bf4(x[0], x[1], x[2], x[3]); };
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-
-    // Off-diagonal blocks of A are read before any is overwritten by T.
-    const s16x4 a10 = rowop(1, 0), a21 = rowop(2, 1), a32 = rowop(3, 2);
-    const s16x4 a20 = rowop(2, 0), a30 = rowop(3, 0), a31 = rowop(3, 1);
-
-    // Blocks one below the diagonal: T_{I,I-1} = -T_II A_{I,I-1} T_{I-1,I-1}
-    {
-        const f32x4 y1 = mfma16(a10, colop(0, 0), z4);
-        const f32x4 y2 = mfma16(a21, colop(1, 1), z4);
-        const f32x4 y3 = mfma16(a32, colop(2, 2), z4);
-        const f32x4 t10 = -mfma16(rowop(1, 1), accop(y1), z4);
-        const f32x4 t21 = -mfma16(rowop(2, 2), accop(y2), z4);
-        const f32x4 t32 = -mfma16(rowop(3, 3), accop(y3), z4);
+        for (int qq = 0; qq < 8; ++qq) {
+            const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
+            float tv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = col0 + e;
+                tv[e] = (col >> 4) <= (row >> 4) ? A[row * kAP + col] * sBt[col] : 0.f;
+            }
+            uint4 ot;
+            ot.x = pack_bf2(tv[0], tv[1]); ot.y = pack_bf2(tv[2], tv[3]);
+            ot.z = pack_bf2(tv[4], tv[5]); ot.w = pack_bf2(tv[6], tv[7]);
+            *reinterpret_cast<uint4 *>(rec + row * kChunk + col0) = ot;
+        }
         wave_lds_sync();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            A[(16 + 4 * g4 + j) * kAP + c] = t10[j];
-            A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21[j];
-            A[(48 + 4 * g4 + j) * kAP + 32 + c] = t32[j];
-        }
-    }
-    wave_lds_sync();
-
-    // Lower-left 32 x 32 block: T_[23][01] = -T_[23] A_[23][01] T_[01]
-    {
-        const f32x4 x20 = mfma16(a21, colop(1, 0), mfma16(a20, colop(0, 0), z4));
-        const f32x4 x21 = mfma16(a21, colop(1, 1), z4);
-        const f32x4 x30 = mfma16(a31, colop(1, 0), mfma16(a30, colop(0, 0), z4));
-        const f32x4 x31 = mfma16(a31, colop(1, 1), z4);
-        const s16x4 t22 = rowop(2, 2), t32r = rowop(3, 2), t33 = rowop(3, 3);
-        const f32x4 t20 = -mfma16(t22, accop(x20), z4);
-        const f32x4 t21b = -mfma16(t22, accop(x21), z4);
-        const f32x4 t30 = -mfma16(t33, accop(x30), mfma16(t32r, accop(x20), z4));
-        const f32x4 t31 = -mfma16(t33, accop(x31), mfma16(t32r, accop(x21), z4));
-        wave_lds_sync();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            A[(32 + 4 * g4 + j) * kAP + c] = t20[j];
-            A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21b[j];
-            A[(48 + 4 * g4 + j) * kAP + c] = t30[j];
-            A[(48 + 4 * g4 + j) * kAP + 16 + c] = t31[j];
-        }
-    }
-    wave_lds_sync();
-
-    // T' = T diag(b) (upper blocks zero), bf16 rows, coalesced 16-byte stores
-#pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-        const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
-        float tv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = col0 + e;
-            tv[e] = (col >> 4) <= (row >> 4) ? A[row * kAP + col] * sBt[col] : 0.f;
-        }
-        uint4 ot;
-        ot.x = pack_bf2(tv[0], tv[1]); ot.y = pack_bf2(tv[2], tv[3]);
-        ot.z = pack_bf2(tv[4], tv[5]); ot.w = pack_bf2(tv[6], tv[7]);
-        *reinterpret_cast<uint4 *>(rec + row * kChunk + col0) = ot;
     }
 }
 
@@ -391,24 +352,22 @@ constexpr int kSlabW = 32;                 // d_v columns per scan workgroup
 constexpr int kSlabsW = kD / kSlabW;       // 4
 constexpr int kVP = kSlabW + 8;            // LDS row stride (bf16) of the v staging rows
 
-// Per-lane inputs.  Every load reads a valid address (rows past the end of a
-// sequence are clamped to its last row, chunk indices past the last chunk to
-// the last chunk), so no load sits behind a branch; rows past the end only
-// ever meet zero columns of T' and P, and results of the clamped chunks past
-// the end are never used.
-struct StateRegs {        // waves 0-3, used during chunk c (loaded during c - 1)
-    uint4 kA[4];          // K_{c+1} row 16 w + c, d_k 32 s + 8 g4 .. +7
-    uint4 tA[2];          // T'_c row 16 w + c, columns 32 s + 8 g4 .. +7
-    uint4 mA[2];          // M_c = K_{c+1} K_c^T row 16 w + c, columns 32 s + 8 g4 .. +7
-    uint4 ktA[2][2];      // K_c^T row 32 w + 16 t + c, chunk rows 32 s + 8 g4 .. +7
-    uint4 vrow;           // v_{c+1} row 16 w + lane/4, slab columns 8 (lane%4) .. +7
-    float4 G4;            // G_{c+1} of rows 16 w + 4 g4 + j
-    float GL;             // G_{c+1} of the last row
+// Per-lane inputs of one chunk.  Every load reads a valid address (rows past
+// the end of a sequence are clamped to its last row, chunk indices past the
+// last chunk to the last chunk), so no load sits behind a branch; rows past
+// the end only ever meet zero columns of T' and P, and results of the clamped
+// chunks past the end are never used.
+struct StateRegs {        // waves 0-3
+    uint4 kA[4];          // K row 16 w + c, d_k 32 s + 8 g4 .. +7
+    uint4 tA[2];          // T' row 16 w + c, columns 32 s + 8 g4 .. +7
+    uint4 vrow;           // v row 16 w + lane/4, slab columns 8 (lane%4) .. +7
+    float4 G4;            // G of rows 16 w + 4 g4 + j
+    float GL;             // G of the chunk's last row
 };
-struct OutRegs {          // waves 4-7, used during chunk c
-    uint4 qA[4];          // Q_c row 16 w + c, d_k 32 s + 8 g4 .. +7
-    uint4 pA[2];          // P_c row 16 w + c, columns 32 s + 8 g4 .. +7
-    float Gown;           // G_c of row 16 w + c
+struct OutRegs {          // waves 4-7
+    uint4 qA[4];          // Q row 16 w + c, d_k 32 s + 8 g4 .. +7
+    uint4 pA[2];          // P row 16 w + c, columns 32 s + 8 g4 .. +7
+    float Gown;           // G of row 16 w + c
 };
 
 __device__ __forceinline__ uint32_t pk2(float a, float b) {
@@ -420,24 +379,22 @@ __device__ __forceinline__ uint2 pk4(float a, float b, float c, float d) {
     return make_uint2(pk2(a, b), pk2(c, d));
 }
 
-// 512 threads: waves 0-3 carry the state through the chunks, waves 4-7
-// produce the outputs from the LDS copies of S and U; waves w and w + 4 share a
-// SIMD.  Wave w (mod 4) owns chunk rows 16 w .. +15 and d_k columns 32 w .. +31
-// of the state.  With the chunk-to-chunk lookahead
-//   X_{c+1} = K_{c+1} S_{c+1}^T = gamma_L Y_c + M_c Ut_c,   Y_c = K_{c+1} S_c^T,
-// (Ut_c = diag(exp(G_L - G)) U_c, M_c = K_{c+1} K_c^T) each chunk needs two
-// workgroup barriers: (1) after R_c, (2) after U_c.  Y_c and S Q^T are formed
-// between them; X_{c+1} and S_{c+1} after (2).
+// 512 threads: waves 0-3 carry the state through the chunks (X = K S^T, R,
+// U = T' R, S' update), waves 4-7 produce the outputs (S Q^T, U^T P^T) from the
+// LDS copies of S and U; waves w and w + 4 share a SIMD.  Wave w (mod 4) owns
+// chunk rows 16 w .. +15 and d_k columns 32 w .. +31 of the state.  Three
+// workgroup barriers per chunk: (1) R complete, (2) U complete, (3) S' complete.
+// Inputs are loaded two chunks ahead into three rotating register sets.
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    const uint16_t *__restrict__ ws, const uint16_t *__restrict__ ws_kt,
-    uint16_t *__restrict__ o) {
+    const uint16_t *__restrict__ ws, uint16_t *__restrict__ o) {
     __shared__ __attribute__((aligned(16))) uint16_t sS[kSlabW * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sU[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sUs[kSlabW * kRP];
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[kD * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * kVP];
 
     // Workgroup -> (sequence, V-head, slab).  Workgroups are handed to the 8
@@ -458,7 +415,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const int e0 = kSlabW * slab;           // first d_v column of the slab
     const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
     auto rec_of = [&](int ci) { return ws + ((size_t)(cbase + ci) * H_v + h) * kRecElems; };
-    auto qkrec_of = [&](int ci) { return ws_kt + ((size_t)(cbase + ci) * H_qk + hq) * kQkRecElems; };
     auto chunk_len = [&](int ci) { return min(kChunk, s1 - (s0 + kChunk * ci)); };
     auto krow_off = [&](int ci) {   // offset of K/Q row 16 w + c (clamped) of chunk ci
         return (size_t)(s0 + kChunk * ci) * H_qk * kD +
@@ -489,11 +445,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     *reinterpret_cast<uint2 *>(sS + (16 * nt + c) * kKP + 32 * w + 16 * t + 4 * g4) =
                         pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
         };
-        // loads of the set used during chunk ci, in three groups
-        auto fetch1 = [&](int ci, StateRegs &R) {
+        auto fetch_a = [&](int ci, StateRegs &R) {
             ci = min(ci, nchunks - 1);
-            const int cn = min(ci + 1, nchunks - 1);
-            const uint16_t *kp = k + krow_off(cn);
+            const uint16_t *kp = k + krow_off(ci);
 #pragma unroll
             for (int s = 0; s < 4; ++s) R.kA[s] = *reinterpret_cast<const uint4 *>(kp + 32 * s);
             const uint16_t *rec = rec_of(ci);
@@ -501,59 +455,53 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int s = 0; s < 2; ++s)
                 R.tA[s] = *reinterpret_cast<const uint4 *>(rec + (16 * w + c) * kChunk + 32 * s + 8 * g4);
         };
-        auto fetch2 = [&](int ci, StateRegs &R) {
+        auto fetch_b = [&](int ci, StateRegs &R) {
             ci = min(ci, nchunks - 1);
-            const uint16_t *kt = qkrec_of(ci);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    R.ktA[t][s] = *reinterpret_cast<const uint4 *>(kt + (32 * w + 16 * t + c) * kChunk + 32 * s + 8 * g4);
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                R.mA[s] = *reinterpret_cast<const uint4 *>(kt + kKtElems + (16 * w + c) * kChunk + 32 * s + 8 * g4);
-        };
-        auto fetch3 = [&](int ci, StateRegs &R) {
-            const int cn = min(ci + 1, nchunks - 1);
-            const float *Gp = reinterpret_cast<const float *>(rec_of(cn) + 2 * kTileElems);
+            const float *Gp = reinterpret_cast<const float *>(rec_of(ci) + 2 * kTileElems);
             R.G4 = *reinterpret_cast<const float4 *>(Gp + 16 * w + 4 * g4);
             R.GL = Gp[kChunk - 1];
-            const int vr = min(16 * w + (lane >> 2), chunk_len(cn) - 1);
-            R.vrow = *reinterpret_cast<const uint4 *>(v + ((size_t)(s0 + kChunk * cn + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
-        };
-
-        // chunk-local values carried into the loop for chunk c
-        f32x4 ax[2];           // X_c, rows 16 w + 4 g4 + j
-        float vr[2][4];        // v_c in the same layout
-        float gam[4], dec[4], gamL;
-        auto stage_v = [&](uint4 vrow) {
-            *reinterpret_cast<uint4 *>(sV + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = vrow;
-            wave_lds_sync();
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) vr[nt][j] = bf2f(sV[(16 * w + 4 * g4 + j) * kVP + 16 * nt + c]);
-        };
-        auto set_gates = [&](float4 G4, float GL) {
-            const float Gr4[4] = {G4.x, G4.y, G4.z, G4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                gam[j] = __expf(Gr4[j]);
-                dec[j] = __expf(GL - Gr4[j]);
-            }
-            gamL = __expf(GL);
+            const int vr = min(16 * w + (lane >> 2), chunk_len(ci) - 1);
+            R.vrow = *reinterpret_cast<const uint4 *>(v + ((size_t)(s0 + kChunk * ci + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
         };
 
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
-            // R_c = V_c - diag(gamma) X_c, stored transposed ([d_v column][chunk row])
+            // this wave's 16 rows of v, regrouped through LDS into C-layout columns
+            *reinterpret_cast<uint4 *>(sV + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
+            // K^T for this chunk's state update (row = d_k, column = chunk row)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                *reinterpret_cast<uint2 *>(sR + (16 * nt + c) * kRP + 16 * w + 4 * g4) =
-                    pk4(vr[nt][0] - gam[0] * ax[nt][0], vr[nt][1] - gam[1] * ax[nt][1],
-                        vr[nt][2] - gam[2] * ax[nt][2], vr[nt][3] - gam[3] * ax[nt][3]);
-            fetch1(ci + 1, pf);
-            __syncthreads();                                   // (1) R_c and S_c complete
-            // U_c = T'_c R_c (lower triangular: k-steps up to this row block)
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    sKt[(32 * s + 8 * g4 + i) * kRP + 16 * w + c] = elem(cur.kA[s], i);
+            fetch_a(ci + 2, pf);
+            float gam[4], dec[4];
+            const float Gr4[4] = {cur.G4.x, cur.G4.y, cur.G4.z, cur.G4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                gam[j] = __expf(Gr4[j]);
+                dec[j] = __expf(cur.GL - Gr4[j]);
+            }
+            const float gamL = __expf(cur.GL);
+
+            // X = K S^T for chunk rows 16 w .. +15, both d_v tiles
+            f32x4 ax[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    ax[nt] = mfma32(cur.kA[s], *reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), ax[nt]);
+            // R = V - diag(gamma) X, stored transposed ([d_v column][chunk row])
+            wave_lds_sync();
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float r[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    r[j] = bf2f(sV[(16 * w + 4 * g4 + j) * kVP + 16 * nt + c]) - gam[j] * ax[nt][j];
+                *reinterpret_cast<uint2 *>(sR + (16 * nt + c) * kRP + 16 * w + 4 * g4) = pk4(r[0], r[1], r[2], r[3]);
+            }
+            __syncthreads();                                   // (1) R complete
+            // U = T' R (T' is lower triangular: k-steps up to this row block)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 f32x4 au = mfma32(cur.tA[0], *reinterpret_cast<const uint4 *>(sR + (16 * nt + c) * kRP + 8 * g4),
@@ -564,78 +512,47 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 *reinterpret_cast<uint2 *>(sUs + (16 * nt + c) * kRP + 16 * w + 4 * g4) =
                     pk4(dec[0] * au[0], dec[1] * au[1], dec[2] * au[2], dec[3] * au[3]);
             }
-            // Y_c = K_{c+1} S_c^T
-            f32x4 ay[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            fetch_b(ci + 2, pf);
+            __syncthreads();                                   // (2) U complete
+            // S' = gamma_L S + (diag(exp(G_L - G)) U)^T K   (d_k 32 w .. +31)
+            uint4 ub[2][2], ka[2][2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    ay[nt] = mfma32(cur.kA[s], *reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), ay[nt]);
-            fetch2(ci + 1, pf);
-            __syncthreads();                                   // (2) U_c complete, S_c reads done
-            uint4 ub[2][2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < 2; ++s) {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     ub[nt][s] = *reinterpret_cast<const uint4 *>(sUs + (16 * nt + c) * kRP + 32 * s + 8 * g4);
-            // X_{c+1} = gamma_L Y_c + M_c Ut_c
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x4 a = gamL * ay[nt];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) a = mfma32(cur.mA[s], ub[nt][s], a);
-                ax[nt] = a;
+                for (int t = 0; t < 2; ++t)
+                    ka[t][s] = *reinterpret_cast<const uint4 *>(sKt + (32 * w + 16 * t + c) * kRP + 32 * s + 8 * g4);
             }
-            // S_{c+1} = gamma_L S_c + K_c^T Ut_c   (d_k 32 w .. +31)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     f32x4 as = gamL * st[t][nt];
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) as = mfma32(cur.ktA[t][s], ub[nt][s], as);
+                    for (int s = 0; s < 2; ++s) as = mfma32(ka[t][s], ub[nt][s], as);
                     st[t][nt] = as;
                 }
             write_state_lds();
-            fetch3(ci + 1, pf);
-            // chunk c+1: its v rows and gates (loaded during chunk c - 1)
-            stage_v(cur.vrow);
-            set_gates(cur.G4, cur.GL);
+            __syncthreads();                                   // (3) S' complete
         };
 
         write_state_lds();
-        StateRegs r0, r1;
+        StateRegs r0, r1, r2;
         if (nchunks > 0) {
-            // chunk 0: X_0 = K_0 S_0^T, v_0 and G_0 directly; then the set of chunk 0
-            uint4 k0[4];
-            const uint16_t *kp = k + krow_off(0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) k0[s] = *reinterpret_cast<const uint4 *>(kp + 32 * s);
-            const float *Gp = reinterpret_cast<const float *>(rec_of(0) + 2 * kTileElems);
-            const float4 G4 = *reinterpret_cast<const float4 *>(Gp + 16 * w + 4 * g4);
-            const float GL = Gp[kChunk - 1];
-            const int vr0 = min(16 * w + (lane >> 2), chunk_len(0) - 1);
-            const uint4 v0 = *reinterpret_cast<const uint4 *>(v + ((size_t)(s0 + vr0) * H_v + h) * kD + e0 + 8 * (lane & 3));
-            fetch1(0, r0);
-            fetch2(0, r0);
-            fetch3(0, r0);
-            __syncthreads();                                   // S_0 complete
-            ax[0] = ax[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    ax[nt] = mfma32(k0[s], *reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), ax[nt]);
-            stage_v(v0);
-            set_gates(G4, GL);
-        } else {
-            __syncthreads();
+            fetch_a(0, r0);
+            fetch_b(0, r0);
+            fetch_a(1, r1);
+            fetch_b(1, r1);
         }
-        for (int ci = 0; ci < nchunks; ci += 2) {
-            body(ci, r0, r1);
+        __syncthreads();
+        for (int ci = 0; ci < nchunks; ci += 3) {
+            body(ci, r0, r2);
             if (ci + 1 >= nchunks) break;
             body(ci + 1, r1, r0);
+            if (ci + 2 >= nchunks) break;
+            body(ci + 2, r2, r1);
         }
         if (final_state) {
 #pragma unroll
@@ -661,9 +578,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
         auto body = [&](int ci, OutRegs &cur, OutRegs &pf) {
             const int c0 = s0 + kChunk * ci;
             const int L = min(kChunk, s1 - c0);
-            fetch(ci + 1, pf);
-            __syncthreads();                                   // (1) S_c complete
-            // O^T = S_c Q_c^T (the S fragments are the A operand); lane holds
+            fetch(ci + 2, pf);
+            // O^T = S Q^T (the S fragments are the A operand); lane holds
             // O[16 w + c][16 nt + 4 g4 + j]
             f32x4 ao[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -672,8 +588,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 for (int nt = 0; nt < 2; ++nt)
                     ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), cur.qA[s], ao[nt]);
             const float gq = scale * __expf(cur.Gown);
-            __syncthreads();                                   // (2) U_c complete
-            // O^T += U_c^T P_c^T  (P is lower triangular: k-steps up to this row block)
+            __syncthreads();                                   // (1)
+            __syncthreads();                                   // (2) U complete
+            // O^T += U^T P^T  (P is lower triangular: k-steps up to this row block)
             const bool row_ok = 16 * w + c < L;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
@@ -685,14 +602,20 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     *reinterpret_cast<uint2 *>(o + ((size_t)(c0 + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
                         pk4(a[0], a[1], a[2], a[3]);
             }
+            __syncthreads();                                   // (3)
         };
-        OutRegs r0, r1;
-        if (nchunks > 0) fetch(0, r0);
+        OutRegs r0, r1, r2;
+        if (nchunks > 0) {
+            fetch(0, r0);
+            fetch(1, r1);
+        }
         __syncthreads();                                       // matches the state waves' first barrier
-        for (int ci = 0; ci < nchunks; ci += 2) {
-            body(ci, r0, r1);
+        for (int ci = 0; ci < nchunks; ci += 3) {
+            body(ci, r0, r2);
             if (ci + 1 >= nchunks) break;
             body(ci + 1, r1, r0);
+            if (ci + 2 >= nchunks) break;
+            body(ci + 2, r2, r1);
         }
     }
 }
@@ -702,10 +625,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v) {
+    (void)H_qk;
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
     return align256((size_t)(N + 1) * sizeof(int32_t)) +
-           max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t) +
-           max_chunks * (size_t)H_qk * kQkRecElems * sizeof(uint16_t);
+           max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);
 }
 
 hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -716,19 +639,18 @@ hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, c
     int32_t *chunk_base = static_cast<int32_t *>(workspace);
     uint16_t *ws = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
                                                 align256((size_t)(N + 1) * sizeof(int32_t)));
-    uint16_t *ws_kt = ws + max_chunks * (size_t)H_v * kRecElems;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, chunk_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)max_chunks, H_v), dim3(64), 0, stream,
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)max_chunks, H_qk), dim3(64), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta,
-                       cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, ws, ws_kt);
+                       cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(scan_kernel, dim3(N * H_v * kSlabsW), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), S0, S_final, cu_seqlens, chunk_base, N, T,
-                       H_qk, H_v, scale, ws, ws_kt, static_cast<uint16_t *>(o));
+                       H_qk, H_v, scale, ws, static_cast<uint16_t *>(o));
     return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace gdn {
 
 constexpr int kD = 128;       // d_k = d_v built
 constexpr int kChunk = 64;    // prefill chunk length
+constexpr int kMaxPrepGroup = 8;   // V-heads per QK head the bf16 prefill handles
 constexpr int kIoF32 = 0;
 constexpr int kIoBF16 = 1;
 
