@@ -24,8 +24,8 @@
 //            (16.25 KiB per chunk and V-head).
 //   scan  -- sequential over the chunks of one (sequence, V-head, 32-column slab
 //            of d_v).  Four state waves split the 64 chunk rows (X = K S^T, R, U)
-//            and the 128 d_k columns of the fp32 state (S' update, K^T built by
-//            an LDS transpose of the K rows they hold); four output waves on the
+//            and the 128 d_k columns of the fp32 state (S' update, K^T read from
+//            the K rows in LDS with transposing reads); four output waves on the
 //            same SIMDs form O from the LDS copies of S and U, off the
 //            recurrence's critical path.  The slab state never leaves the chip
 //            between chunks: fp32 in MFMA accumulators, plus a bf16 copy in LDS
@@ -66,6 +66,18 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 __device__ __forceinline__ uint16_t elem(uint4 u, int i) {
     const uint32_t w = i < 2 ? u.x : i < 4 ? u.y : i < 6 ? u.z : u.w;
     return (i & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xFFFFu);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// if lane q points at row (r0 + q / 4), columns c0 + 4 (q % 4) .. + 3 of a
+// row-major bf16 matrix, lane p receives column c0 + p, rows r0 .. r0 + 3:
+// a 16 x 4 block read transposed.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+    typedef short s4v __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4v lds_s4v;
+    const s4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4v *)(__attribute__((address_space(3))) uint16_t *)p);
+    return __builtin_bit_cast(uint2, r);
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
@@ -394,8 +406,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sU[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sUs[kSlabW * kRP];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[kD * kRP];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * kVP];
+    __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];   // K rows of the chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * kVP];    // v rows of the chunk (slab columns)
 
     // Workgroup -> (sequence, V-head, slab).  Workgroups are handed to the 8
     // XCDs round-robin; consecutive units (all slabs of a head, neighbouring
@@ -465,14 +477,11 @@ __global__ __launch_bounds__(512) void scan_kernel(
         };
 
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
-            // this wave's 16 rows of v, regrouped through LDS into C-layout columns
+            // this wave's 16 rows of v and of K into LDS, row-major
             *reinterpret_cast<uint4 *>(sV + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
-            // K^T for this chunk's state update (row = d_k, column = chunk row)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    sKt[(32 * s + 8 * g4 + i) * kRP + 16 * w + c] = elem(cur.kA[s], i);
+                *reinterpret_cast<uint4 *>(sKr + (16 * w + c) * kKP + 32 * s + 8 * g4) = cur.kA[s];
             fetch_a(ci + 2, pf);
             float gam[4], dec[4];
             const float Gr4[4] = {cur.G4.x, cur.G4.y, cur.G4.z, cur.G4.w};
@@ -490,14 +499,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     ax[nt] = mfma32(cur.kA[s], *reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), ax[nt]);
-            // R = V - diag(gamma) X, stored transposed ([d_v column][chunk row])
+            // R = V - diag(gamma) X, stored transposed ([d_v column][chunk row]);
+            // v arrives in the C layout of X through a transposing read
             wave_lds_sync();
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
+                const uint2 vv = lds_read_tr16(sV + (16 * w + 4 * g4 + (c >> 2)) * kVP + 16 * nt + 4 * (c & 3));
                 float r[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    r[j] = bf2f(sV[(16 * w + 4 * g4 + j) * kVP + 16 * nt + c]) - gam[j] * ax[nt][j];
+                r[0] = __uint_as_float(vv.x << 16) - gam[0] * ax[nt][0];
+                r[1] = __uint_as_float(vv.x & 0xFFFF0000u) - gam[1] * ax[nt][1];
+                r[2] = __uint_as_float(vv.y << 16) - gam[2] * ax[nt][2];
+                r[3] = __uint_as_float(vv.y & 0xFFFF0000u) - gam[3] * ax[nt][3];
                 *reinterpret_cast<uint2 *>(sR + (16 * nt + c) * kRP + 16 * w + 4 * g4) = pk4(r[0], r[1], r[2], r[3]);
             }
             __syncthreads();                                   // (1) R complete
@@ -521,9 +533,14 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     ub[nt][s] = *reinterpret_cast<const uint4 *>(sUs + (16 * nt + c) * kRP + 32 * s + 8 * g4);
+                // K^T row 32 w + 16 t + c, chunk rows 32 s + 8 g4 .. +7: two transposing reads
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    ka[t][s] = *reinterpret_cast<const uint4 *>(sKt + (32 * w + 16 * t + c) * kRP + 32 * s + 8 * g4);
+                for (int t = 0; t < 2; ++t) {
+                    const uint16_t *base = sKr + (32 * s + 8 * g4 + (c >> 2)) * kKP + 32 * w + 16 * t + 4 * (c & 3);
+                    const uint2 lo = lds_read_tr16(base);
+                    const uint2 hi = lds_read_tr16(base + 4 * kKP);
+                    ka[t][s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t)
