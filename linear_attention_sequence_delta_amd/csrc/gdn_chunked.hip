@@ -39,13 +39,15 @@ namespace gdn {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 8 bf16, kept in registers without copies
 
 constexpr int kKP = kD + 8;          // LDS row stride (bf16) of 128-wide rows
 constexpr int kAP = kChunk + 4;      // LDS row stride (fp32) of 64-wide rows
 constexpr int kRP = kChunk + 8;      // LDS row stride (bf16) of 64-wide rows
 constexpr int kTileElems = kChunk * kChunk;   // one 64 x 64 bf16 matrix
 
-__device__ __forceinline__ f32x4 mfma32(uint4 a, uint4 b, f32x4 c) {
+template <class A, class B>
+__device__ __forceinline__ f32x4 mfma32(A a, B b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -137,9 +139,15 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 }
 
 // ------------------------------------------------------------------- prep
-// Workspace record of one (chunk, V-head): T' and P as bf16 64 x 64 row-major,
-// then the chunk's cumulative log decay G as 64 fp32.
+// Workspace record of one (chunk, V-head): T', then P, then the chunk's
+// cumulative log decay G as 64 fp32.  T' and P (bf16 64 x 64) are stored as
+// MFMA operand fragments: block (a, s) = 2 a + s holds, for lane (c, g4), the
+// 16 bytes of row 16 a + c, columns 32 s + 8 g4 .. +7, lanes in order -- so
+// the scan loads each fragment as one contiguous 1 KiB block.  (A fragment
+// read from a row-major tile would touch half of 16 cache lines, which halves
+// the rate the vector memory pipe delivers.)
 constexpr int kRecElems = 2 * kTileElems + 2 * kChunk;   // in bf16 units (16640 bytes)
+__device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a + s) * 64 + lane) * 8; }
 
 // One wave per (chunk, QK head).  The K and Q rows of the chunk are loaded
 // straight into MFMA operand registers: the A operand of a 16-row block and
@@ -254,12 +262,12 @@ __global__ __launch_bounds__(64) void prep_kernel(
         wave_lds_sync();
 
         uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
-        // P rows out (coalesced 16-byte stores) and G
+        // P out as fragment blocks, and G
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
-            const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
-            *reinterpret_cast<uint4 *>(rec + kTileElems + row * kChunk + col0) =
-                *reinterpret_cast<const uint4 *>(sO + row * kRP + col0);
+            const int a = qq >> 1, s = qq & 1;
+            *reinterpret_cast<uint4 *>(rec + kTileElems + frag_off(a, s, lane)) =
+                *reinterpret_cast<const uint4 *>(sO + (16 * a + c) * kRP + 32 * s + 8 * g4);
         }
         reinterpret_cast<float *>(rec + 2 * kTileElems)[lane] = G;
 
@@ -340,10 +348,10 @@ __global__ __launch_bounds__(64) void prep_kernel(
         }
         wave_lds_sync();
 
-        // T' = T diag(b) (upper blocks zero), bf16 rows, coalesced 16-byte stores
+        // T' = T diag(b) (upper blocks zero) out as fragment blocks
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
-            const int idx = qq * 64 + lane, row = idx >> 3, col0 = (idx & 7) * 8;
+            const int row = 16 * (qq >> 1) + c, col0 = 32 * (qq & 1) + 8 * g4;
             float tv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -353,7 +361,7 @@ __global__ __launch_bounds__(64) void prep_kernel(
             uint4 ot;
             ot.x = pack_bf2(tv[0], tv[1]); ot.y = pack_bf2(tv[2], tv[3]);
             ot.z = pack_bf2(tv[4], tv[5]); ot.w = pack_bf2(tv[6], tv[7]);
-            *reinterpret_cast<uint4 *>(rec + row * kChunk + col0) = ot;
+            *reinterpret_cast<uint4 *>(rec + frag_off(qq >> 1, qq & 1, lane)) = ot;
         }
         wave_lds_sync();
     }
@@ -370,15 +378,15 @@ constexpr int kVP = kSlabW + 8;            // LDS row stride (bf16) of the v sta
 // the end only ever meet zero columns of T' and P, and results of the clamped
 // chunks past the end are never used.
 struct StateRegs {        // waves 0-3
-    uint4 kA[4];          // K row 16 w + c, d_k 32 s + 8 g4 .. +7
-    uint4 tA[2];          // T' row 16 w + c, columns 32 s + 8 g4 .. +7
-    uint4 vrow;           // v row 16 w + lane/4, slab columns 8 (lane%4) .. +7
+    u32x4 kr[4];          // K row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
+    u32x4 tA[2];          // T' row 16 w + c, columns 32 s + 8 g4 .. +7
+    u32x4 vrow;           // v row 16 w + lane/4, slab columns 8 (lane%4) .. +7
     float4 G4;            // G of rows 16 w + 4 g4 + j
     float GL;             // G of the chunk's last row
 };
 struct OutRegs {          // waves 4-7
-    uint4 qA[4];          // Q row 16 w + c, d_k 32 s + 8 g4 .. +7
-    uint4 pA[2];          // P row 16 w + c, columns 32 s + 8 g4 .. +7
+    u32x4 qr[4];          // Q row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
+    u32x4 pA[2];          // P row 16 w + c, columns 32 s + 8 g4 .. +7
     float Gown;           // G of row 16 w + c
 };
 
@@ -408,6 +416,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sUs[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];   // K rows of the chunk
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * kVP];    // v rows of the chunk (slab columns)
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[4][16 * kKP];     // each output wave's Q rows
 
     // Workgroup -> (sequence, V-head, slab).  Workgroups are handed to the 8
     // XCDs round-robin; consecutive units (all slabs of a head, neighbouring
@@ -428,9 +437,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
     auto rec_of = [&](int ci) { return ws + ((size_t)(cbase + ci) * H_v + h) * kRecElems; };
     auto chunk_len = [&](int ci) { return min(kChunk, s1 - (s0 + kChunk * ci)); };
-    auto krow_off = [&](int ci) {   // offset of K/Q row 16 w + c (clamped) of chunk ci
+    // K and Q rows are loaded whole (16 lanes x 16 B per row, 4 rows per
+    // instruction: every cache line fully used) and regrouped into MFMA
+    // fragments through LDS.  Offset of row 16 w + 4 i + lane / 16 (clamped),
+    // 16-byte piece lane % 16, of chunk ci:
+    auto krow_off = [&](int ci, int i) {
         return (size_t)(s0 + kChunk * ci) * H_qk * kD +
-               (size_t)((min(16 * w + c, chunk_len(ci) - 1) * H_qk + hq) * kD + 8 * g4);
+               (size_t)((min(16 * w + 4 * i + (lane >> 4), chunk_len(ci) - 1) * H_qk + hq) * kD + 8 * (lane & 15));
     };
 
     if (wave < 4) {
@@ -459,13 +472,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
         };
         auto fetch_a = [&](int ci, StateRegs &R) {
             ci = min(ci, nchunks - 1);
-            const uint16_t *kp = k + krow_off(ci);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) R.kA[s] = *reinterpret_cast<const uint4 *>(kp + 32 * s);
+            for (int i = 0; i < 4; ++i) R.kr[i] = *reinterpret_cast<const u32x4 *>(k + krow_off(ci, i));
             const uint16_t *rec = rec_of(ci);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                R.tA[s] = *reinterpret_cast<const uint4 *>(rec + (16 * w + c) * kChunk + 32 * s + 8 * g4);
+                R.tA[s] = *reinterpret_cast<const u32x4 *>(rec + frag_off(w, s, lane));
         };
         auto fetch_b = [&](int ci, StateRegs &R) {
             ci = min(ci, nchunks - 1);
@@ -473,15 +485,20 @@ __global__ __launch_bounds__(512) void scan_kernel(
             R.G4 = *reinterpret_cast<const float4 *>(Gp + 16 * w + 4 * g4);
             R.GL = Gp[kChunk - 1];
             const int vr = min(16 * w + (lane >> 2), chunk_len(ci) - 1);
-            R.vrow = *reinterpret_cast<const uint4 *>(v + ((size_t)(s0 + kChunk * ci + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
+            R.vrow = *reinterpret_cast<const u32x4 *>(v + ((size_t)(s0 + kChunk * ci + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
         };
 
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
-            // this wave's 16 rows of v and of K into LDS, row-major
-            *reinterpret_cast<uint4 *>(sV + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
+            // this wave's 16 rows of v and of K into LDS, row-major; K's MFMA
+            // fragments come back out of its own rows
+            *reinterpret_cast<u32x4 *>(sV + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                *reinterpret_cast<uint4 *>(sKr + (16 * w + c) * kKP + 32 * s + 8 * g4) = cur.kA[s];
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4 *>(sKr + (16 * w + 4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = cur.kr[i];
+            wave_lds_sync();
+            uint4 kA[4];          // K row 16 w + c, d_k 32 s + 8 g4 .. +7
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kA[s] = *reinterpret_cast<const uint4 *>(sKr + (16 * w + c) * kKP + 32 * s + 8 * g4);
             fetch_a(ci + 2, pf);
             float gam[4], dec[4];
             const float Gr4[4] = {cur.G4.x, cur.G4.y, cur.G4.z, cur.G4.w};
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    ax[nt] = mfma32(cur.kA[s], *reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), ax[nt]);
+                    ax[nt] = mfma32(kA[s], *reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), ax[nt]);
             // R = V - diag(gamma) X, stored transposed ([d_v column][chunk row]);
             // v arrives in the C layout of X through a transposing read
             wave_lds_sync();
@@ -583,19 +600,27 @@ __global__ __launch_bounds__(512) void scan_kernel(
         // ---------------- output waves
         auto fetch = [&](int ci, OutRegs &R) {
             ci = min(ci, nchunks - 1);
-            const uint16_t *qp = q + krow_off(ci);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) R.qA[s] = *reinterpret_cast<const uint4 *>(qp + 32 * s);
+            for (int i = 0; i < 4; ++i) R.qr[i] = *reinterpret_cast<const u32x4 *>(q + krow_off(ci, i));
             const uint16_t *rec = rec_of(ci);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                R.pA[s] = *reinterpret_cast<const uint4 *>(rec + kTileElems + (16 * w + c) * kChunk + 32 * s + 8 * g4);
+                R.pA[s] = *reinterpret_cast<const u32x4 *>(rec + kTileElems + frag_off(w, s, lane));
             R.Gown = reinterpret_cast<const float *>(rec + 2 * kTileElems)[16 * w + c];
         };
         auto body = [&](int ci, OutRegs &cur, OutRegs &pf) {
             const int c0 = s0 + kChunk * ci;
             const int L = min(kChunk, s1 - c0);
+            // this wave's Q rows through its LDS area into MFMA fragments
+            uint16_t *q_lds = sQ[w];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4 *>(q_lds + (4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = cur.qr[i];
             fetch(ci + 2, pf);
+            wave_lds_sync();
+            uint4 qA[4];          // Q row 16 w + c, d_k 32 s + 8 g4 .. +7
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qA[s] = *reinterpret_cast<const uint4 *>(q_lds + c * kKP + 32 * s + 8 * g4);
             // O^T = S Q^T (the S fragments are the A operand); lane holds
             // O[16 w + c][16 nt + 4 g4 + j]
             f32x4 ao[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -603,7 +628,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), cur.qA[s], ao[nt]);
+                    ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), qA[s], ao[nt]);
             const float gq = scale * __expf(cur.Gown);
             __syncthreads();                                   // (1)
             __syncthreads();                                   // (2) U complete
