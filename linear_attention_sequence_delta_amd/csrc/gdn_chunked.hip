@@ -616,7 +616,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<u32x4 *>(q_lds + (4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = cur.qr[i];
-            fetch(ci + 2, pf);
             wave_lds_sync();
             uint4 qA[4];          // Q row 16 w + c, d_k 32 s + 8 g4 .. +7
 #pragma unroll
@@ -631,6 +630,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), qA[s], ao[nt]);
             const float gq = scale * __expf(cur.Gown);
             __syncthreads();                                   // (1)
+            // next loads issued while the state waves form U: the vector
+            // memory pipe is then quiet while they form X and R
+            fetch(ci + 2, pf);
             __syncthreads();                                   // (2) U complete
             // O^T += U^T P^T  (P is lower triangular: k-steps up to this row block)
             const bool row_ok = 16 * w + c < L;
