@@ -62,12 +62,14 @@ __device__ __forceinline__ s16x4 to_bf4(float a, float b, float c, float d) {
     r[3] = (short)f2bf(d);
     return r;
 }
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-    return make_uint2(pack_bf2(a, b), pack_bf2(c, d));
+// fp32 -> bf16 (round to nearest even), two or four at a time
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
 }
-__device__ __forceinline__ uint16_t elem(uint4 u, int i) {
-    const uint32_t w = i < 2 ? u.x : i < 4 ? u.y : i < 6 ? u.z : u.w;
-    return (i & 1) ? uint16_t(w >> 16) : uint16_t(w & 0xFFFFu);
+__device__ __forceinline__ uint2 pk4(float a, float b, float c, float d) {
+    return make_uint2(pk2(a, b), pk2(c, d));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
@@ -153,16 +155,17 @@ __device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a
 // straight into MFMA operand registers: the A operand of a 16-row block and
 // the B operand of K^T for the same block are the same fragment (row c of the
 // block, 8 consecutive d_k), so K K^T and Q K^T need no LDS staging.  They are
-// formed once and kept in registers for all V-heads of the QK head.
+// formed once, with the operands ordered so that each lane holds 4 consecutive
+// columns of one row, and kept in registers for all V-heads of the QK head.
 __global__ __launch_bounds__(64) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
     uint16_t *__restrict__ ws) {
     __shared__ __attribute__((aligned(16))) float sA[kChunk * kAP];
-    __shared__ __attribute__((aligned(16))) uint16_t sO[kChunk * kRP];
-    __shared__ float sG[kChunk];
-    __shared__ float sBt[kChunk];
+    __shared__ __attribute__((aligned(16))) uint16_t sP[kChunk * kRP];
+    __shared__ __attribute__((aligned(16))) float sG[kChunk];
+    __shared__ __attribute__((aligned(16))) float sBt[kChunk];
 
     const int gc = blockIdx.x, hq = blockIdx.y;
     if (gc >= chunk_base[N]) return;
@@ -173,14 +176,15 @@ __global__ __launch_bounds__(64) void prep_kernel(
     const int L = min(kChunk, s1 - c0);
     const int lane = threadIdx.x, g4 = lane >> 4, c = lane & 15;
 
-    // gates of every V-head of the group (zero past the end), loaded up front
+    // gates of every V-head of the group (clamped indices: no load behind a branch)
     constexpr int kMaxGroup = kMaxPrepGroup;
     float graw[kMaxGroup], braw[kMaxGroup];
     const size_t grow = (size_t)(c0 + min(lane, L - 1)) * H_v + (size_t)hq * group;
 #pragma unroll
     for (int vv = 0; vv < kMaxGroup; ++vv) {
-        graw[vv] = vv < group ? g[grow + vv] : 0.f;
-        braw[vv] = vv < group ? beta[grow + vv] : 0.f;
+        const int vc = min(vv, group - 1);
+        graw[vv] = g[grow + vc];
+        braw[vv] = beta[grow + vc];
     }
 
     // K and Q fragments: block I, k-step s -> row 16 I + c, d_k 32 s + 8 g4 .. +7
@@ -206,7 +210,9 @@ __global__ __launch_bounds__(64) void prep_kernel(
         }
     }
 
-    // K K^T and Q K^T, lower 16 x 16 tiles (J <= I), kept in registers
+    // lower 16 x 16 tiles (J <= I); lane holds row 16 I + c, columns 16 J + 4 g4 + j:
+    //   kk[I][J] = k_{16 I + c} . k_{16 J + 4 g4 + j}   (K K^T is symmetric)
+    //   qk[I][J] = q_{16 I + c} . k_{16 J + 4 g4 + j}
     f32x4 kk[4][4], qk[4][4];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
@@ -216,8 +222,8 @@ __global__ __launch_bounds__(64) void prep_kernel(
             qk[I][J] = kk[I][J];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                kk[I][J] = mfma32(kf[I][s], kf[J][s], kk[I][J]);
-                qk[I][J] = mfma32(qf[I][s], kf[J][s], qk[I][J]);
+                kk[I][J] = mfma32(kf[J][s], kf[I][s], kk[I][J]);
+                qk[I][J] = mfma32(kf[J][s], qf[I][s], qk[I][J]);
             }
         }
 
@@ -230,46 +236,44 @@ __global__ __launch_bounds__(64) void prep_kernel(
         const float G = wave_scan(gl);
         sG[lane] = G;
         sBt[lane] = bl;
+        uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
+        reinterpret_cast<float *>(rec + 2 * kTileElems)[lane] = G;
         wave_lds_sync();
 
-        // gated K K^T -> A (fp32, lower tiles), gated Q K^T -> P (bf16, all tiles)
+        // gated K K^T -> A (fp32 rows in LDS, lower tiles); gated Q K^T -> P
+        // (bf16 rows in LDS, zero above the diagonal)
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            float Gr[4], br[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Gr[j] = sG[16 * I + 4 * g4 + j];
-                br[j] = sBt[16 * I + 4 * g4 + j];
-            }
+            const int row = 16 * I + c;
+            const float Gr = sG[row], br = sBt[row];
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
-                const int col = 16 * J + c;
                 if (J > I) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sO[(16 * I + 4 * g4 + j) * kRP + col] = 0;
+                    *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = make_uint2(0, 0);
                     continue;
                 }
-                const float Gi = sG[col];
+                const float4 Gv = *reinterpret_cast<const float4 *>(sG + 16 * J + 4 * g4);
+                const float gi[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
+                float av[4], pv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int row = 16 * I + 4 * g4 + j;
-                    const float e = __expf(Gr[j] - Gi);
-                    sA[row * kAP + col] = col < row ? br[j] * e * kk[I][J][j] : 0.f;
-                    sO[row * kRP + col] = f2bf(col <= row ? scale * e * qk[I][J][j] : 0.f);
+                    const int col = 16 * J + 4 * g4 + j;
+                    const float e = __expf(Gr - gi[j]);
+                    av[j] = col < row ? br * e * kk[I][J][j] : 0.f;
+                    pv[j] = col <= row ? scale * e * qk[I][J][j] : 0.f;
                 }
+                *reinterpret_cast<float4 *>(sA + row * kAP + 16 * J + 4 * g4) = make_float4(av[0], av[1], av[2], av[3]);
+                *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = pk4(pv[0], pv[1], pv[2], pv[3]);
             }
         }
         wave_lds_sync();
-
-        uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
-        // P out as fragment blocks, and G
+        // P out as fragment blocks
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
             const int a = qq >> 1, s = qq & 1;
             *reinterpret_cast<uint4 *>(rec + kTileElems + frag_off(a, s, lane)) =
-                *reinterpret_cast<const uint4 *>(sO + (16 * a + c) * kRP + 32 * s + 8 * g4);
+                *reinterpret_cast<const uint4 *>(sP + (16 * a + c) * kRP + 32 * s + 8 * g4);
         }
-        reinterpret_cast<float *>(rec + 2 * kTileElems)[lane] = G;
 
         float *A = sA;
         // Diagonal 16 x 16 blocks: lane (b, c) solves column c of block b by
@@ -348,22 +352,21 @@ __global__ __launch_bounds__(64) void prep_kernel(
         }
         wave_lds_sync();
 
-        // T' = T diag(b) (upper blocks zero) out as fragment blocks
+        // T' = T diag(b) (zero above the diagonal blocks) out as fragment blocks
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
-            const int row = 16 * (qq >> 1) + c, col0 = 32 * (qq & 1) + 8 * g4;
-            float tv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = col0 + e;
-                tv[e] = (col >> 4) <= (row >> 4) ? A[row * kAP + col] * sBt[col] : 0.f;
-            }
-            uint4 ot;
-            ot.x = pack_bf2(tv[0], tv[1]); ot.y = pack_bf2(tv[2], tv[3]);
-            ot.z = pack_bf2(tv[4], tv[5]); ot.w = pack_bf2(tv[6], tv[7]);
-            *reinterpret_cast<uint4 *>(rec + frag_off(qq >> 1, qq & 1, lane)) = ot;
+            const int a = qq >> 1, s = qq & 1;
+            const int row = 16 * a + c, ca = 32 * s + 8 * g4, cb = ca + 4;
+            const float4 t0 = *reinterpret_cast<const float4 *>(A + row * kAP + ca);
+            const float4 t1 = *reinterpret_cast<const float4 *>(A + row * kAP + cb);
+            const float4 b0 = *reinterpret_cast<const float4 *>(sBt + ca);
+            const float4 b1 = *reinterpret_cast<const float4 *>(sBt + cb);
+            const bool la = (ca >> 4) <= a, lb = la;   // 8 columns in one 16-column block
+            const uint2 u0 = la ? pk4(t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w) : make_uint2(0, 0);
+            const uint2 u1 = lb ? pk4(t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w) : make_uint2(0, 0);
+            *reinterpret_cast<uint4 *>(rec + frag_off(a, s, lane)) = make_uint4(u0.x, u0.y, u1.x, u1.y);
         }
-        wave_lds_sync();
+        wave_lds_sync();                 // T read before the next V-head's A is written
     }
 }
 
@@ -389,15 +392,6 @@ struct OutRegs {          // waves 4-7
     u32x4 pA[2];          // P row 16 w + c, columns 32 s + 8 g4 .. +7
     float Gown;           // G of row 16 w + c
 };
-
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
-}
-__device__ __forceinline__ uint2 pk4(float a, float b, float c, float d) {
-    return make_uint2(pk2(a, b), pk2(c, d));
-}
 
 // 512 threads: waves 0-3 carry the state through the chunks (X = K S^T, R,
 // U = T' R, S' update), waves 4-7 produce the outputs (S Q^T, U^T P^T) from the
