@@ -26,6 +26,9 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 from typing import Optional
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 # Layer shape of the linear-attention layers ("拆解 Qwen3.8-27B ..." sec. 2.1):
@@ -34,7 +37,6 @@ H_V = 48
 D_K = 128
 D_V = 128
 CONV_W = 4
-BLOCK = 4096
 
 
 def c_raw(H_qk: int = H_QK, H_v: int = H_V, dk: int = D_K, dv: int = D_V) -> int:
@@ -74,11 +76,21 @@ def _gates(rng_a, rng_b, A_log, dt_bias, T):
     return g.astype(np.float32), beta.astype(np.float32)
 
 
-def _raw_bf16(rng, T, C):
+def _raw_bf16(seq, T, C, block: int = 128):
+    """[T, C] bf16 bits ~ N(0, 1): channel block b (``block`` channels) is drawn
+    from its own PCG64 stream, child b of ``seq``, as float32 normals in
+    row-major order.  Blocks are independent, so they are drawn in parallel."""
     out = np.empty((T, C), dtype=np.uint16)
-    for t0 in range(0, T, BLOCK):
-        t1 = min(T, t0 + BLOCK)
-        out[t0:t1] = bf16_bits(rng.standard_normal((t1 - t0, C), dtype=np.float32))
+    nb = (C + block - 1) // block
+    kids = seq.spawn(nb)
+
+    def fill(b):
+        c0, c1 = b * block, min(C, (b + 1) * block)
+        r = np.random.Generator(np.random.PCG64(kids[b]))
+        out[:, c0:c1] = bf16_bits(r.standard_normal((T, c1 - c0), dtype=np.float32))
+
+    with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(nb)))
     return out
 
 
@@ -157,7 +169,8 @@ def raw_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int = H_
                 state_std: float = 0.02) -> Prefill:
     """Prefill from raw projections: x ~ N(0,1) bf16 [T, C_raw]; conv weights
     ~ N(0, 0.5) bf16; gates per the module recipe; optional initial states
-    ~ N(0, state_std).  Generators: x, w, a, b, A_log, dt_bias, S0."""
+    ~ N(0, state_std).  Streams: x (one child stream per 128-channel block), w,
+    a, b, A_log, dt_bias, S0."""
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
         T = int(lengths.sum())
@@ -165,9 +178,10 @@ def raw_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int = H_
         N = len(lengths)
     else:
         cu, N = None, 1
-    rx, rw, ra, rb, rA, rd, rs = _rngs(seed, 7)
+    seqs = np.random.SeedSequence(seed).spawn(7)
+    rw, ra, rb, rA, rd, rs = [np.random.Generator(np.random.PCG64(q)) for q in seqs[1:]]
     C = c_raw(H_qk, H_v, dk, dv)
-    x = _raw_bf16(rx, T, C)
+    x = _raw_bf16(seqs[0], T, C)
     w = bf16_bits(rw.normal(0.0, 0.5, (C, CONV_W)).astype(np.float32))
     A_log = rA.uniform(-1.0, 1.0, H_v)
     dt_bias = rd.uniform(-1.0, 1.0, H_v)
@@ -216,19 +230,23 @@ def direct_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int =
 
 def decode_inputs(seed: int, B: int, P: Optional[int] = None, H_qk: int = H_QK,
                   H_v: int = H_V, dk: int = D_K, dv: int = D_V, state_std: float = 0.02,
-                  pool: Optional[np.ndarray] = None, slot_idx=None) -> Decode:
+                  pool: Optional[np.ndarray] = None, slot_idx=None, A_log=None,
+                  dt_bias=None) -> Decode:
     """One decode step: unit q, k (bf16), v ~ N(0,1) (bf16), gates per the module
     recipe, a pool of P slots whose B addressed slots hold N(0, state_std) states
     and whose other slots hold a NaN canary; slot_idx = the first B entries of a
-    seeded permutation of 0..P-1.  A given ``pool``/``slot_idx`` is used as is.
+    seeded permutation of 0..P-1.  A given ``pool``/``slot_idx`` is used as is,
+    and a given ``A_log``/``dt_bias`` (the layer's weights) replaces the drawn ones.
     Generators: q, k, v, a, b, A_log, dt_bias, perm, states."""
     P = P if P is not None else (pool.shape[0] if pool is not None else 2 * B)
     rq, rk, rv, ra, rb, rA, rd, rp, rs = _rngs(seed, 9)
     q = bf16_bits(_unit_rows(rq.standard_normal((B, H_qk, dk))).astype(np.float32))
     k = bf16_bits(_unit_rows(rk.standard_normal((B, H_qk, dk))).astype(np.float32))
     v = bf16_bits(rv.standard_normal((B, H_v, dv), dtype=np.float32))
-    A_log = rA.uniform(-1.0, 1.0, H_v)
-    dt_bias = rd.uniform(-1.0, 1.0, H_v)
+    A_draw = rA.uniform(-1.0, 1.0, H_v)
+    dt_draw = rd.uniform(-1.0, 1.0, H_v)
+    A_log = A_draw if A_log is None else np.asarray(A_log, dtype=np.float64)
+    dt_bias = dt_draw if dt_bias is None else np.asarray(dt_bias, dtype=np.float64)
     g, beta = _gates(ra, rb, A_log, dt_bias, B)
     if slot_idx is None:
         slot_idx = rp.permutation(P)[:B].astype(np.int32)
@@ -272,6 +290,10 @@ def workload_longctx_prefill(T: int = 262144):
     return raw_prefill(1005, T=T)
 
 
-def workload_longctx_decode(step: int, B: int = 256, pool=None, slot_idx=None):
-    """Per-step decode inputs of the long-context hand-off (fresh draws per step)."""
-    return decode_inputs((1005, 1, step), B=B, P=B, pool=pool, slot_idx=slot_idx)
+def workload_longctx_decode(step: int, B: int = 256, pool=None, slot_idx=None, A_log=None,
+                            dt_bias=None):
+    """Per-step decode inputs of the long-context hand-off: fresh q, k, v and gate
+    draws per step; pass the prefill's A_log / dt_bias (its ``meta``) so that the
+    steps use the same layer's gate weights."""
+    return decode_inputs((1005, 1, step), B=B, P=B, pool=pool, slot_idx=slot_idx, A_log=A_log,
+                         dt_bias=dt_bias)
