@@ -13,6 +13,12 @@ before the timed regions start; timing uses HIP events on the stream the
 kernels run on.  The fp64 oracle is timed on the host's cores over a bounded
 sample of the same workload and reported as "cpu_baseline".
 
+The long-context hand-off is timed in the same run and reported under
+"longctx": a 262144-token prelude + prefill, then 64 decode steps of 256
+sequences that continue from its final state, and a stack of 48 independently
+seeded layers (one decode step each, B = 256) per decode token.
+`--no-longctx` skips it.
+
 `--copy-calibration BYTES` runs a plain device copy of BYTES bytes instead: the
 reference run for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings.
 """
@@ -48,7 +54,10 @@ PRELUDE_BYTES_PER_TOKEN = 2 * 2 * (2 * H_QK * D + H_V * D)
 # once in fp32, plus q, k, v, o in bf16 and g, beta in fp32
 DECODE_BYTES_PER_SEQ = (H_V * (2 * D * D * 4 + 2 * D * 2 + 2 * 4) + 2 * H_QK * D * 2)
 
+T_LONG, LONG_STEPS, STACK_LAYERS = 262144, 64, 48
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T32768.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_prefill_T32768.txt")
 CHUNKED_SRC = os.path.join(ROOT, "linear_attention_sequence_delta_amd", "csrc", "gdn_chunked.hip")
 
 
@@ -56,20 +65,28 @@ def _sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def _traffic_bytes():
-    """HBM bytes per prefill launch from the committed counter summary, or
-    None when it is missing or the kernels changed since it was taken."""
+def _profile_value(path, key):
+    """A per-launch figure from a committed counter summary, or None when it is
+    missing or the kernels changed since the counters were taken."""
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if "=" in line and not line.startswith("#"):
-                key, val = line.split("=", 1)
-                kv[key.strip()] = val.strip()
+                k, val = line.split("=", 1)
+                kv[k.strip()] = val.strip()
         if kv.get("source_sha256_16") != _sha(CHUNKED_SRC):
             return None
-        return float(kv["hbm_bytes_per_prefill"])
+        return float(kv[key])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def _traffic_bytes():
+    return _profile_value(TRAFFIC_FILE, "hbm_bytes_per_prefill")
+
+
+def _issued_mfma_flops():
+    return _profile_value(MFMA_FILE, "bf16_mfma_flop_per_prefill")
 
 
 def _events(torch):
@@ -149,6 +166,106 @@ def run_gpu(steps, warmup):
     return dict(pre_us=pre_us, pf_us=pf_us, step_ms=step_ms, dec_us=dec_us)
 
 
+def run_longctx():
+    """T = 262144 prelude + prefill, then 64 decode steps of 256 sequences that
+    all continue from its final state, then a 48-layer decode stack."""
+    import numpy as np
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    import synth
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    p = synth.workload_longctx_prefill(T_LONG)
+    x, w, g, beta = to_dev(p.x), to_dev(p.w), to_dev(p.g), to_dev(p.beta)
+    del p.x
+    q = torch.empty((T_LONG, H_QK, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((T_LONG, H_V, D), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((T_LONG, H_V, D), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((1, H_V, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, T_LONG, H_QK, H_V),
+                     dtype=torch.uint8, device=dev)
+
+    def layer():
+        gdn.gdn_conv_prelude(x, w, None, H_qk=H_QK, H_v=H_V, out=(q, k, v))
+        gdn.gdn_prefill(q, k, v, g, beta, None, None, final_state=fs, o=o, workspace=ws)
+
+    layer()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    layer()
+    e1.record()
+    torch.cuda.synchronize()
+    pre_us = e0.elapsed_time(e1) * 1e3
+    del x, q, k, v, o, ws
+
+    # hand-off: 256 sequences continue from the prefill's final state
+    pool = fs[0].unsqueeze(0).expand(B_DECODE, -1, -1, -1).contiguous()
+    steps = []
+    slot = None
+    for st in range(LONG_STEPS):
+        d = synth.workload_longctx_decode(st, B=B_DECODE, pool=np.zeros((1,), np.float32),
+                                          slot_idx=slot, A_log=p.meta["A_log"],
+                                          dt_bias=p.meta["dt_bias"])
+        slot = d.slot_idx
+        steps.append(tuple(to_dev(a) for a in (d.q, d.k, d.v, d.g, d.beta)))
+    slot_d = to_dev(slot)
+    od = torch.empty((B_DECODE, H_V, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    e0.record()
+    for (dq, dk, dv_, dg, db) in steps:
+        gdn.gdn_decode_step(dq, dk, dv_, dg, db, pool, slot_d, o=od)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1e3 / LONG_STEPS
+    del pool, steps
+
+    # 48 independently seeded layers, one decode step each per token.  Pools
+    # (768 MiB each) and per-layer inputs are drawn on the GPU from seeded
+    # generators (layer l: seed 1005000 + l); rows of q and k are normalised.
+    gen = torch.Generator(device=dev)
+    layers = []
+    for l in range(STACK_LAYERS):
+        gen.manual_seed(1005000 + l)
+        lp = torch.randn((B_DECODE, H_V, D, D), generator=gen, device=dev) * 0.02
+        lq = torch.nn.functional.normalize(
+            torch.randn((B_DECODE, H_QK, D), generator=gen, device=dev), dim=-1).to(torch.bfloat16)
+        lk = torch.nn.functional.normalize(
+            torch.randn((B_DECODE, H_QK, D), generator=gen, device=dev), dim=-1).to(torch.bfloat16)
+        lv = torch.randn((B_DECODE, H_V, D), generator=gen, device=dev).to(torch.bfloat16)
+        lg = -torch.rand((B_DECODE, H_V), generator=gen, device=dev) * 0.5
+        lb = torch.sigmoid(torch.randn((B_DECODE, H_V), generator=gen, device=dev))
+        layers.append((lq, lk, lv, lg, lb, lp))
+    slots = torch.arange(B_DECODE, dtype=torch.int32, device=dev)
+    for (lq, lk, lv, lg, lb, lp) in layers:
+        gdn.gdn_decode_step(lq, lk, lv, lg, lb, lp, slots, o=od)
+    torch.cuda.synchronize()
+    tokens = 3
+    e0.record()
+    for _ in range(tokens):
+        for (lq, lk, lv, lg, lb, lp) in layers:
+            gdn.gdn_decode_step(lq, lk, lv, lg, lb, lp, slots, o=od)
+    e1.record()
+    torch.cuda.synchronize()
+    stack_ms = e0.elapsed_time(e1) / tokens
+    return {"prefill": {"T": T_LONG, "us": pre_us, "tokens_per_s": T_LONG / (pre_us * 1e-6),
+                        "what": "conv prelude + chunked prefill of one 262144-token sequence"},
+            "decode": {"B": B_DECODE, "steps": LONG_STEPS, "us_per_step": dec_us,
+                       "tokens_per_s": B_DECODE / (dec_us * 1e-6),
+                       "what": "256 sequences continuing from the prefill's final state"},
+            "stack48": {"layers": STACK_LAYERS, "ms_per_token": stack_ms,
+                        "tokens_per_s": B_DECODE / (stack_ms * 1e-3),
+                        "what": "48 independently seeded layers, one B = 256 decode step each"}}
+
+
 def cpu_baseline(T_sample=T_PREFILL):
     """The fp64 oracle (prelude + token recurrence) on the first T_sample tokens
     (by default all of them) of the same prefill workload, all 48 V-heads."""
@@ -185,6 +302,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -206,6 +324,7 @@ def main():
     flops = PREFILL_FLOP_PER_TOKEN * T
     achieved_tflops = flops / (r["pf_us"] * 1e-6) / 1e12
     traffic = _traffic_bytes()
+    issued = _issued_mfma_flops()
     pre_bytes = PRELUDE_BYTES_PER_TOKEN * T
     dec_bytes = DECODE_BYTES_PER_SEQ * B_DECODE
     out = {
@@ -230,7 +349,10 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
                      "kernel": "gdn_prefill (plan + prep + scan kernels)",
-                     "algorithmic_flop_per_launch": flops},
+                     "algorithmic_flop_per_launch": flops,
+                     "issued_mfma_flop_per_launch": issued,
+                     "issued_frac": (None if issued is None else
+                                     issued / (r["pf_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS)},
         "phases_us": {"prelude": r["pre_us"], "prefill": r["pf_us"],
                       "wall_per_step": r["step_ms"] * 1e3},
         "prelude_roofline": {"bound": "hbm", "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
@@ -245,6 +367,8 @@ def main():
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}},
     }
+    if not args.no_longctx:
+        out["longctx"] = run_longctx()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
