@@ -38,8 +38,14 @@
  *   - Array contents are not inspected on the host (that would need a sync):
  *     cu_seqlens must be non-decreasing from 0 to T, slot ids distinct and in
  *     [0, P).  With GDN_DEBUG=1 these preconditions are checked on the device.
- *   - Thread safety: calls may be made concurrently from several threads; the
- *     library keeps no mutable state except the per-thread error text.
+ *   - Thread safety: calls may be made concurrently from several threads.  The
+ *     library's only mutable state is the per-thread error text and, per device,
+ *     one auxiliary stream (default priority) with a few events, made on the
+ *     first bf16 prefill of a long single sequence and kept until the process
+ *     ends; the enqueues on it are serialised by a lock.  Such a prefill runs
+ *     part of its work on that stream, forked from and joined back into
+ *     `stream` with events, so to the caller it is ordered like any other call
+ *     on `stream`.
  */
 #ifndef GDN_H_
 #define GDN_H_

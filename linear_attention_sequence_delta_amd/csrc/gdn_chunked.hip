@@ -31,6 +31,10 @@
 //            between chunks: fp32 in MFMA accumulators, plus a bf16 copy in LDS
 //            that feeds the next chunk's products.  Inputs are prefetched two
 //            chunks ahead into three rotating register sets.
+#include <stdint.h>
+
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -142,7 +146,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 
 // ------------------------------------------------------------------- prep
 // Workspace record of one (chunk, V-head): T', then P, then the chunk's
-// cumulative log decay G as 64 fp32.  T' and P (bf16 64 x 64) are stored as
+// cumulative log decay G as 64 fp32.  Records are written with non-temporal
+// stores: the scan reads them long after (a segment later, when prep and scan
+// overlap), and they would otherwise displace the K and Q rows the scan's
+// workgroups share through L2.  T' and P (bf16 64 x 64) are stored as
 // MFMA operand fragments: block (a, s) = 2 a + s holds, for lane (c, g4), the
 // 16 bytes of row 16 a + c, columns 32 s + 8 g4 .. +7, lanes in order -- so
 // the scan loads each fragment as one contiguous 1 KiB block.  (A fragment
@@ -151,222 +158,235 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 constexpr int kRecElems = 2 * kTileElems + 2 * kChunk;   // in bf16 units (16640 bytes)
 __device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a + s) * 64 + lane) * 8; }
 
-// One wave per (chunk, QK head).  The K and Q rows of the chunk are loaded
+// One wave per (chunk, QK head) item; a workgroup holds kPrepWaves independent
+// waves, each with its own LDS area, that step through the items
+// [item_lo, item_hi) (item = chunk * H_qk + QK head) with the grid's stride.
+// A workgroup fills one CU (one wave per SIMD), so a small grid stays on as
+// many CUs as it has workgroups.  The K and Q rows of the chunk are loaded
 // straight into MFMA operand registers: the A operand of a 16-row block and
 // the B operand of K^T for the same block are the same fragment (row c of the
 // block, 8 consecutive d_k), so K K^T and Q K^T need no LDS staging.  They are
 // formed once, with the operands ordered so that each lane holds 4 consecutive
 // columns of one row, and kept in registers for all V-heads of the QK head.
-__global__ __launch_bounds__(64) void prep_kernel(
+constexpr int kPrepWaves = 4;
+__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    uint16_t *__restrict__ ws) {
-    __shared__ __attribute__((aligned(16))) float sA[kChunk * kAP];
-    __shared__ __attribute__((aligned(16))) uint16_t sP[kChunk * kRP];
-    __shared__ __attribute__((aligned(16))) float sG[kChunk];
-    __shared__ __attribute__((aligned(16))) float sBt[kChunk];
+    int item_lo, int item_hi, uint16_t *__restrict__ ws) {
+    __shared__ __attribute__((aligned(16))) float sA_w[kPrepWaves][kChunk * kAP];
+    __shared__ __attribute__((aligned(16))) uint16_t sP_w[kPrepWaves][kChunk * kRP];
+    __shared__ __attribute__((aligned(16))) float sG_w[kPrepWaves][kChunk];
+    __shared__ __attribute__((aligned(16))) float sBt_w[kPrepWaves][kChunk];
 
-    const int gc = blockIdx.x, hq = blockIdx.y;
-    if (gc >= chunk_base[N]) return;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float *sA = sA_w[wv];
+    uint16_t *sP = sP_w[wv];
+    float *sG = sG_w[wv];
+    float *sBt = sBt_w[wv];
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c = lane & 15;
     const int group = H_v / H_qk;
-    const int n = seq_of_chunk(chunk_base, N, gc);
-    const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
-    const int c0 = s0 + kChunk * (gc - chunk_base[n]);
-    const int L = min(kChunk, s1 - c0);
-    const int lane = threadIdx.x, g4 = lane >> 4, c = lane & 15;
+    const int hi = min(item_hi, chunk_base[N] * H_qk);
+    for (int it = item_lo + (int)blockIdx.x * kPrepWaves + wv; it < hi; it += (int)gridDim.x * kPrepWaves) {
+        const int gc = it / H_qk, hq = it - gc * H_qk;
+        const int n = seq_of_chunk(chunk_base, N, gc);
+        const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
+        const int c0 = s0 + kChunk * (gc - chunk_base[n]);
+        const int L = min(kChunk, s1 - c0);
 
-    // gates of every V-head of the group (clamped indices: no load behind a branch)
-    constexpr int kMaxGroup = kMaxPrepGroup;
-    float graw[kMaxGroup], braw[kMaxGroup];
-    const size_t grow = (size_t)(c0 + min(lane, L - 1)) * H_v + (size_t)hq * group;
+        // gates of every V-head of the group (clamped indices: no load behind a branch)
+        constexpr int kMaxGroup = kMaxPrepGroup;
+        float graw[kMaxGroup], braw[kMaxGroup];
+        const size_t grow = (size_t)(c0 + min(lane, L - 1)) * H_v + (size_t)hq * group;
 #pragma unroll
-    for (int vv = 0; vv < kMaxGroup; ++vv) {
-        const int vc = min(vv, group - 1);
-        graw[vv] = g[grow + vc];
-        braw[vv] = beta[grow + vc];
-    }
-
-    // K and Q fragments: block I, k-step s -> row 16 I + c, d_k 32 s + 8 g4 .. +7
-    uint4 kf[4][4], qf[4][4];
-    const uint16_t *kc = k + (size_t)c0 * H_qk * kD;
-    const uint16_t *qc = q + (size_t)c0 * H_qk * kD;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const int off = (min(16 * I + c, L - 1) * H_qk + hq) * kD + 8 * g4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            kf[I][s] = *reinterpret_cast<const uint4 *>(kc + off + 32 * s);
-            qf[I][s] = *reinterpret_cast<const uint4 *>(qc + off + 32 * s);
-        }
-    }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        const bool ok = 16 * I + c < L;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (!ok) kf[I][s] = make_uint4(0, 0, 0, 0);
-            if (!ok) qf[I][s] = make_uint4(0, 0, 0, 0);
-        }
-    }
-
-    // lower 16 x 16 tiles (J <= I); lane holds row 16 I + c, columns 16 J + 4 g4 + j:
-    //   kk[I][J] = k_{16 I + c} . k_{16 J + 4 g4 + j}   (K K^T is symmetric)
-    //   qk[I][J] = q_{16 I + c} . k_{16 J + 4 g4 + j}
-    f32x4 kk[4][4], qk[4][4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int J = 0; J <= I; ++J) {
-            kk[I][J] = f32x4{0.f, 0.f, 0.f, 0.f};
-            qk[I][J] = kk[I][J];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                kk[I][J] = mfma32(kf[J][s], kf[I][s], kk[I][J]);
-                qk[I][J] = mfma32(kf[J][s], qf[I][s], qk[I][J]);
-            }
+        for (int vv = 0; vv < kMaxGroup; ++vv) {
+            const int vc = min(vv, group - 1);
+            graw[vv] = g[grow + vc];
+            braw[vv] = beta[grow + vc];
         }
 
-#pragma unroll
-    for (int vv = 0; vv < kMaxGroup; ++vv) {
-        if (vv >= group) break;
-        const int h = hq * group + vv;
-        const float gl = lane < L ? graw[vv] : 0.f;
-        const float bl = lane < L ? braw[vv] : 0.f;
-        const float G = wave_scan(gl);
-        sG[lane] = G;
-        sBt[lane] = bl;
-        uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
-        reinterpret_cast<float *>(rec + 2 * kTileElems)[lane] = G;
-        wave_lds_sync();
-
-        // gated K K^T -> A (fp32 rows in LDS, lower tiles); gated Q K^T -> P
-        // (bf16 rows in LDS, zero above the diagonal)
+        // K and Q fragments: block I, k-step s -> row 16 I + c, d_k 32 s + 8 g4 .. +7
+        uint4 kf[4][4], qf[4][4];
+        const uint16_t *kc = k + (size_t)c0 * H_qk * kD;
+        const uint16_t *qc = q + (size_t)c0 * H_qk * kD;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const int row = 16 * I + c;
-            const float Gr = sG[row], br = sBt[row];
+            const int off = (min(16 * I + c, L - 1) * H_qk + hq) * kD + 8 * g4;
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J > I) {
-                    *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = make_uint2(0, 0);
-                    continue;
+            for (int s = 0; s < 4; ++s) {
+                kf[I][s] = *reinterpret_cast<const uint4 *>(kc + off + 32 * s);
+                qf[I][s] = *reinterpret_cast<const uint4 *>(qc + off + 32 * s);
+            }
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const bool ok = 16 * I + c < L;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (!ok) kf[I][s] = make_uint4(0, 0, 0, 0);
+                if (!ok) qf[I][s] = make_uint4(0, 0, 0, 0);
+            }
+        }
+
+        // lower 16 x 16 tiles (J <= I); lane holds row 16 I + c, columns 16 J + 4 g4 + j:
+        //   kk[I][J] = k_{16 I + c} . k_{16 J + 4 g4 + j}   (K K^T is symmetric)
+        //   qk[I][J] = q_{16 I + c} . k_{16 J + 4 g4 + j}
+        f32x4 kk[4][4], qk[4][4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                kk[I][J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                qk[I][J] = kk[I][J];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    kk[I][J] = mfma32(kf[J][s], kf[I][s], kk[I][J]);
+                    qk[I][J] = mfma32(kf[J][s], qf[I][s], qk[I][J]);
                 }
-                const float4 Gv = *reinterpret_cast<const float4 *>(sG + 16 * J + 4 * g4);
-                const float gi[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
-                float av[4], pv[4];
+            }
+
+#pragma unroll
+        for (int vv = 0; vv < kMaxGroup; ++vv) {
+            if (vv >= group) break;
+            const int h = hq * group + vv;
+            const float gl = lane < L ? graw[vv] : 0.f;
+            const float bl = lane < L ? braw[vv] : 0.f;
+            const float G = wave_scan(gl);
+            sG[lane] = G;
+            sBt[lane] = bl;
+            uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
+            __builtin_nontemporal_store(G, reinterpret_cast<float *>(rec + 2 * kTileElems) + lane);
+            wave_lds_sync();
+
+            // gated K K^T -> A (fp32 rows in LDS, lower tiles); gated Q K^T -> P
+            // (bf16 rows in LDS, zero above the diagonal)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int row = 16 * I + c;
+                const float Gr = sG[row], br = sBt[row];
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    if (J > I) {
+                        *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = make_uint2(0, 0);
+                        continue;
+                    }
+                    const float4 Gv = *reinterpret_cast<const float4 *>(sG + 16 * J + 4 * g4);
+                    const float gi[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
+                    float av[4], pv[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int col = 16 * J + 4 * g4 + j;
+                        const float e = __expf(Gr - gi[j]);
+                        av[j] = col < row ? br * e * kk[I][J][j] : 0.f;
+                        pv[j] = col <= row ? scale * e * qk[I][J][j] : 0.f;
+                    }
+                    *reinterpret_cast<float4 *>(sA + row * kAP + 16 * J + 4 * g4) = make_float4(av[0], av[1], av[2], av[3]);
+                    *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = pk4(pv[0], pv[1], pv[2], pv[3]);
+                }
+            }
+            wave_lds_sync();
+            // P out as fragment blocks
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+                const int a = qq >> 1, s = qq & 1;
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(sP + (16 * a + c) * kRP + 32 * s + 8 * g4),
+                                            reinterpret_cast<u32x4 *>(rec + kTileElems + frag_off(a, s, lane)));
+            }
+
+            float *A = sA;
+            // Diagonal 16 x 16 blocks: lane (b, c) solves column c of block b by
+            // forward substitution, T_bb = (I + A_bb)^{-1}, in fp32.
+            {
+                const int b = g4;
+                float tc[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = (r == c) ? 1.f : 0.f;
+                    const float *Ar = A + (16 * b + r) * kAP + 16 * b;
+#pragma unroll
+                    for (int i = 0; i < r; ++i) acc -= Ar[i] * tc[i];
+                    tc[r] = acc;
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int r = 0; r < 16; ++r) A[(16 * b + r) * kAP + 16 * b + c] = tc[r];
+            }
+            wave_lds_sync();
+
+            // 16 x 16 x 16 MFMA operands from the fp32 block matrix: rows of block
+            // (I, J) as an A operand, columns of block (I, J) as a B operand.
+            auto rowop = [&](int I, int J) {
+                const float *p = A + (16 * I + c) * kAP + 16 * J + 4 * g4;
+                return to_bf4(p[0], p[1], p[2], p[3]);
+            };
+            auto colop = [&](int I, int J) {
+                const float *p = A + (16 * I + 4 * g4) * kAP + 16 * J + c;
+                return to_bf4(p[0], p[kAP], p[2 * kAP], p[3 * kAP]);
+            };
+            auto accop = [](f32x4 x) { return to_bf4(x[0], x[1], x[2], x[3]); };
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+            // Off-diagonal blocks of A are read before any is overwritten by T.
+            const s16x4 a10 = rowop(1, 0), a21 = rowop(2, 1), a32 = rowop(3, 2);
+            const s16x4 a20 = rowop(2, 0), a30 = rowop(3, 0), a31 = rowop(3, 1);
+
+            // Blocks one below the diagonal: T_{I,I-1} = -T_II A_{I,I-1} T_{I-1,I-1}
+            {
+                const f32x4 y1 = mfma16(a10, colop(0, 0), z4);
+                const f32x4 y2 = mfma16(a21, colop(1, 1), z4);
+                const f32x4 y3 = mfma16(a32, colop(2, 2), z4);
+                const f32x4 t10 = -mfma16(rowop(1, 1), accop(y1), z4);
+                const f32x4 t21 = -mfma16(rowop(2, 2), accop(y2), z4);
+                const f32x4 t32 = -mfma16(rowop(3, 3), accop(y3), z4);
+                wave_lds_sync();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int col = 16 * J + 4 * g4 + j;
-                    const float e = __expf(Gr - gi[j]);
-                    av[j] = col < row ? br * e * kk[I][J][j] : 0.f;
-                    pv[j] = col <= row ? scale * e * qk[I][J][j] : 0.f;
+                    A[(16 + 4 * g4 + j) * kAP + c] = t10[j];
+                    A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21[j];
+                    A[(48 + 4 * g4 + j) * kAP + 32 + c] = t32[j];
                 }
-                *reinterpret_cast<float4 *>(sA + row * kAP + 16 * J + 4 * g4) = make_float4(av[0], av[1], av[2], av[3]);
-                *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = pk4(pv[0], pv[1], pv[2], pv[3]);
-            }
-        }
-        wave_lds_sync();
-        // P out as fragment blocks
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-            const int a = qq >> 1, s = qq & 1;
-            *reinterpret_cast<uint4 *>(rec + kTileElems + frag_off(a, s, lane)) =
-                *reinterpret_cast<const uint4 *>(sP + (16 * a + c) * kRP + 32 * s + 8 * g4);
-        }
-
-        float *A = sA;
-        // Diagonal 16 x 16 blocks: lane (b, c) solves column c of block b by
-        // forward substitution, T_bb = (I + A_bb)^{-1}, in fp32.
-        {
-            const int b = g4;
-            float tc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == c) ? 1.f : 0.f;
-                const float *Ar = A + (16 * b + r) * kAP + 16 * b;
-#pragma unroll
-                for (int i = 0; i < r; ++i) acc -= Ar[i] * tc[i];
-                tc[r] = acc;
             }
             wave_lds_sync();
+
+            // Lower-left 32 x 32 block: T_[23][01] = -T_[23] A_[23][01] T_[01]
+            {
+                const f32x4 x20 = mfma16(a21, colop(1, 0), mfma16(a20, colop(0, 0), z4));
+                const f32x4 x21 = mfma16(a21, colop(1, 1), z4);
+                const f32x4 x30 = mfma16(a31, colop(1, 0), mfma16(a30, colop(0, 0), z4));
+                const f32x4 x31 = mfma16(a31, colop(1, 1), z4);
+                const s16x4 t22 = rowop(2, 2), t32r = rowop(3, 2), t33 = rowop(3, 3);
+                const f32x4 t20 = -mfma16(t22, accop(x20), z4);
+                const f32x4 t21b = -mfma16(t22, accop(x21), z4);
+                const f32x4 t30 = -mfma16(t33, accop(x30), mfma16(t32r, accop(x20), z4));
+                const f32x4 t31 = -mfma16(t33, accop(x31), mfma16(t32r, accop(x21), z4));
+                wave_lds_sync();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) A[(16 * b + r) * kAP + 16 * b + c] = tc[r];
-        }
-        wave_lds_sync();
-
-        // 16 x 16 x 16 MFMA operands from the fp32 block matrix: rows of block
-        // (I, J) as an A operand, columns of block (I, J) as a B operand.
-        auto rowop = [&](int I, int J) {
-            const float *p = A + (16 * I + c) * kAP + 16 * J + 4 * g4;
-            return to_bf4(p[0], p[1], p[2], p[3]);
-        };
-        auto colop = [&](int I, int J) {
-            const float *p = A + (16 * I + 4 * g4) * kAP + 16 * J + c;
-            return to_bf4(p[0], p[kAP], p[2 * kAP], p[3 * kAP]);
-        };
-        auto accop = [](f32x4 x) { return to_bf4(x[0], x[1], x[2], x[3]); };
-        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-
-        // Off-diagonal blocks of A are read before any is overwritten by T.
-        const s16x4 a10 = rowop(1, 0), a21 = rowop(2, 1), a32 = rowop(3, 2);
-        const s16x4 a20 = rowop(2, 0), a30 = rowop(3, 0), a31 = rowop(3, 1);
-
-        // Blocks one below the diagonal: T_{I,I-1} = -T_II A_{I,I-1} T_{I-1,I-1}
-        {
-            const f32x4 y1 = mfma16(a10, colop(0, 0), z4);
-            const f32x4 y2 = mfma16(a21, colop(1, 1), z4);
-            const f32x4 y3 = mfma16(a32, colop(2, 2), z4);
-            const f32x4 t10 = -mfma16(rowop(1, 1), accop(y1), z4);
-            const f32x4 t21 = -mfma16(rowop(2, 2), accop(y2), z4);
-            const f32x4 t32 = -mfma16(rowop(3, 3), accop(y3), z4);
-            wave_lds_sync();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                A[(16 + 4 * g4 + j) * kAP + c] = t10[j];
-                A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21[j];
-                A[(48 + 4 * g4 + j) * kAP + 32 + c] = t32[j];
+                for (int j = 0; j < 4; ++j) {
+                    A[(32 + 4 * g4 + j) * kAP + c] = t20[j];
+                    A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21b[j];
+                    A[(48 + 4 * g4 + j) * kAP + c] = t30[j];
+                    A[(48 + 4 * g4 + j) * kAP + 16 + c] = t31[j];
+                }
             }
-        }
-        wave_lds_sync();
-
-        // Lower-left 32 x 32 block: T_[23][01] = -T_[23] A_[23][01] T_[01]
-        {
-            const f32x4 x20 = mfma16(a21, colop(1, 0), mfma16(a20, colop(0, 0), z4));
-            const f32x4 x21 = mfma16(a21, colop(1, 1), z4);
-            const f32x4 x30 = mfma16(a31, colop(1, 0), mfma16(a30, colop(0, 0), z4));
-            const f32x4 x31 = mfma16(a31, colop(1, 1), z4);
-            const s16x4 t22 = rowop(2, 2), t32r = rowop(3, 2), t33 = rowop(3, 3);
-            const f32x4 t20 = -mfma16(t22, accop(x20), z4);
-            const f32x4 t21b = -mfma16(t22, accop(x21), z4);
-            const f32x4 t30 = -mfma16(t33, accop(x30), mfma16(t32r, accop(x20), z4));
-            const f32x4 t31 = -mfma16(t33, accop(x31), mfma16(t32r, accop(x21), z4));
             wave_lds_sync();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                A[(32 + 4 * g4 + j) * kAP + c] = t20[j];
-                A[(32 + 4 * g4 + j) * kAP + 16 + c] = t21b[j];
-                A[(48 + 4 * g4 + j) * kAP + c] = t30[j];
-                A[(48 + 4 * g4 + j) * kAP + 16 + c] = t31[j];
-            }
-        }
-        wave_lds_sync();
 
-        // T' = T diag(b) (zero above the diagonal blocks) out as fragment blocks
+            // T' = T diag(b) (zero above the diagonal blocks) out as fragment blocks
 #pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-            const int a = qq >> 1, s = qq & 1;
-            const int row = 16 * a + c, ca = 32 * s + 8 * g4, cb = ca + 4;
-            const float4 t0 = *reinterpret_cast<const float4 *>(A + row * kAP + ca);
-            const float4 t1 = *reinterpret_cast<const float4 *>(A + row * kAP + cb);
-            const float4 b0 = *reinterpret_cast<const float4 *>(sBt + ca);
-            const float4 b1 = *reinterpret_cast<const float4 *>(sBt + cb);
-            const bool la = (ca >> 4) <= a, lb = la;   // 8 columns in one 16-column block
-            const uint2 u0 = la ? pk4(t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w) : make_uint2(0, 0);
-            const uint2 u1 = lb ? pk4(t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w) : make_uint2(0, 0);
-            *reinterpret_cast<uint4 *>(rec + frag_off(a, s, lane)) = make_uint4(u0.x, u0.y, u1.x, u1.y);
+            for (int qq = 0; qq < 8; ++qq) {
+                const int a = qq >> 1, s = qq & 1;
+                const int row = 16 * a + c, ca = 32 * s + 8 * g4, cb = ca + 4;
+                const float4 t0 = *reinterpret_cast<const float4 *>(A + row * kAP + ca);
+                const float4 t1 = *reinterpret_cast<const float4 *>(A + row * kAP + cb);
+                const float4 b0 = *reinterpret_cast<const float4 *>(sBt + ca);
+                const float4 b1 = *reinterpret_cast<const float4 *>(sBt + cb);
+                const bool la = (ca >> 4) <= a, lb = la;   // 8 columns in one 16-column block
+                const uint2 u0 = la ? pk4(t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w) : make_uint2(0, 0);
+                const uint2 u1 = lb ? pk4(t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w) : make_uint2(0, 0);
+                __builtin_nontemporal_store(u32x4{u0.x, u0.y, u1.x, u1.y},
+                                            reinterpret_cast<u32x4 *>(rec + frag_off(a, s, lane)));
+            }
+            wave_lds_sync();                 // T read before the next V-head's A is written
         }
-        wave_lds_sync();                 // T read before the next V-head's A is written
     }
 }
 
@@ -403,7 +423,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    const uint16_t *__restrict__ ws, uint16_t *__restrict__ o) {
+    int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *__restrict__ o) {
     __shared__ __attribute__((aligned(16))) uint16_t sS[kSlabW * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sU[kSlabW * kRP];
@@ -425,7 +445,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const int w = wave & 3;
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c = lane & 15;
     const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
-    const int nchunks = (s1 - s0 + kChunk - 1) / kChunk;
+    // chunks [c_lo, c_end) of the sequence: the state enters as initial_state
+    // and leaves as final_state, so a sequence can be scanned in segments
+    const int c_end = min((s1 - s0 + kChunk - 1) / kChunk, c_hi);
     const int cbase = chunk_base[n];
     const int e0 = kSlabW * slab;           // first d_v column of the slab
     const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
@@ -465,7 +487,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                         pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
         };
         auto fetch_a = [&](int ci, StateRegs &R) {
-            ci = min(ci, nchunks - 1);
+            ci = min(ci, c_end - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) R.kr[i] = *reinterpret_cast<const u32x4 *>(k + krow_off(ci, i));
             const uint16_t *rec = rec_of(ci);
@@ -474,7 +496,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 R.tA[s] = *reinterpret_cast<const u32x4 *>(rec + frag_off(w, s, lane));
         };
         auto fetch_b = [&](int ci, StateRegs &R) {
-            ci = min(ci, nchunks - 1);
+            ci = min(ci, c_end - 1);
             const float *Gp = reinterpret_cast<const float *>(rec_of(ci) + 2 * kTileElems);
             R.G4 = *reinterpret_cast<const float4 *>(Gp + 16 * w + 4 * g4);
             R.GL = Gp[kChunk - 1];
@@ -568,18 +590,18 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
         write_state_lds();
         StateRegs r0, r1, r2;
-        if (nchunks > 0) {
-            fetch_a(0, r0);
-            fetch_b(0, r0);
-            fetch_a(1, r1);
-            fetch_b(1, r1);
+        if (c_lo < c_end) {
+            fetch_a(c_lo, r0);
+            fetch_b(c_lo, r0);
+            fetch_a(c_lo + 1, r1);
+            fetch_b(c_lo + 1, r1);
         }
         __syncthreads();
-        for (int ci = 0; ci < nchunks; ci += 3) {
+        for (int ci = c_lo; ci < c_end; ci += 3) {
             body(ci, r0, r2);
-            if (ci + 1 >= nchunks) break;
+            if (ci + 1 >= c_end) break;
             body(ci + 1, r1, r0);
-            if (ci + 2 >= nchunks) break;
+            if (ci + 2 >= c_end) break;
             body(ci + 2, r2, r1);
         }
         if (final_state) {
@@ -593,7 +615,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
     } else {
         // ---------------- output waves
         auto fetch = [&](int ci, OutRegs &R) {
-            ci = min(ci, nchunks - 1);
+            ci = min(ci, c_end - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) R.qr[i] = *reinterpret_cast<const u32x4 *>(q + krow_off(ci, i));
             const uint16_t *rec = rec_of(ci);
@@ -643,16 +665,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
             __syncthreads();                                   // (3)
         };
         OutRegs r0, r1, r2;
-        if (nchunks > 0) {
-            fetch(0, r0);
-            fetch(1, r1);
+        if (c_lo < c_end) {
+            fetch(c_lo, r0);
+            fetch(c_lo + 1, r1);
         }
         __syncthreads();                                       // matches the state waves' first barrier
-        for (int ci = 0; ci < nchunks; ci += 3) {
+        for (int ci = c_lo; ci < c_end; ci += 3) {
             body(ci, r0, r2);
-            if (ci + 1 >= nchunks) break;
+            if (ci + 1 >= c_end) break;
             body(ci + 1, r1, r0);
-            if (ci + 2 >= nchunks) break;
+            if (ci + 2 >= c_end) break;
             body(ci + 2, r2, r1);
         }
     }
@@ -660,13 +682,76 @@ __global__ __launch_bounds__(512) void scan_kernel(
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// A single sequence leaves CUs idle during the scan (one workgroup per
+// (V-head, slab)).  Its chunks are then split into segments: the prep of
+// segment i + 1 runs on the idle CUs, on an auxiliary stream, while segment i
+// is scanned; only the first segment's prep runs alone.  The prep on the idle
+// CUs takes about 0.85 of the scan's time per chunk, so segment i holds a
+// share of the chunks proportional to kSegGrowth^i (a little below 1 / 0.85,
+// to leave room for the event hand-over), with the count chosen so that the
+// first segment is at most about kFirstSegChunks long.
+constexpr int kMaxSegments = 12;
+constexpr double kSegGrowth = 1.1;
+constexpr int kFirstSegChunks = 128;
+constexpr int kSegMinChunks = 64;     // shorter sequences are not split
+constexpr int kMinIdleCUs = 32;       // fewer idle CUs: not split
+
+// Segment bounds b[0] = 0 < b[1] < ... < b[count] = nch; returns count.
+int segment_bounds(int nch, int *b) {
+    int count = 2;
+    double wsum = 1.0 + kSegGrowth, wnext = kSegGrowth * kSegGrowth;
+    while (count < kMaxSegments && nch / wsum > kFirstSegChunks) {
+        wsum += wnext;
+        wnext *= kSegGrowth;
+        ++count;
+    }
+    double w = 1.0, acc = 0.0;
+    b[0] = 0;
+    for (int i = 1; i < count; ++i, w *= kSegGrowth) {
+        acc += w;
+        b[i] = max(b[i - 1] + 1, (int)(nch * acc / wsum));
+    }
+    b[count] = nch;
+    return count;
+}
+
+struct DeviceAux {           // per device, created on first use, never destroyed
+    bool tried = false, ok = false;
+    int cus = 0;
+    hipStream_t stream = nullptr;
+    hipEvent_t ev[kMaxSegments] = {};
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu;         // guards g_aux and every enqueue on an auxiliary stream
+DeviceAux g_aux[kMaxDevices];
+
+// The current device's auxiliary stream (default priority) and events, or
+// nullptr if they cannot be made.  Caller holds g_aux_mu.
+DeviceAux *device_aux() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    DeviceAux &a = g_aux[dev];
+    if (!a.tried) {
+        a.tried = true;
+        bool ok = hipDeviceGetAttribute(&a.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                  hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; ok && i < kMaxSegments; ++i)
+            ok = hipEventCreateWithFlags(&a.ev[i], hipEventDisableTiming | hipEventReleaseToDevice) ==
+                 hipSuccess;
+        a.ok = ok;
+    }
+    return a.ok ? &a : nullptr;
+}
+
 }  // namespace
 
 size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v) {
     (void)H_qk;
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
+    // chunk offsets | chunk records | (one sequence) state carried between segments
     return align256((size_t)(N + 1) * sizeof(int32_t)) +
-           max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);
+           max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t) +
+           (N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0);
 }
 
 hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -677,19 +762,61 @@ hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, c
     int32_t *chunk_base = static_cast<int32_t *>(workspace);
     uint16_t *ws = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
                                                 align256((size_t)(N + 1) * sizeof(int32_t)));
+    const auto *q16 = static_cast<const uint16_t *>(q);
+    const auto *k16 = static_cast<const uint16_t *>(k);
+    const auto *v16 = static_cast<const uint16_t *>(v);
+    auto *o16 = static_cast<uint16_t *>(o);
+    const int scan_grid = N * H_v * kSlabsW;
+    auto prep = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
+        const int items = (c_hi - c_lo) * H_qk;
+        const int grid = min((items + kPrepWaves - 1) / kPrepWaves, max_grid);
+        hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(64 * kPrepWaves), 0, s, q16, k16, g, beta,
+                           cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo * H_qk,
+                           c_hi * H_qk, ws);
+        return hipGetLastError();
+    };
+    auto scan = [&](int c_lo, int c_hi, const float *init, float *fin) {
+        hipLaunchKernelGGL(scan_kernel, dim3(scan_grid), dim3(512), 0, stream, q16, k16, v16, init,
+                           fin, cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo, c_hi, ws, o16);
+        return hipGetLastError();
+    };
+
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, chunk_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)max_chunks, H_qk), dim3(64), 0, stream,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), g, beta,
-                       cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_kernel, dim3(N * H_v * kSlabsW), dim3(512), 0, stream,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                       static_cast<const uint16_t *>(v), S0, S_final, cu_seqlens, chunk_base, N, T,
-                       H_qk, H_v, scale, ws, static_cast<uint16_t *>(o));
-    return hipGetLastError();
+
+    // one sequence (cu_seqlens, if given, is {0, T}): nch chunks known on the host
+    const int nch = (T + kChunk - 1) / kChunk;
+    std::unique_lock<std::mutex> lock(g_aux_mu);
+    DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux() : nullptr;
+    const int idle = aux ? aux->cus - scan_grid : 0;
+    if (idle < kMinIdleCUs) {
+        lock.unlock();
+        const int all = (int)max_chunks;
+        if ((e = prep(0, all, (all * H_qk + kPrepWaves - 1) / kPrepWaves, stream)) != hipSuccess) return e;
+        return scan(0, all, S0, S_final);
+    }
+
+    // The state passes from segment to segment through final_state, or the
+    // workspace's carry area when the caller wants no final state.  The last
+    // wait joins the auxiliary stream back into the caller's stream.
+    float *carry = S_final ? S_final
+                           : reinterpret_cast<float *>(ws + max_chunks * (size_t)H_v * kRecElems);
+    int b[kMaxSegments + 1];
+    const int nseg = segment_bounds(nch, b);
+    if ((e = prep(b[0], b[1], INT32_MAX, stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(aux->ev[0], stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(aux->stream, aux->ev[0], 0)) != hipSuccess) return e;
+    for (int i = 1; i < nseg; ++i) {
+        if ((e = prep(b[i], b[i + 1], idle, aux->stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->ev[i], aux->stream)) != hipSuccess) return e;
+    }
+    for (int i = 0; i < nseg; ++i) {
+        if (i > 0 && (e = hipStreamWaitEvent(stream, aux->ev[i], 0)) != hipSuccess) return e;
+        if ((e = scan(b[i], b[i + 1], i == 0 ? S0 : carry, i == nseg - 1 ? S_final : carry)) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdn

@@ -69,9 +69,9 @@ def test_bf16_varlen_mid_chunk_boundaries():
 
 def test_bf16_split_handoff():
     """A prefill split at token s with the final state handed over equals the
-    unsplit run to the bf16 bar (the chunked kernels form the first chunk's
-    K S^T directly but later chunks through the chunk-to-chunk lookahead, so
-    even chunk-aligned splits round differently)."""
+    unsplit run: bit for bit at a chunk boundary (the fp32 state passes
+    through memory unchanged), to the bf16 bar inside a chunk (the chunking of
+    the rest moves)."""
     p = synth.direct_prefill(4300, T=700, init_state=True)
     o, S = _prefill(p)
     for s in (512, 333):
@@ -84,6 +84,8 @@ def test_bf16_split_handoff():
         ob, Sb = _prefill(b)
         assert_close(np.concatenate([oa, ob]), o, TOL_BF16, f"o split at {s}")
         assert_close(Sb, S, TOL_BF16, f"S split at {s}")
+        if s % 64 == 0:
+            assert np.array_equal(np.concatenate([oa, ob]), o) and np.array_equal(Sb, S)
 
 
 def test_bf16_deterministic_and_inplace_state():
@@ -117,6 +119,45 @@ def test_prefill_equals_decode_steps():
     torch.cuda.synchronize()
     assert_close(np.concatenate(outs), o, TOL_BF16, "o")
     assert_close(pool.cpu().numpy(), S, TOL_BF16, "S")
+
+
+def test_bf16_long_sequence_segments():
+    """One sequence of 65 chunks (ragged tail) is prepared and scanned in
+    segments, the prep of each segment overlapping the scan of the one before.
+    Checked against the oracle on every head and token; bit-identical to the
+    same sequence run as chained calls split at chunk boundaries (each too
+    short to be segmented: the state hand-off at a chunk boundary is exact),
+    with no final state asked for, and with the state updated in place."""
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    nch = 65
+    p = synth.direct_prefill(4600, T=64 * (nch - 1) + 37, init_state=True)
+    print("segmented prefill T", p.T, flush=True)
+    o, S = _prefill(p)
+    o_ref, S_ref = oracle.recurrent(p.q, p.k, p.v, p.g, p.beta, p.S0)
+    assert_close(o, o_ref, TOL_BF16, "o")
+    assert_close(S, S_ref, TOL_BF16, "S")
+
+    bounds = [0, 64 * 20, 64 * 41, 64 * 50, p.T]   # chunk-aligned, unlike the segments
+    St, outs = p.S0, []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        part = synth.Prefill(T=b - a, N=1, H_qk=p.H_qk, H_v=p.H_v, dk=p.dk, dv=p.dv, io="bf16",
+                             g=p.g[a:b], beta=p.beta[a:b], q=p.q[a:b], k=p.k[a:b], v=p.v[a:b],
+                             S0=St)
+        oi, Si = _prefill(part)
+        outs.append(oi)
+        St = Si.astype(np.float32)
+    assert np.array_equal(np.concatenate(outs), o)
+    assert np.array_equal(St, S.astype(np.float32))
+
+    args = (dev(p.q), dev(p.k), dev(p.v), dev(p.g), dev(p.beta))
+    o2, none = gdn.gdn_prefill(*args, dev(p.S0), final_state=None)
+    st = dev(p.S0)
+    o3, S3 = gdn.gdn_prefill(*args, st, final_state=st)
+    torch.cuda.synchronize()
+    assert none is None and S3 is st
+    assert np.array_equal(host(o2), o) and np.array_equal(host(o3), o)
+    assert np.array_equal(st.cpu().numpy(), S.astype(np.float32))
 
 
 def _sampled_heads_end_to_end(p, heads, what):
