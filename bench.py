@@ -3,10 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 A step is one pass of the layer's prefill path over one batch of synthetic
-input: the conv/SiLU/L2 prelude on raw bf16 projections followed by the
-chunked prefill (plan, prep and scan kernels), for one sequence of 32768
-tokens with 16 QK heads, 48 V heads and d_k = d_v = 128.  `value` is prefill
-tokens/s over the K timed steps.  The decode side of the metric (one decode
+input: the conv/SiLU/L2 prelude on raw bf16 projections and the chunked
+prefill, for one sequence of 32768 tokens with 16 QK heads, 48 V heads and
+d_k = d_v = 128, as one gdn_prefill_raw call (prelude fused into the prefill's
+plan, prep and scan kernels).  `value` is prefill tokens/s over the K timed
+steps.  The same step as two calls (gdn_conv_prelude, then gdn_prefill) is
+timed beside it and reported under "phases_us".  `--path fused|unfused`
+times one of the two only (for profiling runs).  The decode side of the metric (one decode
 step for 256 sequences over a 256-slot state pool) is timed in the same run
 and reported under "decode".  Every input is generated and resident in HBM
 before the timed regions start; timing uses HIP events on the stream the
@@ -93,7 +96,7 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def run_gpu(steps, warmup):
+def run_gpu(steps, warmup, path="both"):
     import torch
     import linear_attention_sequence_delta_amd as gdn
     import synth
@@ -112,38 +115,61 @@ def run_gpu(steps, warmup):
     p = synth.workload_prefill_32k(T_PREFILL)
     x, w = to_dev(p.x), to_dev(p.w)
     g, beta = to_dev(p.g), to_dev(p.beta)
-    q = torch.empty((p.T, H_QK, D), dtype=torch.bfloat16, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
     o = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
     fs = torch.empty((1, H_V, D, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, p.T, H_QK, H_V),
-                     dtype=torch.uint8, device=dev)
+    res = {}
 
-    def prelude():
-        gdn.gdn_conv_prelude(x, w, None, H_qk=H_QK, H_v=H_V, out=(q, k, v))
+    if path in ("both", "fused"):
+        wsr = torch.empty(gdn.gdn_prefill_raw_workspace_size(1, p.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
 
-    def prefill():
-        gdn.gdn_prefill(q, k, v, g, beta, None, None, final_state=fs, o=o, workspace=ws)
+        def fused():
+            gdn.gdn_prefill_raw(x, w, g, beta, None, None, H_qk=H_QK, H_v=H_V,
+                                final_state=fs, o=o, workspace=wsr)
 
-    for _ in range(warmup):
-        prelude()
-        prefill()
-    torch.cuda.synchronize()
-    ev = [(_events(torch), _events(torch)) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for (a0, a1), (b0, b1) in ev:
-        a0.record()
-        prelude()
-        a1.record()
-        b0.record()
-        prefill()
-        b1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_us = sum(a0.elapsed_time(a1) for (a0, a1), _ in ev) / steps * 1e3
-    pf_us = sum(b0.elapsed_time(b1) for _, (b0, b1) in ev) / steps * 1e3
-    step_ms = wall / steps * 1e3
+        for _ in range(warmup):
+            fused()
+        torch.cuda.synchronize()
+        ev = [_events(torch) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a0, a1 in ev:
+            a0.record()
+            fused()
+            a1.record()
+        torch.cuda.synchronize()
+        res["wall_fused"] = (time.perf_counter() - t0) / steps * 1e6
+        res["fused_us"] = sum(a0.elapsed_time(a1) for a0, a1 in ev) / steps * 1e3
+        del wsr
+
+    if path in ("both", "unfused"):
+        q = torch.empty((p.T, H_QK, D), dtype=torch.bfloat16, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, p.T, H_QK, H_V),
+                         dtype=torch.uint8, device=dev)
+
+        def prelude():
+            gdn.gdn_conv_prelude(x, w, None, H_qk=H_QK, H_v=H_V, out=(q, k, v))
+
+        def prefill():
+            gdn.gdn_prefill(q, k, v, g, beta, None, None, final_state=fs, o=o, workspace=ws)
+
+        for _ in range(warmup):
+            prelude()
+            prefill()
+        torch.cuda.synchronize()
+        ev = [(_events(torch), _events(torch)) for _ in range(steps)]
+        for (a0, a1), (b0, b1) in ev:
+            a0.record()
+            prelude()
+            a1.record()
+            b0.record()
+            prefill()
+            b1.record()
+        torch.cuda.synchronize()
+        res["pre_us"] = sum(a0.elapsed_time(a1) for (a0, a1), _ in ev) / steps * 1e3
+        res["pf_us"] = sum(b0.elapsed_time(b1) for _, (b0, b1) in ev) / steps * 1e3
+        del q, k, v, ws
 
     # ---------------- decode workload: B = 256 over rotating 256-slot pools
     d = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
@@ -151,6 +177,7 @@ def run_gpu(steps, warmup):
     dq, dk, dv_, dg, db = (to_dev(a) for a in (d.q, d.k, d.v, d.g, d.beta))
     slots = to_dev(d.slot_idx)
     od = torch.empty((B_DECODE, H_V, D), dtype=torch.bfloat16, device=dev)
+    del x, o
     dsteps = max(steps * 4, 8)
     for i in range(max(warmup, 2)):
         gdn.gdn_decode_step(dq, dk, dv_, dg, db, pools[i % 2], slots, o=od)
@@ -163,7 +190,8 @@ def run_gpu(steps, warmup):
     torch.cuda.synchronize()
     dec_us = e0.elapsed_time(e1) / dsteps * 1e3
 
-    return dict(pre_us=pre_us, pf_us=pf_us, step_ms=step_ms, dec_us=dec_us)
+    res["dec_us"] = dec_us
+    return res
 
 
 def run_longctx():
@@ -185,27 +213,36 @@ def run_longctx():
     p = synth.workload_longctx_prefill(T_LONG)
     x, w, g, beta = to_dev(p.x), to_dev(p.w), to_dev(p.g), to_dev(p.beta)
     del p.x
+    o = torch.empty((T_LONG, H_V, D), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((1, H_V, D, D), dtype=torch.float32, device=dev)
+    e0, e1 = _events(torch)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
     q = torch.empty((T_LONG, H_QK, D), dtype=torch.bfloat16, device=dev)
     k = torch.empty_like(q)
     v = torch.empty((T_LONG, H_V, D), dtype=torch.bfloat16, device=dev)
-    o = torch.empty((T_LONG, H_V, D), dtype=torch.bfloat16, device=dev)
-    fs = torch.empty((1, H_V, D, D), dtype=torch.float32, device=dev)
     ws = torch.empty(gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, 1, T_LONG, H_QK, H_V),
                      dtype=torch.uint8, device=dev)
 
-    def layer():
+    def two_calls():
         gdn.gdn_conv_prelude(x, w, None, H_qk=H_QK, H_v=H_V, out=(q, k, v))
         gdn.gdn_prefill(q, k, v, g, beta, None, None, final_state=fs, o=o, workspace=ws)
 
-    layer()
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    layer()
-    e1.record()
-    torch.cuda.synchronize()
-    pre_us = e0.elapsed_time(e1) * 1e3
-    del x, q, k, v, o, ws
+    unfused_us = timed(two_calls)
+    del q, k, v, ws
+    wsr = torch.empty(gdn.gdn_prefill_raw_workspace_size(1, T_LONG, H_QK, H_V),
+                      dtype=torch.uint8, device=dev)
+    pre_us = timed(lambda: gdn.gdn_prefill_raw(x, w, g, beta, None, None, H_qk=H_QK, H_v=H_V,
+                                               final_state=fs, o=o, workspace=wsr))
+    del x, o, wsr
 
     # hand-off: 256 sequences continue from the prefill's final state
     pool = fs[0].unsqueeze(0).expand(B_DECODE, -1, -1, -1).contiguous()
@@ -257,7 +294,9 @@ def run_longctx():
     torch.cuda.synchronize()
     stack_ms = e0.elapsed_time(e1) / tokens
     return {"prefill": {"T": T_LONG, "us": pre_us, "tokens_per_s": T_LONG / (pre_us * 1e-6),
-                        "what": "conv prelude + chunked prefill of one 262144-token sequence"},
+                        "what": "conv prelude fused into the chunked prefill (gdn_prefill_raw), "
+                                "one 262144-token sequence",
+                        "two_calls_us": unfused_us},
             "decode": {"B": B_DECODE, "steps": LONG_STEPS, "us_per_step": dec_us,
                        "tokens_per_s": B_DECODE / (dec_us * 1e-6),
                        "what": "256 sequences continuing from the prefill's final state"},
@@ -304,6 +343,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-longctx", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--path", choices=("both", "fused", "unfused"), default="both")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer shards by "
@@ -318,15 +358,25 @@ def main():
         from linear_attention_sequence_delta_amd import build as _b
         _b.build()
 
-    r = run_gpu(args.steps, args.warmup)
+    r = run_gpu(args.steps, args.warmup, args.path)
     T = T_PREFILL
-    step_us = r["pre_us"] + r["pf_us"]
+    fused = "fused_us" in r
+    # the timed step and the call the roofline is for
+    step_us = r["fused_us"] if fused else r["pre_us"] + r["pf_us"]
+    call_us = r["fused_us"] if fused else r["pf_us"]
     flops = PREFILL_FLOP_PER_TOKEN * T
-    achieved_tflops = flops / (r["pf_us"] * 1e-6) / 1e12
-    traffic = _traffic_bytes()
-    issued = _issued_mfma_flops()
+    achieved_tflops = flops / (call_us * 1e-6) / 1e12
+    traffic = _traffic_bytes() if fused else None
+    issued = _issued_mfma_flops() if fused else None
     pre_bytes = PRELUDE_BYTES_PER_TOKEN * T
     dec_bytes = DECODE_BYTES_PER_SEQ * B_DECODE
+    phases = {}
+    if fused:
+        phases["fused_call"] = r["fused_us"]
+        phases["fused_wall_per_call"] = r["wall_fused"]
+    if "pre_us" in r:
+        phases.update({"prelude": r["pre_us"], "prefill": r["pf_us"],
+                       "two_calls": r["pre_us"] + r["pf_us"]})
     out = {
         "metric": "GDN layer tokens/s (prefill T=32K; decode B=256) + % of MFMA/HBM roofline",
         "value": T / (step_us * 1e-6),
@@ -344,20 +394,18 @@ def main():
         "config": {"workload": "prefill of one 32768-token sequence from raw bf16 projections "
                                "(conv prelude + chunked prefill), 16 QK / 48 V heads, d=128, "
                                "chunk 64, fp32 state",
-                   "T": T, "H_qk": H_QK, "H_v": H_V, "d_k": D, "d_v": D, "chunk": CHUNK},
+                   "T": T, "H_qk": H_QK, "H_v": H_V, "d_k": D, "d_v": D, "chunk": CHUNK,
+                   "entry": "gdn_prefill_raw" if fused else "gdn_conv_prelude + gdn_prefill"},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "gdn_prefill (plan + prep + scan kernels)",
+                     "kernel": ("gdn_prefill_raw (plan + prep + scan kernels, prelude fused)"
+                                if fused else "gdn_prefill (plan + prep + scan kernels)"),
                      "algorithmic_flop_per_launch": flops,
                      "issued_mfma_flop_per_launch": issued,
                      "issued_frac": (None if issued is None else
-                                     issued / (r["pf_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS)},
-        "phases_us": {"prelude": r["pre_us"], "prefill": r["pf_us"],
-                      "wall_per_step": r["step_ms"] * 1e3},
-        "prelude_roofline": {"bound": "hbm", "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
-                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                             "frac": pre_bytes / (r["pre_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+                                     issued / (call_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS)},
+        "phases_us": phases,
         "decode": {"value": B_DECODE / (r["dec_us"] * 1e-6), "unit": "tokens/s",
                    "us_per_step": r["dec_us"],
                    "workload": "one decode step of 256 sequences, 16 QK / 48 V heads, fp32 "
@@ -367,6 +415,11 @@ def main():
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}},
     }
+    if "pre_us" in r:
+        out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",
+                                   "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
+                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                   "frac": pre_bytes / (r["pre_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}
     if not args.no_longctx:
         out["longctx"] = run_longctx()
     if not args.no_cpu_baseline:

@@ -130,6 +130,35 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
                 float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * gdn_prefill_raw_workspace_size -- bytes of device workspace gdn_prefill_raw
+ * needs (host-only; 0 when T = 0).  Bounds the chunk count as
+ * gdn_prefill_workspace_size does; about 1.7 times its bf16 figure (the
+ * normalised q and k rows are kept there as well).
+ */
+size_t gdn_prefill_raw_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v);
+
+/*
+ * gdn_prefill_raw -- the layer's prefill from its raw projections: the conv
+ * prelude ([Dissect sec. 2.1]: width-4 causal depthwise conv, SiLU, L2 norm of
+ * each q and k head) fused into the bf16 chunked prefill ([Dissect sec. 2.2],
+ * gated by a_t = exp(g_t)).  The result is bit-identical to gdn_conv_prelude
+ * followed by gdn_prefill(GDN_BF16, ...) on the same arguments; the
+ * normalised q, k and the v that pass between the two are never written out
+ * (q and k go through the workspace once, v stays on chip).
+ *
+ *   x_raw, conv_w, l2_eps   as for gdn_conv_prelude (bf16 [T][C_raw], bf16 [C_raw][4])
+ *   g, beta, initial_state, final_state, cu_seqlens, scale, o
+ *                           as for gdn_prefill with io_dtype GDN_BF16 (o is bf16
+ *                           [T][H_v][d_v]; at most 8 V-heads per QK head)
+ *   workspace      device scratch of at least gdn_prefill_raw_workspace_size(...)
+ *                  bytes (may be NULL when that size is 0); contents on entry ignored
+ */
+int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
+                    const float *beta, const float *initial_state, float *final_state,
+                    const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                    float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * gdn_decode_step -- one token for each of B sequences whose states live in a
  * slot pool; each addressed state is read once and overwritten in place.
  * [OOM sec. 1.2] per-token step (q, k, v, S_prev, gates) -> (o, S); the update

@@ -28,7 +28,8 @@ GDN_F32 = 0
 GDN_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
-           "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step")
+           "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_raw_workspace_size",
+           "gdn_prefill_raw", "gdn_decode_step")
 
 _lib = None
 
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_workspace_size.restype = Z
     L.gdn_prefill.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
     L.gdn_prefill.restype = I
+    L.gdn_prefill_raw_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_prefill_raw_workspace_size.restype = Z
+    L.gdn_prefill_raw.argtypes = [P, P, F, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
+    L.gdn_prefill_raw.restype = I
     L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_decode_step.restype = I
     _lib = L
@@ -210,6 +215,65 @@ def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale:
     return o, fs
 
 
+def gdn_prefill_raw_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
+                                   d_v: int = 128) -> int:
+    return int(lib().gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+
+
+def gdn_prefill_raw(x, conv_w, g, beta, initial_state=None, cu_seqlens=None, *, H_qk: int = 16,
+                    H_v: int = 48, d_k: int = 128, d_v: int = 128, l2_eps: float = 1e-6,
+                    scale: float = 1.0, final_state=True, o=None, workspace=None):
+    """Prefill from the raw projections, conv prelude fused.  x: bf16 [T, C_raw];
+    conv_w: bf16 [C_raw, 4]; g, beta: fp32 [T, H_v]; initial_state: fp32
+    [N, H_v, 128, 128] or None; final_state as for gdn_prefill.  Returns
+    (o bf16 [T, H_v, d_v], final_state or None)."""
+    torch = _torch()
+    dev = _device_of(x)
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, dev, 2)
+    T = x.shape[0]
+    if x.shape[1] != 2 * H_qk * d_k + H_v * d_v or tuple(conv_w.shape) != (x.shape[1], 4):
+        raise ValueError("x / conv_w shapes do not match the head configuration")
+    _need(g, "g", torch.float32, dev, 2)
+    _need(beta, "beta", torch.float32, dev, 2)
+    if tuple(g.shape) != (T, H_v) or tuple(beta.shape) != (T, H_v):
+        raise ValueError("g and beta must be [T, H_v]")
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    sshape = (N, H_v, d_v, d_k)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev, 4)
+        if tuple(initial_state.shape) != sshape:
+            raise ValueError(f"initial_state must be {sshape}")
+    if final_state is True:
+        fs = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif final_state is None or final_state is False:
+        fs = None
+    else:
+        fs = final_state
+        _need(fs, "final_state", torch.float32, dev, 4)
+        if tuple(fs.shape) != sshape:
+            raise ValueError(f"final_state must be {sshape}")
+    if o is None:
+        o = torch.empty((T, H_v, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(o, "o", torch.bfloat16, dev, 3)
+        if tuple(o.shape) != (T, H_v, d_v):
+            raise ValueError("o must be [T, H_v, d_v]")
+    ws_need = gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_prefill_raw(_ptr(x), _ptr(conv_w), float(l2_eps), _ptr(g), _ptr(beta),
+                               _ptr(initial_state), _ptr(fs), _ptr(cu_seqlens), N, T, H_qk, H_v,
+                               d_k, d_v, float(scale), _ptr(o), _ptr(workspace), ws_bytes,
+                               _stream(dev))
+    _check(rc, "gdn_prefill_raw")
+    return o, fs
+
+
 def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.0, o=None):
     """One token per sequence; states in state_pool[slot_idx[b]] advance in place.
     q, k: bf16 [B, H_qk, 128]; v: bf16 [B, H_v, 128]; g, beta: fp32 [B, H_v];
@@ -241,4 +305,5 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.
 
 
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
-           "gdn_prefill_workspace_size", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]
+           "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
+           "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

@@ -122,7 +122,7 @@ size_t gdn_prefill_workspace_size(int io_dtype, int N, int T, int H_qk, int H_v,
     (void)d_k;
     (void)d_v;
     if (io_dtype != GDN_BF16 || N < 1 || T < 1 || H_qk < 1 || H_v < 1) return 0;
-    return gdn::chunked_workspace_bytes(N, T, H_qk, H_v);
+    return gdn::chunked_workspace_bytes(N, T, H_qk, H_v, false);
 }
 
 int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const float *g,
@@ -165,13 +165,72 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
     hipError_t e;
-    if (io_dtype == GDN_F32)
-        e = gdn::launch_recurrent_prefill(gdn::kIoF32, q, k, v, g, beta, initial_state,
-                                          final_state, cu_seqlens, N, T, H_qk, H_v, scale, o, s);
+    if (io_dtype == GDN_F32 || T == 0)   // T = 0: only the final state (no workspace)
+        e = gdn::launch_recurrent_prefill(io_dtype == GDN_F32 ? gdn::kIoF32 : gdn::kIoBF16, q, k,
+                                          v, g, beta, initial_state, final_state, cu_seqlens, N,
+                                          T, H_qk, H_v, scale, o, s);
     else
         e = gdn::launch_chunked_prefill(q, k, v, g, beta, initial_state, final_state, cu_seqlens,
                                         N, T, H_qk, H_v, scale, o, workspace, s);
     return finish(e, s, "gdn_prefill launch");
+}
+
+size_t gdn_prefill_raw_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (N < 1 || T < 1 || H_qk < 1 || H_v < 1) return 0;
+    return gdn::chunked_workspace_bytes(N, T, H_qk, H_v, true);
+}
+
+int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
+                    const float *beta, const float *initial_state, float *final_state,
+                    const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                    float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps))
+        return fail(GDN_ERR_INVALID_ARG, "l2_eps must be finite and >= 0");
+    if (H_v / H_qk > gdn::kMaxPrepGroup)
+        return fail(GDN_ERR_UNSUPPORTED, "bf16 prefill supports at most %d V-heads per QK head (got %d)",
+                    gdn::kMaxPrepGroup, H_v / H_qk);
+    const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
+    const size_t nx = (size_t)T * craw * 2, nw = craw * 4 * 2, nv = (size_t)T * H_v * gdn::kD * 2;
+    const size_t ng = (size_t)T * H_v * 4, ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
+    if (T > 0 && (!x_raw || !conv_w || !g || !beta || !o))
+        return fail(GDN_ERR_INVALID_ARG, "x_raw, conv_w, g, beta and o must be non-NULL");
+    if (overlaps(o, nv, x_raw, nx) || overlaps(o, nv, conv_w, nw) || overlaps(o, nv, g, ng) ||
+        overlaps(o, nv, beta, ng) || overlaps(o, nv, initial_state, ns) ||
+        overlaps(o, nv, final_state, ns))
+        return fail(GDN_ERR_INVALID_ARG, "o must not overlap any input or state");
+    if (final_state && initial_state && final_state != initial_state &&
+        overlaps(final_state, ns, initial_state, ns))
+        return fail(GDN_ERR_INVALID_ARG, "final_state must equal initial_state or not overlap it");
+    if (final_state && (overlaps(final_state, ns, x_raw, nx) || overlaps(final_state, ns, conv_w, nw) ||
+                        overlaps(final_state, ns, g, ng) || overlaps(final_state, ns, beta, ng)))
+        return fail(GDN_ERR_INVALID_ARG, "final_state must not overlap x_raw, conv_w, g or beta");
+    const size_t need = gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+    if (ws_bytes < need || (need > 0 && !workspace))
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (need > 0 && (overlaps(workspace, need, o, nv) || overlaps(workspace, need, x_raw, nx) ||
+                     overlaps(workspace, need, conv_w, nw) || overlaps(workspace, need, g, ng) ||
+                     overlaps(workspace, need, beta, ng) ||
+                     overlaps(workspace, need, final_state, ns) ||
+                     overlaps(workspace, need, initial_state, ns)))
+        return fail(GDN_ERR_INVALID_ARG, "workspace must not overlap inputs or outputs");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
+    hipError_t e;
+    if (T == 0)   // only the final state (no workspace; nothing else is read)
+        e = gdn::launch_recurrent_prefill(gdn::kIoBF16, nullptr, nullptr, nullptr, g, beta,
+                                          initial_state, final_state, cu_seqlens, N, T, H_qk, H_v,
+                                          scale, o, s);
+    else
+        e = gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
+                                            final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
+                                            workspace, s);
+    return finish(e, s, "gdn_prefill_raw launch");
 }
 
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -168,10 +168,29 @@ __device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a
 // block, 8 consecutive d_k), so K K^T and Q K^T need no LDS staging.  They are
 // formed once, with the operands ordered so that each lane holds 4 consecutive
 // columns of one row, and kept in registers for all V-heads of the QK head.
+//
+// With the prelude fused (kRaw), the wave first forms the chunk's K and Q rows
+// from the raw projections: conv, SiLU and L2 norm with the conv prelude
+// kernel's arithmetic and lane layout (16 lanes per row, 8 channels each, the
+// norm reduced over the 16-lane row), so the rows come out bit-identical to
+// the prelude's.  Each lane walks 16 consecutive rows, keeping the conv window
+// in registers.  The normalised rows go to the workspace, where the scan reads
+// them, and through LDS into the MFMA fragments.
 constexpr int kPrepWaves = 4;
+static_assert(kChunk * kKP * sizeof(uint16_t) <= kChunk * kAP * sizeof(float),
+              "a chunk's bf16 K or Q rows fit in a wave's A area");
+
+struct RawIn {             // fused prelude inputs
+    const uint16_t *x;     // [T][C_raw] bf16 raw projections, channels [q | k | v]
+    const uint16_t *w;     // [C_raw][4] bf16 conv taps
+    float eps;             // L2-norm epsilon
+    uint16_t *kws, *qws;   // [chunks * 64][H_qk][128] bf16 normalised K and Q rows
+};
+
+template <bool kRaw>
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, const int32_t *__restrict__ cu,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const RawIn raw,
+    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
     int item_lo, int item_hi, uint16_t *__restrict__ ws) {
     __shared__ __attribute__((aligned(16))) float sA_w[kPrepWaves][kChunk * kAP];
@@ -207,15 +226,76 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
 
         // K and Q fragments: block I, k-step s -> row 16 I + c, d_k 32 s + 8 g4 .. +7
         uint4 kf[4][4], qf[4][4];
-        const uint16_t *kc = k + (size_t)c0 * H_qk * kD;
-        const uint16_t *qc = q + (size_t)c0 * H_qk * kD;
+        if constexpr (kRaw) {
+            // lane (sg, cg): rows 16 sg .. +15 of the chunk, channels 8 cg .. +7 of the head
+            const int sg = lane >> 4, cg = lane & 15;
+            const size_t C = (size_t)(2 * H_qk + H_v) * kD;
+            uint16_t *rows = reinterpret_cast<uint16_t *>(sA);     // [64][kKP] bf16
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const int off = (min(16 * I + c, L - 1) * H_qk + hq) * kD + 8 * g4;
+            for (int m = 0; m < 2; ++m) {                           // K, then Q
+                const size_t ch = (size_t)(m == 0 ? H_qk + hq : hq) * kD + 8 * cg;
+                float wt[4][8];
+                load_taps8(raw.w, ch, wt);
+                // window x[r-3], x[r-2], x[r-1] for r = 16 sg; taps before the
+                // sequence start read zero
+                float win[3][8];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                kf[I][s] = *reinterpret_cast<const uint4 *>(kc + off + 32 * s);
-                qf[I][s] = *reinterpret_cast<const uint4 *>(qc + off + 32 * s);
+                for (int j = 0; j < 3; ++j) {
+                    const int r = 16 * sg - 3 + j;
+                    const int rc = max(min(r, L - 1), s0 - c0);
+                    unpack8(*reinterpret_cast<const uint4 *>(raw.x + (size_t)(c0 + rc) * C + ch), win[j]);
+                    if (c0 + r < s0) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+                    }
+                }
+                uint16_t *dst = (m == 0 ? raw.kws : raw.qws) + ((size_t)gc * kChunk * H_qk + hq) * kD + 8 * cg;
+                // all 16 rows in flight before any arithmetic (one wave per
+                // SIMD: nothing else hides the memory latency)
+                u32x4 xr[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    xr[j] = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + min(16 * sg + j, L - 1)) * C + ch);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int r = 16 * sg + j;
+                    float cur[8], y[8], ss = 0.f;
+                    unpack8(__builtin_bit_cast(uint4, xr[j]), cur);
+                    conv_silu8(wt, win[0], win[1], win[2], cur, y, ss);
+                    const float rn = rsqrtf(row16_sum(ss) + raw.eps);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] *= rn;
+                    const uint4 u = pack_bf8(y);
+                    *reinterpret_cast<uint4 *>(dst + (size_t)r * H_qk * kD) = u;
+                    *reinterpret_cast<uint4 *>(rows + r * kKP + 8 * cg) = u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        win[0][e] = win[1][e];
+                        win[1][e] = win[2][e];
+                        win[2][e] = cur[e];
+                    }
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint4 f = *reinterpret_cast<const uint4 *>(rows + (16 * I + c) * kKP + 32 * s + 8 * g4);
+                        if (m == 0) kf[I][s] = f; else qf[I][s] = f;
+                    }
+                wave_lds_sync();                                    // read before the rows are rewritten
+            }
+        } else {
+            const uint16_t *kc = k + (size_t)c0 * H_qk * kD;
+            const uint16_t *qc = q + (size_t)c0 * H_qk * kD;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int off = (min(16 * I + c, L - 1) * H_qk + hq) * kD + 8 * g4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    kf[I][s] = *reinterpret_cast<const uint4 *>(kc + off + 32 * s);
+                    qf[I][s] = *reinterpret_cast<const uint4 *>(qc + off + 32 * s);
+                }
             }
         }
 #pragma unroll
@@ -411,6 +491,8 @@ struct OutRegs {          // waves 4-7
     u32x4 qr[4];          // Q row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
     u32x4 pA[2];          // P row 16 w + c, columns 32 s + 8 g4 .. +7
     float Gown;           // G of row 16 w + c
+    u32x4 xv, xvh;        // prelude fused: raw v row 16 w + lane / 4 and (lanes < 12)
+                          // row 16 w - 3 + lane / 4, slab columns 8 (lane % 4) .. +7
 };
 
 // 512 threads: waves 0-3 carry the state through the chunks (X = K S^T, R,
@@ -419,24 +501,34 @@ struct OutRegs {          // waves 4-7
 // chunk rows 16 w .. +15 and d_k columns 32 w .. +31 of the state.  Three
 // workgroup barriers per chunk: (1) R complete, (2) U complete, (3) S' complete.
 // Inputs are loaded two chunks ahead into three rotating register sets.
+//
+// With the prelude fused (kRaw), K and Q rows come from prep's normalised rows
+// in the workspace, and the output waves form the v slab: during chunk ci they
+// apply conv and SiLU (the prelude's arithmetic) to the raw v rows of chunk
+// ci + 1 and write them into the other half of a double-buffered v tile.
+template <bool kRaw>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
+    const RawIn raw, const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
     int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *__restrict__ o) {
+    constexpr int kVBufs = kRaw ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t sS[kSlabW * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sU[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sUs[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];   // K rows of the chunk
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * kVP];    // v rows of the chunk (slab columns)
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kVBufs][kChunk * kVP];   // v rows of the chunk (slab columns)
     __shared__ __attribute__((aligned(16))) uint16_t sQ[4][16 * kKP];     // each output wave's Q rows
+    __shared__ __attribute__((aligned(16))) uint16_t sXv[kRaw ? 4 : 1][20 * kVP];   // raw v rows per output wave
 
     // Workgroup -> (sequence, V-head, slab).  Workgroups are handed to the 8
     // XCDs round-robin; consecutive units (all slabs of a head, neighbouring
-    // heads of one QK group) are kept on one XCD so that they share its L2.
-    const int per_xcd = gridDim.x >> 3;
-    const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    // heads of one QK group) are kept on one XCD so that they share its L2:
+    // XCD x takes the contiguous range of units that starts at
+    // x * (G / 8) + min(x, G % 8) (a bijection for any grid size G).
+    const int xcd = blockIdx.x & 7;
+    const int u = xcd * ((int)gridDim.x >> 3) + min(xcd, (int)gridDim.x & 7) + (int)(blockIdx.x >> 3);
     const int slab = u % kSlabsW;
     const int nh = u / kSlabsW;
     const int h = nh % H_v, n = nh / H_v;
@@ -456,11 +548,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
     // K and Q rows are loaded whole (16 lanes x 16 B per row, 4 rows per
     // instruction: every cache line fully used) and regrouped into MFMA
     // fragments through LDS.  Offset of row 16 w + 4 i + lane / 16 (clamped),
-    // 16-byte piece lane % 16, of chunk ci:
+    // 16-byte piece lane % 16, of chunk ci (rows of the q, k inputs, or of
+    // prep's chunk-aligned rows in the workspace):
     auto krow_off = [&](int ci, int i) {
-        return (size_t)(s0 + kChunk * ci) * H_qk * kD +
+        const size_t row0 = kRaw ? (size_t)(cbase + ci) * kChunk : (size_t)(s0 + kChunk * ci);
+        return row0 * H_qk * kD +
                (size_t)((min(16 * w + 4 * i + (lane >> 4), chunk_len(ci) - 1) * H_qk + hq) * kD + 8 * (lane & 15));
     };
+    const uint16_t *kin = kRaw ? raw.kws : k;
+    const uint16_t *qin = kRaw ? raw.qws : q;
 
     if (wave < 4) {
         // ---------------- state waves
@@ -489,7 +585,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         auto fetch_a = [&](int ci, StateRegs &R) {
             ci = min(ci, c_end - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R.kr[i] = *reinterpret_cast<const u32x4 *>(k + krow_off(ci, i));
+            for (int i = 0; i < 4; ++i) R.kr[i] = *reinterpret_cast<const u32x4 *>(kin + krow_off(ci, i));
             const uint16_t *rec = rec_of(ci);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -500,14 +596,19 @@ __global__ __launch_bounds__(512) void scan_kernel(
             const float *Gp = reinterpret_cast<const float *>(rec_of(ci) + 2 * kTileElems);
             R.G4 = *reinterpret_cast<const float4 *>(Gp + 16 * w + 4 * g4);
             R.GL = Gp[kChunk - 1];
-            const int vr = min(16 * w + (lane >> 2), chunk_len(ci) - 1);
-            R.vrow = *reinterpret_cast<const u32x4 *>(v + ((size_t)(s0 + kChunk * ci + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
+            if constexpr (!kRaw) {
+                const int vr = min(16 * w + (lane >> 2), chunk_len(ci) - 1);
+                R.vrow = *reinterpret_cast<const u32x4 *>(v + ((size_t)(s0 + kChunk * ci + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
+            }
         };
 
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
             // this wave's 16 rows of v and of K into LDS, row-major; K's MFMA
-            // fragments come back out of its own rows
-            *reinterpret_cast<u32x4 *>(sV + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
+            // fragments come back out of its own rows (with the prelude
+            // fused, the output waves have already written v)
+            const uint16_t *sVc = sV[kRaw ? (ci & 1) : 0];
+            if constexpr (!kRaw)
+                *reinterpret_cast<u32x4 *>(sV[0] + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<u32x4 *>(sKr + (16 * w + 4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = cur.kr[i];
@@ -537,7 +638,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             wave_lds_sync();
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                const uint2 vv = lds_read_tr16(sV + (16 * w + 4 * g4 + (c >> 2)) * kVP + 16 * nt + 4 * (c & 3));
+                const uint2 vv = lds_read_tr16(sVc + (16 * w + 4 * g4 + (c >> 2)) * kVP + 16 * nt + 4 * (c & 3));
                 float r[4];
                 r[0] = __uint_as_float(vv.x << 16) - gam[0] * ax[nt][0];
                 r[1] = __uint_as_float(vv.x & 0xFFFF0000u) - gam[1] * ax[nt][1];
@@ -614,17 +715,47 @@ __global__ __launch_bounds__(512) void scan_kernel(
         }
     } else {
         // ---------------- output waves
+        // prelude fused: raw v rows of the slab, rows x row stride C
+        const size_t C = (size_t)(2 * H_qk + H_v) * kD;
+        const size_t vch = (size_t)(2 * H_qk + h) * kD + e0 + 8 * (lane & 3);
+        const int pr = lane >> 2;                  // this lane's row within the wave's 16
         auto fetch = [&](int ci, OutRegs &R) {
             ci = min(ci, c_end - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R.qr[i] = *reinterpret_cast<const u32x4 *>(q + krow_off(ci, i));
+            for (int i = 0; i < 4; ++i) R.qr[i] = *reinterpret_cast<const u32x4 *>(qin + krow_off(ci, i));
             const uint16_t *rec = rec_of(ci);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 R.pA[s] = *reinterpret_cast<const u32x4 *>(rec + kTileElems + frag_off(w, s, lane));
             R.Gown = reinterpret_cast<const float *>(rec + 2 * kTileElems)[16 * w + c];
+            if constexpr (kRaw) {
+                // rows clamped into the sequence; halo rows before its start
+                // are replaced by zero when used
+                const int Lc = chunk_len(ci), c0 = s0 + kChunk * ci;
+                const int r = min(16 * w + pr, Lc - 1);
+                const int rh = max(min(16 * w - 3 + min(pr, 2), Lc - 1), -kChunk * ci);
+                R.xv = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + r) * C + vch);
+                R.xvh = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + rh) * C + vch);
+            }
         };
-        auto body = [&](int ci, OutRegs &cur, OutRegs &pf) {
+        // v of chunk cj (raw rows in R) -> conv, SiLU -> sV[cj & 1], rows 16 w .. +15
+        float wv[4][8];
+        if constexpr (kRaw) load_taps8(raw.w, vch, wv);
+        auto v_conv = [&](int cj, const OutRegs &R) {
+            uint16_t *xs = sXv[w];                 // rows 0-2: halo, 3-18: the wave's rows, 19: unused
+            const int pc = 8 * (lane & 3);
+            *reinterpret_cast<u32x4 *>(xs + (3 + pr) * kVP + pc) = R.xv;
+            const bool before = kChunk * cj + 16 * w - 3 + pr < 0;       // ahead of the sequence start
+            *reinterpret_cast<u32x4 *>(xs + (lane < 12 ? pr : 19) * kVP + pc) =
+                before ? u32x4{0u, 0u, 0u, 0u} : R.xvh;
+            wave_lds_sync();
+            float xm[4][8], y[8], ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) unpack8(*reinterpret_cast<const uint4 *>(xs + (pr + j) * kVP + pc), xm[j]);
+            conv_silu8(wv, xm[0], xm[1], xm[2], xm[3], y, ss);
+            *reinterpret_cast<uint4 *>(sV[cj & 1] + (16 * w + pr) * kVP + pc) = pack_bf8(y);
+        };
+        auto body = [&](int ci, OutRegs &cur, OutRegs &nxt, OutRegs &pf) {
             const int c0 = s0 + kChunk * ci;
             const int L = min(kChunk, s1 - c0);
             // this wave's Q rows through its LDS area into MFMA fragments
@@ -649,6 +780,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             // next loads issued while the state waves form U: the vector
             // memory pipe is then quiet while they form X and R
             fetch(ci + 2, pf);
+            if constexpr (kRaw) v_conv(ci + 1, nxt);   // past the last chunk: written, never read
             __syncthreads();                                   // (2) U complete
             // O^T += U^T P^T  (P is lower triangular: k-steps up to this row block)
             const bool row_ok = 16 * w + c < L;
@@ -668,14 +800,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
         if (c_lo < c_end) {
             fetch(c_lo, r0);
             fetch(c_lo + 1, r1);
+            if constexpr (kRaw) v_conv(c_lo, r0);
         }
         __syncthreads();                                       // matches the state waves' first barrier
         for (int ci = c_lo; ci < c_end; ci += 3) {
-            body(ci, r0, r2);
+            body(ci, r0, r1, r2);
             if (ci + 1 >= c_end) break;
-            body(ci + 1, r1, r0);
+            body(ci + 1, r1, r2, r0);
             if (ci + 2 >= c_end) break;
-            body(ci + 2, r2, r1);
+            body(ci + 2, r2, r0, r1);
         }
     }
 }
@@ -685,29 +818,35 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // A single sequence leaves CUs idle during the scan (one workgroup per
 // (V-head, slab)).  Its chunks are then split into segments: the prep of
 // segment i + 1 runs on the idle CUs, on an auxiliary stream, while segment i
-// is scanned; only the first segment's prep runs alone.  The prep on the idle
-// CUs takes about 0.85 of the scan's time per chunk, so segment i holds a
-// share of the chunks proportional to kSegGrowth^i (a little below 1 / 0.85,
-// to leave room for the event hand-over), with the count chosen so that the
-// first segment is at most about kFirstSegChunks long.
+// is scanned; only the first segment's prep runs alone.  Segment i holds a
+// share of the chunks proportional to growth^i, with the count chosen so that
+// the first segment is at most about kFirstSegChunks long.  The growth is a
+// little below the ratio of the scan's time per chunk to the prep's on the
+// idle CUs (about 1 / 0.85 for the prep alone), which leaves room for the
+// event hand-over.  With the prelude fused the prep also forms K and Q and
+// the ratio differs.
 constexpr int kMaxSegments = 12;
+#ifndef GDN_SEG_GROWTH_RAW
+#define GDN_SEG_GROWTH_RAW 1.0
+#endif
 constexpr double kSegGrowth = 1.1;
+constexpr double kSegGrowthRaw = GDN_SEG_GROWTH_RAW;
 constexpr int kFirstSegChunks = 128;
 constexpr int kSegMinChunks = 64;     // shorter sequences are not split
 constexpr int kMinIdleCUs = 32;       // fewer idle CUs: not split
 
 // Segment bounds b[0] = 0 < b[1] < ... < b[count] = nch; returns count.
-int segment_bounds(int nch, int *b) {
+int segment_bounds(int nch, double growth, int *b) {
     int count = 2;
-    double wsum = 1.0 + kSegGrowth, wnext = kSegGrowth * kSegGrowth;
+    double wsum = 1.0 + growth, wnext = growth * growth;
     while (count < kMaxSegments && nch / wsum > kFirstSegChunks) {
         wsum += wnext;
-        wnext *= kSegGrowth;
+        wnext *= growth;
         ++count;
     }
     double w = 1.0, acc = 0.0;
     b[0] = 0;
-    for (int i = 1; i < count; ++i, w *= kSegGrowth) {
+    for (int i = 1; i < count; ++i, w *= growth) {
         acc += w;
         b[i] = max(b[i - 1] + 1, (int)(nch * acc / wsum));
     }
@@ -745,39 +884,57 @@ DeviceAux *device_aux() {
 
 }  // namespace
 
-size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v) {
-    (void)H_qk;
+namespace {
+
+// Workspace: chunk offsets | chunk records | (prelude fused) K rows, Q rows |
+// (one sequence) the state carried between segments.
+struct Workspace {
+    int32_t *chunk_base;
+    uint16_t *rec, *kws, *qws;
+    float *carry;
+};
+size_t workspace_layout(int N, int T, int H_qk, int H_v, bool raw, void *base, Workspace *wsp) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
-    // chunk offsets | chunk records | (one sequence) state carried between segments
-    return align256((size_t)(N + 1) * sizeof(int32_t)) +
-           max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t) +
-           (N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0);
+    const size_t head = align256((size_t)(N + 1) * sizeof(int32_t));
+    const size_t rec = max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);   // 256-byte multiple
+    const size_t rows = raw ? max_chunks * kChunk * (size_t)H_qk * kD * sizeof(uint16_t) : 0;
+    const size_t carry = N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0;
+    if (wsp) {
+        char *p = static_cast<char *>(base);
+        wsp->chunk_base = reinterpret_cast<int32_t *>(p);
+        wsp->rec = reinterpret_cast<uint16_t *>(p + head);
+        wsp->kws = reinterpret_cast<uint16_t *>(p + head + rec);
+        wsp->qws = reinterpret_cast<uint16_t *>(p + head + rec + rows);
+        wsp->carry = reinterpret_cast<float *>(p + head + rec + 2 * rows);
+    }
+    return head + rec + 2 * rows + carry;
 }
 
-hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
-                                  const float *beta, const float *S0, float *S_final,
-                                  const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
-                                  float scale, void *o, void *workspace, hipStream_t stream) {
+template <bool kRaw>
+hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, RawIn raw,
+                       const float *g, const float *beta, const float *S0, float *S_final,
+                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, float scale,
+                       uint16_t *o16, void *workspace, hipStream_t stream) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
-    int32_t *chunk_base = static_cast<int32_t *>(workspace);
-    uint16_t *ws = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) +
-                                                align256((size_t)(N + 1) * sizeof(int32_t)));
-    const auto *q16 = static_cast<const uint16_t *>(q);
-    const auto *k16 = static_cast<const uint16_t *>(k);
-    const auto *v16 = static_cast<const uint16_t *>(v);
-    auto *o16 = static_cast<uint16_t *>(o);
+    Workspace W;
+    workspace_layout(N, T, H_qk, H_v, kRaw, workspace, &W);
+    raw.kws = W.kws;
+    raw.qws = W.qws;
+    int32_t *chunk_base = W.chunk_base;
+    uint16_t *ws = W.rec;
     const int scan_grid = N * H_v * kSlabsW;
     auto prep = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
         const int items = (c_hi - c_lo) * H_qk;
         const int grid = min((items + kPrepWaves - 1) / kPrepWaves, max_grid);
-        hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(64 * kPrepWaves), 0, s, q16, k16, g, beta,
-                           cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo * H_qk,
+        hipLaunchKernelGGL(prep_kernel<kRaw>, dim3(grid), dim3(64 * kPrepWaves), 0, s, q16, k16, raw,
+                           g, beta, cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo * H_qk,
                            c_hi * H_qk, ws);
         return hipGetLastError();
     };
     auto scan = [&](int c_lo, int c_hi, const float *init, float *fin) {
-        hipLaunchKernelGGL(scan_kernel, dim3(scan_grid), dim3(512), 0, stream, q16, k16, v16, init,
-                           fin, cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo, c_hi, ws, o16);
+        hipLaunchKernelGGL(scan_kernel<kRaw>, dim3(scan_grid), dim3(512), 0, stream, q16, k16, v16,
+                           raw, init, fin, cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo,
+                           c_hi, ws, o16);
         return hipGetLastError();
     };
 
@@ -800,10 +957,9 @@ hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, c
     // The state passes from segment to segment through final_state, or the
     // workspace's carry area when the caller wants no final state.  The last
     // wait joins the auxiliary stream back into the caller's stream.
-    float *carry = S_final ? S_final
-                           : reinterpret_cast<float *>(ws + max_chunks * (size_t)H_v * kRecElems);
+    float *carry = S_final ? S_final : W.carry;
     int b[kMaxSegments + 1];
-    const int nseg = segment_bounds(nch, b);
+    const int nseg = segment_bounds(nch, kRaw ? kSegGrowthRaw : kSegGrowth, b);
     if ((e = prep(b[0], b[1], INT32_MAX, stream)) != hipSuccess) return e;
     if ((e = hipEventRecord(aux->ev[0], stream)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(aux->stream, aux->ev[0], 0)) != hipSuccess) return e;
@@ -817,6 +973,31 @@ hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, c
             return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw) {
+    return workspace_layout(N, T, H_qk, H_v, raw, nullptr, nullptr);
+}
+
+hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *S0, float *S_final,
+                                  const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
+                                  float scale, void *o, void *workspace, hipStream_t stream) {
+    return launch_impl<false>(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                              static_cast<const uint16_t *>(v), RawIn{}, g, beta, S0, S_final,
+                              cu_seqlens, N, T, H_qk, H_v, scale, static_cast<uint16_t *>(o),
+                              workspace, stream);
+}
+
+hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, const float *g,
+                                      const float *beta, const float *S0, float *S_final,
+                                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
+                                      float scale, void *o, void *workspace, hipStream_t stream) {
+    RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr};
+    return launch_impl<true>(nullptr, nullptr, nullptr, raw, g, beta, S0, S_final, cu_seqlens, N, T,
+                             H_qk, H_v, scale, static_cast<uint16_t *>(o), workspace, stream);
 }
 
 }  // namespace gdn

@@ -37,6 +37,58 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// 8 bf16 (one 16-byte piece) -> fp32.
+__device__ __forceinline__ void unpack8(uint4 u, float *d) {
+    d[0] = __uint_as_float(u.x << 16); d[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    d[2] = __uint_as_float(u.y << 16); d[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    d[4] = __uint_as_float(u.z << 16); d[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    d[6] = __uint_as_float(u.w << 16); d[7] = __uint_as_float(u.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// Conv prelude arithmetic, shared by every kernel that applies it so that all
+// of them produce the same bits.  wt[j][e] is tap j of channel e (tap 3 on the
+// current token); xm3, xm2, xm1, x0 are the inputs 3, 2, 1 and 0 tokens back.
+// y = SiLU(conv); ss accumulates y^2 over the 8 channels, in channel order.
+__device__ __forceinline__ void conv_silu8(const float (&wt)[4][8], const float *xm3,
+                                           const float *xm2, const float *xm1, const float *x0,
+                                           float *y, float &ss) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float acc = wt[3][e] * x0[e];
+        acc = __builtin_fmaf(wt[2][e], xm1[e], acc);
+        acc = __builtin_fmaf(wt[1][e], xm2[e], acc);
+        acc = __builtin_fmaf(wt[0][e], xm3[e], acc);
+        y[e] = silu(acc);
+        ss = __builtin_fmaf(y[e], y[e], ss);
+    }
+}
+
+// The 4 conv taps of 8 consecutive channels starting at channel ch:
+// w is [channels][4] bf16; wt[j][e] = w[ch + e][j].
+__device__ __forceinline__ void load_taps8(const uint16_t *w, size_t ch, float (&wt)[4][8]) {
+    const uint4 *wp = reinterpret_cast<const uint4 *>(w + ch * 4);
+    float tmp[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack8(wp[i], tmp + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[j][e] = tmp[e * 4 + j];
+}
+
+__device__ __forceinline__ uint4 pack_bf8(const float *y) {
+    uint4 out;
+    out.x = pack_bf2(y[0], y[1]);
+    out.y = pack_bf2(y[2], y[3]);
+    out.z = pack_bf2(y[4], y[5]);
+    out.w = pack_bf2(y[6], y[7]);
+    return out;
+}
+
 // Load 4 consecutive values (bf16 bits or fp32) as fp32.
 __device__ __forceinline__ void load4(const uint16_t *p, float *d) {
     uint2 u = *reinterpret_cast<const uint2 *>(p);

@@ -27,12 +27,17 @@ hipError_t launch_recurrent_prefill(int io_dtype, const void *q, const void *k, 
                                     float *S_final, const int32_t *cu_seqlens, int N, int T,
                                     int H_qk, int H_v, float scale, void *o, hipStream_t stream);
 
-// Chunked bf16 prefill (64-token chunks, bf16 matrix-core products).
-size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v);
+// Chunked bf16 prefill (64-token chunks, bf16 matrix-core products); `raw`:
+// from the raw projections, with the conv prelude fused.
+size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw);
 hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, const float *S0, float *S_final,
                                   const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                   float scale, void *o, void *workspace, hipStream_t stream);
+hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, const float *g,
+                                      const float *beta, const float *S0, float *S_final,
+                                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
+                                      float scale, void *o, void *workspace, hipStream_t stream);
 
 // Device-side precondition checks (GDN_DEBUG=1): launch a one-workgroup scan,
 // wait for the stream, and return the violation bits in *result (0 = ok).

@@ -24,17 +24,6 @@ namespace {
 constexpr int kRun = 32;          // tokens walked by one lane group
 constexpr int kGroupsPerBlock = 16;
 
-__device__ __forceinline__ void unpack8(uint4 u, float *d) {
-    d[0] = __uint_as_float(u.x << 16); d[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    d[2] = __uint_as_float(u.y << 16); d[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    d[4] = __uint_as_float(u.z << 16); d[5] = __uint_as_float(u.z & 0xFFFF0000u);
-    d[6] = __uint_as_float(u.w << 16); d[7] = __uint_as_float(u.w & 0xFFFF0000u);
-}
-
-__device__ __forceinline__ float silu(float x) {
-    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
-
 __global__ __launch_bounds__(256) void conv_prelude_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const int32_t *__restrict__ cu_seqlens, int N, int T, int H_qk, int H_v, float eps,
@@ -51,16 +40,7 @@ __global__ __launch_bounds__(256) void conv_prelude_kernel(
     const int ch0 = cb * kD + c16 * 8;                 // first of this lane's 8 channels
 
     float wt[4][8];
-    {
-        const uint4 *wp = reinterpret_cast<const uint4 *>(w + (size_t)ch0 * 4);
-        float tmp[32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) unpack8(wp[i], tmp + 8 * i);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wt[j][e] = tmp[e * 4 + j];
-    }
+    load_taps8(w, (size_t)ch0, wt);
 
     // Sequence containing t0: largest n with cu[n] <= t0 (skipping empty ones).
     int n = 0, s0 = 0, s1 = T;
@@ -117,26 +97,13 @@ __global__ __launch_bounds__(256) void conv_prelude_kernel(
         }
         float y[8];
         float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float acc = wt[3][e] * cur[e];
-            acc += wt[2][e] * win[2][e];
-            acc += wt[1][e] * win[1][e];
-            acc += wt[0][e] * win[0][e];
-            y[e] = silu(acc);
-            ss += y[e] * y[e];
-        }
+        conv_silu8(wt, win[0], win[1], win[2], cur, y, ss);
         if (normalise) {
             const float r = rsqrtf(row16_sum(ss) + eps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] *= r;
         }
-        uint4 out;
-        out.x = pack_bf2(y[0], y[1]);
-        out.y = pack_bf2(y[2], y[3]);
-        out.z = pack_bf2(y[4], y[5]);
-        out.w = pack_bf2(y[6], y[7]);
-        *reinterpret_cast<uint4 *>(dst + (size_t)t * dst_stride) = out;
+        *reinterpret_cast<uint4 *>(dst + (size_t)t * dst_stride) = pack_bf8(y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             win[0][e] = win[1][e];

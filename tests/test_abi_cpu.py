@@ -103,3 +103,44 @@ def test_prelude_rejects_bad_arguments():
     assert L.gdn_conv_prelude(*a) == gdn.GDN_ERR_UNSUPPORTED
     a = list(base); a[0] = None
     assert L.gdn_conv_prelude(*a) == gdn.GDN_ERR_INVALID_ARG
+
+
+def _prefill_raw(L, **kw):
+    a = dict(x=1, w=2, eps=1e-6, g=4, beta=5, S0=None, Sf=None, cu=None, N=1, T=64, H_qk=16,
+             H_v=48, d_k=128, d_v=128, scale=1.0, o=1 << 40, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.gdn_prefill_raw(a["x"], a["w"], a["eps"], a["g"], a["beta"], a["S0"], a["Sf"],
+                             a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"],
+                             a["scale"], a["o"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_k=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(H_qk=1, H_v=16), gdn.GDN_ERR_UNSUPPORTED),          # 16 V-heads per QK head
+    (dict(H_v=47), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(x=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(eps=-1.0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=1), gdn.GDN_ERR_INVALID_ARG),                     # o overlaps x_raw
+    (dict(), gdn.GDN_ERR_WORKSPACE),                          # no workspace
+])
+def test_prefill_raw_rejects_bad_arguments(kw, code):
+    L = gdn.lib()
+    assert _prefill_raw(L, **kw) == code
+    assert L.gdn_last_error().decode()
+
+
+def test_prefill_raw_workspace_size():
+    """The fused path keeps the unfused records plus the normalised q and k rows."""
+    for N, T in ((1, 1), (1, 4133), (8, 65536)):
+        plain = gdn.gdn_prefill_workspace_size(gdn.GDN_BF16, N, T, 16, 48)
+        fused = gdn.gdn_prefill_raw_workspace_size(N, T, 16, 48)
+        chunks = (T + 63) // 64 + N
+        assert fused == plain + 2 * chunks * 64 * 16 * 128 * 2
+    assert gdn.gdn_prefill_raw_workspace_size(1, 0, 16, 48) == 0
+    L = gdn.lib()
+    need = gdn.gdn_prefill_raw_workspace_size(1, 64, 16, 48)
+    assert _prefill_raw(L, ws=1 << 41, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE

@@ -1,5 +1,6 @@
 """Long-context hand-off at full size: a 262144-token prefill from raw
-projections (prelude + chunked prefill), whose final state seeds 256 decode
+projections (the conv prelude fused into the chunked prefill), whose final
+state seeds 256 decode
 sequences that then take 64 autoregressive steps.  A sampled V-head is checked
 against the fp64 oracle at every token of the prefill, at every decode step and
 in the final pool.  The oracle runs only the sampled head (its QK head's q, k
@@ -26,11 +27,10 @@ def test_longctx_262144_prefill_then_decode_sampled_head():
     p = synth.workload_longctx_prefill(T_LONG)
     print("inputs generated", flush=True)
     xd = dev(p.x)
-    q, k, v = gdn.gdn_conv_prelude(xd, dev(p.w), None, H_qk=p.H_qk, H_v=p.H_v)
-    del xd
-    o, S = gdn.gdn_prefill(q, k, v, dev(p.g), dev(p.beta), None, None)
+    o, S = gdn.gdn_prefill_raw(xd, dev(p.w), dev(p.g), dev(p.beta), None, None, H_qk=p.H_qk,
+                               H_v=p.H_v)
     torch.cuda.synchronize()
-    del q, k, v
+    del xd
     o_h = host(o[:, HEAD])
     del o
     print("GPU prefill done", flush=True)

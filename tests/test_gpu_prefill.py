@@ -160,17 +160,23 @@ def test_bf16_long_sequence_segments():
     assert np.array_equal(st.cpu().numpy(), S.astype(np.float32))
 
 
-def _sampled_heads_end_to_end(p, heads, what):
-    """prelude + prefill on the GPU; the oracle runs prelude + recurrence for the
-    sampled V-heads only (their QK head's channels and their own v channels)."""
+def _sampled_heads_end_to_end(p, heads, what, fused=False):
+    """prelude + prefill on the GPU (two calls, or fused in one); the oracle runs
+    prelude + recurrence for the sampled V-heads only (their QK head's channels
+    and their own v channels)."""
     import torch
     import linear_attention_sequence_delta_amd as gdn
     cu = None if p.cu_seqlens is None else dev(p.cu_seqlens)
     xd = dev(p.x)
-    q, k, v = gdn.gdn_conv_prelude(xd, dev(p.w), cu, H_qk=p.H_qk, H_v=p.H_v)
-    del xd
-    o, S = gdn.gdn_prefill(q, k, v, dev(p.g), dev(p.beta),
-                           None if p.S0 is None else dev(p.S0), cu)
+    S0 = None if p.S0 is None else dev(p.S0)
+    if fused:
+        o, S = gdn.gdn_prefill_raw(xd, dev(p.w), dev(p.g), dev(p.beta), S0, cu, H_qk=p.H_qk,
+                                   H_v=p.H_v)
+        del xd
+    else:
+        q, k, v = gdn.gdn_conv_prelude(xd, dev(p.w), cu, H_qk=p.H_qk, H_v=p.H_v)
+        del xd
+        o, S = gdn.gdn_prefill(q, k, v, dev(p.g), dev(p.beta), S0, cu)
     torch.cuda.synchronize()
     grp = p.H_v // p.H_qk
     D = p.dk
@@ -200,3 +206,15 @@ def test_prefill_varlen_8seq_sampled_heads():
     """8 packed sequences (lengths U{512..16384}), nonzero initial states."""
     p = synth.workload_varlen()
     _sampled_heads_end_to_end(p, [4, 38], "varlen")
+
+
+def test_prefill_raw_32k_sampled_heads():
+    """The 32768-token workload through the fused prelude + prefill."""
+    p = synth.workload_prefill_32k()
+    _sampled_heads_end_to_end(p, [2, 30, 46], "T32768 fused", fused=True)
+
+
+def test_prefill_raw_varlen_8seq_sampled_heads():
+    """The packed varlen workload through the fused prelude + prefill."""
+    p = synth.workload_varlen()
+    _sampled_heads_end_to_end(p, [7, 41], "varlen fused", fused=True)
