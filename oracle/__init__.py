@@ -52,7 +52,9 @@ def _load():
     lib.orc_recurrent.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, I, I]
     lib.orc_chunked.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P, P, I, I]
     lib.orc_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P]
-    for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step):
+    lib.orc_gates.argtypes = [P, P, P, P, I, I, P, P]
+    for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step,
+              lib.orc_gates):
         f.restype = I
     _lib = lib
     return lib
@@ -168,3 +170,59 @@ def decode_step(q, k, v, g, beta, pool, slot_idx, scale=1.0):
                                  _ptr(slots), B, P, H_qk, H_v, dk, dv, float(scale), _ptr(o))
     _check(rc, "decode_step")
     return o, pool
+
+
+def gates(a, b, A_log, dt_bias):
+    """g = -softplus(a + dt_bias) * exp(A_log), beta = sigmoid(b), per token and
+    V-head.  a, b [T, H_v]; A_log, dt_bias [H_v].  Returns fp64 (g, beta)."""
+    a, b, A_log, dt_bias = (f64(x) for x in (a, b, A_log, dt_bias))
+    T, H_v = a.shape
+    if b.shape != (T, H_v) or A_log.shape != (H_v,) or dt_bias.shape != (H_v,):
+        raise ValueError("gates shape mismatch")
+    g = np.zeros((T, H_v))
+    beta = np.zeros((T, H_v))
+    _check(_load().orc_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), T, H_v, _ptr(g),
+                             _ptr(beta)), "gates")
+    return g, beta
+
+
+def conv_state(x, cu_seqlens=None):
+    """The conv history a sequence leaves for its next token: its last three raw
+    rows, oldest first ([N, 3, C_raw], same dtype as x), zero where the sequence
+    has fewer than three rows."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    cu, N = _cu(cu_seqlens, T)
+    bounds = [(0, T)] if cu is None else [(int(cu[n]), int(cu[n + 1])) for n in range(N)]
+    out = np.zeros((N, 3, x.shape[1]), dtype=x.dtype)
+    for n, (s0, s1) in enumerate(bounds):
+        for j in range(3):
+            t = s1 - 3 + j
+            if t >= s0:
+                out[n, j] = x[t]
+    return out
+
+
+def decode_step_raw(x, w, conv_state_pool, a, b, A_log, dt_bias, pool, slot_idx, *, H_qk, H_v,
+                    dk, dv, eps=1e-6, scale=1.0):
+    """One token per sequence from the raw projections x [B, C_raw]: the conv
+    window of sequence b is the three raw rows kept in conv_state_pool[slot]
+    followed by x[b]; conv, SiLU and L2 norm as in ``prelude``; gates as in
+    ``gates``; then ``decode_step``.  Returns (o, new conv-state pool, new
+    state pool); the new conv state of an addressed slot is its rows 1, 2 and
+    x[b] (same dtype as the pool given), the inputs are not modified."""
+    slots = np.ascontiguousarray(slot_idx, dtype=np.int32)
+    cs = np.asarray(conv_state_pool)
+    x = np.asarray(x)
+    B, C = x.shape
+    if cs.shape[1:] != (3, C) or slots.shape != (B,):
+        raise ValueError("decode_step_raw shape mismatch")
+    # each window is its own 4-row sequence; only its last row's outputs are used
+    win = np.concatenate([f64(cs[slots]), f64(x)[:, None, :]], axis=1).reshape(4 * B, C)
+    cu = np.arange(0, 4 * B + 1, 4, dtype=np.int32)
+    q, k, v = prelude(win, w, cu, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, eps=eps)
+    g, beta = gates(a, b, A_log, dt_bias)
+    o, new_pool = decode_step(q[3::4], k[3::4], v[3::4], g, beta, pool, slots, scale)
+    new_cs = cs.copy()
+    new_cs[slots] = np.concatenate([cs[slots][:, 1:], x[:, None, :]], axis=1)
+    return o, new_cs, new_pool

@@ -413,4 +413,31 @@ int orc_chunked(const double *q, const double *k, const double *v, const double 
     return status;
 }
 
+/*
+ * Gates from the raw per-token projections a, b of each V-head:
+ *   g    = -softplus(a + dt_bias[h]) * exp(A_log[h])   (log of the decay a_t)
+ *   beta = sigmoid(b) = 1 / (1 + exp(-b))
+ * [Dissect sec. 2.1] names the layer's A_log and dt_bias weights; the formula
+ * is the layer's gate parameterisation as the workloads state it.  softplus is
+ * log(1 + exp(x)), written as max(x, 0) + log1p(exp(-|x|)), the same value
+ * without overflow.
+ * a, b [T][H_v]; A_log, dt_bias [H_v]; g, beta [T][H_v] outputs.
+ */
+int orc_gates(const double *a, const double *b, const double *A_log, const double *dt_bias,
+              int T, int H_v, double *g, double *beta)
+{
+    if (T < 0 || H_v < 1)
+        return ORC_EINVAL;
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H_v; ++h) {
+            const size_t i = (size_t)t * H_v + h;
+            const double x = a[i] + dt_bias[h];
+            const double softplus = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+            g[i] = -softplus * exp(A_log[h]);
+            beta[i] = 1.0 / (1.0 + exp(-b[i]));
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_version(void) { return 1; }

@@ -68,12 +68,16 @@ def _unit_rows(z):
 
 
 def _gates(rng_a, rng_b, A_log, dt_bias, T):
+    """The workloads' gate recipe: raw a, b ~ N(0, 1) per token and V-head, then
+    g = -softplus(a + dt_bias) exp(A_log), beta = sigmoid(b) in fp64, stored
+    fp32.  Returns (g, beta, a, b); a, b as fp32 (what a layer kernel that
+    forms the gates itself is given)."""
     a = rng_a.standard_normal((T, A_log.size))
     b = rng_b.standard_normal((T, A_log.size))
     sp = np.log1p(np.exp(a + dt_bias[None, :]))
     g = -sp * np.exp(A_log[None, :])
     beta = 1.0 / (1.0 + np.exp(-b))
-    return g.astype(np.float32), beta.astype(np.float32)
+    return g.astype(np.float32), beta.astype(np.float32), a.astype(np.float32), b.astype(np.float32)
 
 
 def _raw_bf16(seq, T, C, block: int = 128):
@@ -185,14 +189,14 @@ def raw_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int = H_
     w = bf16_bits(rw.normal(0.0, 0.5, (C, CONV_W)).astype(np.float32))
     A_log = rA.uniform(-1.0, 1.0, H_v)
     dt_bias = rd.uniform(-1.0, 1.0, H_v)
-    g, beta = _gates(ra, rb, A_log, dt_bias, T)
+    g, beta, a, b = _gates(ra, rb, A_log, dt_bias, T)
     S0 = None
     if init_state:
         S0 = rs.normal(0.0, state_std, (N, H_v, dv, dk)).astype(np.float32)
     return Prefill(T=T, N=N, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, io="bf16", g=g, beta=beta,
                    x=x, w=w, S0=S0, cu_seqlens=cu,
                    meta={"seed": seed, "recipe": "raw_prefill", "A_log": A_log,
-                         "dt_bias": dt_bias})
+                         "dt_bias": dt_bias, "a": a, "b": b})
 
 
 def direct_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int = H_QK,
@@ -217,7 +221,7 @@ def direct_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int =
         q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
     A_log = rA.uniform(-1.0, 1.0, H_v)
     dt_bias = rd.uniform(-1.0, 1.0, H_v)
-    g, beta = _gates(ra, rb, A_log, dt_bias, T)
+    g, beta, _, _ = _gates(ra, rb, A_log, dt_bias, T)
     if g_range is not None:
         g = (-ra.uniform(g_range[0], g_range[1], (T, H_v))).astype(np.float32)
     S0 = None
@@ -247,7 +251,7 @@ def decode_inputs(seed: int, B: int, P: Optional[int] = None, H_qk: int = H_QK,
     dt_draw = rd.uniform(-1.0, 1.0, H_v)
     A_log = A_draw if A_log is None else np.asarray(A_log, dtype=np.float64)
     dt_bias = dt_draw if dt_bias is None else np.asarray(dt_bias, dtype=np.float64)
-    g, beta = _gates(ra, rb, A_log, dt_bias, B)
+    g, beta, a, b = _gates(ra, rb, A_log, dt_bias, B)
     if slot_idx is None:
         slot_idx = rp.permutation(P)[:B].astype(np.int32)
     slot_idx = np.ascontiguousarray(slot_idx, dtype=np.int32)
@@ -257,7 +261,74 @@ def decode_inputs(seed: int, B: int, P: Optional[int] = None, H_qk: int = H_QK,
         for b in range(B):
             pool[slot_idx[b]] = rs.normal(0.0, state_std, (H_v, dv, dk)).astype(np.float32)
     return Decode(B=B, P=P, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, q=q, k=k, v=v, g=g, beta=beta,
-                  pool=pool, slot_idx=slot_idx, meta={"seed": seed, "recipe": "decode_inputs"})
+                  pool=pool, slot_idx=slot_idx,
+                  meta={"seed": seed, "recipe": "decode_inputs", "A_log": A_log,
+                        "dt_bias": dt_bias, "a": a, "b": b})
+
+
+# bf16 canary (a quiet NaN) for conv-state slots a call must not touch
+CONV_CANARY_BITS = 0x7FC1
+
+
+@dataclass
+class LayerDecode:
+    """Host inputs of one decode step from raw projections (all numpy)."""
+    B: int
+    P: int
+    H_qk: int
+    H_v: int
+    dk: int
+    dv: int
+    x: np.ndarray          # [B, C_raw] bf16 bits, the new token's raw projections
+    w: np.ndarray          # [C_raw, 4] bf16 bits, conv taps
+    a: np.ndarray          # [B, H_v] fp32 raw gate projections
+    b: np.ndarray          # [B, H_v] fp32
+    A_log: np.ndarray      # [H_v] fp32
+    dt_bias: np.ndarray    # [H_v] fp32
+    conv_pool: np.ndarray  # [P, 3, C_raw] bf16 bits, the last three raw rows of each slot
+    pool: np.ndarray       # [P, H_v, dv, dk] fp32 states
+    slot_idx: np.ndarray   # [B] int32
+    meta: dict = field(default_factory=dict)
+
+
+def layer_decode_inputs(seed, B: int, P: Optional[int] = None, H_qk: int = H_QK, H_v: int = H_V,
+                        dk: int = D_K, dv: int = D_V, state_std: float = 0.02, w=None,
+                        A_log=None, dt_bias=None, conv_pool=None, pool=None,
+                        slot_idx=None) -> LayerDecode:
+    """One decode step from raw projections: x ~ N(0, 1) bf16; a, b ~ N(0, 1);
+    conv taps ~ N(0, 0.5) bf16 and A_log, dt_bias ~ U(-1, 1) unless the layer's
+    weights are given; the addressed slots of a fresh conv-state pool hold
+    N(0, 1) bf16 rows and of a fresh state pool N(0, state_std) states, the
+    other slots a NaN canary; slot_idx = the first B entries of a seeded
+    permutation.  Given pools / slot_idx are used as they are.
+    Generators: x, w, a, b, A_log, dt_bias, perm, conv rows, states."""
+    rx, rw, ra, rb, rA, rd, rp, rc, rs = _rngs(seed, 9)
+    C = c_raw(H_qk, H_v, dk, dv)
+    P = P if P is not None else (pool.shape[0] if pool is not None else 2 * B)
+    x = bf16_bits(rx.standard_normal((B, C), dtype=np.float32))
+    w_draw = bf16_bits(rw.normal(0.0, 0.5, (C, CONV_W)).astype(np.float32))
+    w = w_draw if w is None else w
+    A_draw = rA.uniform(-1.0, 1.0, H_v)
+    dt_draw = rd.uniform(-1.0, 1.0, H_v)
+    A_log = (A_draw if A_log is None else np.asarray(A_log, dtype=np.float64)).astype(np.float32)
+    dt_bias = (dt_draw if dt_bias is None else np.asarray(dt_bias, dtype=np.float64)).astype(np.float32)
+    a = ra.standard_normal((B, H_v)).astype(np.float32)
+    b = rb.standard_normal((B, H_v)).astype(np.float32)
+    if slot_idx is None:
+        slot_idx = rp.permutation(P)[:B].astype(np.int32)
+    slot_idx = np.ascontiguousarray(slot_idx, dtype=np.int32)
+    if conv_pool is None:
+        conv_pool = np.full((P, 3, C), CONV_CANARY_BITS, dtype=np.uint16)
+        for i in range(B):
+            conv_pool[slot_idx[i]] = bf16_bits(rc.standard_normal((3, C), dtype=np.float32))
+    if pool is None:
+        pool = np.empty((P, H_v, dv, dk), dtype=np.float32)
+        pool.view(np.uint32)[...] = CANARY_BITS
+        for i in range(B):
+            pool[slot_idx[i]] = rs.normal(0.0, state_std, (H_v, dv, dk)).astype(np.float32)
+    return LayerDecode(B=B, P=P, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, x=x, w=w, a=a, b=b,
+                       A_log=A_log, dt_bias=dt_bias, conv_pool=conv_pool, pool=pool,
+                       slot_idx=slot_idx, meta={"seed": seed, "recipe": "layer_decode_inputs"})
 
 
 # ------------------------------------------------- the five named workloads

@@ -316,6 +316,88 @@ def test_decode_step_matches_one_token_prefill_and_spares_other_slots(orc):
     assert (pool[untouched].astype(np.float32).view(np.uint32) == synth.CANARY_BITS).all()
 
 
+# ------------------------------------------------------------------- gates
+def test_gates_against_library_forms_and_identities(orc):
+    """g = -softplus(a + dt_bias) exp(A_log), beta = sigmoid(b): against numpy's
+    logaddexp (softplus(x) = log(e^0 + e^x)) and the logistic function, the
+    closed values at zero, and softplus(x) - softplus(-x) = x."""
+    rng = np.random.default_rng(31)
+    T, H = 50, 6
+    a = rng.normal(0.0, 4.0, (T, H))
+    b = rng.normal(0.0, 4.0, (T, H))
+    A_log = rng.uniform(-1, 1, H)
+    dt = rng.uniform(-1, 1, H)
+    g, beta = orc.gates(a, b, A_log, dt)
+    np.testing.assert_allclose(g, -np.logaddexp(0.0, a + dt) * np.exp(A_log), rtol=1e-13)
+    np.testing.assert_allclose(beta, 1.0 / (1.0 + np.exp(-b)), rtol=1e-13)
+    np.testing.assert_allclose(beta + orc.gates(a, -b, A_log, dt)[1], 1.0, rtol=1e-14)
+    g_neg, _ = orc.gates(-a - 2 * dt, b, A_log, dt)          # softplus(-(a + dt))
+    np.testing.assert_allclose((-g + g_neg) / np.exp(A_log), a + dt, atol=1e-12)
+    z = np.zeros((1, 2))
+    g0, b0 = orc.gates(z, z, np.array([0.0, np.log(2.0)]), np.zeros(2))
+    np.testing.assert_allclose(g0, [[-np.log(2.0), -2 * np.log(2.0)]], rtol=1e-15)
+    np.testing.assert_allclose(b0, 0.5, rtol=0)
+    big = orc.gates(np.array([[-800.0, 800.0]]), z, np.zeros(2), np.zeros(2))[0]
+    assert big[0, 0] == -0.0 or abs(big[0, 0]) < 1e-300
+    assert big[0, 1] == -800.0                               # no overflow for large a
+
+
+def test_gates_match_the_workload_recipe(orc):
+    """The oracle's gates reproduce the g, beta the input recipe stores (an
+    independent numpy evaluation, rounded to fp32)."""
+    p = synth.raw_prefill(41, T=100, H_qk=2, H_v=6, dk=8, dv=8)
+    g, beta = orc.gates(p.meta["a"].astype(np.float64), p.meta["b"].astype(np.float64),
+                        p.meta["A_log"], p.meta["dt_bias"])
+    np.testing.assert_allclose(g, p.g, rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(beta, p.beta, rtol=2e-6, atol=1e-7)
+
+
+# --------------------------------------------------- decode from raw rows
+def test_conv_state_is_last_three_rows(orc):
+    x = np.arange(10 * 3, dtype=np.float64).reshape(10, 3)
+    cs = orc.conv_state(x, np.array([0, 5, 7, 7, 10], dtype=np.int32))
+    np.testing.assert_array_equal(cs[0], x[2:5])
+    np.testing.assert_array_equal(cs[1], np.vstack([np.zeros((1, 3)), x[5:7]]))
+    np.testing.assert_array_equal(cs[2], np.zeros((3, 3)))       # empty sequence
+    np.testing.assert_array_equal(cs[3], x[7:10])
+
+
+def test_raw_decode_chain_equals_prefill(orc):
+    """T decode steps from raw rows, each conv window being the slot's three
+    previous raw rows plus the new row, starting from zero history, give the
+    outputs, final states and final conv history of one prelude + gates +
+    recurrence over the T-token sequences (rolling conv state = causal conv)."""
+    rng = np.random.default_rng(51)
+    B, T, H_qk, H_v, dk, dv = 3, 7, 2, 4, 8, 6
+    C = 2 * H_qk * dk + H_v * dv
+    x = synth.bf16_bits(rng.standard_normal((B, T, C)).astype(np.float32))
+    w = synth.bf16_bits(rng.normal(0, 0.5, (C, 4)).astype(np.float32))
+    a = rng.standard_normal((B, T, H_v))
+    b = rng.standard_normal((B, T, H_v))
+    A_log, dt = rng.uniform(-1, 1, H_v), rng.uniform(-1, 1, H_v)
+    S0 = rng.normal(0, 0.1, (B, H_v, dv, dk))
+    P = 5
+    slots = np.array([4, 0, 2], dtype=np.int32)
+    pool = np.full((P, H_v, dv, dk), np.nan)
+    pool[slots] = S0
+    cs = np.zeros((P, 3, C), dtype=np.uint16)
+    outs = []
+    for t in range(T):
+        o, cs, pool = orc.decode_step_raw(x[:, t], w, cs, a[:, t], b[:, t], A_log, dt, pool,
+                                          slots, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv)
+        outs.append(o)
+    xs = x.reshape(B * T, C)
+    cu = np.arange(0, B * T + 1, T, dtype=np.int32)
+    q, k, v = orc.prelude(xs, w, cu, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv)
+    g, beta = orc.gates(a.reshape(B * T, H_v), b.reshape(B * T, H_v), A_log, dt)
+    o_ref, S_ref = orc.recurrent(q, k, v, g, beta, S0, cu)
+    np.testing.assert_allclose(np.stack(outs, axis=1).reshape(B * T, H_v, dv), o_ref,
+                               rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(pool[slots], S_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_array_equal(cs[slots], orc.conv_state(xs, cu))
+    assert np.isnan(pool[[1, 3]]).all() and (cs[[1, 3]] == 0).all()
+
+
 # ------------------------------------------------------------- size pins
 def test_sizes_printed_on_pages():
     """The layer shape and the fp32 state dtype reproduce the state and KV-cache
