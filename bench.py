@@ -191,6 +191,24 @@ def run_gpu(steps, warmup, path="both"):
     dec_us = e0.elapsed_time(e1) / dsteps * 1e3
 
     res["dec_us"] = dec_us
+    del pools
+
+    # the same step from raw projections (conv history in a slot pool, gates
+    # from raw a, b): gdn_layer_decode_step, pools rotated the same way
+    ld = synth.layer_decode_inputs(1005, B=B_DECODE, P=B_DECODE)
+    lpools = [to_dev(ld.pool) for _ in range(2)]
+    cpools = [to_dev(ld.conv_pool) for _ in range(2)]
+    lx, lw, la, lb, lA, ldt, lsl = (to_dev(a) for a in (ld.x, ld.w, ld.a, ld.b, ld.A_log,
+                                                         ld.dt_bias, ld.slot_idx))
+    for i in range(max(warmup, 2)):
+        gdn.gdn_layer_decode_step(lx, lw, la, lb, lA, ldt, cpools[i % 2], lpools[i % 2], lsl, o=od)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(dsteps):
+        gdn.gdn_layer_decode_step(lx, lw, la, lb, lA, ldt, cpools[i % 2], lpools[i % 2], lsl, o=od)
+    e1.record()
+    torch.cuda.synchronize()
+    res["layer_dec_us"] = e0.elapsed_time(e1) / dsteps * 1e3
     return res
 
 
@@ -413,7 +431,12 @@ def main():
                    "roofline": {"bound": "hbm",
                                 "achieved": dec_bytes / (r["dec_us"] * 1e-6) / 1e9,
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}},
+                                "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+                   "from_raw_projections": {
+                       "us_per_step": r["layer_dec_us"],
+                       "tokens_per_s": B_DECODE / (r["layer_dec_us"] * 1e-6),
+                       "what": "gdn_layer_decode_step: conv from each slot's 3-row history + the "
+                               "new raw row, gates from raw a, b, the update, history shift"}},
     }
     if "pre_us" in r:
         out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",

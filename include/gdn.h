@@ -159,6 +159,70 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
                     float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * gdn_gates -- the layer's gates from its raw per-token projections a, b:
+ *     g    = -softplus(a + dt_bias[h]) * exp(A_log[h])   (log decay, a_t = exp(g))
+ *     beta = sigmoid(b)
+ * [Dissect sec. 2.1] names the A_log and dt_bias weights of each layer.
+ *
+ *   a, b        device fp32 [T][H_v]
+ *   A_log, dt_bias  device fp32 [H_v]
+ *   g, beta     device fp32 [T][H_v] outputs (must not overlap the inputs)
+ * T = 0 is a no-op.
+ */
+int gdn_gates(const float *a, const float *b, const float *A_log, const float *dt_bias, int T,
+              int H_v, float *g, float *beta, void *stream);
+
+/*
+ * gdn_layer_prefill_workspace_size -- bytes of device workspace
+ * gdn_layer_prefill needs (host-only; 0 when T = 0): the gates' 8 bytes per
+ * token and V-head plus gdn_prefill_raw_workspace_size.
+ */
+size_t gdn_layer_prefill_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v);
+
+/*
+ * gdn_layer_prefill -- the layer's whole prefill from its raw projections
+ * ([Dissect sec. 2.1, 2.2]): gdn_gates on a, b into the workspace, then
+ * gdn_prefill_raw (conv prelude fused into the bf16 chunked prefill), then,
+ * if conv_state_out is given, each sequence's conv history for decoding on:
+ * its last three raw rows, oldest first, zero where the sequence is shorter.
+ * Bit-identical to those calls made one after the other.
+ *
+ *   x_raw, conv_w, l2_eps, initial_state, final_state, cu_seqlens, scale, o
+ *                   as for gdn_prefill_raw
+ *   a, b            device fp32 [T][H_v];  A_log, dt_bias  device fp32 [H_v]
+ *   conv_state_out  device bf16 [N][3][C_raw] output, or NULL
+ *   workspace       at least gdn_layer_prefill_workspace_size(...) bytes
+ */
+int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                      const float *A_log, const float *dt_bias, float l2_eps,
+                      const float *initial_state, float *final_state, void *conv_state_out,
+                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                      float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_layer_decode_step -- one token for each of B sequences from its raw
+ * projections: the conv window of sequence b is its slot's conv history (the
+ * three previous raw rows) followed by x_raw[b]; conv, SiLU and q/k L2 norm as
+ * in gdn_conv_prelude ([Dissect sec. 2.1]); gates as in gdn_gates; then the
+ * update of gdn_decode_step ([OOM sec. 1.2], [Dissect sec. 2.2]).  Afterwards
+ * the slot's history holds its rows 1, 2 and x_raw[b].  Bit-identical to
+ * gdn_conv_prelude on each 4-row window, gdn_gates and gdn_decode_step.
+ *
+ *   x_raw           device bf16 [B][C_raw], the new token's raw projections
+ *   conv_w, l2_eps  as for gdn_conv_prelude
+ *   a, b            device fp32 [B][H_v];  A_log, dt_bias  device fp32 [H_v]
+ *   conv_state_pool device bf16 [P][3][C_raw], updated in place for the
+ *                   addressed slots (a prefill's conv_state_out rows fit here)
+ *   state_pool, slot_idx, B, P, scale, o   as for gdn_decode_step
+ * Slots not named in slot_idx are neither read nor written. B = 0 is a no-op.
+ */
+int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                          const float *A_log, const float *dt_bias, float l2_eps,
+                          void *conv_state_pool, float *state_pool, const int32_t *slot_idx, int B,
+                          int P, int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                          void *stream);
+
+/*
  * gdn_decode_step -- one token for each of B sequences whose states live in a
  * slot pool; each addressed state is read once and overwritten in place.
  * [OOM sec. 1.2] per-token step (q, k, v, S_prev, gates) -> (o, S); the update

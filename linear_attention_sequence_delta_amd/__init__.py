@@ -29,7 +29,8 @@ GDN_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_raw_workspace_size",
-           "gdn_prefill_raw", "gdn_decode_step")
+           "gdn_prefill_raw", "gdn_gates", "gdn_layer_prefill_workspace_size",
+           "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_step")
 
 _lib = None
 
@@ -64,6 +65,15 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_raw_workspace_size.restype = Z
     L.gdn_prefill_raw.argtypes = [P, P, F, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
     L.gdn_prefill_raw.restype = I
+    L.gdn_gates.argtypes = [P, P, P, P, I, I, P, P, P]
+    L.gdn_gates.restype = I
+    L.gdn_layer_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_layer_prefill_workspace_size.restype = Z
+    L.gdn_layer_prefill.argtypes = [P, P, P, P, P, P, F, P, P, P, P, I, I, I, I, I, I, F, P, P,
+                                    Z, P]
+    L.gdn_layer_prefill.restype = I
+    L.gdn_layer_decode_step.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, F, P, P]
+    L.gdn_layer_decode_step.restype = I
     L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_decode_step.restype = I
     _lib = L
@@ -274,6 +284,137 @@ def gdn_prefill_raw(x, conv_w, g, beta, initial_state=None, cu_seqlens=None, *, 
     return o, fs
 
 
+def gdn_gates(a, b, A_log, dt_bias, *, out=None):
+    """g = -softplus(a + dt_bias) exp(A_log), beta = sigmoid(b).  a, b: fp32
+    [T, H_v]; A_log, dt_bias: fp32 [H_v].  Returns fp32 (g, beta)."""
+    torch = _torch()
+    dev = _device_of(a)
+    _need(a, "a", torch.float32, dev, 2)
+    _need(b, "b", torch.float32, dev, 2)
+    T, H_v = a.shape
+    if tuple(b.shape) != (T, H_v):
+        raise ValueError("a and b must have the same shape")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev, 1)
+        if t.numel() != H_v:
+            raise ValueError(f"{name} must have H_v = {H_v} entries")
+    if out is None:
+        g, beta = torch.empty_like(a), torch.empty_like(a)
+    else:
+        g, beta = out
+        for name, t in (("g", g), ("beta", beta)):
+            _need(t, name, torch.float32, dev, 2)
+            if tuple(t.shape) != (T, H_v):
+                raise ValueError(f"{name} must be [T, H_v]")
+    _check(lib().gdn_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), T, H_v, _ptr(g),
+                           _ptr(beta), _stream(dev)), "gdn_gates")
+    return g, beta
+
+
+def gdn_layer_prefill_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
+                                     d_v: int = 128) -> int:
+    return int(lib().gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+
+
+def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_seqlens=None, *,
+                      H_qk: int = 16, H_v: int = 48, d_k: int = 128, d_v: int = 128,
+                      l2_eps: float = 1e-6, scale: float = 1.0, final_state=True,
+                      conv_state=True, o=None, workspace=None):
+    """The layer's prefill from raw projections: gates from a, b, then the fused
+    prelude + chunked prefill, then each sequence's conv history.  x: bf16
+    [T, C_raw]; a, b: fp32 [T, H_v]; A_log, dt_bias: fp32 [H_v].  final_state /
+    conv_state: True (allocate), False/None (skip) or a tensor to write
+    (conv_state: bf16 [N, 3, C_raw]).  Returns (o, final_state, conv_state)."""
+    torch = _torch()
+    dev = _device_of(x)
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, dev, 2)
+    T, C = x.shape
+    if C != 2 * H_qk * d_k + H_v * d_v or tuple(conv_w.shape) != (C, 4):
+        raise ValueError("x / conv_w shapes do not match the head configuration")
+    for name, t in (("a", a), ("b", b)):
+        _need(t, name, torch.float32, dev, 2)
+        if tuple(t.shape) != (T, H_v):
+            raise ValueError(f"{name} must be [T, H_v]")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev, 1)
+        if t.numel() != H_v:
+            raise ValueError(f"{name} must have H_v = {H_v} entries")
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    sshape = (N, H_v, d_v, d_k)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev, 4)
+        if tuple(initial_state.shape) != sshape:
+            raise ValueError(f"initial_state must be {sshape}")
+
+    def out_arg(val, shape, dtype, name):
+        if val is True:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        if val is None or val is False:
+            return None
+        _need(val, name, dtype, dev, len(shape))
+        if tuple(val.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+        return val
+
+    fs = out_arg(final_state, sshape, torch.float32, "final_state")
+    cs = out_arg(conv_state, (N, 3, C), torch.bfloat16, "conv_state")
+    o = out_arg(True if o is None else o, (T, H_v, d_v), torch.bfloat16, "o")
+    ws_need = gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_layer_prefill(_ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log),
+                                 _ptr(dt_bias), float(l2_eps), _ptr(initial_state), _ptr(fs),
+                                 _ptr(cs), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v,
+                                 float(scale), _ptr(o), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(rc, "gdn_layer_prefill")
+    return o, fs, cs
+
+
+def gdn_layer_decode_step(x, conv_w, a, b, A_log, dt_bias, conv_state_pool, state_pool,
+                          slot_idx, *, H_qk: int = 16, H_v: int = 48, d_k: int = 128,
+                          d_v: int = 128, l2_eps: float = 1e-6, scale: float = 1.0, o=None):
+    """One token per sequence from raw projections x: bf16 [B, C_raw]; a, b:
+    fp32 [B, H_v]; conv_state_pool: bf16 [P, 3, C_raw] and state_pool: fp32
+    [P, H_v, 128, 128], both advanced in place at slot_idx.  Returns o (bf16)."""
+    torch = _torch()
+    dev = _device_of(x)
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, dev, 2)
+    B, C = x.shape
+    if C != 2 * H_qk * d_k + H_v * d_v or tuple(conv_w.shape) != (C, 4):
+        raise ValueError("x / conv_w shapes do not match the head configuration")
+    for name, t in (("a", a), ("b", b)):
+        _need(t, name, torch.float32, dev, 2)
+        if tuple(t.shape) != (B, H_v):
+            raise ValueError(f"{name} must be [B, H_v]")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev, 1)
+        if t.numel() != H_v:
+            raise ValueError(f"{name} must have H_v = {H_v} entries")
+    _need(conv_state_pool, "conv_state_pool", torch.bfloat16, dev, 3)
+    _need(state_pool, "state_pool", torch.float32, dev, 4)
+    _need(slot_idx, "slot_idx", torch.int32, dev, 1)
+    P = state_pool.shape[0]
+    if (tuple(conv_state_pool.shape) != (P, 3, C) or tuple(state_pool.shape[1:]) != (H_v, d_v, d_k)
+            or slot_idx.numel() != B):
+        raise ValueError("decode shapes disagree")
+    if o is None:
+        o = torch.empty((B, H_v, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(o, "o", torch.bfloat16, dev, 3)
+    rc = lib().gdn_layer_decode_step(_ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log),
+                                     _ptr(dt_bias), float(l2_eps), _ptr(conv_state_pool),
+                                     _ptr(state_pool), _ptr(slot_idx), B, P, H_qk, H_v, d_k, d_v,
+                                     float(scale), _ptr(o), _stream(dev))
+    _check(rc, "gdn_layer_decode_step")
+    return o
+
+
 def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.0, o=None):
     """One token per sequence; states in state_pool[slot_idx[b]] advance in place.
     q, k: bf16 [B, H_qk, 128]; v: bf16 [B, H_v, 128]; g, beta: fp32 [B, H_v];
@@ -306,4 +447,5 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.
 
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
-           "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]
+           "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
+           "gdn_layer_decode_step", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

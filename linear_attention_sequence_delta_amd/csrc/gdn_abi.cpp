@@ -182,10 +182,15 @@ size_t gdn_prefill_raw_workspace_size(int N, int T, int H_qk, int H_v, int d_k, 
     return gdn::chunked_workspace_bytes(N, T, H_qk, H_v, true);
 }
 
-int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
-                    const float *beta, const float *initial_state, float *final_state,
-                    const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                    float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a prefill from raw projections (nothing is enqueued).
+int check_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
+                      const float *beta, const float *initial_state, const float *final_state,
+                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                      float scale, const void *o, const void *workspace, size_t ws_bytes) {
     int rc;
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
@@ -219,6 +224,20 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
                      overlaps(workspace, need, final_state, ns) ||
                      overlaps(workspace, need, initial_state, ns)))
         return fail(GDN_ERR_INVALID_ARG, "workspace must not overlap inputs or outputs");
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
+                    const float *beta, const float *initial_state, float *final_state,
+                    const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                    float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state, final_state,
+                               cu_seqlens, N, T, H_qk, H_v, d_k, d_v, scale, o, workspace, ws_bytes);
+    if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
     hipError_t e;
@@ -231,6 +250,127 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
                                             final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
                                             workspace, s);
     return finish(e, s, "gdn_prefill_raw launch");
+}
+
+int gdn_gates(const float *a, const float *b, const float *A_log, const float *dt_bias, int T,
+              int H_v, float *g, float *beta, void *stream) {
+    if (T < 0 || H_v < 1) return fail(GDN_ERR_INVALID_ARG, "T must be >= 0 and H_v >= 1");
+    if (T == 0) return ok();
+    if (!a || !b || !A_log || !dt_bias || !g || !beta)
+        return fail(GDN_ERR_INVALID_ARG, "a, b, A_log, dt_bias, g and beta must be non-NULL");
+    const size_t n = (size_t)T * H_v * 4, nh = (size_t)H_v * 4;
+    if (overlaps(g, n, beta, n) || overlaps(g, n, a, n) || overlaps(g, n, b, n) ||
+        overlaps(beta, n, a, n) || overlaps(beta, n, b, n) || overlaps(g, n, A_log, nh) ||
+        overlaps(g, n, dt_bias, nh) || overlaps(beta, n, A_log, nh) || overlaps(beta, n, dt_bias, nh))
+        return fail(GDN_ERR_INVALID_ARG, "g and beta must not overlap each other or the inputs");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdn::launch_gates(a, b, A_log, dt_bias, T, H_v, g, beta, s), s, "gdn_gates launch");
+}
+
+size_t gdn_layer_prefill_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v) {
+    if (N < 1 || T < 1 || H_qk < 1 || H_v < 1) return 0;
+    const size_t gate = ((size_t)T * H_v * 4 + 255) & ~size_t(255);
+    return 2 * gate + gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+}
+
+int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                      const float *A_log, const float *dt_bias, float l2_eps,
+                      const float *initial_state, float *final_state, void *conv_state_out,
+                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                      float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
+    const size_t need = gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+    if (ws_bytes < need || (need > 0 && !workspace))
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (T > 0 && (!a || !b || !A_log || !dt_bias))
+        return fail(GDN_ERR_INVALID_ARG, "a, b, A_log and dt_bias must be non-NULL");
+    const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
+    const size_t ng = (size_t)T * H_v * 4, nh = (size_t)H_v * 4, nc = (size_t)N * 3 * craw * 2;
+    const size_t nx = (size_t)T * craw * 2, nv = (size_t)T * H_v * gdn::kD * 2;
+    const size_t ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
+    if (need > 0 && (overlaps(workspace, need, a, ng) || overlaps(workspace, need, b, ng) ||
+                     overlaps(workspace, need, A_log, nh) || overlaps(workspace, need, dt_bias, nh) ||
+                     overlaps(workspace, need, conv_state_out, nc)))
+        return fail(GDN_ERR_INVALID_ARG, "workspace must not overlap inputs or outputs");
+    if (conv_state_out &&
+        (overlaps(conv_state_out, nc, x_raw, nx) || overlaps(conv_state_out, nc, o, nv) ||
+         overlaps(conv_state_out, nc, final_state, ns) || overlaps(conv_state_out, nc, initial_state, ns) ||
+         overlaps(conv_state_out, nc, a, ng) || overlaps(conv_state_out, nc, b, ng)))
+        return fail(GDN_ERR_INVALID_ARG, "conv_state_out must not overlap inputs or outputs");
+    if (overlaps(o, nv, a, ng) || overlaps(o, nv, b, ng) ||
+        (final_state && (overlaps(final_state, ns, a, ng) || overlaps(final_state, ns, b, ng))))
+        return fail(GDN_ERR_INVALID_ARG, "o and final_state must not overlap a or b");
+    // the gates go to the front of the workspace, the prefill's workspace follows
+    const size_t gate = need > 0 ? ((size_t)T * H_v * 4 + 255) & ~size_t(255) : 0;
+    float *g = need > 0 ? static_cast<float *>(workspace) : nullptr;
+    float *beta = need > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + gate) : nullptr;
+    void *rest = need > 0 ? static_cast<char *>(workspace) + 2 * gate : nullptr;
+    const size_t rest_bytes = need > 0 ? ws_bytes - 2 * gate : 0;
+    rc = check_prefill_raw(x_raw, conv_w, l2_eps, T > 0 ? g : nullptr, T > 0 ? beta : nullptr,
+                           initial_state, final_state, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
+                           scale, o, rest, rest_bytes);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
+    hipError_t e = hipSuccess;
+    if (T == 0)
+        e = gdn::launch_recurrent_prefill(gdn::kIoBF16, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                          initial_state, final_state, cu_seqlens, N, T, H_qk, H_v,
+                                          scale, o, s);
+    else if ((e = gdn::launch_gates(a, b, A_log, dt_bias, T, H_v, g, beta, s)) == hipSuccess)
+        e = gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
+                                            final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
+                                            rest, s);
+    if (e == hipSuccess && conv_state_out)
+        e = gdn::launch_conv_hist(x_raw, cu_seqlens, N, T, (int)craw, conv_state_out, s);
+    return finish(e, s, "gdn_layer_prefill launch");
+}
+
+int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                          const float *A_log, const float *dt_bias, float l2_eps,
+                          void *conv_state_pool, float *state_pool, const int32_t *slot_idx, int B,
+                          int P, int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                          void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if (B < 0) return fail(GDN_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (P < 1) return fail(GDN_ERR_INVALID_ARG, "P must be >= 1 (got %d)", P);
+    if (B > P) return fail(GDN_ERR_INVALID_ARG, "B (%d) distinct slots cannot fit a pool of P=%d", B, P);
+    if ((long long)B * H_v > 0x7FFFFFFFLL) return fail(GDN_ERR_INVALID_ARG, "B * H_v too large");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps))
+        return fail(GDN_ERR_INVALID_ARG, "l2_eps must be finite and >= 0");
+    if (B == 0) return ok();
+    if (!x_raw || !conv_w || !a || !b || !A_log || !dt_bias || !conv_state_pool || !state_pool ||
+        !slot_idx || !o)
+        return fail(GDN_ERR_INVALID_ARG, "every pointer argument must be non-NULL");
+    const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
+    const size_t nx = (size_t)B * craw * 2, nc = (size_t)P * 3 * craw * 2, nw = craw * 4 * 2;
+    const size_t npool = (size_t)P * H_v * gdn::kD * gdn::kD * 4, no = (size_t)B * H_v * gdn::kD * 2;
+    const size_t ng = (size_t)B * H_v * 4;
+    if (overlaps(o, no, state_pool, npool) || overlaps(o, no, conv_state_pool, nc) ||
+        overlaps(o, no, x_raw, nx) || overlaps(o, no, a, ng) || overlaps(o, no, b, ng))
+        return fail(GDN_ERR_INVALID_ARG, "o must not overlap inputs or the pools");
+    if (overlaps(conv_state_pool, nc, state_pool, npool) || overlaps(conv_state_pool, nc, x_raw, nx) ||
+        overlaps(conv_state_pool, nc, conv_w, nw) || overlaps(state_pool, npool, x_raw, nx) ||
+        overlaps(state_pool, npool, conv_w, nw))
+        return fail(GDN_ERR_INVALID_ARG, "the pools must not overlap each other or the inputs");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        int bad = 0;
+        hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
+        if (e != hipSuccess) return hip_fail(e, "slot_idx check");
+        if (bad) return fail(GDN_ERR_DEVICE_CHECK, "slot_idx has ids outside [0, %d) or repeated ids", P);
+    }
+    // the decode reads every addressed slot's history; the shift that follows
+    // on the same stream rewrites it
+    hipError_t e = gdn::launch_decode_step_raw(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps,
+                                               conv_state_pool, state_pool, slot_idx, B, H_qk, H_v,
+                                               scale, o, s);
+    if (e == hipSuccess) e = gdn::launch_conv_shift(x_raw, slot_idx, B, (int)craw, conv_state_pool, s);
+    return finish(e, s, "gdn_layer_decode_step launch");
 }
 
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -89,6 +89,17 @@ __device__ __forceinline__ uint4 pack_bf8(const float *y) {
     return out;
 }
 
+// Gates from the raw per-token projections a, b of a V-head and the layer's
+// A_log, dt_bias: log decay g = -softplus(a + dt_bias) * exp(A_log) (softplus
+// written max(x, 0) + log1p(exp(-|x|)), which cannot overflow) and write
+// strength beta = sigmoid(b).  Shared by every kernel that forms gates.
+__device__ __forceinline__ float gate_log_decay(float a, float A_log, float dt_bias) {
+    const float x = a + dt_bias;
+    const float softplus = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    return -softplus * expf(A_log);
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.f / (1.f + expf(-b)); }
+
 // Load 4 consecutive values (bf16 bits or fp32) as fp32.
 __device__ __forceinline__ void load4(const uint16_t *p, float *d) {
     uint2 u = *reinterpret_cast<const uint2 *>(p);

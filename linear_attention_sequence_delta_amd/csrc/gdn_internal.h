@@ -39,6 +39,19 @@ hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, c
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                       float scale, void *o, void *workspace, hipStream_t stream);
 
+// The layer's forward from raw projections: gates, conv history, decode.
+hipError_t launch_gates(const float *a, const float *b, const float *A_log, const float *dt_bias,
+                        int T, int H_v, float *g, float *beta, hipStream_t stream);
+hipError_t launch_conv_hist(const void *x, const int32_t *cu_seqlens, int N, int T, int C_raw,
+                            void *hist, hipStream_t stream);
+hipError_t launch_conv_shift(const void *x, const int32_t *slot_idx, int B, int C_raw, void *hist,
+                             hipStream_t stream);
+hipError_t launch_decode_step_raw(const void *x, const void *w, const float *a, const float *b,
+                                  const float *A_log, const float *dt_bias, float eps,
+                                  const void *conv_hist, float *pool, const int32_t *slot_idx,
+                                  int B, int H_qk, int H_v, float scale, void *o,
+                                  hipStream_t stream);
+
 // Device-side precondition checks (GDN_DEBUG=1): launch a one-workgroup scan,
 // wait for the stream, and return the violation bits in *result (0 = ok).
 hipError_t debug_check_cu_seqlens(const int32_t *cu_seqlens, int N, int T, hipStream_t stream,

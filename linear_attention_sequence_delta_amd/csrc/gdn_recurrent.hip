@@ -71,11 +71,30 @@ __device__ __forceinline__ float delta_rows(float (&s)[8][8], const float *kk, c
     return mine;
 }
 
+// Decode from the raw projections: the new token's raw row, each slot's
+// three previous raw rows (its conv history), the conv taps, the raw gate
+// projections and the layer's A_log, dt_bias.
+struct RawDecodeIn {
+    const uint16_t *x;       // [B][C_raw] bf16
+    const uint16_t *w;       // [C_raw][4] bf16
+    const uint16_t *conv;    // [P][3][C_raw] bf16, read only here
+    const float *a, *b;      // [B][H_v]
+    const float *A_log, *dt_bias;   // [H_v]
+    float eps;
+};
+
+// With kRaw, the workgroup first forms its own q, k (its QK head) and v (its
+// V-head) from the raw rows with the conv prelude's arithmetic and lane layout
+// (16 lanes x 8 channels per 128-channel block, the norm reduced over the
+// 16-lane row), rounds them to bf16 as the prelude does, and hands them to the
+// other threads through LDS; the gates come from the shared gate helpers.  The
+// state loads are issued first, so this overlaps them.
+template <bool kRaw>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ pool,
     const int32_t *__restrict__ slot_idx, int H_qk, int H_v, float scale,
-    uint16_t *__restrict__ o) {
+    uint16_t *__restrict__ o, const RawDecodeIn raw) {
     const RowMap m;
     const int b = blockIdx.x / H_v;
     const int h = blockIdx.x - b * H_v;
@@ -90,15 +109,48 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         load4(S + m.row(j) * kD + m.col(1), s[j] + 4);
     }
     float kk[8], qq[8], vr[8];
-    load_vec8(k + ((size_t)b * H_qk + hq) * kD, m, kk);
-    load_vec8(q + ((size_t)b * H_qk + hq) * kD, m, qq);
+    float alpha, bt;
+    if constexpr (kRaw) {
+        __shared__ __attribute__((aligned(16))) uint16_t sqkv[3][kD];   // q, k, v (bf16)
+        if (threadIdx.x < 48) {                    // wave 0, lanes 0-15 q, 16-31 k, 32-47 v
+            const int part = threadIdx.x >> 4, cg = threadIdx.x & 15;
+            const size_t C = (size_t)(2 * H_qk + H_v) * kD;
+            const size_t ch = (size_t)(part == 0 ? hq : part == 1 ? H_qk + hq : 2 * H_qk + h) * kD + 8 * cg;
+            float wt[4][8];
+            load_taps8(raw.w, ch, wt);
+            const uint16_t *hist = raw.conv + (size_t)slot * 3 * C + ch;
+            float xm[4][8];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) unpack8(*reinterpret_cast<const uint4 *>(hist + j * C), xm[j]);
+            unpack8(*reinterpret_cast<const uint4 *>(raw.x + (size_t)b * C + ch), xm[3]);
+            float y[8], ss = 0.f;
+            conv_silu8(wt, xm[0], xm[1], xm[2], xm[3], y, ss);
+            const float rn = rsqrtf(row16_sum(ss) + raw.eps);   // full 16-lane rows: 0-15, 16-31, 32-47
+            if (part < 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] *= rn;
+            }
+            *reinterpret_cast<uint4 *>(sqkv[part] + 8 * cg) = pack_bf8(y);
+        }
+        const size_t gi = (size_t)b * H_v + h;
+        alpha = expf(gate_log_decay(raw.a[gi], raw.A_log[h], raw.dt_bias[h]));
+        bt = gate_beta(raw.b[gi]);
+        __syncthreads();
+        load_vec8(sqkv[1], m, kk);
+        load_vec8(sqkv[0], m, qq);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[j] = bf2f(sqkv[2][m.row(j)]);
+    } else {
+        load_vec8(k + ((size_t)b * H_qk + hq) * kD, m, kk);
+        load_vec8(q + ((size_t)b * H_qk + hq) * kD, m, qq);
+        const uint16_t *vb = v + ((size_t)b * H_v + h) * kD;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vr[j] = bf2f(vb[m.row(j)]);
+        alpha = expf(g[(size_t)b * H_v + h]);
+        bt = beta[(size_t)b * H_v + h];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) qq[e] *= scale;
-    const uint16_t *vb = v + ((size_t)b * H_v + h) * kD;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) vr[j] = bf2f(vb[m.row(j)]);
-    const float alpha = expf(g[(size_t)b * H_v + h]);
-    const float bt = beta[(size_t)b * H_v + h];
 
     const float mine = delta_rows(s, kk, qq, vr, alpha, bt, m);
 
@@ -186,10 +238,23 @@ __global__ __launch_bounds__(256) void recurrent_prefill_kernel(
 hipError_t launch_decode_step(const void *q, const void *k, const void *v, const float *g,
                               const float *beta, float *pool, const int32_t *slot_idx, int B,
                               int H_qk, int H_v, float scale, void *o, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_step_kernel, dim3(B * H_v), dim3(256), 0, stream,
+    hipLaunchKernelGGL(decode_step_kernel<false>, dim3(B * H_v), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), g, beta, pool, slot_idx, H_qk, H_v,
-                       scale, static_cast<uint16_t *>(o));
+                       scale, static_cast<uint16_t *>(o), RawDecodeIn{});
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step_raw(const void *x, const void *w, const float *a, const float *b,
+                                  const float *A_log, const float *dt_bias, float eps,
+                                  const void *conv_hist, float *pool, const int32_t *slot_idx,
+                                  int B, int H_qk, int H_v, float scale, void *o,
+                                  hipStream_t stream) {
+    const RawDecodeIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w),
+                          static_cast<const uint16_t *>(conv_hist), a, b, A_log, dt_bias, eps};
+    hipLaunchKernelGGL(decode_step_kernel<true>, dim3(B * H_v), dim3(256), 0, stream, nullptr,
+                       nullptr, nullptr, nullptr, nullptr, pool, slot_idx, H_qk, H_v, scale,
+                       static_cast<uint16_t *>(o), raw);
     return hipGetLastError();
 }
 

@@ -144,3 +144,68 @@ def test_prefill_raw_workspace_size():
     L = gdn.lib()
     need = gdn.gdn_prefill_raw_workspace_size(1, 64, 16, 48)
     assert _prefill_raw(L, ws=1 << 41, ws_bytes=need - 1) == gdn.GDN_ERR_WORKSPACE
+
+
+def test_gates_rejects_bad_arguments():
+    L = gdn.lib()
+    big = 1 << 40
+    assert L.gdn_gates(big, big + (1 << 30), 1 << 39, (1 << 39) + 4096, 64, 48, None, 2 * big,
+                       None) == gdn.GDN_ERR_INVALID_ARG                       # g NULL
+    assert L.gdn_gates(big, big + (1 << 30), 1 << 39, (1 << 39) + 4096, 64, 48, big, 2 * big,
+                       None) == gdn.GDN_ERR_INVALID_ARG                       # g overlaps a
+    assert L.gdn_gates(None, None, None, None, 0, 48, None, None, None) == gdn.GDN_OK   # T = 0
+    assert L.gdn_gates(None, None, None, None, 4, 0, None, None, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def _layer_prefill(L, **kw):
+    big = 1 << 40
+    a = dict(x=big, w=2 * big, a=3 * big, b=4 * big, A=5 * big, dt=6 * big, eps=1e-6, S0=None,
+             Sf=None, cs=None, cu=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0,
+             o=7 * big, ws=8 * big, ws_bytes=gdn.gdn_layer_prefill_workspace_size(1, 64, 16, 48),
+             stream=None)
+    a.update(kw)
+    return L.gdn_layer_prefill(a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"], a["S0"],
+                               a["Sf"], a["cs"], a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"],
+                               a["d_k"], a["d_v"], a["scale"], a["o"], a["ws"], a["ws_bytes"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(A=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(ws_bytes=1), gdn.GDN_ERR_WORKSPACE),
+    (dict(cs=1 << 40), gdn.GDN_ERR_INVALID_ARG),        # conv history out overlaps x_raw
+    (dict(o=3 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),    # o overlaps a
+    (dict(eps=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(d_v=64), gdn.GDN_ERR_UNSUPPORTED),
+])
+def test_layer_prefill_rejects_bad_arguments(kw, code):
+    L = gdn.lib()
+    assert _layer_prefill(L, **kw) == code
+    assert L.gdn_last_error().decode()
+
+
+def test_layer_prefill_workspace_size():
+    for N, T in ((1, 1), (1, 4133), (8, 65536)):
+        gate = (T * 48 * 4 + 255) // 256 * 256
+        assert (gdn.gdn_layer_prefill_workspace_size(N, T, 16, 48)
+                == 2 * gate + gdn.gdn_prefill_raw_workspace_size(N, T, 16, 48))
+    assert gdn.gdn_layer_prefill_workspace_size(1, 0, 16, 48) == 0
+
+
+def test_layer_decode_rejects_bad_arguments():
+    L = gdn.lib()
+    big = 1 << 40
+
+    def call(**kw):
+        a = dict(x=big, w=2 * big, a=3 * big, b=4 * big, A=5 * big, dt=6 * big, eps=1e-6,
+                 cs=7 * big, pool=8 * big, slots=9 * big, B=4, P=8, o=10 * big)
+        a.update(kw)
+        return L.gdn_layer_decode_step(a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"],
+                                       a["cs"], a["pool"], a["slots"], a["B"], a["P"], 16, 48, 128,
+                                       128, 1.0, a["o"], None)
+    assert call(cs=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(B=9) == gdn.GDN_ERR_INVALID_ARG                 # more sequences than slots
+    assert call(cs=8 * big) == gdn.GDN_ERR_INVALID_ARG          # the two pools overlap
+    assert call(o=8 * big) == gdn.GDN_ERR_INVALID_ARG           # o overlaps the state pool
+    assert call(B=0, x=None) == gdn.GDN_OK                      # B = 0: no-op
