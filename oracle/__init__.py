@@ -226,3 +226,36 @@ def decode_step_raw(x, w, conv_state_pool, a, b, A_log, dt_bias, pool, slot_idx,
     new_cs = cs.copy()
     new_cs[slots] = np.concatenate([cs[slots][:, 1:], x[:, None, :]], axis=1)
     return o, new_cs, new_pool
+
+
+def decode_multi_step(q, k, v, g, beta, pool, slot_idx, scale=1.0):
+    """n tokens per sequence in order (speculative-decoding verification):
+    q, k [B, n, H_qk, dk]; v [B, n, H_v, dv]; g, beta [B, n, H_v].  Token j of
+    sequence b is ``decode_step`` applied to slot slot_idx[b] after tokens
+    0..j-1.  Returns (o [B, n, H_v, dv], snapshots [B, n, H_v, dv, dk] with
+    snapshots[b, j] the slot's state before token j, new pool) in fp64."""
+    q, k, v, g, beta = (f64(a) for a in (q, k, v, g, beta))
+    B, n = q.shape[:2]
+    pool = f64(pool).copy()
+    slots = np.ascontiguousarray(slot_idx, dtype=np.int32)
+    o = np.zeros((B, n) + v.shape[2:])
+    snaps = np.zeros((B, n) + pool.shape[1:])
+    for j in range(n):
+        snaps[:, j] = pool[slots]
+        o[:, j], pool = decode_step(q[:, j], k[:, j], v[:, j], g[:, j], beta[:, j], pool, slots,
+                                    scale)
+    return o, snaps, pool
+
+
+def state_rollback(snapshots, n_keep, pool, slot_idx):
+    """Keep the first n_keep[b] of sequence b's n verified tokens: its slot
+    takes snapshots[b, n_keep[b]] (the state after n_keep[b] tokens) when
+    n_keep[b] < n, and is left as it is when n_keep[b] == n.  Returns the new
+    pool (a copy, same dtype)."""
+    pool = np.array(pool, copy=True)
+    snaps = np.asarray(snapshots)
+    n = snaps.shape[1]
+    for b, s in enumerate(np.asarray(slot_idx)):
+        if n_keep[b] < n:
+            pool[s] = snaps[b, n_keep[b]]
+    return pool

@@ -398,6 +398,41 @@ def test_raw_decode_chain_equals_prefill(orc):
     assert np.isnan(pool[[1, 3]]).all() and (cs[[1, 3]] == 0).all()
 
 
+# ----------------------------------------------- multi-token verification
+def test_decode_multi_step_equals_prefill_and_rollback(orc):
+    """n tokens per sequence through decode_multi_step equal a prefill of those
+    n tokens from each slot's state (outputs and final state); every snapshot j
+    equals the prefill of the first j tokens; rolling back to n_keep gives the
+    state after n_keep tokens."""
+    rng = np.random.default_rng(61)
+    B, n, H_qk, H_v, dk, dv, P = 3, 4, 2, 4, 8, 6, 5
+    q = rng.standard_normal((B, n, H_qk, dk))
+    k = rng.standard_normal((B, n, H_qk, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, n, H_v, dv))
+    g = -rng.uniform(0.01, 0.5, (B, n, H_v))
+    beta = rng.uniform(0, 1, (B, n, H_v))
+    slots = np.array([2, 4, 0], dtype=np.int32)
+    pool = rng.normal(0, 0.1, (P, H_v, dv, dk))
+    o, snaps, new_pool = orc.decode_multi_step(q, k, v, g, beta, pool, slots)
+    for b in range(B):
+        s = slots[b]
+        o_ref, S_ref = orc.recurrent(q[b], k[b], v[b], g[b], beta[b], pool[s:s + 1])
+        np.testing.assert_allclose(o[b], o_ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(new_pool[s], S_ref[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_array_equal(snaps[b, 0], pool[s])
+        for j in range(1, n):
+            _, S_j = orc.recurrent(q[b, :j], k[b, :j], v[b, :j], g[b, :j], beta[b, :j],
+                                   pool[s:s + 1])
+            np.testing.assert_allclose(snaps[b, j], S_j[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(new_pool[[1, 3]], pool[[1, 3]])
+    keep = np.array([0, 4, 2])
+    rolled = orc.state_rollback(snaps, keep, new_pool, slots)
+    np.testing.assert_array_equal(rolled[2], pool[2])           # nothing kept
+    np.testing.assert_array_equal(rolled[4], new_pool[4])       # everything kept
+    np.testing.assert_array_equal(rolled[0], snaps[2, 2])
+
+
 # ------------------------------------------------------------- size pins
 def test_sizes_printed_on_pages():
     """The layer shape and the fp32 state dtype reproduce the state and KV-cache
