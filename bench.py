@@ -58,6 +58,7 @@ PRELUDE_BYTES_PER_TOKEN = 2 * 2 * (2 * H_QK * D + H_V * D)
 DECODE_BYTES_PER_SEQ = (H_V * (2 * D * D * 4 + 2 * D * 2 + 2 * 4) + 2 * H_QK * D * 2)
 
 T_LONG, LONG_STEPS, STACK_LAYERS = 262144, 64, 48
+MULTI_TOKENS = 4
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T32768.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_prefill_T32768.txt")
@@ -97,6 +98,7 @@ def _events(torch):
 
 
 def run_gpu(steps, warmup, path="both"):
+    import numpy as np
     import torch
     import linear_attention_sequence_delta_amd as gdn
     import synth
@@ -209,6 +211,26 @@ def run_gpu(steps, warmup, path="both"):
     e1.record()
     torch.cuda.synchronize()
     res["layer_dec_us"] = e0.elapsed_time(e1) / dsteps * 1e3
+    del lpools, cpools
+
+    # 4 tokens per sequence in one call (speculative verification), B = 256,
+    # with and without the per-token state snapshots
+    n_mt = MULTI_TOKENS
+    mq, mk, mv, mg, mb = (to_dev(np.repeat(a[:, None], n_mt, axis=1))
+                          for a in (d.q, d.k, d.v, d.g, d.beta))
+    mo = torch.empty((B_DECODE, n_mt, H_V, D), dtype=torch.bfloat16, device=dev)
+    mpools = [to_dev(d.pool) for _ in range(2)]
+    snaps = torch.empty((B_DECODE, n_mt, H_V, D, D), dtype=torch.float32, device=dev)
+    for key, sn in (("multi_us", None), ("multi_snap_us", snaps)):
+        for i in range(2):
+            gdn.gdn_decode_multi_step(mq, mk, mv, mg, mb, mpools[i % 2], slots, o=mo, snapshots=sn)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(dsteps):
+            gdn.gdn_decode_multi_step(mq, mk, mv, mg, mb, mpools[i % 2], slots, o=mo, snapshots=sn)
+        e1.record()
+        torch.cuda.synchronize()
+        res[key] = e0.elapsed_time(e1) / dsteps * 1e3
     return res
 
 
@@ -432,6 +454,14 @@ def main():
                                 "achieved": dec_bytes / (r["dec_us"] * 1e-6) / 1e9,
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+                   "multi_token": {
+                       "tokens_per_call": MULTI_TOKENS,
+                       "us_per_call": r["multi_us"],
+                       "tokens_per_s": B_DECODE * MULTI_TOKENS / (r["multi_us"] * 1e-6),
+                       "us_per_call_with_snapshots": r["multi_snap_us"],
+                       "what": "gdn_decode_multi_step: 4 tokens per sequence in one pass over "
+                               "the state (speculative verification); with snapshots it also "
+                               "writes the state before each token for rollback"},
                    "from_raw_projections": {
                        "us_per_step": r["layer_dec_us"],
                        "tokens_per_s": B_DECODE / (r["layer_dec_us"] * 1e-6),

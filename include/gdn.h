@@ -223,6 +223,41 @@ int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a,
                           void *stream);
 
 /*
+ * gdn_decode_multi_step -- n_tok tokens for each of B sequences, applied in
+ * order to the slot's state, as when a speculative decoder verifies n_tok
+ * drafted tokens in one call ([Dissect sec. 2.2] update per token).  Token j
+ * of sequence b sees the state after tokens 0..j-1; o is the output of every
+ * token; the slot ends with the state after all n_tok tokens.
+ *
+ *   q, k        device bf16 [B][n_tok][H_qk][d_k];  v  device bf16 [B][n_tok][H_v][d_v]
+ *   g, beta     device fp32 [B][n_tok][H_v]
+ *   state_pool, slot_idx, B, P, scale   as for gdn_decode_step
+ *   o           device bf16 [B][n_tok][H_v][d_v] output
+ *   snapshots   device fp32 [B][n_tok][H_v][d_v][d_k] output, or NULL: entry
+ *               [b][j] is the slot's state before token j (so after j tokens),
+ *               for gdn_state_rollback
+ * B = 0 is a no-op; n_tok >= 1.
+ */
+int gdn_decode_multi_step(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, float *state_pool, const int32_t *slot_idx, int B,
+                          int P, int n_tok, int H_qk, int H_v, int d_k, int d_v, float scale,
+                          void *o, float *snapshots, void *stream);
+
+/*
+ * gdn_state_rollback -- after gdn_decode_multi_step, keep only the first
+ * n_keep[b] tokens of sequence b: its slot takes snapshots[b][n_keep[b]]
+ * when n_keep[b] < n_tok and is left alone when n_keep[b] = n_tok.
+ *
+ *   snapshots   device fp32 [B][n_tok][H_v][d_v][d_k] (from gdn_decode_multi_step)
+ *   n_keep      device int32 [B], each in [0, n_tok] (clamped to it)
+ *   state_pool, slot_idx, B, P   as for gdn_decode_step (same slot_idx as the
+ *               gdn_decode_multi_step call)
+ */
+int gdn_state_rollback(const float *snapshots, const int32_t *n_keep, int n_tok, float *state_pool,
+                       const int32_t *slot_idx, int B, int P, int H_v, int d_k, int d_v,
+                       void *stream);
+
+/*
  * gdn_decode_step -- one token for each of B sequences whose states live in a
  * slot pool; each addressed state is read once and overwritten in place.
  * [OOM sec. 1.2] per-token step (q, k, v, S_prev, gates) -> (o, S); the update

@@ -30,7 +30,8 @@ GDN_BF16 = 1
 EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_raw", "gdn_gates", "gdn_layer_prefill_workspace_size",
-           "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_step")
+           "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_multi_step",
+           "gdn_state_rollback", "gdn_decode_step")
 
 _lib = None
 
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_layer_prefill.restype = I
     L.gdn_layer_decode_step.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_layer_decode_step.restype = I
+    L.gdn_decode_multi_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P]
+    L.gdn_decode_multi_step.restype = I
+    L.gdn_state_rollback.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
+    L.gdn_state_rollback.restype = I
     L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_decode_step.restype = I
     _lib = L
@@ -415,6 +420,63 @@ def gdn_layer_decode_step(x, conv_w, a, b, A_log, dt_bias, conv_state_pool, stat
     return o
 
 
+def gdn_decode_multi_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.0, o=None,
+                          snapshots=False):
+    """n tokens per sequence in order.  q, k: bf16 [B, n, H_qk, 128]; v: bf16
+    [B, n, H_v, 128]; g, beta: fp32 [B, n, H_v]; the pool advances in place.
+    snapshots: True (allocate), False/None (skip) or an fp32
+    [B, n, H_v, 128, 128] tensor that receives the state before each token.
+    Returns (o bf16 [B, n, H_v, 128], snapshots or None)."""
+    torch = _torch()
+    dev = _device_of(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev, 4)
+    B, n, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    _need(g, "g", torch.float32, dev, 3)
+    _need(beta, "beta", torch.float32, dev, 3)
+    _need(state_pool, "state_pool", torch.float32, dev, 4)
+    _need(slot_idx, "slot_idx", torch.int32, dev, 1)
+    P = state_pool.shape[0]
+    if (tuple(k.shape) != (B, n, H_qk, d_k) or tuple(v.shape[:2]) != (B, n)
+            or tuple(g.shape) != (B, n, H_v) or tuple(beta.shape) != (B, n, H_v)
+            or tuple(state_pool.shape[1:]) != (H_v, d_v, d_k) or slot_idx.numel() != B):
+        raise ValueError("multi-token decode shapes disagree")
+    if o is None:
+        o = torch.empty((B, n, H_v, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(o, "o", torch.bfloat16, dev, 4)
+    if snapshots is True:
+        snapshots = torch.empty((B, n, H_v, d_v, d_k), dtype=torch.float32, device=dev)
+    elif snapshots is False:
+        snapshots = None
+    elif snapshots is not None:
+        _need(snapshots, "snapshots", torch.float32, dev, 5)
+    rc = lib().gdn_decode_multi_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(state_pool), _ptr(slot_idx), B, P, n, H_qk, H_v, d_k,
+                                     d_v, float(scale), _ptr(o), _ptr(snapshots), _stream(dev))
+    _check(rc, "gdn_decode_multi_step")
+    return o, snapshots
+
+
+def gdn_state_rollback(snapshots, n_keep, state_pool, slot_idx):
+    """Slot slot_idx[b] takes snapshots[b, n_keep[b]] when n_keep[b] < n (kept
+    otherwise).  snapshots: fp32 [B, n, H_v, 128, 128]; n_keep: int32 [B]."""
+    torch = _torch()
+    dev = _device_of(snapshots)
+    _need(snapshots, "snapshots", torch.float32, dev, 5)
+    _need(n_keep, "n_keep", torch.int32, dev, 1)
+    _need(state_pool, "state_pool", torch.float32, dev, 4)
+    _need(slot_idx, "slot_idx", torch.int32, dev, 1)
+    B, n, H_v, d_v, d_k = snapshots.shape
+    if n_keep.numel() != B or slot_idx.numel() != B or tuple(state_pool.shape[1:]) != (H_v, d_v, d_k):
+        raise ValueError("rollback shapes disagree")
+    rc = lib().gdn_state_rollback(_ptr(snapshots), _ptr(n_keep), n, _ptr(state_pool),
+                                  _ptr(slot_idx), B, state_pool.shape[0], H_v, d_k, d_v,
+                                  _stream(dev))
+    _check(rc, "gdn_state_rollback")
+
+
 def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.0, o=None):
     """One token per sequence; states in state_pool[slot_idx[b]] advance in place.
     q, k: bf16 [B, H_qk, 128]; v: bf16 [B, H_v, 128]; g, beta: fp32 [B, H_v];
@@ -448,4 +510,5 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
            "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
-           "gdn_layer_decode_step", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]
+           "gdn_layer_decode_step", "gdn_decode_multi_step", "gdn_state_rollback",
+           "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

@@ -373,6 +373,70 @@ int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a,
     return finish(e, s, "gdn_layer_decode_step launch");
 }
 
+int gdn_decode_multi_step(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, float *state_pool, const int32_t *slot_idx, int B,
+                          int P, int n_tok, int H_qk, int H_v, int d_k, int d_v, float scale,
+                          void *o, float *snapshots, void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if (B < 0) return fail(GDN_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (P < 1) return fail(GDN_ERR_INVALID_ARG, "P must be >= 1 (got %d)", P);
+    if (n_tok < 1) return fail(GDN_ERR_INVALID_ARG, "n_tok must be >= 1 (got %d)", n_tok);
+    if (B > P) return fail(GDN_ERR_INVALID_ARG, "B (%d) distinct slots cannot fit a pool of P=%d", B, P);
+    if ((long long)B * H_v > 0x7FFFFFFFLL || (long long)B * n_tok * H_v > 0x7FFFFFFFLL)
+        return fail(GDN_ERR_INVALID_ARG, "B * n_tok * H_v too large");
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (B == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !state_pool || !slot_idx || !o)
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta, state_pool, slot_idx and o must be non-NULL");
+    const size_t st = (size_t)gdn::kD * gdn::kD * 4;
+    const size_t npool = (size_t)P * H_v * st, nsnap = (size_t)B * n_tok * H_v * st;
+    const size_t nqk = (size_t)B * n_tok * H_qk * gdn::kD * 2, nv = (size_t)B * n_tok * H_v * gdn::kD * 2;
+    const size_t ng = (size_t)B * n_tok * H_v * 4;
+    if (overlaps(o, nv, state_pool, npool) || overlaps(o, nv, q, nqk) || overlaps(o, nv, k, nqk) ||
+        overlaps(o, nv, v, nv) || overlaps(o, nv, snapshots, nsnap))
+        return fail(GDN_ERR_INVALID_ARG, "o must not overlap inputs, the pool or the snapshots");
+    if (snapshots && (overlaps(snapshots, nsnap, state_pool, npool) || overlaps(snapshots, nsnap, q, nqk) ||
+                      overlaps(snapshots, nsnap, k, nqk) || overlaps(snapshots, nsnap, v, nv) ||
+                      overlaps(snapshots, nsnap, g, ng) || overlaps(snapshots, nsnap, beta, ng)))
+        return fail(GDN_ERR_INVALID_ARG, "snapshots must not overlap the pool or the inputs");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        int bad = 0;
+        hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
+        if (e != hipSuccess) return hip_fail(e, "slot_idx check");
+        if (bad) return fail(GDN_ERR_DEVICE_CHECK, "slot_idx has ids outside [0, %d) or repeated ids", P);
+    }
+    hipError_t e = gdn::launch_decode_multi(q, k, v, g, beta, state_pool, slot_idx, B, n_tok, H_qk,
+                                            H_v, scale, o, snapshots, s);
+    return finish(e, s, "gdn_decode_multi_step launch");
+}
+
+int gdn_state_rollback(const float *snapshots, const int32_t *n_keep, int n_tok, float *state_pool,
+                       const int32_t *slot_idx, int B, int P, int H_v, int d_k, int d_v,
+                       void *stream) {
+    int rc;
+    if ((rc = check_heads(1, H_v, d_k, d_v))) return rc;
+    if (B < 0 || P < 1 || n_tok < 1 || B > P)
+        return fail(GDN_ERR_INVALID_ARG, "need B >= 0, P >= 1, n_tok >= 1 and B <= P");
+    if ((long long)B * n_tok * H_v > 0x7FFFFFFFLL) return fail(GDN_ERR_INVALID_ARG, "B * n_tok * H_v too large");
+    if (B == 0) return ok();
+    if (!snapshots || !n_keep || !state_pool || !slot_idx)
+        return fail(GDN_ERR_INVALID_ARG, "snapshots, n_keep, state_pool and slot_idx must be non-NULL");
+    const size_t st = (size_t)gdn::kD * gdn::kD * 4;
+    if (overlaps(snapshots, (size_t)B * n_tok * H_v * st, state_pool, (size_t)P * H_v * st))
+        return fail(GDN_ERR_INVALID_ARG, "snapshots must not overlap the pool");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        int bad = 0;
+        hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
+        if (e != hipSuccess) return hip_fail(e, "slot_idx check");
+        if (bad) return fail(GDN_ERR_DEVICE_CHECK, "slot_idx has ids outside [0, %d) or repeated ids", P);
+    }
+    hipError_t e = gdn::launch_state_rollback(snapshots, n_keep, n_tok, state_pool, slot_idx, B, H_v, s);
+    return finish(e, s, "gdn_state_rollback launch");
+}
+
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                     const float *beta, float *state_pool, const int32_t *slot_idx, int B, int P,
                     int H_qk, int H_v, int d_k, int d_v, float scale, void *o, void *stream) {

@@ -52,6 +52,14 @@ hipError_t launch_decode_step_raw(const void *x, const void *w, const float *a, 
                                   int B, int H_qk, int H_v, float scale, void *o,
                                   hipStream_t stream);
 
+// n tokens per sequence with optional per-position state snapshots; rollback.
+hipError_t launch_decode_multi(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *pool, const int32_t *slot_idx, int B,
+                               int n, int H_qk, int H_v, float scale, void *o, float *snapshots,
+                               hipStream_t stream);
+hipError_t launch_state_rollback(const float *snapshots, const int32_t *n_keep, int n, float *pool,
+                                 const int32_t *slot_idx, int B, int H_v, hipStream_t stream);
+
 // Device-side precondition checks (GDN_DEBUG=1): launch a one-workgroup scan,
 // wait for the stream, and return the violation bits in *result (0 = ok).
 hipError_t debug_check_cu_seqlens(const int32_t *cu_seqlens, int N, int T, hipStream_t stream,

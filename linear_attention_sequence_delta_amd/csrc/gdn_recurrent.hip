@@ -164,6 +164,95 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     if (m.c16 < 8) o[((size_t)b * H_v + h) * kD + m.wave * 32 + m.c16 * 4 + m.r4] = f2bf(mine);
 }
 
+// n tokens per sequence (speculative-decoding verification): the state stays
+// in registers across the tokens, each token's inputs are loaded during the
+// previous token's arithmetic, and, when snapshots is given, the state before
+// each token is stored there ([B][n][H_v][d_v][d_k]) so that a caller can
+// return the slot to any prefix of the tokens.  Per (sequence, V-head): one
+// state read, one state write, n snapshot writes.
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ pool,
+    const int32_t *__restrict__ slot_idx, int n, int H_qk, int H_v, float scale,
+    uint16_t *__restrict__ o, float *__restrict__ snapshots) {
+    const RowMap m;
+    const int b = blockIdx.x / H_v;
+    const int h = blockIdx.x - b * H_v;
+    const int hq = h / (H_v / H_qk);
+    float *S = pool + ((size_t)slot_idx[b] * H_v + h) * (kD * kD);
+
+    float s[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        load4(S + m.row(j) * kD + m.col(0), s[j]);
+        load4(S + m.row(j) * kD + m.col(1), s[j] + 4);
+    }
+    float kk[8], qq[8], vr[8], gt, bt;
+    auto fetch = [&](int t, float *kd, float *qd, float *vd, float &gd, float &bd) {
+        const size_t bt_ = (size_t)b * n + t;
+        load_vec8(k + (bt_ * H_qk + hq) * kD, m, kd);
+        load_vec8(q + (bt_ * H_qk + hq) * kD, m, qd);
+        const uint16_t *vb = v + (bt_ * H_v + h) * kD;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vd[j] = bf2f(vb[m.row(j)]);
+        gd = g[bt_ * H_v + h];
+        bd = beta[bt_ * H_v + h];
+    };
+    fetch(0, kk, qq, vr, gt, bt);
+    for (int t = 0; t < n; ++t) {
+        if (snapshots) {
+            float *snap = snapshots + (((size_t)b * n + t) * H_v + h) * (kD * kD);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                *reinterpret_cast<float4 *>(snap + m.row(j) * kD + m.col(0)) =
+                    make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+                *reinterpret_cast<float4 *>(snap + m.row(j) * kD + m.col(1)) =
+                    make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
+            }
+        }
+        float kn[8], qn[8], vn[8], gn, bn;
+        fetch(min(t + 1, n - 1), kn, qn, vn, gn, bn);   // clamped: the last fetch is unused
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qq[e] *= scale;
+        const float mine = delta_rows(s, kk, qq, vr, expf(gt), bt, m);
+        if (m.c16 < 8)
+            o[(((size_t)b * n + t) * H_v + h) * kD + m.wave * 32 + m.c16 * 4 + m.r4] = f2bf(mine);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kk[e] = kn[e];
+            qq[e] = qn[e];
+            vr[e] = vn[e];
+        }
+        gt = gn;
+        bt = bn;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(0)) =
+            make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(1)) =
+            make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
+    }
+}
+
+// Return slot_idx[b] to the state after its first n_keep[b] tokens:
+// snapshots[b][n_keep[b]] when n_keep[b] < n (clamped to [0, n]; n keeps it).
+__global__ __launch_bounds__(256) void state_rollback_kernel(const float *__restrict__ snapshots,
+                                                             const int32_t *__restrict__ n_keep,
+                                                             int n, float *__restrict__ pool,
+                                                             const int32_t *__restrict__ slot_idx,
+                                                             int H_v) {
+    const int b = blockIdx.x / H_v;
+    const int h = blockIdx.x - b * H_v;
+    const int keep = min(max(n_keep[b], 0), n);
+    if (keep == n) return;
+    const float4 *src = reinterpret_cast<const float4 *>(
+        snapshots + (((size_t)b * n + keep) * H_v + h) * (kD * kD));
+    float4 *dst = reinterpret_cast<float4 *>(pool + ((size_t)slot_idx[b] * H_v + h) * (kD * kD));
+#pragma unroll
+    for (int i = 0; i < kD * kD / 4 / 256; ++i) dst[i * 256 + threadIdx.x] = src[i * 256 + threadIdx.x];
+}
+
 // Token-by-token prefill: one workgroup per (sequence, V-head) carries the
 // state through the sequence in registers.  The next token's inputs are
 // loaded before the current token's arithmetic.
@@ -242,6 +331,24 @@ hipError_t launch_decode_step(const void *q, const void *k, const void *v, const
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), g, beta, pool, slot_idx, H_qk, H_v,
                        scale, static_cast<uint16_t *>(o), RawDecodeIn{});
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_multi(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *pool, const int32_t *slot_idx, int B,
+                               int n, int H_qk, int H_v, float scale, void *o, float *snapshots,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(decode_multi_kernel, dim3(B * H_v), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), g, beta, pool, slot_idx, n, H_qk, H_v,
+                       scale, static_cast<uint16_t *>(o), snapshots);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_rollback(const float *snapshots, const int32_t *n_keep, int n, float *pool,
+                                 const int32_t *slot_idx, int B, int H_v, hipStream_t stream) {
+    hipLaunchKernelGGL(state_rollback_kernel, dim3(B * H_v), dim3(256), 0, stream, snapshots,
+                       n_keep, n, pool, slot_idx, H_v);
     return hipGetLastError();
 }
 

@@ -209,3 +209,27 @@ def test_layer_decode_rejects_bad_arguments():
     assert call(cs=8 * big) == gdn.GDN_ERR_INVALID_ARG          # the two pools overlap
     assert call(o=8 * big) == gdn.GDN_ERR_INVALID_ARG           # o overlaps the state pool
     assert call(B=0, x=None) == gdn.GDN_OK                      # B = 0: no-op
+
+
+def test_multi_step_and_rollback_reject_bad_arguments():
+    L = gdn.lib()
+    big = 1 << 40
+
+    def multi(**kw):
+        a = dict(q=big, k=2 * big, v=3 * big, g=4 * big, beta=5 * big, pool=6 * big,
+                 slots=7 * big, B=4, P=8, n=3, o=8 * big, snaps=9 * big)
+        a.update(kw)
+        return L.gdn_decode_multi_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"],
+                                       a["slots"], a["B"], a["P"], a["n"], 16, 48, 128, 128, 1.0,
+                                       a["o"], a["snaps"], None)
+    assert multi(n=0) == gdn.GDN_ERR_INVALID_ARG
+    assert multi(q=None) == gdn.GDN_ERR_INVALID_ARG
+    assert multi(snaps=6 * big) == gdn.GDN_ERR_INVALID_ARG      # snapshots overlap the pool
+    assert multi(o=6 * big) == gdn.GDN_ERR_INVALID_ARG          # o overlaps the pool
+    assert multi(B=0, q=None) == gdn.GDN_OK
+    assert L.gdn_state_rollback(None, big, 3, 2 * big, 3 * big, 4, 8, 48, 128, 128,
+                                None) == gdn.GDN_ERR_INVALID_ARG
+    assert L.gdn_state_rollback(big, 2 * big, 0, 3 * big, 4 * big, 4, 8, 48, 128, 128,
+                                None) == gdn.GDN_ERR_INVALID_ARG
+    assert L.gdn_state_rollback(big, 2 * big, 3, big, 4 * big, 4, 8, 48, 128, 128,
+                                None) == gdn.GDN_ERR_INVALID_ARG    # snapshots overlap the pool
