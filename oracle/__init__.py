@@ -53,8 +53,9 @@ def _load():
     lib.orc_chunked.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, I, P, P, I, I]
     lib.orc_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P]
     lib.orc_gates.argtypes = [P, P, P, P, I, I, P, P]
+    lib.orc_gated_norm.argtypes = [P, P, P, I, I, D, P]
     for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step,
-              lib.orc_gates):
+              lib.orc_gates, lib.orc_gated_norm):
         f.restype = I
     _lib = lib
     return lib
@@ -259,3 +260,17 @@ def state_rollback(snapshots, n_keep, pool, slot_idx):
         if n_keep[b] < n:
             pool[s] = snaps[b, n_keep[b]]
     return pool
+
+
+def gated_norm(o, z, w, eps=1e-6):
+    """Output gate: o / sqrt(mean(o^2) + eps) * w * SiLU(z) over the last axis
+    (d_v) of o and z; w [d_v].  Returns fp64 with o's shape."""
+    o, z, w = f64(o), f64(z), f64(w)
+    if o.shape != z.shape or w.shape != (o.shape[-1],):
+        raise ValueError("gated_norm shape mismatch")
+    dv = o.shape[-1]
+    R = o.size // dv
+    y = np.zeros(o.shape)
+    _check(_load().orc_gated_norm(_ptr(np.ascontiguousarray(o)), _ptr(np.ascontiguousarray(z)),
+                                  _ptr(w), R, dv, float(eps), _ptr(y)), "gated_norm")
+    return y

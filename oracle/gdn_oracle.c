@@ -440,4 +440,33 @@ int orc_gates(const double *a, const double *b, const double *A_log, const doubl
     return ORC_OK;
 }
 
+/*
+ * Output gate of the layer, per token and V-head: the d_v outputs o are
+ * divided by their root mean square, scaled per channel by the norm weight w
+ * and multiplied by SiLU(z):
+ *   y[c] = o[c] / sqrt(mean_c(o^2) + eps) * w[c] * z[c] * sigmoid(z[c])
+ * [Dissect sec. 2.1] lists the layer's norm and in_proj_z weights; the form
+ * above is this oracle's reading of how they apply (the pages print no
+ * formula).  o, z [R][dv]; w [dv]; y [R][dv]; R = rows (tokens x V-heads).
+ */
+int orc_gated_norm(const double *o, const double *z, const double *w, int R, int dv, double eps,
+                   double *y)
+{
+    if (R < 0 || dv < 1)
+        return ORC_EINVAL;
+    for (int r = 0; r < R; ++r) {
+        const double *orow = o + (size_t)r * dv;
+        const double *zrow = z + (size_t)r * dv;
+        double ss = 0.0;
+        for (int c = 0; c < dv; ++c)
+            ss += orow[c] * orow[c];
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        for (int c = 0; c < dv; ++c) {
+            const double silu = zrow[c] / (1.0 + exp(-zrow[c]));
+            y[(size_t)r * dv + c] = orow[c] * inv * w[c] * silu;
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_version(void) { return 1; }

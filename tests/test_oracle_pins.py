@@ -433,6 +433,31 @@ def test_decode_multi_step_equals_prefill_and_rollback(orc):
     np.testing.assert_array_equal(rolled[0], snaps[2, 2])
 
 
+# ------------------------------------------------------------ output gate
+def test_gated_norm_against_torch_and_invariants(orc):
+    """Against torch's rms_norm and silu (library routines the oracle does not
+    use), scale invariance of the norm, and zero output where z = 0."""
+    rng = np.random.default_rng(71)
+    o = rng.normal(0, 3, (5, 7, 16))
+    z = rng.normal(0, 2, (5, 7, 16))
+    w = rng.uniform(0.5, 1.5, 16)
+    y = orc.gated_norm(o, z, w, eps=1e-6)
+    ref = (torch.nn.functional.rms_norm(torch.from_numpy(o), (16,), torch.from_numpy(w), eps=1e-6)
+           * torch.nn.functional.silu(torch.from_numpy(z))).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(orc.gated_norm(37.5 * o, z, w, eps=0.0),
+                               orc.gated_norm(o, z, w, eps=0.0), rtol=1e-13)
+    z0 = z.copy()
+    z0[:, :, 3] = 0.0
+    assert (orc.gated_norm(o, z0, w)[:, :, 3] == 0).all()
+    # one-hot rows: the norm maps e_c to sqrt(d_v) e_c
+    oh = np.zeros((1, 16))
+    oh[0, 5] = 2.0
+    big = np.full((1, 16), 60.0)                    # SiLU(60) = 60 to double precision
+    np.testing.assert_allclose(orc.gated_norm(oh, big, np.ones(16), eps=0.0)[0, 5], 4.0 * 60.0,
+                               rtol=1e-13)
+
+
 # ------------------------------------------------------------- size pins
 def test_sizes_printed_on_pages():
     """The layer shape and the fp32 state dtype reproduce the state and KV-cache
