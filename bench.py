@@ -173,6 +173,24 @@ def run_gpu(steps, warmup, path="both"):
         res["pf_us"] = sum(b0.elapsed_time(b1) for _, (b0, b1) in ev) / steps * 1e3
         del q, k, v, ws
 
+    # the output gate on the prefill's o (z ~ N(0, 1), norm weight ~ U(0.5, 1.5))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1003001)
+    z = torch.randn(o.shape, generator=gen, device=dev).to(torch.bfloat16)
+    wn = torch.rand((D,), generator=gen, device=dev) + 0.5
+    y = torch.empty_like(o)
+    for _ in range(2):
+        gdn.gdn_gated_norm(o, z, wn, out=y)
+    torch.cuda.synchronize()
+    g0, g1 = _events(torch)
+    g0.record()
+    for _ in range(steps):
+        gdn.gdn_gated_norm(o, z, wn, out=y)
+    g1.record()
+    torch.cuda.synchronize()
+    res["gate_us"] = g0.elapsed_time(g1) / steps * 1e3
+    del z, y
+
     # ---------------- decode workload: B = 256 over rotating 256-slot pools
     d = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
     pools = [to_dev(d.pool) for _ in range(2)]     # 768 MiB each, larger than the on-die cache
@@ -468,6 +486,12 @@ def main():
                        "what": "gdn_layer_decode_step: conv from each slot's 3-row history + the "
                                "new raw row, gates from raw a, b, the update, history shift"}},
     }
+    gate_bytes = 3 * T * H_V * D * 2
+    out["output_gate"] = {"us": r["gate_us"], "what": "gdn_gated_norm on the prefill's o "
+                          "(RMS norm per head, norm weight, SiLU(z)); not part of the step",
+                          "roofline": {"bound": "hbm", "achieved": gate_bytes / (r["gate_us"] * 1e-6) / 1e9,
+                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                       "frac": gate_bytes / (r["gate_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}}
     if "pre_us" in r:
         out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",
                                    "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,

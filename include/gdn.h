@@ -258,6 +258,21 @@ int gdn_state_rollback(const float *snapshots, const int32_t *n_keep, int n_tok,
                        void *stream);
 
 /*
+ * gdn_gated_norm -- the layer's output gate on rows of d_v outputs (one row
+ * per token and V-head): y = o / sqrt(mean(o^2) + eps) * w * SiLU(z).
+ * [Dissect sec. 2.1] lists the layer's norm and in_proj_z weights; the pages
+ * print no formula, and this per-head RMS norm gated by SiLU(z) is the reading
+ * taken.  Apply it to the o of gdn_prefill / gdn_decode_step (rows = T * H_v
+ * or B * H_v).
+ *
+ *   o, z    device bf16 [rows][d_v];  w  device fp32 [d_v] (the norm weight)
+ *   out     device bf16 [rows][d_v]; may be o itself (in place)
+ * Only d_v = 128 is built.  rows = 0 is a no-op.
+ */
+int gdn_gated_norm(const void *o, const void *z, const float *w, int rows, int d_v, float eps,
+                   void *out, void *stream);
+
+/*
  * gdn_decode_step -- one token for each of B sequences whose states live in a
  * slot pool; each addressed state is read once and overwritten in place.
  * [OOM sec. 1.2] per-token step (q, k, v, S_prev, gates) -> (o, S); the update

@@ -31,7 +31,7 @@ EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_raw", "gdn_gates", "gdn_layer_prefill_workspace_size",
            "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_multi_step",
-           "gdn_state_rollback", "gdn_decode_step")
+           "gdn_state_rollback", "gdn_gated_norm", "gdn_decode_step")
 
 _lib = None
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_decode_multi_step.restype = I
     L.gdn_state_rollback.argtypes = [P, P, I, P, P, I, I, I, I, I, P]
     L.gdn_state_rollback.restype = I
+    L.gdn_gated_norm.argtypes = [P, P, P, I, I, F, P, P]
+    L.gdn_gated_norm.restype = I
     L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_decode_step.restype = I
     _lib = L
@@ -477,6 +479,30 @@ def gdn_state_rollback(snapshots, n_keep, state_pool, slot_idx):
     _check(rc, "gdn_state_rollback")
 
 
+def gdn_gated_norm(o, z, w, *, eps: float = 1e-6, out=None):
+    """Output gate: o / sqrt(mean(o^2) + eps) * w * SiLU(z) over the last axis.
+    o, z: bf16 [..., 128]; w: fp32 [128]; out: bf16 like o (may be o).
+    Returns out."""
+    torch = _torch()
+    dev = _device_of(o)
+    _need(o, "o", torch.bfloat16, dev)
+    _need(z, "z", torch.bfloat16, dev)
+    _need(w, "w", torch.float32, dev, 1)
+    d_v = o.shape[-1]
+    if tuple(z.shape) != tuple(o.shape) or w.numel() != d_v:
+        raise ValueError("o and z must have the same shape and w d_v entries")
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _need(out, "out", torch.bfloat16, dev)
+        if tuple(out.shape) != tuple(o.shape):
+            raise ValueError("out must have o's shape")
+    rows = o.numel() // d_v
+    _check(lib().gdn_gated_norm(_ptr(o), _ptr(z), _ptr(w), rows, d_v, float(eps), _ptr(out),
+                                _stream(dev)), "gdn_gated_norm")
+    return out
+
+
 def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.0, o=None):
     """One token per sequence; states in state_pool[slot_idx[b]] advance in place.
     q, k: bf16 [B, H_qk, 128]; v: bf16 [B, H_v, 128]; g, beta: fp32 [B, H_v];
@@ -511,4 +537,4 @@ __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefil
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
            "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
            "gdn_layer_decode_step", "gdn_decode_multi_step", "gdn_state_rollback",
-           "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]
+           "gdn_gated_norm", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

@@ -437,6 +437,21 @@ int gdn_state_rollback(const float *snapshots, const int32_t *n_keep, int n_tok,
     return finish(e, s, "gdn_state_rollback launch");
 }
 
+int gdn_gated_norm(const void *o, const void *z, const float *w, int rows, int d_v, float eps,
+                   void *out, void *stream) {
+    if (d_v != gdn::kD) return fail(GDN_ERR_UNSUPPORTED, "only d_v = 128 is built (got %d)", d_v);
+    if (rows < 0) return fail(GDN_ERR_INVALID_ARG, "rows must be >= 0 (got %d)", rows);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (rows == 0) return ok();
+    if (!o || !z || !w || !out) return fail(GDN_ERR_INVALID_ARG, "o, z, w and out must be non-NULL");
+    const size_t n = (size_t)rows * gdn::kD * 2;
+    if ((out != o && overlaps(out, n, o, n)) || overlaps(out, n, z, n) ||
+        overlaps(out, n, w, (size_t)gdn::kD * 4))
+        return fail(GDN_ERR_INVALID_ARG, "out must equal o or not overlap it, and not overlap z or w");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdn::launch_gated_norm(o, z, w, rows, eps, out, s), s, "gdn_gated_norm launch");
+}
+
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                     const float *beta, float *state_pool, const int32_t *slot_idx, int B, int P,
                     int H_qk, int H_v, int d_k, int d_v, float scale, void *o, void *stream) {

@@ -46,6 +46,8 @@ hipError_t launch_conv_hist(const void *x, const int32_t *cu_seqlens, int N, int
                             void *hist, hipStream_t stream);
 hipError_t launch_conv_shift(const void *x, const int32_t *slot_idx, int B, int C_raw, void *hist,
                              hipStream_t stream);
+hipError_t launch_gated_norm(const void *o, const void *z, const float *w, int rows, float eps,
+                             void *out, hipStream_t stream);
 hipError_t launch_decode_step_raw(const void *x, const void *w, const float *a, const float *b,
                                   const float *A_log, const float *dt_bias, float eps,
                                   const void *conv_hist, float *pool, const int32_t *slot_idx,

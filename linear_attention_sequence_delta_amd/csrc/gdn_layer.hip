@@ -7,8 +7,11 @@
 //                      the next token), zero where the sequence is shorter
 //   conv_shift_kernel  after a decode step: a slot's history drops its oldest
 //                      row and takes the new token's row
-// All three are elementwise copies or maps, HBM-bound and tiny next to the
-// prefill and the decode step; rows move in 16-byte pieces.
+//   gated_norm_kernel  the output gate: each (token, V-head) row of o divided
+//                      by its root mean square, times the norm weight and
+//                      SiLU(z) (the pages list the norm and in_proj_z
+//                      weights; this is the reading taken of how they apply)
+// All are elementwise copies or maps, HBM-bound; rows move in 16-byte pieces.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -58,7 +61,42 @@ __global__ __launch_bounds__(256) void conv_shift_kernel(const uint16_t *__restr
     hs[2 * (size_t)pieces] = xn;
 }
 
+// 16 lanes per 128-channel row (8 channels each), the sum of squares reduced
+// over the 16-lane DPP row; 16 rows per 256-thread workgroup.  out may be o.
+__global__ __launch_bounds__(256) void gated_norm_kernel(const uint16_t *o,
+                                                         const uint16_t *__restrict__ z,
+                                                         const float *__restrict__ w, int rows,
+                                                         float eps, uint16_t *out) {
+    const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int cg = threadIdx.x & 15;
+    const int rr = min(row, rows - 1);              // a whole DPP row stays active
+    const size_t off = (size_t)rr * kD + 8 * cg;
+    float ov[8], zv[8];
+    unpack8(*reinterpret_cast<const uint4 *>(o + off), ov);
+    unpack8(*reinterpret_cast<const uint4 *>(z + off), zv);
+    const float4 w0 = *reinterpret_cast<const float4 *>(w + 8 * cg);
+    const float4 w1 = *reinterpret_cast<const float4 *>(w + 8 * cg + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(ov[e], ov[e], ss);
+    const float inv = rsqrtf(row16_sum(ss) * (1.f / kD) + eps);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = ov[e] * inv * wv[e] * silu(zv[e]);
+    if (row < rows) *reinterpret_cast<uint4 *>(out + off) = pack_bf8(y);
+}
+
 }  // namespace
+
+hipError_t launch_gated_norm(const void *o, const void *z, const float *w, int rows, float eps,
+                             void *out, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(gated_norm_kernel, dim3((rows + 15) / 16), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(z), w,
+                       rows, eps, static_cast<uint16_t *>(out));
+    return hipGetLastError();
+}
 
 hipError_t launch_gates(const float *a, const float *b, const float *A_log, const float *dt_bias,
                         int T, int H_v, float *g, float *beta, hipStream_t stream) {

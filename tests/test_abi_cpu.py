@@ -233,3 +233,13 @@ def test_multi_step_and_rollback_reject_bad_arguments():
                                 None) == gdn.GDN_ERR_INVALID_ARG
     assert L.gdn_state_rollback(big, 2 * big, 3, big, 4 * big, 4, 8, 48, 128, 128,
                                 None) == gdn.GDN_ERR_INVALID_ARG    # snapshots overlap the pool
+
+
+def test_gated_norm_rejects_bad_arguments():
+    L = gdn.lib()
+    big = 1 << 40
+    assert L.gdn_gated_norm(big, 2 * big, 3 * big, 10, 64, 1e-6, 4 * big, None) == gdn.GDN_ERR_UNSUPPORTED
+    assert L.gdn_gated_norm(big, 2 * big, 3 * big, 10, 128, float("nan"), 4 * big, None) == gdn.GDN_ERR_INVALID_ARG
+    assert L.gdn_gated_norm(big, 2 * big, 3 * big, 10, 128, 1e-6, big + 64, None) == gdn.GDN_ERR_INVALID_ARG
+    assert L.gdn_gated_norm(big, 2 * big, 3 * big, 10, 128, 1e-6, 2 * big, None) == gdn.GDN_ERR_INVALID_ARG
+    assert L.gdn_gated_norm(None, None, None, 0, 128, 1e-6, None, None) == gdn.GDN_OK

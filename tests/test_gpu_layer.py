@@ -169,3 +169,21 @@ def test_layer_prefill_then_decode_chain_against_oracle():
     dec_rows = np.stack([starts[:-1] + np.array(lens) + t for t in range(D)])     # [D, 2]
     assert_close(np.stack(outs), o_ref[dec_rows], TOL_BF16, "decode o")
     assert_close(pool.cpu().numpy()[slots], S_ref, TOL_BF16, "final states")
+
+
+@pytest.mark.parametrize("rows", [1, 17, 48 * 700])
+def test_gated_norm_against_oracle(rows):
+    """The output gate on bf16 rows of 128 (in place and out of place)."""
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    rng = np.random.default_rng(rows)
+    o = synth.bf16_bits(rng.normal(0, 2, (rows, 128)).astype(np.float32))
+    z = synth.bf16_bits(rng.normal(0, 2, (rows, 128)).astype(np.float32))
+    w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    y = gdn.gdn_gated_norm(dev(o), dev(z), dev(w))
+    od = dev(o)
+    gdn.gdn_gated_norm(od, dev(z), dev(w), out=od)
+    torch.cuda.synchronize()
+    ref = oracle.gated_norm(o, z, w)
+    assert_close(host(y), ref, TOL_BF16, "y")
+    assert np.array_equal(_bits(od), _bits(y))
