@@ -469,4 +469,144 @@ int orc_gated_norm(const double *o, const double *z, const double *w, int R, int
     return ORC_OK;
 }
 
+/*
+ * Gradients of the token recurrence (reverse mode, the chain rule applied to
+ * each step of orc_recurrent in reverse order).  [Local sec. 2.1] names a fused
+ * forward and backward kernel for the GDN layer; the layer is trained, so its
+ * gradients are part of what it computes.  Nothing about the method is new
+ * here: for one step, with S = S_{t-1}, a = exp(g_t), u = S k_t and G the
+ * gradient of the loss with respect to S_t (the later tokens' share plus
+ * do_t (scale q_t)^T from o_t = S_t scale q_t):
+ *     S_t   = a S + b (v_t - a u) k_t^T
+ *     dq_t += scale S_t^T do_t           (summed over the V-heads of a QK head)
+ *     w     = G k_t
+ *     dv_t  = b w
+ *     db_t  = (v_t - a u) . w
+ *     dg_t  = a (<G, S> - b u . w)       (d/dg = a d/da)
+ *     dk_t += b G^T (v_t - a u) - a b S^T w
+ *     dS    = a (G - b w k_t^T)          (the gradient with respect to S_{t-1})
+ * The states S_{t-1} are recomputed forward and kept for the whole sequence.
+ *
+ * Inputs as orc_recurrent, plus d_o [T][H_v][dv] (gradient of the loss with
+ * respect to o) and dS_final [N][H_v][dv][dk] or NULL (with respect to the
+ * final states; NULL = zero).  Outputs: dq, dk [T][H_qk][dk]; dv [T][H_v][dv];
+ * dg, dbeta [T][H_v]; dS0 [N][H_v][dv][dk] or NULL (with respect to the
+ * initial states).  Outputs are overwritten, not accumulated.  Work is split
+ * over (sequence, QK head) so that the V-heads of a group, which add into the
+ * same dq and dk, run in one thread.
+ */
+int orc_recurrent_backward(const double *q, const double *k, const double *v, const double *g,
+                           const double *beta, const double *S0, const int32_t *cu, int N,
+                           int T, int H_qk, int H_v, int dk, int dv, double scale,
+                           const double *d_o, const double *dS_final, double *dq, double *dkk,
+                           double *dvv, double *dg, double *dbeta, double *dS0)
+{
+    if (N < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0 || dk < 1 || dv < 1)
+        return ORC_EINVAL;
+    for (int n = 0; n < N; ++n) {
+        int s0 = 0, s1 = 0;
+        if (seq_bounds(cu, N, T, n, &s0, &s1))
+            return ORC_EINVAL;
+    }
+    memset(dq, 0, sizeof(double) * (size_t)T * H_qk * dk);
+    memset(dkk, 0, sizeof(double) * (size_t)T * H_qk * dk);
+    const int group = H_v / H_qk;
+    const size_t ssz = (size_t)dv * dk;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < N * H_qk; ++u) {
+        const int n = u / H_qk, hq = u % H_qk;
+        int s0 = 0, s1 = 0;
+        seq_bounds(cu, N, T, n, &s0, &s1);
+        const int len = s1 - s0;
+        double *St = (double *)malloc(sizeof(double) * ssz * ((size_t)len + 1));  /* S_{s0-1} .. S_{s1-1} */
+        double *G = (double *)malloc(sizeof(double) * ssz);
+        double *Sk = (double *)malloc(sizeof(double) * dv);
+        double *w = (double *)malloc(sizeof(double) * dv);
+        double *r = (double *)malloc(sizeof(double) * dv);
+        if (!St || !G || !Sk || !w || !r) {
+            free(St);
+            free(G);
+            free(Sk);
+            free(w);
+            free(r);
+#pragma omp atomic write
+            status = ORC_ENOMEM;
+            continue;
+        }
+        for (int h = hq * group; h < (hq + 1) * group; ++h) {
+            const size_t st_off = ((size_t)n * H_v + h) * ssz;
+            if (S0)
+                memcpy(St, S0 + st_off, sizeof(double) * ssz);
+            else
+                memset(St, 0, sizeof(double) * ssz);
+            for (int t = s0; t < s1; ++t) {
+                double *S = St + (size_t)(t - s0 + 1) * ssz;
+                memcpy(S, S - ssz, sizeof(double) * ssz);
+                delta_step(S, dk, dv, q + ((size_t)t * H_qk + hq) * dk,
+                           k + ((size_t)t * H_qk + hq) * dk, v + ((size_t)t * H_v + h) * dv,
+                           g[(size_t)t * H_v + h], beta[(size_t)t * H_v + h], scale, NULL, Sk);
+            }
+            if (dS_final)
+                memcpy(G, dS_final + st_off, sizeof(double) * ssz);
+            else
+                memset(G, 0, sizeof(double) * ssz);
+            for (int t = s1 - 1; t >= s0; --t) {
+                const double *S = St + (size_t)(t - s0) * ssz;      /* S_{t-1} */
+                const double *Snew = S + ssz;                      /* S_t */
+                const double *qt = q + ((size_t)t * H_qk + hq) * dk;
+                const double *kt = k + ((size_t)t * H_qk + hq) * dk;
+                const double *vt = v + ((size_t)t * H_v + h) * dv;
+                const double *dot = d_o + ((size_t)t * H_v + h) * dv;
+                double *dqt = dq + ((size_t)t * H_qk + hq) * dk;
+                double *dkt = dkk + ((size_t)t * H_qk + hq) * dk;
+                const double a = exp(g[(size_t)t * H_v + h]), b = beta[(size_t)t * H_v + h];
+                /* o_t = S_t (scale q_t) */
+                for (int i = 0; i < dv; ++i)
+                    for (int j = 0; j < dk; ++j) {
+                        G[(size_t)i * dk + j] += dot[i] * scale * qt[j];
+                        dqt[j] += scale * Snew[(size_t)i * dk + j] * dot[i];
+                    }
+                double gs = 0.0, uw = 0.0, rw = 0.0;
+                for (int i = 0; i < dv; ++i) {
+                    double su = 0.0, gw = 0.0;
+                    for (int j = 0; j < dk; ++j) {
+                        su += S[(size_t)i * dk + j] * kt[j];
+                        gw += G[(size_t)i * dk + j] * kt[j];
+                        gs += G[(size_t)i * dk + j] * S[(size_t)i * dk + j];
+                    }
+                    Sk[i] = su;
+                    w[i] = gw;
+                    r[i] = vt[i] - a * su;
+                    uw += su * gw;
+                    rw += r[i] * gw;
+                }
+                for (int i = 0; i < dv; ++i)
+                    dvv[((size_t)t * H_v + h) * dv + i] = b * w[i];
+                dbeta[(size_t)t * H_v + h] = rw;
+                dg[(size_t)t * H_v + h] = a * (gs - b * uw);
+                for (int j = 0; j < dk; ++j) {
+                    double gr = 0.0, sw = 0.0;
+                    for (int i = 0; i < dv; ++i) {
+                        gr += G[(size_t)i * dk + j] * r[i];
+                        sw += S[(size_t)i * dk + j] * w[i];
+                    }
+                    dkt[j] += b * gr - a * b * sw;
+                }
+                for (int i = 0; i < dv; ++i)
+                    for (int j = 0; j < dk; ++j)
+                        G[(size_t)i * dk + j] = a * (G[(size_t)i * dk + j] - b * w[i] * kt[j]);
+            }
+            if (dS0)
+                memcpy(dS0 + st_off, G, sizeof(double) * ssz);
+        }
+        free(St);
+        free(G);
+        free(Sk);
+        free(w);
+        free(r);
+    }
+    return status;
+}
+
 int orc_version(void) { return 1; }

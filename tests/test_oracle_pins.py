@@ -458,6 +458,100 @@ def test_gated_norm_against_torch_and_invariants(orc):
                                rtol=1e-13)
 
 
+# ------------------------------------------------------------- backward
+def _loss_weights(rng, o_shape, S_shape):
+    return rng.standard_normal(o_shape), rng.standard_normal(S_shape)
+
+
+@pytest.mark.parametrize("with_state", [True, False])
+def test_backward_equals_finite_differences(orc, with_state):
+    """Every gradient of the recurrence against central differences of the
+    forward oracle (L = <W_o, o> + <W_S, S_final>, step 1e-6): two QK groups
+    of two V-heads, d_k != d_v, packed sequences of lengths 4, 1, 0, 3, and
+    with and without an initial state and a final-state gradient."""
+    rng = np.random.default_rng(80 + with_state)
+    H_qk, H_v, dk, dv = 2, 4, 3, 2
+    cu = np.array([0, 4, 5, 5, 8], dtype=np.int32)
+    T, N = 8, 4
+    q, k, v, g, beta = _rand_case(rng, T, H_qk, H_v, dk, dv, unit_k=True)
+    S0 = rng.standard_normal((N, H_v, dv, dk)) if with_state else None
+    Wo, WS = _loss_weights(rng, (T, H_v, dv), (N, H_v, dv, dk))
+    if not with_state:
+        WS = None
+    scale = 0.7
+
+    def loss(q, k, v, g, beta, S0):
+        o, S = orc.recurrent(q, k, v, g, beta, S0, cu, scale=scale)
+        return (o * Wo).sum() + (0.0 if WS is None else (S * WS).sum())
+
+    grads = orc.recurrent_backward(q, k, v, g, beta, Wo, S0, WS, cu, scale=scale)
+    args = [q, k, v, g, beta] + ([S0] if with_state else [])
+    names = ["dq", "dk", "dv", "dg", "dbeta", "dS0"]
+    for ai, a in enumerate(args):
+        fd = np.zeros_like(a)
+        for idx in np.ndindex(a.shape):
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[ai][idx] += 1e-6
+            am[ai][idx] -= 1e-6
+            if not with_state:
+                ap.append(None)
+                am.append(None)
+            fd[idx] = (loss(*ap) - loss(*am)) / 2e-6
+        np.testing.assert_allclose(grads[ai], fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()),
+                                   err_msg=names[ai])
+    if not with_state:
+        # no initial state is a zero initial state; its gradient is still defined
+        S0z = np.zeros((N, H_v, dv, dk))
+        gz = orc.recurrent_backward(q, k, v, g, beta, Wo, S0z, None, cu, scale=scale)
+        for a, b in zip(grads[:5], gz[:5]):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_backward_against_torch_autograd(orc):
+    """Against torch autograd (fp64) through a plain step loop written with
+    torch ops, an implementation that shares nothing with the oracle's."""
+    rng = np.random.default_rng(83)
+    T, H_qk, H_v, dk, dv = 12, 1, 3, 5, 4
+    q, k, v, g, beta = _rand_case(rng, T, H_qk, H_v, dk, dv, unit_k=True, g_hi=1.5)
+    S0 = rng.standard_normal((1, H_v, dv, dk))
+    Wo, WS = _loss_weights(rng, (T, H_v, dv), (1, H_v, dv, dk))
+    ts = [torch.tensor(a, requires_grad=True) for a in (q, k, v, g, beta, S0)]
+    tq, tk, tv, tg, tb, tS0 = ts
+    loss = 0.0
+    for h in range(H_v):
+        S = tS0[0, h]
+        for t in range(T):
+            kt = tk[t, 0]
+            S = torch.exp(tg[t, h]) * (S - tb[t, h] * torch.outer(S @ kt, kt)) \
+                + tb[t, h] * torch.outer(tv[t, h], kt)
+            loss = loss + (S @ (0.5 * tq[t, 0])) @ torch.from_numpy(Wo[t, h])
+        loss = loss + (S * torch.from_numpy(WS[0, h])).sum()
+    loss.backward()
+    grads = orc.recurrent_backward(q, k, v, g, beta, Wo, S0, WS, scale=0.5)
+    for got, t in zip(grads, ts):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_adjoint_identities(orc):
+    """(o, S_final) is linear in (v, S_0) jointly and o is linear in q, so for
+    any output gradients <dv, v> + <dS0, S_0> = <d_o, o> + <dS_T, S_T> and
+    <dq, q> = <d_o, o> (Euler's identity for degree-1 homogeneous maps); at the
+    real head size, several V-heads per QK head, ragged sequences."""
+    rng = np.random.default_rng(84)
+    cu = np.array([0, 70, 71, 200], dtype=np.int32)
+    T, N, H_qk, H_v, d = 200, 3, 1, 3, 128
+    q, k, v, g, beta = _rand_case(rng, T, H_qk, H_v, d, d, unit_k=True)
+    S0 = rng.standard_normal((N, H_v, d, d))
+    Wo, WS = _loss_weights(rng, (T, H_v, d), (N, H_v, d, d))
+    o, S = orc.recurrent(q, k, v, g, beta, S0, cu)
+    dq, dk_, dv, dg, db, dS0 = orc.recurrent_backward(q, k, v, g, beta, Wo, S0, WS, cu)
+    lhs = (dv * v).sum() + (dS0 * S0).sum()
+    rhs = (Wo * o).sum() + (WS * S).sum()
+    assert abs(lhs - rhs) <= 1e-10 * (abs(rhs) + np.abs(Wo * o).sum())
+    assert abs((dq * q).sum() - (Wo * o).sum()) <= 1e-10 * np.abs(Wo * o).sum()
+
+
 # ------------------------------------------------------------- size pins
 def test_sizes_printed_on_pages():
     """The layer shape and the fp32 state dtype reproduce the state and KV-cache
