@@ -16,6 +16,9 @@
  *   [OOM]     "Qwen3.8-27B 混合线性注意力到底解决了什么" (www.mhpn.cn): sec. 1.2 gives a
  *             per-token step taking (q_t, k_t, v_t, S_prev, two gates) and returning
  *             (o_t, S_t) -- the argument set of gdn_decode_step.
+ *   [Local]   "Qwen3.8-27B：27B 如何打出千亿级效果，且塞进单张消费级显卡" (www.nzsm.cn):
+ *             sec. 2.1 names a fused forward/backward kernel for the GDN layer
+ *             (the reason gdn_prefill_backward exists).
  *
  * Conventions shared by every entry point
  *   - Pointers marked "device" are HIP device pointers (or host-coherent memory
@@ -157,6 +160,50 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
                     const float *beta, const float *initial_state, float *final_state,
                     const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
                     float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_prefill_backward_workspace_size -- bytes of device workspace
+ * gdn_prefill_backward needs (host-only; 0 for invalid sizes, > 0 for any
+ * valid N >= 1, T >= 0).  It holds, per (64-token chunk, V-head), the
+ * forward and backward chunk records and the bf16 state and state gradient
+ * at the chunk's boundaries: about 110 KB per chunk and V-head (2.7 GB for
+ * one 32768-token sequence with 48 V-heads).
+ */
+size_t gdn_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v);
+
+/*
+ * gdn_prefill_backward -- gradients of gdn_prefill (io_dtype GDN_BF16) with
+ * respect to all its inputs, given the gradients of the loss with respect to
+ * its outputs.  [Local sec. 2.1] names a fused forward and backward kernel for
+ * the GDN layer, which is trained.  The result is the derivative of the
+ * recurrence of gdn_prefill; it is computed in the same 64-token chunked form
+ * (bf16 matrix-core products, fp32 accumulation, fp32 state gradient): the
+ * forward states at chunk boundaries are recomputed, then a reverse scan
+ * carries the state gradient from the last chunk to the first.
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, N, T, H_qk, H_v, d_k, d_v, scale
+ *                   the forward's inputs, as for gdn_prefill (bf16 q, k, v; at
+ *                   most 8 V-heads per QK head)
+ *   d_o             device bf16 [T][H_v][d_v]: gradient with respect to o
+ *   d_final_state   device fp32 [N][H_v][d_v][d_k], or NULL (zero): gradient
+ *                   with respect to the final states
+ *   dq, dk          device bf16 [T][H_qk][d_k] outputs (summed over the V-heads
+ *                   that read each QK head)
+ *   dv              device bf16 [T][H_v][d_v] output
+ *   dg, dbeta       device fp32 [T][H_v] outputs
+ *   d_initial_state device fp32 [N][H_v][d_v][d_k] output, or NULL to skip it
+ *                   (its value does not depend on whether initial_state is NULL)
+ *   workspace       device scratch of at least gdn_prefill_backward_workspace_size
+ *                   bytes; contents on entry ignored
+ * Outputs and workspace must not overlap each other or any input.  T = 0
+ * writes only d_initial_state (= d_final_state, or zero).
+ */
+int gdn_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                         const void *d_o, const float *d_final_state, int N, int T, int H_qk,
+                         int H_v, int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
+                         float *dg, float *dbeta, float *d_initial_state, void *workspace,
+                         size_t ws_bytes, void *stream);
 
 /*
  * gdn_gates -- the layer's gates from its raw per-token projections a, b:

@@ -29,7 +29,8 @@ GDN_BF16 = 1
 
 EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_raw_workspace_size",
-           "gdn_prefill_raw", "gdn_gates", "gdn_layer_prefill_workspace_size",
+           "gdn_prefill_raw", "gdn_prefill_backward_workspace_size", "gdn_prefill_backward",
+           "gdn_gates", "gdn_layer_prefill_workspace_size",
            "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_multi_step",
            "gdn_state_rollback", "gdn_gated_norm", "gdn_decode_step")
 
@@ -66,6 +67,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_raw_workspace_size.restype = Z
     L.gdn_prefill_raw.argtypes = [P, P, F, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
     L.gdn_prefill_raw.restype = I
+    L.gdn_prefill_backward_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_prefill_backward_workspace_size.restype = Z
+    L.gdn_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P,
+                                       P, P, P, Z, P]
+    L.gdn_prefill_backward.restype = I
     L.gdn_gates.argtypes = [P, P, P, P, I, I, P, P, P]
     L.gdn_gates.restype = I
     L.gdn_layer_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -230,6 +236,68 @@ def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale:
                            _stream(dev))
     _check(rc, "gdn_prefill")
     return o, fs
+
+
+def gdn_prefill_backward_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
+                                        d_v: int = 128) -> int:
+    return int(lib().gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+
+
+def gdn_prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
+                         cu_seqlens=None, *, scale: float = 1.0, d_initial_state=True,
+                         workspace=None):
+    """Gradients of the bf16 gdn_prefill.  q, k: bf16 [T, H_qk, 128]; v, d_o:
+    bf16 [T, H_v, 128]; g, beta: fp32 [T, H_v]; initial_state, d_final_state:
+    fp32 [N, H_v, 128, 128] or None.  d_initial_state: True (allocate and
+    return it), False/None (skip it) or an fp32 tensor to write.  Returns
+    (dq, dk, dv, dg, dbeta, d_initial_state or None)."""
+    torch = _torch()
+    dev = _device_of(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
+        _need(t, name, torch.bfloat16, dev, 3)
+    T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if tuple(k.shape) != (T, H_qk, d_k) or v.shape[0] != T or tuple(d_o.shape) != tuple(v.shape):
+        raise ValueError("q, k, v, d_o shapes disagree")
+    _need(g, "g", torch.float32, dev, 2)
+    _need(beta, "beta", torch.float32, dev, 2)
+    if tuple(g.shape) != (T, H_v) or tuple(beta.shape) != (T, H_v):
+        raise ValueError("g and beta must be [T, H_v]")
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    sshape = (N, H_v, d_v, d_k)
+    for t, name in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None:
+            _need(t, name, torch.float32, dev, 4)
+            if tuple(t.shape) != sshape:
+                raise ValueError(f"{name} must be {sshape}")
+    if d_initial_state is True:
+        dS0 = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif d_initial_state is None or d_initial_state is False:
+        dS0 = None
+    else:
+        dS0 = d_initial_state
+        _need(dS0, "d_initial_state", torch.float32, dev, 4)
+        if tuple(dS0.shape) != sshape:
+            raise ValueError(f"d_initial_state must be {sshape}")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    db = torch.empty_like(beta)
+    ws_need = gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().gdn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_o),
+                                    _ptr(d_final_state), N, T, H_qk, H_v, d_k, d_v, float(scale),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0),
+                                    _ptr(workspace), ws_bytes, _stream(dev))
+    _check(rc, "gdn_prefill_backward")
+    return dq, dk, dv, dg, db, dS0
 
 
 def gdn_prefill_raw_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
@@ -535,6 +603,7 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.
 
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
+           "gdn_prefill_backward", "gdn_prefill_backward_workspace_size",
            "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
            "gdn_layer_decode_step", "gdn_decode_multi_step", "gdn_state_rollback",
            "gdn_gated_norm", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

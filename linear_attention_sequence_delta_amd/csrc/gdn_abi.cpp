@@ -252,6 +252,56 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
     return finish(e, s, "gdn_prefill_raw launch");
 }
 
+size_t gdn_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (N < 1 || T < 0 || H_qk < 1 || H_v < 1) return 0;
+    return gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v);
+}
+
+int gdn_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                         const void *d_o, const float *d_final_state, int N, int T, int H_qk,
+                         int H_v, int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
+                         float *dg, float *dbeta, float *d_initial_state, void *workspace,
+                         size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (H_v / H_qk > gdn::kMaxPrepGroup)
+        return fail(GDN_ERR_UNSUPPORTED, "bf16 prefill supports at most %d V-heads per QK head (got %d)",
+                    gdn::kMaxPrepGroup, H_v / H_qk);
+    if (T > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return fail(GDN_ERR_INVALID_ARG,
+                    "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+    const size_t nqk = (size_t)T * H_qk * gdn::kD * 2, nv = (size_t)T * H_v * gdn::kD * 2;
+    const size_t ng = (size_t)T * H_v * 4, ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
+    const size_t need = gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+    if (ws_bytes < need || !workspace)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    const struct { const void *p; size_t n; } in[] = {
+        {q, nqk}, {k, nqk}, {v, nv}, {g, ng}, {beta, ng}, {initial_state, ns}, {d_o, nv},
+        {d_final_state, ns}, {cu_seqlens, (size_t)(N + 1) * 4}};
+    const struct { const void *p; size_t n; } out[] = {
+        {dq, nqk}, {dk, nqk}, {dv, nv}, {dg, ng}, {dbeta, ng}, {d_initial_state, ns},
+        {workspace, need}};
+    for (const auto &o : out) {
+        for (const auto &i : in)
+            if (overlaps(o.p, o.n, i.p, i.n))
+                return fail(GDN_ERR_INVALID_ARG, "gradients and workspace must not overlap any input");
+        for (const auto &o2 : out)
+            if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n))
+                return fail(GDN_ERR_INVALID_ARG, "gradients and workspace must not overlap each other");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
+    hipError_t e = gdn::launch_chunked_backward(q, k, v, g, beta, initial_state, cu_seqlens, N, T,
+                                                H_qk, H_v, scale, d_o, d_final_state, dq, dk, dv,
+                                                dg, dbeta, d_initial_state, workspace, s);
+    return finish(e, s, "gdn_prefill_backward launch");
+}
+
 int gdn_gates(const float *a, const float *b, const float *A_log, const float *dt_bias, int T,
               int H_v, float *g, float *beta, void *stream) {
     if (T < 0 || H_v < 1) return fail(GDN_ERR_INVALID_ARG, "T must be >= 0 and H_v >= 1");

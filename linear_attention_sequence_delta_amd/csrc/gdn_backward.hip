@@ -1,0 +1,700 @@
+// gdn_backward.hip -- gradients of the bf16 chunked prefill (64-token chunks).
+//
+// The layer is trained, and the pages name a fused forward/backward kernel for
+// it ("Qwen3.8-27B：27B 如何打出千亿级效果，且塞进单张消费级显卡", sec. 2.1).  The
+// forward per chunk (gdn_chunked.hip), with S the state the chunk starts from,
+// G the running sum of g inside the chunk, gamma = exp(G), lambda_r =
+// exp(G_L - G_r), D_ri = exp(G_r - G_i):
+//   A = strictly-lower(b_r D_ri k_r.k_i),  T = (I + A)^{-1},  T' = T diag(b)
+//   P = lower-incl(scale D_ri q_r.k_i)
+//   R = V - diag(gamma) K S^T,  U = T' R
+//   O = scale diag(gamma) Q S^T + P U,  S' = gamma_L S + U^T diag(lambda) K
+// is differentiated chunk by chunk.  With dS' the gradient with respect to
+// the state the chunk hands on:
+//   reverse scan (sequential over chunks, last to first):
+//     dU = P^T dO + diag(lambda) K dS'^T,   dV = dR = T'^T dU
+//     dS = gamma_L dS' + scale dO^T diag(gamma) Q - dR^T diag(gamma) K
+//   per chunk, in parallel (S from a forward pass that stores it):
+//     dQ = scale diag(gamma) dO S + M_P K
+//     dK = -diag(gamma) dR S + diag(lambda) U dS' + M_P^T Q + M_A' K + M_A'^T K
+//     with dP = dO U^T, M_P = dP * scale D (lower-incl),
+//          dT' = dU R^T (lower-incl), dT = dT' diag(b), dA = -T^T dT T^T,
+//          M_A = dA * D (strictly lower), M_A' = diag(b) M_A
+//     db_i = sum_r dT'_ri T_ri + sum_j M_A,ij k_i.k_j
+//     dG_r = scale gamma_r q_r.(dO S)_r - gamma_r dR_r.(K S^T)_r
+//            - lambda_r k_r.(U dS')_r + rowsum_r - colsum_r of (dP * P) and
+//            of (dA * A), and the last row also takes
+//            gamma_L <dS', S> + sum_r lambda_r k_r.(U dS')_r
+//     dg = the suffix sums of dG inside the chunk (G_r = g_0 + ... + g_r).
+// All products are bf16 MFMA (16 x 16 x 32) with fp32 accumulation; the
+// gradient of the state stays fp32 in registers through the reverse scan.
+#include <stdint.h>
+
+#include "gdn_chunk.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kBSlab = 32;             // d_v columns per reverse-scan workgroup
+constexpr int kBSlabs = kD / kBSlab;   // 4
+constexpr int kSP = kBSlab + 8;        // LDS row stride (bf16) of slab-wide rows
+
+// MFMA operands from row-major bf16 LDS matrices, for lane (c = lane % 16,
+// g4 = lane / 16): frag_rows gives M[r0 + c][k0 + 8 g4 .. +7] (a row piece),
+// frag_cols gives M[k0 + 8 g4 + j][c0 + c], j = 0..7 (a column piece, two
+// transposing reads).  An operand's lane c indexes the output row (A) or
+// column (B) and the 8 values run along the contraction.
+__device__ __forceinline__ uint4 frag_rows(const uint16_t *M, int ld, int r0, int k0) {
+    const int lane = threadIdx.x & 63;
+    return *reinterpret_cast<const uint4 *>(M + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+__device__ __forceinline__ uint4 frag_cols(const uint16_t *M, int ld, int k0, int c0) {
+    const int lane = threadIdx.x & 63, c = lane & 15;
+    const uint16_t *base = M + (k0 + 8 * (lane >> 4) + (c >> 2)) * ld + c0 + 4 * (c & 3);
+    const uint2 lo = lds_read_tr16(base), hi = lds_read_tr16(base + 4 * ld);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+__device__ __forceinline__ void unpack4(uint2 u, float *f) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+    float x[8], y[8], s = 0.f;
+    unpack8(a, x);
+    unpack8(b, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(x[e], y[e], s);
+    return s;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// ------------------------------------------------------------ reverse scan
+// Inputs of one chunk, loaded a chunk ahead.  Rows past the end of a sequence
+// are clamped to its last row on load and replaced by zero in LDS.
+struct RevRegs {
+    u32x4 kr[4];     // K row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
+    u32x4 qr[4];     // Q rows likewise
+    u32x4 dor;       // dO row 16 w + lane / 4, slab columns 8 (lane % 4) .. +7
+    u32x4 pt[2];     // P^T row 16 w + c, columns 32 s + 8 g4 .. +7
+    u32x4 tt[2];     // T'^T likewise
+    float Gown;      // G of row 16 w + c
+    float Gz;        // G of row 16 w + lane / 4
+    float GL;        // G of the chunk's last row
+};
+
+// One workgroup (4 waves) per (sequence, V-head, 32-column d_v slab); wave w
+// owns chunk rows 16 w .. +15 of dU and dR and d_k columns 32 w .. +31 of the
+// fp32 state gradient.  Three barriers per chunk: (1) dU complete, (2) dR
+// complete, (3) dS complete.  Writes, per chunk, the bf16 dS' it starts from
+// (dsw [chunk][H_v][d_v][d_k]) and dU (duw [chunk row][H_v][d_v]); dv rows;
+// and the gradient with respect to the initial state.
+__global__ __launch_bounds__(256) void bwd_scan_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ d_o,
+    const float *__restrict__ dS_final, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
+    const uint16_t *__restrict__ bws, uint16_t *__restrict__ dsw, uint16_t *__restrict__ duw,
+    uint16_t *__restrict__ dv, float *__restrict__ dS0) {
+    __shared__ __attribute__((aligned(16))) uint16_t sS[kBSlab * kKP];       // dS' (bf16), [v][k]
+    __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];      // K rows of the chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sQr[kChunk * kKP];      // Q rows of the chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sDO[2][kChunk * kSP];   // dO rows (slab)
+    __shared__ __attribute__((aligned(16))) uint16_t sZq[2][kChunk * kSP];   // scale gamma_r dO_r
+    __shared__ __attribute__((aligned(16))) uint16_t sDU[kChunk * kSP];      // dU rows (slab)
+    __shared__ __attribute__((aligned(16))) uint16_t sZk[kChunk * kSP];      // -gamma_r dR_r
+
+    const int u = xcd_unit();
+    const int slab = u % kBSlabs;
+    const int nh = u / kBSlabs;
+    const int h = nh % H_v, n = nh / H_v;
+    const int hq = h / (H_v / H_qk);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g4 = lane >> 4, c = lane & 15;
+    const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
+    const int nch = (s1 - s0 + kChunk - 1) / kChunk;
+    const int cbase = chunk_base[n];
+    const int e0 = kBSlab * slab;
+    const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
+    auto chunk_len = [&](int ci) { return min(kChunk, s1 - (s0 + kChunk * ci)); };
+
+    auto fetch = [&](int ci, RevRegs &R) {      // needs nch >= 1
+        ci = max(ci, 0);                        // before the first chunk: loaded, never used
+        const int L = chunk_len(ci);
+        const size_t row0 = (size_t)(s0 + kChunk * ci);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(16 * w + 4 * i + (lane >> 4), L - 1);
+            const size_t off = ((row0 + r) * H_qk + hq) * kD + 8 * (lane & 15);
+            R.kr[i] = *reinterpret_cast<const u32x4 *>(k + off);
+            R.qr[i] = *reinterpret_cast<const u32x4 *>(q + off);
+        }
+        const int rd = min(16 * w + (lane >> 2), L - 1);
+        R.dor = *reinterpret_cast<const u32x4 *>(d_o + ((row0 + rd) * H_v + h) * kD + e0 + 8 * (lane & 3));
+        const uint16_t *rec = bws + ((size_t)(cbase + ci) * H_v + h) * kBwdRecElems;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            R.pt[s] = *reinterpret_cast<const u32x4 *>(rec + kBwdPtOff + frag_off(w, s, lane));
+            R.tt[s] = *reinterpret_cast<const u32x4 *>(rec + kBwdTtOff + frag_off(w, s, lane));
+        }
+        const float *Gp = reinterpret_cast<const float *>(rec + kBwdGOff);
+        R.Gown = Gp[16 * w + c];
+        R.Gz = Gp[16 * w + (lane >> 2)];
+        R.GL = Gp[kChunk - 1];
+    };
+    // dO rows of chunk ci and scale gamma_r dO_r into the buffers of ci's parity
+    auto stage_rows = [&](int ci, const RevRegs &R) {
+        const int r = 16 * w + (lane >> 2), pc = 8 * (lane & 3);
+        u32x4 d = R.dor;
+        if (r >= chunk_len(ci)) d = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(sDO[ci & 1] + r * kSP + pc) = d;
+        float x[8];
+        unpack8(__builtin_bit_cast(uint4, d), x);
+        const float gz = scale * __expf(R.Gz);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= gz;
+        *reinterpret_cast<uint4 *>(sZq[ci & 1] + r * kSP + pc) = pack_bf8(x);
+    };
+
+    // st[t][nt] = dS[e0 + 16 nt + c][32 w + 16 t + 4 g4 + j]
+    f32x4 st[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            if (dS_final) {
+                const float4 x = *reinterpret_cast<const float4 *>(
+                    dS_final + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4);
+                st[t][nt] = f32x4{x.x, x.y, x.z, x.w};
+            } else {
+                st[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    auto write_state_lds = [&]() {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                *reinterpret_cast<uint2 *>(sS + (16 * nt + c) * kKP + 32 * w + 16 * t + 4 * g4) =
+                    pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+    };
+
+    auto body = [&](int ci, const RevRegs &cur, RevRegs &nxt) {
+        const int L = chunk_len(ci);
+        // the gradient this chunk starts from (with respect to its end state)
+        uint16_t *dsp = dsw + ((size_t)(cbase + ci) * H_v + h) * (kD * kD);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                *reinterpret_cast<uint2 *>(dsp + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
+                    pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+        // this wave's K and Q rows into LDS
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * i + (lane >> 4);
+            const bool ok = r < L;
+            *reinterpret_cast<u32x4 *>(sKr + r * kKP + 8 * (lane & 15)) = ok ? cur.kr[i] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(sQr + r * kKP + 8 * (lane & 15)) = ok ? cur.qr[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+        wave_lds_sync();
+        uint4 kB[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kB[s] = frag_rows(sKr, kKP, 16 * w, 32 * s);
+        fetch(ci - 1, nxt);
+        const float lam = __expf(cur.GL - cur.Gown), gam = __expf(cur.Gown), gamL = __expf(cur.GL);
+        const uint16_t *sDOc = sDO[ci & 1];
+        // dU = P^T dO + diag(lambda) K dS'^T: rows 16 w + c, slab columns 16 nt + 4 g4 + j
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) y = mfma32(frag_rows(sS, kKP, 16 * nt, 32 * s), kB[s], y);
+            f32x4 pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s >= (w >> 1)) pd = mfma32(frag_cols(sDOc, kSP, 32 * s, 16 * nt), cur.pt[s], pd);
+            const uint2 p = pk4(pd[0] + lam * y[0], pd[1] + lam * y[1], pd[2] + lam * y[2], pd[3] + lam * y[3]);
+            *reinterpret_cast<uint2 *>(sDU + (16 * w + c) * kSP + 16 * nt + 4 * g4) = p;
+            *reinterpret_cast<uint2 *>(duw + (((size_t)(cbase + ci) * kChunk + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) = p;
+        }
+        __syncthreads();                                    // (1) dU complete
+        // dR = T'^T dU: the gradient of v
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (s >= (w >> 1)) d = mfma32(frag_cols(sDU, kSP, 32 * s, 16 * nt), cur.tt[s], d);
+            if (16 * w + c < L)
+                *reinterpret_cast<uint2 *>(dv + ((size_t)(s0 + kChunk * ci + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
+                    pk4(d[0], d[1], d[2], d[3]);
+            *reinterpret_cast<uint2 *>(sZk + (16 * w + c) * kSP + 16 * nt + 4 * g4) =
+                pk4(-gam * d[0], -gam * d[1], -gam * d[2], -gam * d[3]);
+        }
+        if (ci > 0) stage_rows(ci - 1, nxt);
+        __syncthreads();                                    // (2) dR complete
+        // dS = gamma_L dS' + (scale diag(gamma) dO)^T Q + (-diag(gamma) dR)^T K
+        uint4 zq[2][2], zk[2][2], qa[2][2], ka[2][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                zq[nt][s] = frag_cols(sZq[ci & 1], kSP, 32 * s, 16 * nt);
+                zk[nt][s] = frag_cols(sZk, kSP, 32 * s, 16 * nt);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                qa[t][s] = frag_cols(sQr, kKP, 32 * s, 32 * w + 16 * t);
+                ka[t][s] = frag_cols(sKr, kKP, 32 * s, 32 * w + 16 * t);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 a = gamL * st[t][nt];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    a = mfma32(qa[t][s], zq[nt][s], a);
+                    a = mfma32(ka[t][s], zk[nt][s], a);
+                }
+                st[t][nt] = a;
+            }
+        write_state_lds();
+        __syncthreads();                                    // (3) dS complete
+    };
+
+    write_state_lds();
+    RevRegs ra, rb;
+    if (nch > 0) {
+        fetch(nch - 1, ra);
+        stage_rows(nch - 1, ra);
+    }
+    __syncthreads();
+    for (int ci = nch - 1; ci >= 0; ci -= 2) {
+        body(ci, ra, rb);
+        if (ci == 0) break;
+        body(ci - 1, rb, ra);
+    }
+    if (dS0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                *reinterpret_cast<float4 *>(dS0 + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
+                    make_float4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+    }
+}
+
+// ------------------------------------------------------------ chunk gradients
+// One workgroup (4 waves) per (chunk, QK head), looping over the V-heads of
+// the group; dq and dk of the group accumulate in fp32 registers.  Wave w
+// owns chunk rows 16 w .. +15: every row-wise result is held with lane
+// (c, g4) on row 16 w + c, columns 16 t + 4 g4 .. +3 of each 16-column tile
+// t, which an MFMA gives when the left factor's rows are its B operand and
+// the right factor's columns its A operand.
+__global__ __launch_bounds__(256) void bwd_grad_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ d_o, const uint16_t *__restrict__ dv, const float *__restrict__ beta,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, int N, int T, int H_qk,
+    int H_v, float scale, const uint16_t *__restrict__ bws, const uint16_t *__restrict__ states,
+    const uint16_t *__restrict__ dsw, const uint16_t *__restrict__ duw, uint16_t *__restrict__ dq,
+    uint16_t *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * kKP];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * kKP];
+    __shared__ __attribute__((aligned(16))) uint16_t sSt[kD * kKP];      // S, then dS' ([v][k])
+    __shared__ __attribute__((aligned(16))) uint16_t sR[kChunk * kKP];   // R [r][v]
+    __shared__ __attribute__((aligned(16))) uint16_t sU[kChunk * kKP];   // U [r][v]
+    __shared__ __attribute__((aligned(16))) uint16_t sT[kChunk * kRP];   // T
+    __shared__ __attribute__((aligned(16))) uint16_t sM[kChunk * kRP];   // M_P, then M_A'
+    __shared__ __attribute__((aligned(16))) uint16_t sM2[kChunk * kRP];  // dT
+    __shared__ __attribute__((aligned(16))) uint16_t sF[kChunk * kRP];   // dT T^T
+    __shared__ __attribute__((aligned(16))) float sG[kChunk];
+    __shared__ __attribute__((aligned(16))) float sB[kChunk];
+    __shared__ float sRowG[kChunk], sRowB[kChunk];
+    __shared__ float sColG[4][kChunk], sColB[4][kChunk];
+    __shared__ float sE[4];
+
+    const int gc = blockIdx.x / H_qk, hq = blockIdx.x - gc * H_qk;
+    if (gc >= chunk_base[N]) return;                   // same for the whole workgroup
+    const int n = seq_of_chunk(chunk_base, N, gc);
+    const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
+    const int c0 = s0 + kChunk * (gc - chunk_base[n]);
+    const int L = min(kChunk, s1 - c0);
+    const int group = H_v / H_qk;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g4 = lane >> 4, c = lane & 15;
+    const int row = 16 * w + c;                        // this lane's row
+    const bool row_ok = row < L;
+    const int rr = min(row, L - 1);
+    const int wb = w >> 1;                             // 32-row block of this wave's rows
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * i + (lane >> 4);
+        const size_t off = ((size_t)(c0 + min(r, L - 1)) * H_qk + hq) * kD + 8 * (lane & 15);
+        uint4 kv = *reinterpret_cast<const uint4 *>(k + off), qv = *reinterpret_cast<const uint4 *>(q + off);
+        if (r >= L) kv = qv = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(sK + r * kKP + 8 * (lane & 15)) = kv;
+        *reinterpret_cast<uint4 *>(sQ + r * kKP + 8 * (lane & 15)) = qv;
+    }
+    // x_row . k_(16 t + 4 g4 + j) for the rows x of M (K or Q), tile t
+    auto dot_k = [&](const uint16_t *M, int t) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a = mfma32(frag_rows(sK, kKP, 16 * t, 32 * s), frag_rows(M, kKP, 16 * w, 32 * s), a);
+        return a;
+    };
+    // the 16-lane column sums of x (one per column 16 t + 4 g4 + j) into dst
+    auto col_sums = [&](f32x4 x, float *dst, int t, bool add) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float y = row16_sum(x[j]);
+            if (c == 0) dst[16 * t + 4 * g4 + j] = add ? dst[16 * t + 4 * g4 + j] + y : y;
+        }
+    };
+    f32x4 dQa[8], dKa[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dQa[t] = dKa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int vv = 0; vv < group; ++vv) {
+        const int h = hq * group + vv;
+        const uint16_t *brec = bws + ((size_t)gc * H_v + h) * kBwdRecElems;
+        const uint16_t *Sg = states + ((size_t)gc * H_v + h) * (kD * kD);
+        const uint16_t *dSg = dsw + ((size_t)gc * H_v + h) * (kD * kD);
+        __syncthreads();                               // the previous V-head's LDS reads are done
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + 256 * m, r = e >> 3, cb = e & 7;
+            *reinterpret_cast<uint4 *>(sT + r * kRP + 8 * cb) =
+                *reinterpret_cast<const uint4 *>(brec + kBwdTOff + r * kChunk + 8 * cb);
+        }
+        float e1 = 0.f;                                // this thread's share of <dS', S>
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int e = tid + 256 * m, r = e >> 4, cb = e & 15;
+            const uint4 sv = *reinterpret_cast<const uint4 *>(Sg + r * kD + 8 * cb);
+            const uint4 dsv = *reinterpret_cast<const uint4 *>(dSg + r * kD + 8 * cb);
+            *reinterpret_cast<uint4 *>(sSt + r * kKP + 8 * cb) = sv;
+            e1 += dot8(sv, dsv);
+        }
+        if (tid < kChunk) {
+            sG[tid] = reinterpret_cast<const float *>(brec + kBwdGOff)[tid];
+            sB[tid] = tid < L ? beta[(size_t)(c0 + tid) * H_v + h] : 0.f;
+        }
+        // row `row` of a [T][H_v][128] input (zero past the chunk), columns 32 s + 8 g4 .. +7
+        auto row_frags = [&](const uint16_t *X, uint4 *f) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                f[s] = *reinterpret_cast<const uint4 *>(X + ((size_t)(c0 + rr) * H_v + h) * kD + 32 * s + 8 * g4);
+                if (!row_ok) f[s] = make_uint4(0, 0, 0, 0);
+            }
+        };
+        __syncthreads();
+
+        const float Gr = sG[row], GLast = sG[kChunk - 1];
+        const float gam = __expf(Gr), lam = __expf(GLast - Gr), br = sB[row];
+        float rowG = 0.f, rowB = 0.f, e2 = 0.f;
+
+        // X = K S^T -> R = V - diag(gamma) X; dG: -gamma_r dR_r . X_r
+#pragma unroll 2
+        for (int nt = 0; nt < 8; ++nt) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) x = mfma32(frag_rows(sSt, kKP, 16 * nt, 32 * s), frag_rows(sK, kKP, 16 * w, 32 * s), x);
+            const size_t vo = ((size_t)(c0 + rr) * H_v + h) * kD + 16 * nt + 4 * g4;
+            uint2 vr = *reinterpret_cast<const uint2 *>(v + vo), dvr = *reinterpret_cast<const uint2 *>(dv + vo);
+            if (!row_ok) vr = dvr = make_uint2(0, 0);
+            float vf[4], dvf[4], rv[4];
+            unpack4(vr, vf);
+            unpack4(dvr, dvf);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                rv[j] = vf[j] - gam * x[j];
+                rowG -= gam * dvf[j] * x[j];
+            }
+            *reinterpret_cast<uint2 *>(sR + row * kKP + 16 * nt + 4 * g4) = pk4(rv[0], rv[1], rv[2], rv[3]);
+        }
+        // dO S and dR S: dQ += scale gamma dO S (dG: q_r . that), dK -= gamma dR S
+        {
+        uint4 dOf[4], dVf[4];
+        row_frags(d_o, dOf);
+        row_frags(dv, dVf);
+#pragma unroll 2
+        for (int kt = 0; kt < 8; ++kt) {
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 sf = frag_cols(sSt, kKP, 32 * s, 16 * kt);
+                a1 = mfma32(sf, dOf[s], a1);
+                a2 = mfma32(sf, dVf[s], a2);
+            }
+            float qf[4];
+            unpack4(*reinterpret_cast<const uint2 *>(sQ + row * kKP + 16 * kt + 4 * g4), qf);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = scale * gam * a1[j];
+                dQa[kt][j] += t;
+                rowG += t * qf[j];
+                dKa[kt][j] -= gam * a2[j];
+            }
+        }
+        }
+        __syncthreads();                               // R complete; S no longer read
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int e = tid + 256 * m, r = e >> 4, cb = e & 15;
+            *reinterpret_cast<uint4 *>(sSt + r * kKP + 8 * cb) = *reinterpret_cast<const uint4 *>(dSg + r * kD + 8 * cb);
+        }
+        // U = T' R (T'[row][i] = T[row][i] b_i)
+        {
+            uint4 tB[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float tf[8];
+                unpack8(*reinterpret_cast<const uint4 *>(sT + row * kRP + 32 * s + 8 * g4), tf);
+                const float4 b0 = *reinterpret_cast<const float4 *>(sB + 32 * s + 8 * g4);
+                const float4 b1 = *reinterpret_cast<const float4 *>(sB + 32 * s + 8 * g4 + 4);
+                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tf[e] *= bb[e];
+                tB[s] = pack_bf8(tf);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                f32x4 ua = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s <= wb) ua = mfma32(frag_cols(sR, kKP, 32 * s, 16 * nt), tB[s], ua);
+                *reinterpret_cast<uint2 *>(sU + row * kKP + 16 * nt + 4 * g4) = pk4(ua[0], ua[1], ua[2], ua[3]);
+            }
+        }
+        __syncthreads();                               // U and dS' complete
+
+        // U dS': dK += lambda U dS'; dG: -lambda_r k_r . (U dS')_r (the last row gets the sum)
+        {
+            uint4 uB[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) uB[s] = frag_rows(sU, kKP, 16 * w, 32 * s);
+#pragma unroll 2
+            for (int kt = 0; kt < 8; ++kt) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) a = mfma32(frag_cols(sSt, kKP, 32 * s, 16 * kt), uB[s], a);
+                float kf[4];
+                unpack4(*reinterpret_cast<const uint2 *>(sK + row * kKP + 16 * kt + 4 * g4), kf);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    dKa[kt][j] += lam * a[j];
+                    const float t = lam * a[j] * kf[j];
+                    rowG -= t;
+                    e2 += t;
+                }
+            }
+        }
+        // dP = dO U^T -> M_P; dT' = dU R^T -> dT; row and column sums
+        {
+            uint4 dOf[4], dUf[4];
+            row_frags(d_o, dOf);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                dUf[s] = *reinterpret_cast<const uint4 *>(duw + (((size_t)gc * kChunk + row) * H_v + h) * kD + 32 * s + 8 * g4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dtp = dp, qk = dp;
+                if (t <= w) {
+                    qk = dot_k(sQ, t);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        dp = mfma32(frag_rows(sU, kKP, 16 * t, 32 * s), dOf[s], dp);
+                        dtp = mfma32(frag_rows(sR, kKP, 16 * t, 32 * s), dUf[s], dtp);
+                    }
+                }
+                const float4 Gi = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
+                const float4 Bi = *reinterpret_cast<const float4 *>(sB + 16 * t + 4 * g4);
+                const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+                float tf[4];
+                unpack4(*reinterpret_cast<const uint2 *>(sT + row * kRP + 16 * t + 4 * g4), tf);
+                float mp[4], dt[4];
+                f32x4 cg, cb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool lo = 16 * t + 4 * g4 + j <= row;
+                    mp[j] = lo ? dp[j] * scale * __expf(Gr - gi[j]) : 0.f;
+                    const float wp = lo ? mp[j] * qk[j] : 0.f;
+                    rowG += wp;
+                    cg[j] = -wp;
+                    dt[j] = lo ? dtp[j] * bi[j] : 0.f;
+                    cb[j] = lo ? dtp[j] * tf[j] : 0.f;
+                }
+                *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(mp[0], mp[1], mp[2], mp[3]);
+                *reinterpret_cast<uint2 *>(sM2 + row * kRP + 16 * t + 4 * g4) = pk4(dt[0], dt[1], dt[2], dt[3]);
+                col_sums(cg, sColG[w], t, false);
+                col_sums(cb, sColB[w], t, false);
+            }
+        }
+        __syncthreads();                               // M_P, dT complete
+
+        // dQ += M_P K; dK += M_P^T Q; F = dT T^T
+        {
+            uint4 mB[2], mtB[2], dtB[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s);
+                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w);
+                dtB[s] = frag_rows(sM2, kRP, 16 * w, 32 * s);
+            }
+#pragma unroll 2
+            for (int kt = 0; kt < 8; ++kt) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s <= wb) a = mfma32(frag_cols(sK, kKP, 32 * s, 16 * kt), mB[s], a);
+                    if (s >= wb) b = mfma32(frag_cols(sQ, kKP, 32 * s, 16 * kt), mtB[s], b);
+                }
+                dQa[kt] += a;
+                dKa[kt] += b;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 f = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s <= wb) f = mfma32(frag_rows(sT, kRP, 16 * t, 32 * s), dtB[s], f);
+                *reinterpret_cast<uint2 *>(sF + row * kRP + 16 * t + 4 * g4) = pk4(f[0], f[1], f[2], f[3]);
+            }
+        }
+        __syncthreads();                               // F complete; M_P no longer read
+
+        // dA = -T^T F (strictly lower) -> M_A = dA * D; db: rows of M_A * KK^T;
+        // dG: rows and columns of dA * A; M_A' = diag(b) M_A -> sM
+        {
+            uint4 ttB[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ttB[s] = frag_cols(sT, kRP, 32 * s, 16 * w);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                f32x4 da = {0.f, 0.f, 0.f, 0.f}, kk = da;
+                if (t <= w) {
+                    kk = dot_k(sK, t);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        if (s >= wb) da = mfma32(frag_cols(sF, kRP, 32 * s, 16 * t), ttB[s], da);
+                }
+                const float4 Gj = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
+                const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
+                float ma[4];
+                f32x4 cg;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool lo = 16 * t + 4 * g4 + j < row;
+                    const float m = lo ? -da[j] * __expf(Gr - gj[j]) : 0.f;
+                    const float kkv = lo ? kk[j] : 0.f;
+                    rowB += m * kkv;
+                    const float wa = m * br * kkv;
+                    rowG += wa;
+                    cg[j] = -wa;
+                    ma[j] = m * br;
+                }
+                *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(ma[0], ma[1], ma[2], ma[3]);
+                col_sums(cg, sColG[w], t, true);
+            }
+        }
+        rowG += __shfl_xor(rowG, 16, 64);
+        rowG += __shfl_xor(rowG, 32, 64);
+        rowB += __shfl_xor(rowB, 16, 64);
+        rowB += __shfl_xor(rowB, 32, 64);
+        if (g4 == 0) {
+            sRowG[row] = rowG;
+            sRowB[row] = rowB;
+        }
+        {
+            const float ew = wave_sum(__expf(GLast) * e1 + e2);
+            if (lane == 0) sE[w] = ew;
+        }
+        __syncthreads();                               // M_A' and the sums complete
+
+        // dK += M_A' K + M_A'^T K
+        {
+            uint4 mB[2], mtB[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s);
+                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint4 kf = frag_cols(sK, kKP, 32 * s, 16 * kt);
+                    if (s <= wb) a = mfma32(kf, mB[s], a);
+                    if (s >= wb) a = mfma32(kf, mtB[s], a);
+                }
+                dKa[kt] += a;
+            }
+        }
+        // dg = suffix sums of dG inside the chunk; db
+        if (w == 0) {
+            float dG = sRowG[lane] + sColG[0][lane] + sColG[1][lane] + sColG[2][lane] + sColG[3][lane];
+            if (lane == kChunk - 1) dG += sE[0] + sE[1] + sE[2] + sE[3];
+            const float db = sRowB[lane] + sColB[0][lane] + sColB[1][lane] + sColB[2][lane] + sColB[3][lane];
+            const float suf = wave_scan(__shfl(dG, 63 - lane, 64));
+            const float dgr = __shfl(suf, 63 - lane, 64);
+            if (lane < L) {
+                dg[(size_t)(c0 + lane) * H_v + h] = dgr;
+                dbeta[(size_t)(c0 + lane) * H_v + h] = db;
+            }
+        }
+    }
+    if (row_ok) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            const size_t off = ((size_t)(c0 + row) * H_qk + hq) * kD + 16 * kt + 4 * g4;
+            *reinterpret_cast<uint2 *>(dq + off) = pk4(dQa[kt][0], dQa[kt][1], dQa[kt][2], dQa[kt][3]);
+            *reinterpret_cast<uint2 *>(dk + off) = pk4(dKa[kt][0], dKa[kt][1], dKa[kt][2], dKa[kt][3]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const float *dS_final,
+                           const int32_t *cu_seqlens, const int32_t *chunk_base, int N, int T,
+                           int H_qk, int H_v, float scale, const void *bws, void *dsw, void *duw,
+                           void *dv, float *dS0, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(N * H_v * kBSlabs), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(d_o), dS_final, cu_seqlens, chunk_base, N, T,
+                       H_qk, H_v, scale, static_cast<const uint16_t *>(bws),
+                       static_cast<uint16_t *>(dsw), static_cast<uint16_t *>(duw),
+                       static_cast<uint16_t *>(dv), dS0);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const void *d_o,
+                           const void *dv, const float *beta, const int32_t *cu_seqlens,
+                           const int32_t *chunk_base, int N, int T, int H_qk, int H_v,
+                           int max_chunks, float scale, const void *bws, const void *states,
+                           const void *dsw, const void *duw, void *dq, void *dk, float *dg,
+                           float *dbeta, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3(max_chunks * H_qk), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(d_o),
+                       static_cast<const uint16_t *>(dv), beta, cu_seqlens, chunk_base, N, T, H_qk,
+                       H_v, scale, static_cast<const uint16_t *>(bws),
+                       static_cast<const uint16_t *>(states), static_cast<const uint16_t *>(dsw),
+                       static_cast<const uint16_t *>(duw), static_cast<uint16_t *>(dq),
+                       static_cast<uint16_t *>(dk), dg, dbeta);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

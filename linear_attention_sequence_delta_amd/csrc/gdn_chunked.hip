@@ -35,87 +35,12 @@
 
 #include <mutex>
 
-#include "gdn_device.h"
+#include "gdn_chunk.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 namespace {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 8 bf16, kept in registers without copies
-
-constexpr int kKP = kD + 8;          // LDS row stride (bf16) of 128-wide rows
-constexpr int kAP = kChunk + 4;      // LDS row stride (fp32) of 64-wide rows
-constexpr int kRP = kChunk + 8;      // LDS row stride (bf16) of 64-wide rows
-constexpr int kTileElems = kChunk * kChunk;   // one 64 x 64 bf16 matrix
-
-template <class A, class B>
-__device__ __forceinline__ f32x4 mfma32(A a, B b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ s16x4 to_bf4(float a, float b, float c, float d) {
-    s16x4 r;
-    r[0] = (short)f2bf(a);
-    r[1] = (short)f2bf(b);
-    r[2] = (short)f2bf(c);
-    r[3] = (short)f2bf(d);
-    return r;
-}
-// fp32 -> bf16 (round to nearest even), two or four at a time
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
-}
-__device__ __forceinline__ uint2 pk4(float a, float b, float c, float d) {
-    return make_uint2(pk2(a, b), pk2(c, d));
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// if lane q points at row (r0 + q / 4), columns c0 + 4 (q % 4) .. + 3 of a
-// row-major bf16 matrix, lane p receives column c0 + p, rows r0 .. r0 + 3:
-// a 16 x 4 block read transposed.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
-    typedef short s4v __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s4v lds_s4v;
-    const s4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s4v *)(__attribute__((address_space(3))) uint16_t *)p);
-    return __builtin_bit_cast(uint2, r);
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ float wave_scan(float x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-// Make this wave's earlier LDS writes visible to its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-struct ChunkRange { int n, c0, len; };
-
-// Largest n with chunk_base[n] <= gc (sequences with no chunks are skipped).
-__device__ __forceinline__ int seq_of_chunk(const int32_t *chunk_base, int N, int gc) {
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (chunk_base[mid] <= gc) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
 
 // ------------------------------------------------------------------- plan
 __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ cu, int N, int T,
@@ -145,18 +70,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 }
 
 // ------------------------------------------------------------------- prep
-// Workspace record of one (chunk, V-head): T', then P, then the chunk's
-// cumulative log decay G as 64 fp32.  Records are written with non-temporal
-// stores: the scan reads them long after (a segment later, when prep and scan
-// overlap), and they would otherwise displace the K and Q rows the scan's
-// workgroups share through L2.  T' and P (bf16 64 x 64) are stored as
-// MFMA operand fragments: block (a, s) = 2 a + s holds, for lane (c, g4), the
-// 16 bytes of row 16 a + c, columns 32 s + 8 g4 .. +7, lanes in order -- so
-// the scan loads each fragment as one contiguous 1 KiB block.  (A fragment
-// read from a row-major tile would touch half of 16 cache lines, which halves
-// the rate the vector memory pipe delivers.)
-constexpr int kRecElems = 2 * kTileElems + 2 * kChunk;   // in bf16 units (16640 bytes)
-__device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a + s) * 64 + lane) * 8; }
+// Records (layout in gdn_chunk.h) are written with non-temporal stores: the
+// scan reads them long after (a segment later, when prep and scan overlap),
+// and they would otherwise displace the K and Q rows the scan's workgroups
+// share through L2.
 
 // One wave per (chunk, QK head) item; a workgroup holds kPrepWaves independent
 // waves, each with its own LDS area, that step through the items
@@ -176,6 +93,9 @@ __device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a
 // the prelude's.  Each lane walks 16 consecutive rows, keeping the conv window
 // in registers.  The normalised rows go to the workspace, where the scan reads
 // them, and through LDS into the MFMA fragments.
+//
+// For the backward pass (kBwd) each (chunk, V-head) also gets a backward
+// record (gdn_chunk.h): the fragments of T'^T and P^T, T row-major and G.
 constexpr int kPrepWaves = 4;
 static_assert(kChunk * kKP * sizeof(uint16_t) <= kChunk * kAP * sizeof(float),
               "a chunk's bf16 K or Q rows fit in a wave's A area");
@@ -187,12 +107,12 @@ struct RawIn {             // fused prelude inputs
     uint16_t *kws, *qws;   // [chunks * 64][H_qk][128] bf16 normalised K and Q rows
 };
 
-template <bool kRaw>
+template <bool kRaw, bool kBwd = false>
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const RawIn raw,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    int item_lo, int item_hi, uint16_t *__restrict__ ws) {
+    int item_lo, int item_hi, uint16_t *__restrict__ ws, uint16_t *__restrict__ bws = nullptr) {
     __shared__ __attribute__((aligned(16))) float sA_w[kPrepWaves][kChunk * kAP];
     __shared__ __attribute__((aligned(16))) uint16_t sP_w[kPrepWaves][kChunk * kRP];
     __shared__ __attribute__((aligned(16))) float sG_w[kPrepWaves][kChunk];
@@ -335,7 +255,9 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
             sG[lane] = G;
             sBt[lane] = bl;
             uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
+            uint16_t *brec = kBwd ? bws + ((size_t)gc * H_v + h) * kBwdRecElems : nullptr;
             __builtin_nontemporal_store(G, reinterpret_cast<float *>(rec + 2 * kTileElems) + lane);
+            if constexpr (kBwd) reinterpret_cast<float *>(brec + kBwdGOff)[lane] = G;
             wave_lds_sync();
 
             // gated K K^T -> A (fp32 rows in LDS, lower tiles); gated Q K^T -> P
@@ -371,6 +293,19 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
                 const int a = qq >> 1, s = qq & 1;
                 __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(sP + (16 * a + c) * kRP + 32 * s + 8 * g4),
                                             reinterpret_cast<u32x4 *>(rec + kTileElems + frag_off(a, s, lane)));
+            }
+            if constexpr (kBwd) {
+                // P^T block (a, s): lane (c, g4) holds P[32 s + 8 g4 + j][16 a + c], j = 0..7
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int a = qq >> 1, s = qq & 1;
+                    uint16_t e[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) e[j] = sP[(32 * s + 8 * g4 + j) * kRP + 16 * a + c];
+                    *reinterpret_cast<uint4 *>(brec + kBwdPtOff + frag_off(a, s, lane)) =
+                        make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                                   e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+                }
             }
 
             float *A = sA;
@@ -465,6 +400,37 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
                 __builtin_nontemporal_store(u32x4{u0.x, u0.y, u1.x, u1.y},
                                             reinterpret_cast<u32x4 *>(rec + frag_off(a, s, lane)));
             }
+            if constexpr (kBwd) {
+                // T'^T block (a, s): lane (c, g4) holds T'[r][16 a + c] for the rows
+                // r = 32 s + 8 g4 + j (T' = T diag(b), rounded as above).  T is
+                // held in the blocks at or below the diagonal; the rest is zero.
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int a = qq >> 1, s = qq & 1;
+                    const int col = 16 * a + c;
+                    const float bc = sBt[col];
+                    float e[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = 32 * s + 8 * g4 + j;
+                        e[j] = (r >> 4) >= a ? A[r * kAP + col] * bc : 0.f;
+                    }
+                    const uint2 lo = pk4(e[0], e[1], e[2], e[3]), hi = pk4(e[4], e[5], e[6], e[7]);
+                    *reinterpret_cast<uint4 *>(brec + kBwdTtOff + frag_off(a, s, lane)) =
+                        make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+                // T row-major: lane r writes row r
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb) {
+                    const bool ok = (cb >> 1) <= (lane >> 4);
+                    const float4 t0 = *reinterpret_cast<const float4 *>(A + lane * kAP + 8 * cb);
+                    const float4 t1 = *reinterpret_cast<const float4 *>(A + lane * kAP + 8 * cb + 4);
+                    const uint2 lo = ok ? pk4(t0.x, t0.y, t0.z, t0.w) : make_uint2(0, 0);
+                    const uint2 hi = ok ? pk4(t1.x, t1.y, t1.z, t1.w) : make_uint2(0, 0);
+                    *reinterpret_cast<uint4 *>(brec + kBwdTOff + lane * kChunk + 8 * cb) =
+                        make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+            }
             wave_lds_sync();                 // T read before the next V-head's A is written
         }
     }
@@ -506,12 +472,17 @@ struct OutRegs {          // waves 4-7
 // in the workspace, and the output waves form the v slab: during chunk ci they
 // apply conv and SiLU (the prelude's arithmetic) to the raw v rows of chunk
 // ci + 1 and write them into the other half of a double-buffered v tile.
-template <bool kRaw>
+//
+// For the backward pass (kSave) the state waves store the bf16 state each
+// chunk starts from (the values the chunk's products use) into
+// states [chunk][H_v][d_v][d_k], and o is not written.
+template <bool kRaw, bool kSave = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const RawIn raw, const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *__restrict__ o) {
+    int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *__restrict__ o,
+    uint16_t *__restrict__ states = nullptr) {
     constexpr int kVBufs = kRaw ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t sS[kSlabW * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
@@ -522,13 +493,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sQ[4][16 * kKP];     // each output wave's Q rows
     __shared__ __attribute__((aligned(16))) uint16_t sXv[kRaw ? 4 : 1][20 * kVP];   // raw v rows per output wave
 
-    // Workgroup -> (sequence, V-head, slab).  Workgroups are handed to the 8
-    // XCDs round-robin; consecutive units (all slabs of a head, neighbouring
-    // heads of one QK group) are kept on one XCD so that they share its L2:
-    // XCD x takes the contiguous range of units that starts at
-    // x * (G / 8) + min(x, G % 8) (a bijection for any grid size G).
-    const int xcd = blockIdx.x & 7;
-    const int u = xcd * ((int)gridDim.x >> 3) + min(xcd, (int)gridDim.x & 7) + (int)(blockIdx.x >> 3);
+    // Workgroup -> (sequence, V-head, slab); consecutive units (all slabs of a
+    // head, neighbouring heads of one QK group) share an XCD's L2.
+    const int u = xcd_unit();
     const int slab = u % kSlabsW;
     const int nh = u / kSlabsW;
     const int h = nh % H_v, n = nh / H_v;
@@ -603,6 +570,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
         };
 
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
+            if constexpr (kSave) {
+                uint16_t *sp = states + ((size_t)(cbase + ci) * H_v + h) * (kD * kD);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        *reinterpret_cast<uint2 *>(sp + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
+                            pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+            }
             // this wave's 16 rows of v and of K into LDS, row-major; K's MFMA
             // fragments come back out of its own rows (with the prelude
             // fused, the output waves have already written v)
@@ -790,7 +766,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 8 * g4), cur.pA[0], a);
                 if (w >= 2)
                     a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 32 + 8 * g4), cur.pA[1], a);
-                if (row_ok)
+                if (row_ok && !kSave)
                     *reinterpret_cast<uint2 *>(o + ((size_t)(c0 + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
                         pk4(a[0], a[1], a[2], a[3]);
             }
@@ -975,7 +951,71 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
     return hipSuccess;
 }
 
+// Backward workspace: chunk offsets | forward records | backward records |
+// bf16 state at each chunk start | bf16 state gradient at each chunk end |
+// bf16 dU rows (chunk-aligned).
+struct BwdWorkspace {
+    int32_t *chunk_base;
+    uint16_t *rec, *brec, *states, *dsw, *duw;
+};
+size_t bwd_workspace_layout(int N, int T, int H_v, void *base, BwdWorkspace *wsp) {
+    const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
+    const size_t head = align256((size_t)(N + 1) * sizeof(int32_t));
+    const size_t rec = max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);
+    const size_t brec = max_chunks * (size_t)H_v * kBwdRecElems * sizeof(uint16_t);
+    const size_t st = max_chunks * (size_t)H_v * kD * kD * sizeof(uint16_t);
+    const size_t du = max_chunks * kChunk * (size_t)H_v * kD * sizeof(uint16_t);
+    if (wsp) {
+        char *p = static_cast<char *>(base);
+        wsp->chunk_base = reinterpret_cast<int32_t *>(p);
+        wsp->rec = reinterpret_cast<uint16_t *>(p + head);
+        wsp->brec = reinterpret_cast<uint16_t *>(p + head + rec);
+        wsp->states = reinterpret_cast<uint16_t *>(p + head + rec + brec);
+        wsp->dsw = reinterpret_cast<uint16_t *>(p + head + rec + brec + st);
+        wsp->duw = reinterpret_cast<uint16_t *>(p + head + rec + brec + 2 * st);
+    }
+    return head + rec + brec + 2 * st + du;
+}
+
 }  // namespace
+
+size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v) {
+    (void)H_qk;
+    return bwd_workspace_layout(N, T, H_v, nullptr, nullptr);
+}
+
+// plan -> prep (forward and backward records) -> forward scan storing each
+// chunk's start state -> reverse scan (dv, the initial-state gradient, dS'
+// and dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta).
+hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *S0, const int32_t *cu_seqlens,
+                                   int N, int T, int H_qk, int H_v, float scale, const void *d_o,
+                                   const float *dS_final, void *dq, void *dk, void *dv, float *dg,
+                                   float *dbeta, float *dS0, void *workspace, hipStream_t stream) {
+    const int max_chunks = (T + kChunk - 1) / kChunk + N;
+    BwdWorkspace W;
+    bwd_workspace_layout(N, T, H_v, workspace, &W);
+    const uint16_t *q16 = static_cast<const uint16_t *>(q), *k16 = static_cast<const uint16_t *>(k);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, W.chunk_base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int items = max_chunks * H_qk;
+    hipLaunchKernelGGL((prep_kernel<false, true>), dim3((items + kPrepWaves - 1) / kPrepWaves),
+                       dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
+                       W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_kernel<false, true>), dim3(N * H_v * kSlabsW), dim3(512), 0, stream,
+                       q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
+                       cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
+                       nullptr, W.states);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
+                             W.brec, W.dsw, W.duw, dv, dS0, stream)) != hipSuccess)
+        return e;
+    return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
+                           max_chunks, scale, W.brec, W.states, W.dsw, W.duw, dq, dk, dg, dbeta,
+                           stream);
+}
 
 size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw) {
     return workspace_layout(N, T, H_qk, H_v, raw, nullptr, nullptr);

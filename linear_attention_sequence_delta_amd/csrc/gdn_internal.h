@@ -39,6 +39,24 @@ hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, c
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                       float scale, void *o, void *workspace, hipStream_t stream);
 
+// Gradients of the chunked bf16 prefill (dq, dk, dv bf16; dg, dbeta, dS0 fp32).
+size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v);
+hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *S0, const int32_t *cu_seqlens,
+                                   int N, int T, int H_qk, int H_v, float scale, const void *d_o,
+                                   const float *dS_final, void *dq, void *dk, void *dv, float *dg,
+                                   float *dbeta, float *dS0, void *workspace, hipStream_t stream);
+hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const float *dS_final,
+                           const int32_t *cu_seqlens, const int32_t *chunk_base, int N, int T,
+                           int H_qk, int H_v, float scale, const void *bws, void *dsw, void *duw,
+                           void *dv, float *dS0, hipStream_t stream);
+hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const void *d_o,
+                           const void *dv, const float *beta, const int32_t *cu_seqlens,
+                           const int32_t *chunk_base, int N, int T, int H_qk, int H_v,
+                           int max_chunks, float scale, const void *bws, const void *states,
+                           const void *dsw, const void *duw, void *dq, void *dk, float *dg,
+                           float *dbeta, hipStream_t stream);
+
 // The layer's forward from raw projections: gates, conv history, decode.
 hipError_t launch_gates(const float *a, const float *b, const float *A_log, const float *dt_bias,
                         int T, int H_v, float *g, float *beta, hipStream_t stream);

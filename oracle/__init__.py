@@ -55,7 +55,7 @@ def _load():
     lib.orc_gates.argtypes = [P, P, P, P, I, I, P, P]
     lib.orc_gated_norm.argtypes = [P, P, P, I, I, D, P]
     lib.orc_recurrent_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, P, P,
-                                           P, P, P, P]
+                                           P, P, P, P, I, I]
     for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step,
               lib.orc_gates, lib.orc_gated_norm, lib.orc_recurrent_backward):
         f.restype = I
@@ -138,13 +138,15 @@ def recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, 
 
 
 def recurrent_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
-                       cu_seqlens=None, scale=1.0):
+                       cu_seqlens=None, scale=1.0, qk_heads=None):
     """Gradients of ``recurrent`` by reverse mode through the token steps.
 
     d_o [T, H_v, dv] is the gradient with respect to o, d_final_state
     [N, H_v, dv, dk] (or None = zero) the one with respect to the final states.
     Returns fp64 (dq, dk, dv, dg, dbeta, dS0) with the shapes of q, k, v, g,
-    beta and the initial states [N, H_v, dv, dk]."""
+    beta and the initial states [N, H_v, dv, dk].  ``qk_heads`` = (lo, hi)
+    restricts the work to those QK heads and their V-heads (other entries
+    zero)."""
     q, k, v, g, beta, S0, cu, N, T, H_qk, H_v, dk, dv = _prefill_args(
         q, k, v, g, beta, initial_state, cu_seqlens)
     d_o = f64(d_o)
@@ -157,10 +159,12 @@ def recurrent_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=
     dvv = np.zeros(v.shape)
     dg, db = np.zeros(g.shape), np.zeros(beta.shape)
     dS0 = np.zeros((N, H_v, dv, dk))
+    lo, hi = (0, H_qk) if qk_heads is None else qk_heads
     rc = _load().orc_recurrent_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(S0), _ptr(cu), N, T, H_qk, H_v, dk, dv,
                                         float(scale), _ptr(d_o), _ptr(dSf), _ptr(dq), _ptr(dkk),
-                                        _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dS0))
+                                        _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dS0), int(lo),
+                                        int(hi))
     _check(rc, "recurrent_backward")
     return dq, dkk, dvv, dg, db, dS0
 

@@ -493,29 +493,39 @@ int orc_gated_norm(const double *o, const double *z, const double *w, int R, int
  * dg, dbeta [T][H_v]; dS0 [N][H_v][dv][dk] or NULL (with respect to the
  * initial states).  Outputs are overwritten, not accumulated.  Work is split
  * over (sequence, QK head) so that the V-heads of a group, which add into the
- * same dq and dk, run in one thread.
+ * same dq and dk, run in one thread.  Only QK heads in [hq_lo, hq_hi) and their
+ * V-heads are computed; the other entries of every output are zero.
  */
 int orc_recurrent_backward(const double *q, const double *k, const double *v, const double *g,
                            const double *beta, const double *S0, const int32_t *cu, int N,
                            int T, int H_qk, int H_v, int dk, int dv, double scale,
                            const double *d_o, const double *dS_final, double *dq, double *dkk,
-                           double *dvv, double *dg, double *dbeta, double *dS0)
+                           double *dvv, double *dg, double *dbeta, double *dS0, int hq_lo,
+                           int hq_hi)
 {
     if (N < 1 || T < 0 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0 || dk < 1 || dv < 1)
+        return ORC_EINVAL;
+    if (hq_lo < 0 || hq_hi > H_qk || hq_lo > hq_hi)
         return ORC_EINVAL;
     for (int n = 0; n < N; ++n) {
         int s0 = 0, s1 = 0;
         if (seq_bounds(cu, N, T, n, &s0, &s1))
             return ORC_EINVAL;
     }
-    memset(dq, 0, sizeof(double) * (size_t)T * H_qk * dk);
-    memset(dkk, 0, sizeof(double) * (size_t)T * H_qk * dk);
     const int group = H_v / H_qk;
     const size_t ssz = (size_t)dv * dk;
+    memset(dq, 0, sizeof(double) * (size_t)T * H_qk * dk);
+    memset(dkk, 0, sizeof(double) * (size_t)T * H_qk * dk);
+    memset(dvv, 0, sizeof(double) * (size_t)T * H_v * dv);
+    memset(dg, 0, sizeof(double) * (size_t)T * H_v);
+    memset(dbeta, 0, sizeof(double) * (size_t)T * H_v);
+    if (dS0)
+        memset(dS0, 0, sizeof(double) * (size_t)N * H_v * ssz);
+    const int nq = hq_hi - hq_lo;
     int status = ORC_OK;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int u = 0; u < N * H_qk; ++u) {
-        const int n = u / H_qk, hq = u % H_qk;
+    for (int u = 0; u < N * nq; ++u) {
+        const int n = u / nq, hq = hq_lo + u % nq;
         int s0 = 0, s1 = 0;
         seq_bounds(cu, N, T, n, &s0, &s1);
         const int len = s1 - s0;

@@ -232,6 +232,17 @@ def direct_prefill(seed: int, T: Optional[int] = None, lengths=None, H_qk: int =
                    meta={"seed": seed, "recipe": "direct_prefill"})
 
 
+def output_grads(seed: int, T: int, N: int, H_v: int = H_V, dk: int = D_K, dv: int = D_V,
+                 state_std: float = 0.02):
+    """Gradients handed to a prefill's backward: d_o ~ N(0, 1) as bf16 bits
+    [T, H_v, dv] and d_final_state ~ N(0, state_std) fp32 [N, H_v, dv, dk].
+    Generators: d_o, d_final_state."""
+    ro, rs = _rngs((seed, 0xB0), 2)
+    d_o = bf16_bits(ro.standard_normal((T, H_v, dv), dtype=np.float32))
+    dSf = rs.normal(0.0, state_std, (N, H_v, dv, dk)).astype(np.float32)
+    return d_o, dSf
+
+
 def decode_inputs(seed: int, B: int, P: Optional[int] = None, H_qk: int = H_QK,
                   H_v: int = H_V, dk: int = D_K, dv: int = D_V, state_std: float = 0.02,
                   pool: Optional[np.ndarray] = None, slot_idx=None, A_log=None,
