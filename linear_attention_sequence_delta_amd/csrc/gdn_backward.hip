@@ -30,6 +30,8 @@
 // gradient of the state stays fp32 in registers through the reverse scan.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_chunk.h"
 #include "gdn_internal.h"
 
@@ -45,13 +47,13 @@ constexpr int kSP = kBSlab + 8;        // LDS row stride (bf16) of slab-wide row
 // g4 = lane / 16): frag_rows gives M[r0 + c][k0 + 8 g4 .. +7] (a row piece),
 // frag_cols gives M[k0 + 8 g4 + j][c0 + c], j = 0..7 (a column piece, two
 // transposing reads).  An operand's lane c indexes the output row (A) or
-// column (B) and the 8 values run along the contraction.
-__device__ __forceinline__ uint4 frag_rows(const uint16_t *M, int ld, int r0, int k0) {
-    const int lane = threadIdx.x & 63;
+// column (B) and the 8 values run along the contraction.  `lane` is the
+// caller's lane index (threadIdx.x % 64).
+__device__ __forceinline__ uint4 frag_rows(const uint16_t *M, int ld, int r0, int k0, int lane) {
     return *reinterpret_cast<const uint4 *>(M + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
 }
-__device__ __forceinline__ uint4 frag_cols(const uint16_t *M, int ld, int k0, int c0) {
-    const int lane = threadIdx.x & 63, c = lane & 15;
+__device__ __forceinline__ uint4 frag_cols(const uint16_t *M, int ld, int k0, int c0, int lane) {
+    const int c = lane & 15;
     const uint16_t *base = M + (k0 + 8 * (lane >> 4) + (c >> 2)) * ld + c0 + 4 * (c & 3);
     const uint2 lo = lds_read_tr16(base), hi = lds_read_tr16(base + 4 * ld);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -77,8 +79,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // ------------------------------------------------------------ reverse scan
-// Inputs of one chunk, loaded a chunk ahead.  Rows past the end of a sequence
-// are clamped to its last row on load and replaced by zero in LDS.
+// Inputs of one chunk, loaded two chunks ahead into three rotating register
+// sets.  Rows past the end of a sequence are clamped to its last row on load
+// and replaced by zero in LDS.
 struct RevRegs {
     u32x4 kr[4];     // K row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
     u32x4 qr[4];     // Q rows likewise
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
                     pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
     };
 
-    auto body = [&](int ci, const RevRegs &cur, RevRegs &nxt) {
+    auto body = [&](int ci, const RevRegs &cur, const RevRegs &nxt, RevRegs &pf) {
         const int L = chunk_len(ci);
         // the gradient this chunk starts from (with respect to its end state)
         uint16_t *dsp = dsw + ((size_t)(cbase + ci) * H_v + h) * (kD * kD);
@@ -206,8 +209,8 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
         wave_lds_sync();
         uint4 kB[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kB[s] = frag_rows(sKr, kKP, 16 * w, 32 * s);
-        fetch(ci - 1, nxt);
+        for (int s = 0; s < 4; ++s) kB[s] = frag_rows(sKr, kKP, 16 * w, 32 * s, lane);
+        fetch(ci - 2, pf);
         const float lam = __expf(cur.GL - cur.Gown), gam = __expf(cur.Gown), gamL = __expf(cur.GL);
         const uint16_t *sDOc = sDO[ci & 1];
         // dU = P^T dO + diag(lambda) K dS'^T: rows 16 w + c, slab columns 16 nt + 4 g4 + j
@@ -215,11 +218,11 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) y = mfma32(frag_rows(sS, kKP, 16 * nt, 32 * s), kB[s], y);
+            for (int s = 0; s < 4; ++s) y = mfma32(frag_rows(sS, kKP, 16 * nt, 32 * s, lane), kB[s], y);
             f32x4 pd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                if (s >= (w >> 1)) pd = mfma32(frag_cols(sDOc, kSP, 32 * s, 16 * nt), cur.pt[s], pd);
+                if (s >= (w >> 1)) pd = mfma32(frag_cols(sDOc, kSP, 32 * s, 16 * nt, lane), cur.pt[s], pd);
             const uint2 p = pk4(pd[0] + lam * y[0], pd[1] + lam * y[1], pd[2] + lam * y[2], pd[3] + lam * y[3]);
             *reinterpret_cast<uint2 *>(sDU + (16 * w + c) * kSP + 16 * nt + 4 * g4) = p;
             *reinterpret_cast<uint2 *>(duw + (((size_t)(cbase + ci) * kChunk + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) = p;
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                if (s >= (w >> 1)) d = mfma32(frag_cols(sDU, kSP, 32 * s, 16 * nt), cur.tt[s], d);
+                if (s >= (w >> 1)) d = mfma32(frag_cols(sDU, kSP, 32 * s, 16 * nt, lane), cur.tt[s], d);
             if (16 * w + c < L)
                 *reinterpret_cast<uint2 *>(dv + ((size_t)(s0 + kChunk * ci + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
                     pk4(d[0], d[1], d[2], d[3]);
@@ -246,13 +249,13 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                zq[nt][s] = frag_cols(sZq[ci & 1], kSP, 32 * s, 16 * nt);
-                zk[nt][s] = frag_cols(sZk, kSP, 32 * s, 16 * nt);
+                zq[nt][s] = frag_cols(sZq[ci & 1], kSP, 32 * s, 16 * nt, lane);
+                zk[nt][s] = frag_cols(sZk, kSP, 32 * s, 16 * nt, lane);
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                qa[t][s] = frag_cols(sQr, kKP, 32 * s, 32 * w + 16 * t);
-                ka[t][s] = frag_cols(sKr, kKP, 32 * s, 32 * w + 16 * t);
+                qa[t][s] = frag_cols(sQr, kKP, 32 * s, 32 * w + 16 * t, lane);
+                ka[t][s] = frag_cols(sKr, kKP, 32 * s, 32 * w + 16 * t, lane);
             }
         }
 #pragma unroll
@@ -272,16 +275,19 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
     };
 
     write_state_lds();
-    RevRegs ra, rb;
+    RevRegs r0, r1, r2;
     if (nch > 0) {
-        fetch(nch - 1, ra);
-        stage_rows(nch - 1, ra);
+        fetch(nch - 1, r0);
+        fetch(nch - 2, r1);
+        stage_rows(nch - 1, r0);
     }
     __syncthreads();
-    for (int ci = nch - 1; ci >= 0; ci -= 2) {
-        body(ci, ra, rb);
+    for (int ci = nch - 1; ci >= 0; ci -= 3) {
+        body(ci, r0, r1, r2);
         if (ci == 0) break;
-        body(ci - 1, rb, ra);
+        body(ci - 1, r1, r2, r0);
+        if (ci == 1) break;
+        body(ci - 2, r2, r0, r1);
     }
     if (dS0) {
 #pragma unroll
@@ -294,13 +300,16 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
 }
 
 // ------------------------------------------------------------ chunk gradients
-// One workgroup (4 waves) per (chunk, QK head), looping over the V-heads of
-// the group; dq and dk of the group accumulate in fp32 registers.  Wave w
-// owns chunk rows 16 w .. +15: every row-wise result is held with lane
-// (c, g4) on row 16 w + c, columns 16 t + 4 g4 .. +3 of each 16-column tile
-// t, which an MFMA gives when the left factor's rows are its B operand and
-// the right factor's columns its A operand.
-__global__ __launch_bounds__(256) void bwd_grad_kernel(
+// One workgroup (8 waves) per (chunk, QK head), looping over the V-heads of
+// the group; dq and dk of the group accumulate in fp32 registers.  Waves w
+// and w + 4 own chunk rows 16 (w % 4) .. +15 and split the column tiles of
+// every product: half hf = w / 4 takes the 16-column tiles 4 hf .. 4 hf + 3
+// of a 128-wide result and the tiles t with t % 2 = hf of a 64-wide one.
+// Every row-wise result is held with lane (c, g4) on the row 16 (w % 4) + c,
+// columns 16 t + 4 g4 .. +3 of each tile t, which an MFMA gives when the left
+// factor's rows are its B operand and the right factor's columns its A
+// operand.
+__global__ __launch_bounds__(512) void bwd_grad_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ d_o, const uint16_t *__restrict__ dv, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, int N, int T, int H_qk,
@@ -318,9 +327,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sF[kChunk * kRP];   // dT T^T
     __shared__ __attribute__((aligned(16))) float sG[kChunk];
     __shared__ __attribute__((aligned(16))) float sB[kChunk];
-    __shared__ float sRowG[kChunk], sRowB[kChunk];
+    __shared__ float sRowG[2][kChunk], sRowB[2][kChunk];
     __shared__ float sColG[4][kChunk], sColB[4][kChunk];
-    __shared__ float sE[4];
+    __shared__ float sE[8];
 
     const int gc = blockIdx.x / H_qk, hq = blockIdx.x - gc * H_qk;
     if (gc >= chunk_base[N]) return;                   // same for the whole workgroup
@@ -330,7 +339,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const int L = min(kChunk, s1 - c0);
     const int group = H_v / H_qk;
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = wave & 3;
     const int lane = tid & 63, g4 = lane >> 4, c = lane & 15;
     const int row = 16 * w + c;                        // this lane's row
     const bool row_ok = row < L;
@@ -338,19 +348,21 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     const int wb = w >> 1;                             // 32-row block of this wave's rows
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * i + (lane >> 4);
-        const size_t off = ((size_t)(c0 + min(r, L - 1)) * H_qk + hq) * kD + 8 * (lane & 15);
+    for (int m = 0; m < 2; ++m) {
+        const int e = tid + 512 * m, r = e >> 4, pc = e & 15;
+        const size_t off = ((size_t)(c0 + min(r, L - 1)) * H_qk + hq) * kD + 8 * pc;
         uint4 kv = *reinterpret_cast<const uint4 *>(k + off), qv = *reinterpret_cast<const uint4 *>(q + off);
         if (r >= L) kv = qv = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(sK + r * kKP + 8 * (lane & 15)) = kv;
-        *reinterpret_cast<uint4 *>(sQ + r * kKP + 8 * (lane & 15)) = qv;
+        *reinterpret_cast<uint4 *>(sK + r * kKP + 8 * pc) = kv;
+        *reinterpret_cast<uint4 *>(sQ + r * kKP + 8 * pc) = qv;
     }
+    __syncthreads();
+    int ol = lane;
     // x_row . k_(16 t + 4 g4 + j) for the rows x of M (K or Q), tile t
     auto dot_k = [&](const uint16_t *M, int t) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a = mfma32(frag_rows(sK, kKP, 16 * t, 32 * s), frag_rows(M, kKP, 16 * w, 32 * s), a);
+        for (int s = 0; s < 4; ++s) a = mfma32(frag_rows(sK, kKP, 16 * t, 32 * s, ol), frag_rows(M, kKP, 16 * w, 32 * s, ol), a);
         return a;
     };
     // the 16-lane column sums of x (one per column 16 t + 4 g4 + j) into dst
@@ -361,98 +373,126 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
             if (c == 0) dst[16 * t + 4 * g4 + j] = add ? dst[16 * t + 4 * g4 + j] + y : y;
         }
     };
-    f32x4 dQa[8], dKa[8];
+    f32x4 dQa[4], dKa[4];                              // columns 16 (4 hf + i) + 4 g4 + j
 #pragma unroll
-    for (int t = 0; t < 8; ++t) dQa[t] = dKa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) dQa[i] = dKa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int vv = 0; vv < group; ++vv) {
+    // the V-head step, for a compile-time half (tile offsets fold into
+    // instruction immediates); both halves pass the same barriers in order
+    auto vhead = [&](int vv, auto half) {
+        constexpr int hf = decltype(half)::value;
         const int h = hq * group + vv;
+        // the lane index, opaque to the optimiser: LDS addresses are formed
+        // inside each step instead of being kept in registers across steps
+        ol = lane;
+        asm volatile("" : "+v"(ol));
+        const int c = ol & 15, g4 = ol >> 4, tid = 64 * wave + ol;
+        const int row = 16 * w + c;
+        const bool row_ok = row < L;
+        const int rr = min(row, L - 1);
         const uint16_t *brec = bws + ((size_t)gc * H_v + h) * kBwdRecElems;
         const uint16_t *Sg = states + ((size_t)gc * H_v + h) * (kD * kD);
         const uint16_t *dSg = dsw + ((size_t)gc * H_v + h) * (kD * kD);
-        __syncthreads();                               // the previous V-head's LDS reads are done
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int e = tid + 256 * m, r = e >> 3, cb = e & 7;
-            *reinterpret_cast<uint4 *>(sT + r * kRP + 8 * cb) =
-                *reinterpret_cast<const uint4 *>(brec + kBwdTOff + r * kChunk + 8 * cb);
-        }
+        // this V-head's inputs in flight together: T, S (into LDS) and dS' (for
+        // <dS', S>), G, b; V at this lane's result positions; the rows `row` of
+        // dO and dR as MFMA operands (columns 32 s + 8 g4 .. +7)
+        uint4 dOf[4], dVf[4];
+        uint2 vr[4];
         float e1 = 0.f;                                // this thread's share of <dS', S>
+        {
+            const u32x4 tv = *reinterpret_cast<const u32x4 *>(brec + kBwdTOff + (tid >> 3) * kChunk + 8 * (tid & 7));
+            u32x4 sv[4], dsv[4];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int e = tid + 256 * m, r = e >> 4, cb = e & 15;
-            const uint4 sv = *reinterpret_cast<const uint4 *>(Sg + r * kD + 8 * cb);
-            const uint4 dsv = *reinterpret_cast<const uint4 *>(dSg + r * kD + 8 * cb);
-            *reinterpret_cast<uint4 *>(sSt + r * kKP + 8 * cb) = sv;
-            e1 += dot8(sv, dsv);
-        }
-        if (tid < kChunk) {
-            sG[tid] = reinterpret_cast<const float *>(brec + kBwdGOff)[tid];
-            sB[tid] = tid < L ? beta[(size_t)(c0 + tid) * H_v + h] : 0.f;
-        }
-        // row `row` of a [T][H_v][128] input (zero past the chunk), columns 32 s + 8 g4 .. +7
-        auto row_frags = [&](const uint16_t *X, uint4 *f) {
+            for (int m = 0; m < 4; ++m) {
+                const int e = tid + 512 * m;
+                sv[m] = *reinterpret_cast<const u32x4 *>(Sg + (e >> 4) * kD + 8 * (e & 15));
+                dsv[m] = *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
+            }
+            float gl = 0.f, bl = 0.f;
+            if (tid < kChunk) {
+                gl = reinterpret_cast<const float *>(brec + kBwdGOff)[tid];
+                bl = tid < L ? beta[(size_t)(c0 + tid) * H_v + h] : 0.f;
+            }
+            const size_t ro = ((size_t)(c0 + rr) * H_v + h) * kD;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                f[s] = *reinterpret_cast<const uint4 *>(X + ((size_t)(c0 + rr) * H_v + h) * kD + 32 * s + 8 * g4);
-                if (!row_ok) f[s] = make_uint4(0, 0, 0, 0);
+                dOf[s] = *reinterpret_cast<const uint4 *>(d_o + ro + 32 * s + 8 * g4);
+                dVf[s] = *reinterpret_cast<const uint4 *>(dv + ro + 32 * s + 8 * g4);
             }
-        };
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const uint2 *>(v + ro + 16 * (4 * hf + i) + 4 * g4);
+            __syncthreads();                           // the previous V-head's LDS reads are done
+            *reinterpret_cast<u32x4 *>(sT + (tid >> 3) * kRP + 8 * (tid & 7)) = tv;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = tid + 512 * m;
+                *reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15)) = sv[m];
+                e1 += dot8(__builtin_bit_cast(uint4, sv[m]), __builtin_bit_cast(uint4, dsv[m]));
+            }
+            if (tid < kChunk) {
+                sG[tid] = gl;
+                sB[tid] = bl;
+            }
+        }
+        if (!row_ok) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dOf[s] = dVf[s] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[i] = make_uint2(0, 0);
+        }
         __syncthreads();
 
         const float Gr = sG[row], GLast = sG[kChunk - 1];
         const float gam = __expf(Gr), lam = __expf(GLast - Gr), br = sB[row];
         float rowG = 0.f, rowB = 0.f, e2 = 0.f;
 
-        // X = K S^T -> R = V - diag(gamma) X; dG: -gamma_r dR_r . X_r
-#pragma unroll 2
-        for (int nt = 0; nt < 8; ++nt) {
+        // X = K S^T -> R = V - diag(gamma) X
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int nt = 4 * hf + i;
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) x = mfma32(frag_rows(sSt, kKP, 16 * nt, 32 * s), frag_rows(sK, kKP, 16 * w, 32 * s), x);
-            const size_t vo = ((size_t)(c0 + rr) * H_v + h) * kD + 16 * nt + 4 * g4;
-            uint2 vr = *reinterpret_cast<const uint2 *>(v + vo), dvr = *reinterpret_cast<const uint2 *>(dv + vo);
-            if (!row_ok) vr = dvr = make_uint2(0, 0);
-            float vf[4], dvf[4], rv[4];
-            unpack4(vr, vf);
-            unpack4(dvr, dvf);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                rv[j] = vf[j] - gam * x[j];
-                rowG -= gam * dvf[j] * x[j];
-            }
-            *reinterpret_cast<uint2 *>(sR + row * kKP + 16 * nt + 4 * g4) = pk4(rv[0], rv[1], rv[2], rv[3]);
+            for (int s = 0; s < 4; ++s) x = mfma32(frag_rows(sSt, kKP, 16 * nt, 32 * s, ol), frag_rows(sK, kKP, 16 * w, 32 * s, ol), x);
+            float vf[4];
+            unpack4(vr[i], vf);
+            *reinterpret_cast<uint2 *>(sR + row * kKP + 16 * nt + 4 * g4) =
+                pk4(vf[0] - gam * x[0], vf[1] - gam * x[1], vf[2] - gam * x[2], vf[3] - gam * x[3]);
         }
         // dO S and dR S: dQ += scale gamma dO S (dG: q_r . that), dK -= gamma dR S
-        {
-        uint4 dOf[4], dVf[4];
-        row_frags(d_o, dOf);
-        row_frags(dv, dVf);
-#pragma unroll 2
-        for (int kt = 0; kt < 8; ++kt) {
+        // (dG: -gamma_r dR_r . X_r = -gamma_r k_r . (dR S)_r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kt = 4 * hf + i;
             f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const uint4 sf = frag_cols(sSt, kKP, 32 * s, 16 * kt);
+                const uint4 sf = frag_cols(sSt, kKP, 32 * s, 16 * kt, ol);
                 a1 = mfma32(sf, dOf[s], a1);
                 a2 = mfma32(sf, dVf[s], a2);
             }
-            float qf[4];
+            float qf[4], kf[4];
             unpack4(*reinterpret_cast<const uint2 *>(sQ + row * kKP + 16 * kt + 4 * g4), qf);
+            unpack4(*reinterpret_cast<const uint2 *>(sK + row * kKP + 16 * kt + 4 * g4), kf);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float t = scale * gam * a1[j];
-                dQa[kt][j] += t;
+                dQa[i][j] += t;
                 rowG += t * qf[j];
-                dKa[kt][j] -= gam * a2[j];
+                const float u = gam * a2[j];
+                dKa[i][j] -= u;
+                rowG -= u * kf[j];
             }
         }
-        }
         __syncthreads();                               // R complete; S no longer read
+        uint4 dUf[4];                                  // row `row` of dU, columns 32 s + 8 g4 .. +7
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int e = tid + 256 * m, r = e >> 4, cb = e & 15;
-            *reinterpret_cast<uint4 *>(sSt + r * kKP + 8 * cb) = *reinterpret_cast<const uint4 *>(dSg + r * kD + 8 * cb);
+        for (int s = 0; s < 4; ++s)
+            dUf[s] = *reinterpret_cast<const uint4 *>(duw + (((size_t)gc * kChunk + row) * H_v + h) * kD + 32 * s + 8 * g4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 512 * m;
+            *reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15)) =
+                *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
         }
         // U = T' R (T'[row][i] = T[row][i] b_i)
         {
@@ -469,11 +509,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
                 tB[s] = pack_bf8(tf);
             }
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int i = 0; i < 4; ++i) {
+                const int nt = 4 * hf + i;
                 f32x4 ua = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    if (s <= wb) ua = mfma32(frag_cols(sR, kKP, 32 * s, 16 * nt), tB[s], ua);
+                    if (s <= wb) ua = mfma32(frag_cols(sR, kKP, 32 * s, 16 * nt, ol), tB[s], ua);
                 *reinterpret_cast<uint2 *>(sU + row * kKP + 16 * nt + 4 * g4) = pk4(ua[0], ua[1], ua[2], ua[3]);
             }
         }
@@ -483,17 +524,18 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         {
             uint4 uB[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) uB[s] = frag_rows(sU, kKP, 16 * w, 32 * s);
-#pragma unroll 2
-            for (int kt = 0; kt < 8; ++kt) {
+            for (int s = 0; s < 4; ++s) uB[s] = frag_rows(sU, kKP, 16 * w, 32 * s, ol);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kt = 4 * hf + i;
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a = mfma32(frag_cols(sSt, kKP, 32 * s, 16 * kt), uB[s], a);
+                for (int s = 0; s < 4; ++s) a = mfma32(frag_cols(sSt, kKP, 32 * s, 16 * kt, ol), uB[s], a);
                 float kf[4];
                 unpack4(*reinterpret_cast<const uint2 *>(sK + row * kKP + 16 * kt + 4 * g4), kf);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    dKa[kt][j] += lam * a[j];
+                    dKa[i][j] += lam * a[j];
                     const float t = lam * a[j] * kf[j];
                     rowG -= t;
                     e2 += t;
@@ -501,45 +543,39 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
             }
         }
         // dP = dO U^T -> M_P; dT' = dU R^T -> dT; row and column sums
-        {
-            uint4 dOf[4], dUf[4];
-            row_frags(d_o, dOf);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                dUf[s] = *reinterpret_cast<const uint4 *>(duw + (((size_t)gc * kChunk + row) * H_v + h) * kD + 32 * s + 8 * g4);
+        for (int ti = 0; ti < 2; ++ti) {
+            const int t = 2 * ti + hf;
+            f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dtp = dp, qk = dp;
+            if (t <= w) {
+                qk = dot_k(sQ, t);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dtp = dp, qk = dp;
-                if (t <= w) {
-                    qk = dot_k(sQ, t);
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        dp = mfma32(frag_rows(sU, kKP, 16 * t, 32 * s), dOf[s], dp);
-                        dtp = mfma32(frag_rows(sR, kKP, 16 * t, 32 * s), dUf[s], dtp);
-                    }
+                for (int s = 0; s < 4; ++s) {
+                    dp = mfma32(frag_rows(sU, kKP, 16 * t, 32 * s, ol), dOf[s], dp);
+                    dtp = mfma32(frag_rows(sR, kKP, 16 * t, 32 * s, ol), dUf[s], dtp);
                 }
-                const float4 Gi = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
-                const float4 Bi = *reinterpret_cast<const float4 *>(sB + 16 * t + 4 * g4);
-                const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
-                float tf[4];
-                unpack4(*reinterpret_cast<const uint2 *>(sT + row * kRP + 16 * t + 4 * g4), tf);
-                float mp[4], dt[4];
-                f32x4 cg, cb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool lo = 16 * t + 4 * g4 + j <= row;
-                    mp[j] = lo ? dp[j] * scale * __expf(Gr - gi[j]) : 0.f;
-                    const float wp = lo ? mp[j] * qk[j] : 0.f;
-                    rowG += wp;
-                    cg[j] = -wp;
-                    dt[j] = lo ? dtp[j] * bi[j] : 0.f;
-                    cb[j] = lo ? dtp[j] * tf[j] : 0.f;
-                }
-                *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(mp[0], mp[1], mp[2], mp[3]);
-                *reinterpret_cast<uint2 *>(sM2 + row * kRP + 16 * t + 4 * g4) = pk4(dt[0], dt[1], dt[2], dt[3]);
-                col_sums(cg, sColG[w], t, false);
-                col_sums(cb, sColB[w], t, false);
             }
+            const float4 Gi = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
+            const float4 Bi = *reinterpret_cast<const float4 *>(sB + 16 * t + 4 * g4);
+            const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+            float tf[4];
+            unpack4(*reinterpret_cast<const uint2 *>(sT + row * kRP + 16 * t + 4 * g4), tf);
+            float mp[4], dt[4];
+            f32x4 cg, cb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool lo = 16 * t + 4 * g4 + j <= row;
+                mp[j] = lo ? dp[j] * scale * __expf(Gr - gi[j]) : 0.f;
+                const float wp = lo ? mp[j] * qk[j] : 0.f;
+                rowG += wp;
+                cg[j] = -wp;
+                dt[j] = lo ? dtp[j] * bi[j] : 0.f;
+                cb[j] = lo ? dtp[j] * tf[j] : 0.f;
+            }
+            *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(mp[0], mp[1], mp[2], mp[3]);
+            *reinterpret_cast<uint2 *>(sM2 + row * kRP + 16 * t + 4 * g4) = pk4(dt[0], dt[1], dt[2], dt[3]);
+            col_sums(cg, sColG[w], t, false);
+            col_sums(cb, sColB[w], t, false);
         }
         __syncthreads();                               // M_P, dT complete
 
@@ -548,27 +584,29 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
             uint4 mB[2], mtB[2], dtB[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s);
-                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w);
-                dtB[s] = frag_rows(sM2, kRP, 16 * w, 32 * s);
+                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s, ol);
+                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w, ol);
+                dtB[s] = frag_rows(sM2, kRP, 16 * w, 32 * s, ol);
             }
-#pragma unroll 2
-            for (int kt = 0; kt < 8; ++kt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kt = 4 * hf + i;
                 f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    if (s <= wb) a = mfma32(frag_cols(sK, kKP, 32 * s, 16 * kt), mB[s], a);
-                    if (s >= wb) b = mfma32(frag_cols(sQ, kKP, 32 * s, 16 * kt), mtB[s], b);
+                    if (s <= wb) a = mfma32(frag_cols(sK, kKP, 32 * s, 16 * kt, ol), mB[s], a);
+                    if (s >= wb) b = mfma32(frag_cols(sQ, kKP, 32 * s, 16 * kt, ol), mtB[s], b);
                 }
-                dQa[kt] += a;
-                dKa[kt] += b;
+                dQa[i] += a;
+                dKa[i] += b;
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int ti = 0; ti < 2; ++ti) {
+                const int t = 2 * ti + hf;
                 f32x4 f = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    if (s <= wb) f = mfma32(frag_rows(sT, kRP, 16 * t, 32 * s), dtB[s], f);
+                    if (s <= wb) f = mfma32(frag_rows(sT, kRP, 16 * t, 32 * s, ol), dtB[s], f);
                 *reinterpret_cast<uint2 *>(sF + row * kRP + 16 * t + 4 * g4) = pk4(f[0], f[1], f[2], f[3]);
             }
         }
@@ -579,15 +617,16 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         {
             uint4 ttB[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) ttB[s] = frag_cols(sT, kRP, 32 * s, 16 * w);
+            for (int s = 0; s < 2; ++s) ttB[s] = frag_cols(sT, kRP, 32 * s, 16 * w, ol);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int ti = 0; ti < 2; ++ti) {
+                const int t = 2 * ti + hf;
                 f32x4 da = {0.f, 0.f, 0.f, 0.f}, kk = da;
                 if (t <= w) {
                     kk = dot_k(sK, t);
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
-                        if (s >= wb) da = mfma32(frag_cols(sF, kRP, 32 * s, 16 * t), ttB[s], da);
+                        if (s >= wb) da = mfma32(frag_cols(sF, kRP, 32 * s, 16 * t, ol), ttB[s], da);
                 }
                 const float4 Gj = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
                 const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
@@ -613,12 +652,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
         rowB += __shfl_xor(rowB, 16, 64);
         rowB += __shfl_xor(rowB, 32, 64);
         if (g4 == 0) {
-            sRowG[row] = rowG;
-            sRowB[row] = rowB;
+            sRowG[hf][row] = rowG;
+            sRowB[hf][row] = rowB;
         }
         {
             const float ew = wave_sum(__expf(GLast) * e1 + e2);
-            if (lane == 0) sE[w] = ew;
+            if (lane == 0) sE[wave] = ew;
         }
         __syncthreads();                               // M_A' and the sums complete
 
@@ -627,26 +666,32 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
             uint4 mB[2], mtB[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s);
-                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w);
+                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s, ol);
+                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w, ol);
             }
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
+            for (int i = 0; i < 4; ++i) {
+                const int kt = 4 * hf + i;
                 f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const uint4 kf = frag_cols(sK, kKP, 32 * s, 16 * kt);
+                    const uint4 kf = frag_cols(sK, kKP, 32 * s, 16 * kt, ol);
                     if (s <= wb) a = mfma32(kf, mB[s], a);
                     if (s >= wb) a = mfma32(kf, mtB[s], a);
                 }
-                dKa[kt] += a;
+                dKa[i] += a;
             }
         }
         // dg = suffix sums of dG inside the chunk; db
-        if (w == 0) {
-            float dG = sRowG[lane] + sColG[0][lane] + sColG[1][lane] + sColG[2][lane] + sColG[3][lane];
-            if (lane == kChunk - 1) dG += sE[0] + sE[1] + sE[2] + sE[3];
-            const float db = sRowB[lane] + sColB[0][lane] + sColB[1][lane] + sColB[2][lane] + sColB[3][lane];
+        if (wave == 0) {
+            float dG = sRowG[0][lane] + sRowG[1][lane] + sColG[0][lane] + sColG[1][lane] +
+                       sColG[2][lane] + sColG[3][lane];
+            if (lane == kChunk - 1) {
+#pragma unroll
+                for (int x = 0; x < 8; ++x) dG += sE[x];
+            }
+            const float db = sRowB[0][lane] + sRowB[1][lane] + sColB[0][lane] + sColB[1][lane] +
+                             sColB[2][lane] + sColB[3][lane];
             const float suf = wave_scan(__shfl(dG, 63 - lane, 64));
             const float dgr = __shfl(suf, 63 - lane, 64);
             if (lane < L) {
@@ -654,13 +699,18 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
                 dbeta[(size_t)(c0 + lane) * H_v + h] = db;
             }
         }
+    };
+    for (int vv = 0; vv < group; ++vv) {
+        if (wave < 4) vhead(vv, std::integral_constant<int, 0>{});
+        else vhead(vv, std::integral_constant<int, 1>{});
     }
+    const int hf = wave >> 2;
     if (row_ok) {
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-            const size_t off = ((size_t)(c0 + row) * H_qk + hq) * kD + 16 * kt + 4 * g4;
-            *reinterpret_cast<uint2 *>(dq + off) = pk4(dQa[kt][0], dQa[kt][1], dQa[kt][2], dQa[kt][3]);
-            *reinterpret_cast<uint2 *>(dk + off) = pk4(dKa[kt][0], dKa[kt][1], dKa[kt][2], dKa[kt][3]);
+        for (int i = 0; i < 4; ++i) {
+            const size_t off = ((size_t)(c0 + row) * H_qk + hq) * kD + 16 * (4 * hf + i) + 4 * g4;
+            *reinterpret_cast<uint2 *>(dq + off) = pk4(dQa[i][0], dQa[i][1], dQa[i][2], dQa[i][3]);
+            *reinterpret_cast<uint2 *>(dk + off) = pk4(dKa[i][0], dKa[i][1], dKa[i][2], dKa[i][3]);
         }
     }
 }
@@ -686,7 +736,7 @@ hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const vo
                            int max_chunks, float scale, const void *bws, const void *states,
                            const void *dsw, const void *duw, void *dq, void *dk, float *dg,
                            float *dbeta, hipStream_t stream) {
-    hipLaunchKernelGGL(bwd_grad_kernel, dim3(max_chunks * H_qk), dim3(256), 0, stream,
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3(max_chunks * H_qk), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(d_o),
                        static_cast<const uint16_t *>(dv), beta, cu_seqlens, chunk_base, N, T, H_qk,

@@ -475,7 +475,8 @@ struct OutRegs {          // waves 4-7
 //
 // For the backward pass (kSave) the state waves store the bf16 state each
 // chunk starts from (the values the chunk's products use) into
-// states [chunk][H_v][d_v][d_k], and o is not written.
+// states [chunk][H_v][d_v][d_k]; the kernel is then launched with the 256
+// threads of the state waves only, and o is not written.
 template <bool kRaw, bool kSave = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -985,8 +986,10 @@ size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v) {
 }
 
 // plan -> prep (forward and backward records) -> forward scan storing each
-// chunk's start state -> reverse scan (dv, the initial-state gradient, dS'
-// and dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta).
+// chunk's start state, and beside it the reverse scan (dv, the initial-state
+// gradient, dS' and dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta).
+// The two scans need only prep's records; the forward one runs on the
+// device's auxiliary stream, forked from and joined back into `stream`.
 hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *S0, const int32_t *cu_seqlens,
                                    int N, int T, int H_qk, int H_v, float scale, const void *d_o,
@@ -1004,14 +1007,32 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
                        dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
                        W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<false, true>), dim3(N * H_v * kSlabsW), dim3(512), 0, stream,
-                       q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
-                       cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
-                       nullptr, W.states);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
-                             W.brec, W.dsw, W.duw, dv, dS0, stream)) != hipSuccess)
-        return e;
+    auto fwd_scan = [&](hipStream_t s) {
+        hipLaunchKernelGGL((scan_kernel<false, true>), dim3(N * H_v * kSlabsW), dim3(256), 0, s,
+                           q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
+                           cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
+                           nullptr, W.states);
+        return hipGetLastError();
+    };
+    auto rev_scan = [&]() {
+        return launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
+                               scale, W.brec, W.dsw, W.duw, dv, dS0, stream);
+    };
+    {
+        std::lock_guard<std::mutex> lock(g_aux_mu);
+        DeviceAux *aux = device_aux();
+        if (aux) {
+            if ((e = hipEventRecord(aux->ev[0], stream)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(aux->stream, aux->ev[0], 0)) != hipSuccess) return e;
+            if ((e = fwd_scan(aux->stream)) != hipSuccess) return e;
+            if ((e = hipEventRecord(aux->ev[1], aux->stream)) != hipSuccess) return e;
+            if ((e = rev_scan()) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(stream, aux->ev[1], 0)) != hipSuccess) return e;
+        } else {
+            if ((e = fwd_scan(stream)) != hipSuccess) return e;
+            if ((e = rev_scan()) != hipSuccess) return e;
+        }
+    }
     return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
                            max_chunks, scale, W.brec, W.states, W.dsw, W.duw, dq, dk, dg, dbeta,
                            stream);
