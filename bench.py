@@ -57,6 +57,14 @@ PRELUDE_BYTES_PER_TOKEN = 2 * 2 * (2 * H_QK * D + H_V * D)
 # once in fp32, plus q, k, v, o in bf16 and g, beta in fp32
 DECODE_BYTES_PER_SEQ = (H_V * (2 * D * D * 4 + 2 * D * 2 + 2 * 4) + 2 * H_QK * D * 2)
 
+# backward (gdn_prefill_backward) flops per token per V-head, as executed and
+# counted at the useful half of triangular products: d x d products 18 d^2
+# (forward states again: K S^T and the update, 4 d^2; reverse scan: K dS'^T and
+# the two-term state-gradient update, 6 d^2; per chunk: K S^T, dO S, dR S,
+# U dS', 8 d^2) and C x C x d products 10 C d (P^T dO, T'^T dU, T' R, dO U^T,
+# dU R^T, M_P K, M_P^T Q, the two M_A' K, K K^T with Q K^T).
+BACKWARD_FLOP_PER_TOKEN = H_V * (18 * D * D + 10 * CHUNK * D)
+
 T_LONG, LONG_STEPS, STACK_LAYERS = 262144, 64, 48
 MULTI_TOKENS = 4
 
@@ -172,6 +180,36 @@ def run_gpu(steps, warmup, path="both"):
         res["pre_us"] = sum(a0.elapsed_time(a1) for (a0, a1), _ in ev) / steps * 1e3
         res["pf_us"] = sum(b0.elapsed_time(b1) for _, (b0, b1) in ev) / steps * 1e3
         del q, k, v, ws
+
+    # the backward of the prefill (training step's layer gradient), on the same
+    # workload's q, k, v (from the prelude, untimed), d_o ~ N(0, 1) bf16, no
+    # initial state and no final-state gradient
+    if path == "both":
+        q = torch.empty((p.T, H_QK, D), dtype=torch.bfloat16, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
+        gdn.gdn_conv_prelude(x, w, None, H_qk=H_QK, H_v=H_V, out=(q, k, v))
+        genb = torch.Generator(device=dev)
+        genb.manual_seed(1003002)
+        d_o = torch.randn(v.shape, generator=genb, device=dev).to(torch.bfloat16)
+        wsb = torch.empty(gdn.gdn_prefill_backward_workspace_size(1, p.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
+
+        def backward():
+            gdn.gdn_prefill_backward(q, k, v, g, beta, d_o, workspace=wsb)
+
+        for _ in range(max(warmup, 1)):
+            backward()
+        torch.cuda.synchronize()
+        bsteps = max(steps // 2, 3)
+        b0, b1 = _events(torch)
+        b0.record()
+        for _ in range(bsteps):
+            backward()
+        b1.record()
+        torch.cuda.synchronize()
+        res["bwd_us"] = b0.elapsed_time(b1) / bsteps * 1e3
+        del q, k, v, d_o, wsb
 
     # the output gate on the prefill's o (z ~ N(0, 1), norm weight ~ U(0.5, 1.5))
     gen = torch.Generator(device=dev)
@@ -492,6 +530,17 @@ def main():
                           "roofline": {"bound": "hbm", "achieved": gate_bytes / (r["gate_us"] * 1e-6) / 1e9,
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                        "frac": gate_bytes / (r["gate_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}}
+    if "bwd_us" in r:
+        bflops = BACKWARD_FLOP_PER_TOKEN * T
+        btf = bflops / (r["bwd_us"] * 1e-6) / 1e12
+        out["backward"] = {"us": r["bwd_us"], "tokens_per_s": T / (r["bwd_us"] * 1e-6),
+                           "what": "gdn_prefill_backward on the prefill workload's q, k, v "
+                                   "(d_o ~ N(0,1), no initial state): dq, dk, dv, dg, dbeta; "
+                                   "not part of the step",
+                           "roofline": {"bound": "mfma", "achieved": btf,
+                                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": btf / PEAK_BF16_TFLOPS,
+                                        "algorithmic_flop_per_launch": bflops}}
     if "pre_us" in r:
         out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",
                                    "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
