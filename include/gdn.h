@@ -44,11 +44,11 @@
  *   - Thread safety: calls may be made concurrently from several threads.  The
  *     library's only mutable state is the per-thread error text and, per device,
  *     one auxiliary stream (default priority) with a few events, made on the
- *     first bf16 prefill of a long single sequence or the first backward call
- *     and kept until the process ends; the enqueues on it are serialised by a
- *     lock.  Such a call runs part of its work on that stream, forked from and
- *     joined back into `stream` with events, so to the caller it is ordered
- *     like any other call on `stream`.
+ *     first bf16 prefill of a long single sequence and kept until the process
+ *     ends; the enqueues on it are serialised by a lock.  Such a prefill runs
+ *     part of its work on that stream, forked from and joined back into
+ *     `stream` with events, so to the caller it is ordered like any other call
+ *     on `stream`.
  */
 #ifndef GDN_H_
 #define GDN_H_

@@ -82,24 +82,32 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Inputs of one chunk, loaded two chunks ahead into three rotating register
 // sets.  Rows past the end of a sequence are clamped to its last row on load
 // and replaced by zero in LDS.
-struct RevRegs {
-    u32x4 kr[4];     // K row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
-    u32x4 qr[4];     // Q rows likewise
-    u32x4 dor;       // dO row 16 w + lane / 4, slab columns 8 (lane % 4) .. +7
-    u32x4 pt[2];     // P^T row 16 w + c, columns 32 s + 8 g4 .. +7
-    u32x4 tt[2];     // T'^T likewise
-    float Gown;      // G of row 16 w + c
-    float Gz;        // G of row 16 w + lane / 4
-    float GL;        // G of the chunk's last row
+struct RevState {     // waves 0-3
+    u32x4 kr[4];      // K row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
+    u32x4 tt[2];      // T'^T row 16 w + c, columns 32 s + 8 g4 .. +7
+    float Gown;       // G of row 16 w + c
+    float GL;         // G of the chunk's last row
+};
+struct RevHelp {      // waves 4-7
+    u32x4 qr[4];      // Q row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
+    u32x4 dor;        // dO row 16 w + lane / 4, slab columns 8 (lane % 4) .. +7
+    u32x4 pt[2];      // P^T row 16 w + c, columns 32 s + 8 g4 .. +7
+    float Gz;         // G of row 16 w + lane / 4
 };
 
-// One workgroup (4 waves) per (sequence, V-head, 32-column d_v slab); wave w
-// owns chunk rows 16 w .. +15 of dU and dR and d_k columns 32 w .. +31 of the
-// fp32 state gradient.  Three barriers per chunk: (1) dU complete, (2) dR
-// complete, (3) dS complete.  Writes, per chunk, the bf16 dS' it starts from
-// (dsw [chunk][H_v][d_v][d_k]) and dU (duw [chunk row][H_v][d_v]); dv rows;
-// and the gradient with respect to the initial state.
-__global__ __launch_bounds__(256) void bwd_scan_kernel(
+// One workgroup (512 threads) per (sequence, V-head, 32-column d_v slab).
+// Waves 0-3 carry the fp32 state gradient from the last chunk to the first:
+// wave w owns chunk rows 16 w .. +15 of Y = K dS'^T, dU and dR and d_k columns
+// 32 w .. +31 of dS.  Waves 4-7 (same SIMDs) do everything off that chain:
+// they form P^T dO of the next chunk and the update's Q term
+// W = scale dO^T diag(gamma) Q (handed over in fp32 through LDS), and they
+// write the results out of LDS: per chunk the bf16 dS' it starts from
+// (dsw [chunk][H_v][d_v][d_k]), dU (duw [chunk row][H_v][d_v]) and the dv
+// rows.  (Global stores issued by the state waves lengthen their chain: the
+// waits for their own prefetched loads would also cover the stores.)  Three
+// barriers per chunk: (1) dU complete, (2) dR complete, (3) dS complete.  The
+// state waves write the gradient with respect to the initial state.
+__global__ __launch_bounds__(512) void bwd_scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ d_o,
     const float *__restrict__ dS_final, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
@@ -107,18 +115,22 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
     uint16_t *__restrict__ dv, float *__restrict__ dS0) {
     __shared__ __attribute__((aligned(16))) uint16_t sS[kBSlab * kKP];       // dS' (bf16), [v][k]
     __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];      // K rows of the chunk
-    __shared__ __attribute__((aligned(16))) uint16_t sQr[kChunk * kKP];      // Q rows of the chunk
-    __shared__ __attribute__((aligned(16))) uint16_t sDO[2][kChunk * kSP];   // dO rows (slab)
-    __shared__ __attribute__((aligned(16))) uint16_t sZq[2][kChunk * kSP];   // scale gamma_r dO_r
+    __shared__ __attribute__((aligned(16))) uint16_t sQr[kChunk * kKP];      // Q rows (helpers)
+    __shared__ __attribute__((aligned(16))) uint16_t sDO[kChunk * kSP];      // dO rows (slab)
+    __shared__ __attribute__((aligned(16))) uint16_t sZq[kChunk * kSP];      // scale gamma_r dO_r
     __shared__ __attribute__((aligned(16))) uint16_t sDU[kChunk * kSP];      // dU rows (slab)
     __shared__ __attribute__((aligned(16))) uint16_t sZk[kChunk * kSP];      // -gamma_r dR_r
+    __shared__ __attribute__((aligned(16))) uint16_t sDR[kChunk * kSP];      // dR rows (slab)
+    __shared__ __attribute__((aligned(16))) float sW[4 * 4 * 64 * 4];        // W, in the state layout
+    __shared__ __attribute__((aligned(16))) float sPd[4 * 2 * 64 * 4];      // P^T dO, in dU's layout
 
     const int u = xcd_unit();
     const int slab = u % kBSlabs;
     const int nh = u / kBSlabs;
     const int h = nh % H_v, n = nh / H_v;
     const int hq = h / (H_v / H_qk);
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = wave & 3;
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c = lane & 15;
     const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
     const int nch = (s1 - s0 + kChunk - 1) / kChunk;
@@ -126,176 +138,244 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(
     const int e0 = kBSlab * slab;
     const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
     auto chunk_len = [&](int ci) { return min(kChunk, s1 - (s0 + kChunk * ci)); };
-
-    auto fetch = [&](int ci, RevRegs &R) {      // needs nch >= 1
-        ci = max(ci, 0);                        // before the first chunk: loaded, never used
-        const int L = chunk_len(ci);
-        const size_t row0 = (size_t)(s0 + kChunk * ci);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = min(16 * w + 4 * i + (lane >> 4), L - 1);
-            const size_t off = ((row0 + r) * H_qk + hq) * kD + 8 * (lane & 15);
-            R.kr[i] = *reinterpret_cast<const u32x4 *>(k + off);
-            R.qr[i] = *reinterpret_cast<const u32x4 *>(q + off);
-        }
-        const int rd = min(16 * w + (lane >> 2), L - 1);
-        R.dor = *reinterpret_cast<const u32x4 *>(d_o + ((row0 + rd) * H_v + h) * kD + e0 + 8 * (lane & 3));
-        const uint16_t *rec = bws + ((size_t)(cbase + ci) * H_v + h) * kBwdRecElems;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            R.pt[s] = *reinterpret_cast<const u32x4 *>(rec + kBwdPtOff + frag_off(w, s, lane));
-            R.tt[s] = *reinterpret_cast<const u32x4 *>(rec + kBwdTtOff + frag_off(w, s, lane));
-        }
-        const float *Gp = reinterpret_cast<const float *>(rec + kBwdGOff);
-        R.Gown = Gp[16 * w + c];
-        R.Gz = Gp[16 * w + (lane >> 2)];
-        R.GL = Gp[kChunk - 1];
-    };
-    // dO rows of chunk ci and scale gamma_r dO_r into the buffers of ci's parity
-    auto stage_rows = [&](int ci, const RevRegs &R) {
-        const int r = 16 * w + (lane >> 2), pc = 8 * (lane & 3);
-        u32x4 d = R.dor;
-        if (r >= chunk_len(ci)) d = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(sDO[ci & 1] + r * kSP + pc) = d;
-        float x[8];
-        unpack8(__builtin_bit_cast(uint4, d), x);
-        const float gz = scale * __expf(R.Gz);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= gz;
-        *reinterpret_cast<uint4 *>(sZq[ci & 1] + r * kSP + pc) = pack_bf8(x);
+    auto brec = [&](int ci) { return bws + ((size_t)(cbase + ci) * H_v + h) * kBwdRecElems; };
+    // offset of row 16 w + 4 i + lane / 16 (clamped), 16-byte piece lane % 16,
+    // of chunk ci in q or k
+    auto qk_off = [&](int ci, int i) {
+        const int r = min(16 * w + 4 * i + (lane >> 4), chunk_len(ci) - 1);
+        return ((size_t)(s0 + kChunk * ci + r) * H_qk + hq) * kD + 8 * (lane & 15);
     };
 
-    // st[t][nt] = dS[e0 + 16 nt + c][32 w + 16 t + 4 g4 + j]
-    f32x4 st[2][2];
+    if (wave < 4) {
+        // ---------------- state waves
+        auto fetch = [&](int ci, RevState &R) {     // needs nch >= 1
+            ci = max(ci, 0);                        // before the first chunk: loaded, never used
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i) R.kr[i] = *reinterpret_cast<const u32x4 *>(k + qk_off(ci, i));
+            const uint16_t *rec = brec(ci);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            if (dS_final) {
-                const float4 x = *reinterpret_cast<const float4 *>(
-                    dS_final + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4);
-                st[t][nt] = f32x4{x.x, x.y, x.z, x.w};
-            } else {
-                st[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    auto write_state_lds = [&]() {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                *reinterpret_cast<uint2 *>(sS + (16 * nt + c) * kKP + 32 * w + 16 * t + 4 * g4) =
-                    pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
-    };
-
-    auto body = [&](int ci, const RevRegs &cur, const RevRegs &nxt, RevRegs &pf) {
-        const int L = chunk_len(ci);
-        // the gradient this chunk starts from (with respect to its end state)
-        uint16_t *dsp = dsw + ((size_t)(cbase + ci) * H_v + h) * (kD * kD);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                *reinterpret_cast<uint2 *>(dsp + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
-                    pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
-        // this wave's K and Q rows into LDS
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * i + (lane >> 4);
-            const bool ok = r < L;
-            *reinterpret_cast<u32x4 *>(sKr + r * kKP + 8 * (lane & 15)) = ok ? cur.kr[i] : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(sQr + r * kKP + 8 * (lane & 15)) = ok ? cur.qr[i] : u32x4{0u, 0u, 0u, 0u};
-        }
-        wave_lds_sync();
-        uint4 kB[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kB[s] = frag_rows(sKr, kKP, 16 * w, 32 * s, lane);
-        fetch(ci - 2, pf);
-        const float lam = __expf(cur.GL - cur.Gown), gam = __expf(cur.Gown), gamL = __expf(cur.GL);
-        const uint16_t *sDOc = sDO[ci & 1];
-        // dU = P^T dO + diag(lambda) K dS'^T: rows 16 w + c, slab columns 16 nt + 4 g4 + j
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) y = mfma32(frag_rows(sS, kKP, 16 * nt, 32 * s, lane), kB[s], y);
-            f32x4 pd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s >= (w >> 1)) pd = mfma32(frag_cols(sDOc, kSP, 32 * s, 16 * nt, lane), cur.pt[s], pd);
-            const uint2 p = pk4(pd[0] + lam * y[0], pd[1] + lam * y[1], pd[2] + lam * y[2], pd[3] + lam * y[3]);
-            *reinterpret_cast<uint2 *>(sDU + (16 * w + c) * kSP + 16 * nt + 4 * g4) = p;
-            *reinterpret_cast<uint2 *>(duw + (((size_t)(cbase + ci) * kChunk + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) = p;
-        }
-        __syncthreads();                                    // (1) dU complete
-        // dR = T'^T dU: the gradient of v
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (s >= (w >> 1)) d = mfma32(frag_cols(sDU, kSP, 32 * s, 16 * nt, lane), cur.tt[s], d);
-            if (16 * w + c < L)
-                *reinterpret_cast<uint2 *>(dv + ((size_t)(s0 + kChunk * ci + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
-                    pk4(d[0], d[1], d[2], d[3]);
-            *reinterpret_cast<uint2 *>(sZk + (16 * w + c) * kSP + 16 * nt + 4 * g4) =
-                pk4(-gam * d[0], -gam * d[1], -gam * d[2], -gam * d[3]);
-        }
-        if (ci > 0) stage_rows(ci - 1, nxt);
-        __syncthreads();                                    // (2) dR complete
-        // dS = gamma_L dS' + (scale diag(gamma) dO)^T Q + (-diag(gamma) dR)^T K
-        uint4 zq[2][2], zk[2][2], qa[2][2], ka[2][2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                zq[nt][s] = frag_cols(sZq[ci & 1], kSP, 32 * s, 16 * nt, lane);
-                zk[nt][s] = frag_cols(sZk, kSP, 32 * s, 16 * nt, lane);
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                qa[t][s] = frag_cols(sQr, kKP, 32 * s, 32 * w + 16 * t, lane);
-                ka[t][s] = frag_cols(sKr, kKP, 32 * s, 32 * w + 16 * t, lane);
-            }
-        }
+            for (int s = 0; s < 2; ++s) R.tt[s] = *reinterpret_cast<const u32x4 *>(rec + kBwdTtOff + frag_off(w, s, lane));
+            const float *Gp = reinterpret_cast<const float *>(rec + kBwdGOff);
+            R.Gown = Gp[16 * w + c];
+            R.GL = Gp[kChunk - 1];
+        };
+        // st[t][nt] = dS[e0 + 16 nt + c][32 w + 16 t + 4 g4 + j]
+        f32x4 st[2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                f32x4 a = gamL * st[t][nt];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    a = mfma32(qa[t][s], zq[nt][s], a);
-                    a = mfma32(ka[t][s], zk[nt][s], a);
+                if (dS_final) {
+                    const float4 x = *reinterpret_cast<const float4 *>(
+                        dS_final + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4);
+                    st[t][nt] = f32x4{x.x, x.y, x.z, x.w};
+                } else {
+                    st[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                st[t][nt] = a;
             }
-        write_state_lds();
-        __syncthreads();                                    // (3) dS complete
-    };
+        auto write_state_lds = [&]() {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    *reinterpret_cast<uint2 *>(sS + (16 * nt + c) * kKP + 32 * w + 16 * t + 4 * g4) =
+                        pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+        };
+        auto body = [&](int ci, const RevState &cur, RevState &pf) {
+            const int L = chunk_len(ci);
+            // this wave's K rows into LDS
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * w + 4 * i + (lane >> 4);
+                *reinterpret_cast<u32x4 *>(sKr + r * kKP + 8 * (lane & 15)) =
+                    r < L ? cur.kr[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+            wave_lds_sync();
+            uint4 kB[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kB[s] = frag_rows(sKr, kKP, 16 * w, 32 * s, lane);
+            fetch(ci - 2, pf);
+            const float lam = __expf(cur.GL - cur.Gown), gam = __expf(cur.Gown), gamL = __expf(cur.GL);
+            // dU = P^T dO + diag(lambda) K dS'^T: rows 16 w + c, slab columns 16 nt + 4 g4 + j
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) y = mfma32(frag_rows(sS, kKP, 16 * nt, 32 * s, lane), kB[s], y);
+                const float4 pd = *reinterpret_cast<const float4 *>(sPd + ((w * 2 + nt) * 64 + lane) * 4);
+                *reinterpret_cast<uint2 *>(sDU + (16 * w + c) * kSP + 16 * nt + 4 * g4) =
+                    pk4(pd.x + lam * y[0], pd.y + lam * y[1], pd.z + lam * y[2], pd.w + lam * y[3]);
+            }
+            __syncthreads();                                    // (1) dU complete
+            // dR = T'^T dU: the gradient of v
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s >= (w >> 1)) d = mfma32(frag_cols(sDU, kSP, 32 * s, 16 * nt, lane), cur.tt[s], d);
+                *reinterpret_cast<uint2 *>(sDR + (16 * w + c) * kSP + 16 * nt + 4 * g4) = pk4(d[0], d[1], d[2], d[3]);
+                *reinterpret_cast<uint2 *>(sZk + (16 * w + c) * kSP + 16 * nt + 4 * g4) =
+                    pk4(-gam * d[0], -gam * d[1], -gam * d[2], -gam * d[3]);
+            }
+            __syncthreads();                                    // (2) dR complete
+            // dS = gamma_L dS' + W + (-diag(gamma) dR)^T K
+            uint4 zk[2][2], ka[2][2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) zk[nt][s] = frag_cols(sZk, kSP, 32 * s, 16 * nt, lane);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) ka[t][s] = frag_cols(sKr, kKP, 32 * s, 32 * w + 16 * t, lane);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const float4 wq = *reinterpret_cast<const float4 *>(sW + ((w * 4 + t * 2 + nt) * 64 + lane) * 4);
+                    f32x4 a = gamL * st[t][nt] + f32x4{wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) a = mfma32(ka[t][s], zk[nt][s], a);
+                    st[t][nt] = a;
+                }
+            write_state_lds();
+            __syncthreads();                                    // (3) dS complete
+        };
 
-    write_state_lds();
-    RevRegs r0, r1, r2;
-    if (nch > 0) {
-        fetch(nch - 1, r0);
-        fetch(nch - 2, r1);
-        stage_rows(nch - 1, r0);
-    }
-    __syncthreads();
-    for (int ci = nch - 1; ci >= 0; ci -= 3) {
-        body(ci, r0, r1, r2);
-        if (ci == 0) break;
-        body(ci - 1, r1, r2, r0);
-        if (ci == 1) break;
-        body(ci - 2, r2, r0, r1);
-    }
-    if (dS0) {
+        RevState r0, r1, r2;
+        if (nch > 0) {
+            fetch(nch - 1, r0);
+            fetch(nch - 2, r1);
+        }
+        write_state_lds();
+        __syncthreads();                                        // helpers' first staging
+        __syncthreads();                                        // helpers' first P^T dO
+        for (int ci = nch - 1; ci >= 0; ci -= 3) {
+            body(ci, r0, r2);
+            if (ci == 0) break;
+            body(ci - 1, r1, r0);
+            if (ci == 1) break;
+            body(ci - 2, r2, r1);
+        }
+        if (dS0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                *reinterpret_cast<float4 *>(dS0 + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
-                    make_float4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+                for (int nt = 0; nt < 2; ++nt)
+                    *reinterpret_cast<float4 *>(dS0 + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
+                        make_float4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+        }
+    } else {
+        // ---------------- helper waves
+        auto fetch = [&](int ci, RevHelp &R) {      // needs nch >= 1
+            ci = max(ci, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) R.qr[i] = *reinterpret_cast<const u32x4 *>(q + qk_off(ci, i));
+            const int rd = min(16 * w + (lane >> 2), chunk_len(ci) - 1);
+            R.dor = *reinterpret_cast<const u32x4 *>(d_o + ((size_t)(s0 + kChunk * ci + rd) * H_v + h) * kD + e0 + 8 * (lane & 3));
+            const uint16_t *rec = brec(ci);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) R.pt[s] = *reinterpret_cast<const u32x4 *>(rec + kBwdPtOff + frag_off(w, s, lane));
+            R.Gz = reinterpret_cast<const float *>(rec + kBwdGOff)[16 * w + (lane >> 2)];
+        };
+        const int pr = 16 * w + (lane >> 2), pc = 8 * (lane & 3);    // this lane's dO row piece
+        auto stage_do = [&](int ci, const RevHelp &R) {
+            *reinterpret_cast<u32x4 *>(sDO + pr * kSP + pc) = pr < chunk_len(ci) ? R.dor : u32x4{0u, 0u, 0u, 0u};
+        };
+        // Q rows and scale gamma_r dO_r of chunk ci
+        auto stage_qz = [&](int ci, const RevHelp &R) {
+            const int L = chunk_len(ci);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * w + 4 * i + (lane >> 4);
+                *reinterpret_cast<u32x4 *>(sQr + r * kKP + 8 * (lane & 15)) = r < L ? R.qr[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+            float x[8];
+            unpack8(__builtin_bit_cast(uint4, R.dor), x);
+            const float gz = pr < L ? scale * __expf(R.Gz) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= gz;
+            *reinterpret_cast<uint4 *>(sZq + pr * kSP + pc) = pack_bf8(x);
+        };
+        // P^T dO of the staged chunk (rows 16 w + c, slab columns 16 nt + 4 g4 + j)
+        auto pdo = [&](const RevHelp &R) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (s >= (w >> 1)) pd = mfma32(frag_cols(sDO, kSP, 32 * s, 16 * nt, lane), R.pt[s], pd);
+                *reinterpret_cast<float4 *>(sPd + ((w * 2 + nt) * 64 + lane) * 4) = make_float4(pd[0], pd[1], pd[2], pd[3]);
+            }
+        };
+        const int hl = lane + 64 * w;                               // 0..255
+        auto body = [&](int ci, const RevHelp &nxt, RevHelp &pf) {
+            // dS' of this chunk (bf16, as the state waves left it in LDS)
+            {
+                uint16_t *dsp = dsw + ((size_t)(cbase + ci) * H_v + h) * (kD * kD) + (size_t)e0 * kD;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int e = hl + 256 * m, r = e >> 4, pcs = 8 * (e & 15);
+                    *reinterpret_cast<u32x4 *>(dsp + r * kD + pcs) = *reinterpret_cast<const u32x4 *>(sS + r * kKP + pcs);
+                }
+            }
+            if (ci > 0) stage_do(ci - 1, nxt);
+            fetch(ci - 2, pf);
+            // W = scale dO^T diag(gamma) Q of chunk ci, in the state layout
+            uint4 zq[2][2], qa[2][2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) zq[nt][s] = frag_cols(sZq, kSP, 32 * s, 16 * nt, lane);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) qa[t][s] = frag_cols(sQr, kKP, 32 * s, 32 * w + 16 * t, lane);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) a = mfma32(qa[t][s], zq[nt][s], a);
+                    *reinterpret_cast<float4 *>(sW + ((w * 4 + t * 2 + nt) * 64 + lane) * 4) = make_float4(a[0], a[1], a[2], a[3]);
+                }
+            __syncthreads();                                    // (1)
+            if (ci > 0) {
+                pdo(nxt);
+                stage_qz(ci - 1, nxt);
+            }
+            {
+                const int r = hl >> 2, pcs = 8 * (hl & 3);
+                *reinterpret_cast<u32x4 *>(duw + (((size_t)(cbase + ci) * kChunk + r) * H_v + h) * kD + e0 + pcs) =
+                    *reinterpret_cast<const u32x4 *>(sDU + r * kSP + pcs);
+            }
+            __syncthreads();                                    // (2)
+            {
+                const int r = hl >> 2, pcs = 8 * (hl & 3);
+                if (r < chunk_len(ci))
+                    *reinterpret_cast<u32x4 *>(dv + ((size_t)(s0 + kChunk * ci + r) * H_v + h) * kD + e0 + pcs) =
+                        *reinterpret_cast<const u32x4 *>(sDR + r * kSP + pcs);
+            }
+            __syncthreads();                                    // (3)
+        };
+
+        RevHelp r0, r1, r2;
+        if (nch > 0) {
+            fetch(nch - 1, r0);
+            fetch(nch - 2, r1);
+            stage_do(nch - 1, r0);
+            stage_qz(nch - 1, r0);
+        }
+        __syncthreads();
+        if (nch > 0) pdo(r0);
+        __syncthreads();
+        for (int ci = nch - 1; ci >= 0; ci -= 3) {
+            body(ci, r1, r2);
+            if (ci == 0) break;
+            body(ci - 1, r2, r0);
+            if (ci == 1) break;
+            body(ci - 2, r0, r1);
+        }
     }
 }
 
@@ -721,7 +801,7 @@ hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const 
                            const int32_t *cu_seqlens, const int32_t *chunk_base, int N, int T,
                            int H_qk, int H_v, float scale, const void *bws, void *dsw, void *duw,
                            void *dv, float *dS0, hipStream_t stream) {
-    hipLaunchKernelGGL(bwd_scan_kernel, dim3(N * H_v * kBSlabs), dim3(256), 0, stream,
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(N * H_v * kBSlabs), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(d_o), dS_final, cu_seqlens, chunk_base, N, T,
                        H_qk, H_v, scale, static_cast<const uint16_t *>(bws),

@@ -473,10 +473,11 @@ struct OutRegs {          // waves 4-7
 // apply conv and SiLU (the prelude's arithmetic) to the raw v rows of chunk
 // ci + 1 and write them into the other half of a double-buffered v tile.
 //
-// For the backward pass (kSave) the state waves store the bf16 state each
-// chunk starts from (the values the chunk's products use) into
-// states [chunk][H_v][d_v][d_k]; the kernel is then launched with the 256
-// threads of the state waves only, and o is not written.
+// For the backward pass (kSave) the output waves compute no outputs: they
+// copy the bf16 state each chunk starts from (the values the chunk's products
+// use) out of LDS into states [chunk][H_v][d_v][d_k].  (Stores issued by the
+// state waves would lengthen their chain: the waits for their own prefetched
+// loads would also cover the stores.)
 template <bool kRaw, bool kSave = false>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -571,15 +572,6 @@ __global__ __launch_bounds__(512) void scan_kernel(
         };
 
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
-            if constexpr (kSave) {
-                uint16_t *sp = states + ((size_t)(cbase + ci) * H_v + h) * (kD * kD);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        *reinterpret_cast<uint2 *>(sp + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
-                            pk4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
-            }
             // this wave's 16 rows of v and of K into LDS, row-major; K's MFMA
             // fragments come back out of its own rows (with the prelude
             // fused, the output waves have already written v)
@@ -689,6 +681,22 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 for (int nt = 0; nt < 2; ++nt)
                     *reinterpret_cast<float4 *>(final_state + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
                         make_float4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
+        }
+    } else if constexpr (kSave) {
+        // ---------------- output waves, backward pass: the start states out
+        const int ol = threadIdx.x - 256;
+        __syncthreads();                                       // matches the state waves' first barrier
+        for (int ci = c_lo; ci < c_end; ++ci) {
+            // sS holds the state chunk ci starts from until its barrier (2)
+            uint16_t *sp = states + ((size_t)(cbase + ci) * H_v + h) * (kD * kD) + (size_t)e0 * kD;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int e = ol + 256 * m, r = e >> 4, pcs = 8 * (e & 15);
+                *reinterpret_cast<u32x4 *>(sp + r * kD + pcs) = *reinterpret_cast<const u32x4 *>(sS + r * kKP + pcs);
+            }
+            __syncthreads();                                   // (1)
+            __syncthreads();                                   // (2)
+            __syncthreads();                                   // (3)
         }
     } else {
         // ---------------- output waves
@@ -986,10 +994,10 @@ size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v) {
 }
 
 // plan -> prep (forward and backward records) -> forward scan storing each
-// chunk's start state, and beside it the reverse scan (dv, the initial-state
-// gradient, dS' and dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta).
-// The two scans need only prep's records; the forward one runs on the
-// device's auxiliary stream, forked from and joined back into `stream`.
+// chunk's start state -> reverse scan (dv, the initial-state gradient, dS' and
+// dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta), all on `stream`.
+// (The two scans need only prep's records, but 512-thread workgroups of both
+// do not fit one CU together, so running them side by side gains nothing.)
 hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *S0, const int32_t *cu_seqlens,
                                    int N, int T, int H_qk, int H_v, float scale, const void *d_o,
@@ -1007,32 +1015,14 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
                        dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
                        W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    auto fwd_scan = [&](hipStream_t s) {
-        hipLaunchKernelGGL((scan_kernel<false, true>), dim3(N * H_v * kSlabsW), dim3(256), 0, s,
-                           q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
-                           cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
-                           nullptr, W.states);
-        return hipGetLastError();
-    };
-    auto rev_scan = [&]() {
-        return launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
-                               scale, W.brec, W.dsw, W.duw, dv, dS0, stream);
-    };
-    {
-        std::lock_guard<std::mutex> lock(g_aux_mu);
-        DeviceAux *aux = device_aux();
-        if (aux) {
-            if ((e = hipEventRecord(aux->ev[0], stream)) != hipSuccess) return e;
-            if ((e = hipStreamWaitEvent(aux->stream, aux->ev[0], 0)) != hipSuccess) return e;
-            if ((e = fwd_scan(aux->stream)) != hipSuccess) return e;
-            if ((e = hipEventRecord(aux->ev[1], aux->stream)) != hipSuccess) return e;
-            if ((e = rev_scan()) != hipSuccess) return e;
-            if ((e = hipStreamWaitEvent(stream, aux->ev[1], 0)) != hipSuccess) return e;
-        } else {
-            if ((e = fwd_scan(stream)) != hipSuccess) return e;
-            if ((e = rev_scan()) != hipSuccess) return e;
-        }
-    }
+    hipLaunchKernelGGL((scan_kernel<false, true>), dim3(N * H_v * kSlabsW), dim3(512), 0, stream,
+                       q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
+                       cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
+                       nullptr, W.states);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
+                             W.brec, W.dsw, W.duw, dv, dS0, stream)) != hipSuccess)
+        return e;
     return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
                            max_chunks, scale, W.brec, W.states, W.dsw, W.duw, dq, dk, dg, dbeta,
                            stream);
