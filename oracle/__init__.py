@@ -56,8 +56,11 @@ def _load():
     lib.orc_gated_norm.argtypes = [P, P, P, I, I, D, P]
     lib.orc_recurrent_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, D, P, P, P, P,
                                            P, P, P, P, I, I]
+    lib.orc_prelude_backward.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P, P, P, P]
+    lib.orc_gates_backward.argtypes = [P, P, P, P, I, I, P, P, P, P, P, P]
     for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step,
-              lib.orc_gates, lib.orc_gated_norm, lib.orc_recurrent_backward):
+              lib.orc_gates, lib.orc_gated_norm, lib.orc_recurrent_backward,
+              lib.orc_prelude_backward, lib.orc_gates_backward):
         f.restype = I
     _lib = lib
     return lib
@@ -104,6 +107,38 @@ def prelude(x, w, cu_seqlens=None, *, H_qk, H_v, dk, dv, eps=1e-6):
                              _ptr(q), _ptr(k), _ptr(v))
     _check(rc, "prelude")
     return q, k, v
+
+
+def prelude_backward(x, w, dq, dk, dv, cu_seqlens=None, *, H_qk, H_v, eps=1e-6):
+    """Gradients of ``prelude`` with respect to x [T, C_raw] and w [C_raw, 4],
+    given dq, dk [T, H_qk, dk] and dv [T, H_v, dv].  Returns fp64 (dx, dw)."""
+    x, w, dq, dk, dv = (f64(a) for a in (x, w, dq, dk, dv))
+    T, Craw = x.shape
+    d_k, d_v = dq.shape[2], dv.shape[2]
+    if Craw != 2 * H_qk * d_k + H_v * d_v or w.shape != (Craw, 4) or dk.shape != dq.shape:
+        raise ValueError("prelude_backward shape mismatch")
+    cu, N = _cu(cu_seqlens, T)
+    dx = np.zeros((T, Craw))
+    dw = np.zeros((Craw, 4))
+    _check(_load().orc_prelude_backward(_ptr(x), _ptr(w), _ptr(cu), N, T, H_qk, H_v, d_k, d_v,
+                                        float(eps), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dx),
+                                        _ptr(dw)), "prelude_backward")
+    return dx, dw
+
+
+def gates_backward(a, b, A_log, dt_bias, dg, dbeta):
+    """Gradients of ``gates`` with respect to a, b [T, H_v] and A_log, dt_bias
+    [H_v], given dg, dbeta [T, H_v].  Returns fp64 (da, db, dA_log, ddt_bias)."""
+    a, b, A_log, dt_bias, dg, dbeta = (f64(x) for x in (a, b, A_log, dt_bias, dg, dbeta))
+    T, H_v = a.shape
+    if b.shape != (T, H_v) or dg.shape != (T, H_v) or dbeta.shape != (T, H_v):
+        raise ValueError("gates_backward shape mismatch")
+    da, db = np.zeros((T, H_v)), np.zeros((T, H_v))
+    dA, ddt = np.zeros(H_v), np.zeros(H_v)
+    _check(_load().orc_gates_backward(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), T, H_v,
+                                      _ptr(dg), _ptr(dbeta), _ptr(da), _ptr(db), _ptr(dA),
+                                      _ptr(ddt)), "gates_backward")
+    return da, db, dA, ddt
 
 
 def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens):

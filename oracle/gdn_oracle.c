@@ -619,4 +619,130 @@ int orc_recurrent_backward(const double *q, const double *k, const double *v, co
     return status;
 }
 
+/*
+ * Gradients of orc_prelude (the chain rule through each of its steps, in
+ * reverse): given dq, dk [T][H_qk][dk] and dv [T][H_v][dv] (gradients of the
+ * loss with respect to the prelude's outputs), the gradients with respect to
+ * the raw projections dx [T][C_raw] and the conv taps dw [C_raw][4] (both
+ * overwritten).  For each token, with y the conv output of a channel,
+ * a = SiLU(y), and for a q or k head n = a r, r = (sum a^2 + eps)^(-1/2):
+ *     da = r (dn - n (n . dn))              (L2 norm; v channels: da = dv)
+ *     dy = da sigmoid(y) (1 + y (1 - sigmoid(y)))      (SiLU)
+ *     dx[t - 3 + j] += w[j] dy[t],  dw[j] += x[t - 3 + j] dy[t]
+ * over the taps j whose source token t - 3 + j lies in the sequence
+ * ([Dissect sec. 2.1]: conv of width 4 with the per-layer conv1d weight).
+ */
+int orc_prelude_backward(const double *x, const double *w, const int32_t *cu, int N, int T,
+                         int H_qk, int H_v, int dk, int dv, double eps, const double *dq,
+                         const double *dkk, const double *dvv, double *dx, double *dw)
+{
+    const int Cq = H_qk * dk;
+    const int Craw = 2 * Cq + H_v * dv;
+    if (T < 0 || N < 1 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1)
+        return ORC_EINVAL;
+    double *y = (double *)malloc(sizeof(double) * (size_t)Craw);
+    double *dy = (double *)malloc(sizeof(double) * (size_t)Craw);
+    if (!y || !dy) {
+        free(y);
+        free(dy);
+        return ORC_ENOMEM;
+    }
+    memset(dx, 0, sizeof(double) * (size_t)T * Craw);
+    memset(dw, 0, sizeof(double) * (size_t)Craw * 4);
+    for (int n = 0; n < N; ++n) {
+        int s0 = 0, s1 = 0;
+        if (seq_bounds(cu, N, T, n, &s0, &s1)) {
+            free(y);
+            free(dy);
+            return ORC_EINVAL;
+        }
+        for (int t = s0; t < s1; ++t) {
+            for (int c = 0; c < Craw; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < 4; ++j) {
+                    const int src = t - 3 + j;
+                    if (src >= s0)
+                        acc += w[(size_t)c * 4 + j] * x[(size_t)src * Craw + c];
+                }
+                y[c] = acc;
+            }
+            /* da into dy[], per channel */
+            for (int part = 0; part < 2; ++part) {          /* q heads, then k heads */
+                const double *dn_all = part == 0 ? dq : dkk;
+                for (int h = 0; h < H_qk; ++h) {
+                    const int c0 = part * Cq + h * dk;
+                    const double *dn = dn_all + ((size_t)t * H_qk + h) * dk;
+                    double ss = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = y[c0 + i] / (1.0 + exp(-y[c0 + i]));
+                        ss += a * a;
+                    }
+                    const double r = 1.0 / sqrt(ss + eps);
+                    double ndn = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = y[c0 + i] / (1.0 + exp(-y[c0 + i]));
+                        ndn += a * r * dn[i];
+                    }
+                    for (int i = 0; i < dk; ++i) {
+                        const double a = y[c0 + i] / (1.0 + exp(-y[c0 + i]));
+                        dy[c0 + i] = r * (dn[i] - a * r * ndn);
+                    }
+                }
+            }
+            for (int c = 0; c < H_v * dv; ++c)
+                dy[2 * Cq + c] = dvv[(size_t)t * H_v * dv + c];
+            /* through SiLU, then the conv */
+            for (int c = 0; c < Craw; ++c) {
+                const double sg = 1.0 / (1.0 + exp(-y[c]));
+                const double d = dy[c] * sg * (1.0 + y[c] * (1.0 - sg));
+                for (int j = 0; j < 4; ++j) {
+                    const int src = t - 3 + j;
+                    if (src >= s0) {
+                        dx[(size_t)src * Craw + c] += w[(size_t)c * 4 + j] * d;
+                        dw[(size_t)c * 4 + j] += x[(size_t)src * Craw + c] * d;
+                    }
+                }
+            }
+        }
+    }
+    free(y);
+    free(dy);
+    return ORC_OK;
+}
+
+/*
+ * Gradients of orc_gates: given dg, dbeta [T][H_v], the gradients with respect
+ * to a, b [T][H_v] and A_log, dt_bias [H_v] (all overwritten).  With
+ * g = -softplus(a + dt_bias) exp(A_log) and beta = sigmoid(b):
+ *     da = -dg exp(A_log) sigmoid(a + dt_bias),   ddt_bias = sum over t of da,
+ *     dA_log = sum over t of dg g,                db = dbeta beta (1 - beta).
+ */
+int orc_gates_backward(const double *a, const double *b, const double *A_log,
+                       const double *dt_bias, int T, int H_v, const double *dg,
+                       const double *dbeta, double *da, double *db, double *dA_log,
+                       double *ddt_bias)
+{
+    if (T < 0 || H_v < 1)
+        return ORC_EINVAL;
+    for (int h = 0; h < H_v; ++h) {
+        dA_log[h] = 0.0;
+        ddt_bias[h] = 0.0;
+    }
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H_v; ++h) {
+            const size_t i = (size_t)t * H_v + h;
+            const double xx = a[i] + dt_bias[h];
+            const double softplus = (xx > 0.0 ? xx : 0.0) + log1p(exp(-fabs(xx)));
+            const double g = -softplus * exp(A_log[h]);
+            const double sg = 1.0 / (1.0 + exp(-xx));
+            da[i] = -dg[i] * exp(A_log[h]) * sg;
+            ddt_bias[h] += da[i];
+            dA_log[h] += dg[i] * g;
+            const double be = 1.0 / (1.0 + exp(-b[i]));
+            db[i] = dbeta[i] * be * (1.0 - be);
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_version(void) { return 1; }

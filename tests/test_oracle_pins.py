@@ -552,6 +552,96 @@ def test_backward_adjoint_identities(orc):
     assert abs((dq * q).sum() - (Wo * o).sum()) <= 1e-10 * np.abs(Wo * o).sum()
 
 
+def _fd(loss, args, ai, h=1e-6):
+    """Central differences of loss(*args) with respect to every element of args[ai]."""
+    a = args[ai]
+    fd = np.zeros_like(a)
+    for idx in np.ndindex(a.shape):
+        a[idx] += h
+        lp = loss(*args)
+        a[idx] -= 2 * h
+        lm = loss(*args)
+        a[idx] += h
+        fd[idx] = (lp - lm) / (2 * h)
+    return fd
+
+
+def test_prelude_backward_equals_finite_differences(orc):
+    """dx and dw of the prelude (conv, SiLU, L2 norm of q and k) against
+    central differences of orc.prelude: packed sequences of lengths 3, 1, 5
+    (conv windows cut at sequence starts), two QK heads, d_k != d_v."""
+    rng = np.random.default_rng(90)
+    H_qk, H_v, dk, dv = 2, 2, 3, 2
+    C = 2 * H_qk * dk + H_v * dv
+    cu = np.array([0, 3, 4, 9], dtype=np.int32)
+    x = rng.standard_normal((9, C))
+    w = rng.standard_normal((C, 4))
+    Wq, Wk = rng.standard_normal((9, H_qk, dk)), rng.standard_normal((9, H_qk, dk))
+    Wv = rng.standard_normal((9, H_v, dv))
+
+    def loss(x, w):
+        q, k, v = orc.prelude(x, w, cu, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, eps=1e-3)
+        return (q * Wq).sum() + (k * Wk).sum() + (v * Wv).sum()
+
+    dx, dw = orc.prelude_backward(x, w, Wq, Wk, Wv, cu, H_qk=H_qk, H_v=H_v, eps=1e-3)
+    for got, ai in ((dx, 0), (dw, 1)):
+        fd = _fd(loss, [x, w], ai)
+        np.testing.assert_allclose(got, fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
+
+
+def test_gates_backward_equals_finite_differences(orc):
+    rng = np.random.default_rng(91)
+    T, H = 5, 3
+    a, b = rng.normal(0, 3, (T, H)), rng.normal(0, 3, (T, H))
+    A_log, dt = rng.uniform(-1, 1, H), rng.uniform(-1, 1, H)
+    Wg, Wb = rng.standard_normal((T, H)), rng.standard_normal((T, H))
+
+    def loss(a, b, A_log, dt):
+        g, beta = orc.gates(a, b, A_log, dt)
+        return (g * Wg).sum() + (beta * Wb).sum()
+
+    got = orc.gates_backward(a, b, A_log, dt, Wg, Wb)
+    for ai in range(4):
+        fd = _fd(loss, [a, b, A_log, dt], ai)
+        np.testing.assert_allclose(got[ai], fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
+
+
+def test_layer_backward_composition_equals_finite_differences(orc):
+    """The layer from raw projections (gates, prelude, recurrence): the
+    gradients composed from the three backward functions against central
+    differences of the composed forward, for every input including the
+    initial state."""
+    rng = np.random.default_rng(92)
+    H_qk, H_v, d = 1, 2, 3
+    C = 2 * H_qk * d + H_v * d
+    cu = np.array([0, 4, 7], dtype=np.int32)
+    T, N = 7, 2
+    x, w = rng.standard_normal((T, C)), rng.standard_normal((C, 4))
+    a, b = rng.standard_normal((T, H_v)), rng.standard_normal((T, H_v))
+    A_log, dt = rng.uniform(-1, 1, H_v), rng.uniform(-1, 1, H_v)
+    S0 = rng.standard_normal((N, H_v, d, d))
+    Wo, WS = rng.standard_normal((T, H_v, d)), rng.standard_normal((N, H_v, d, d))
+
+    def fwd(x, w, a, b, A_log, dt, S0):
+        q, k, v = orc.prelude(x, w, cu, H_qk=H_qk, H_v=H_v, dk=d, dv=d, eps=1e-3)
+        g, beta = orc.gates(a, b, A_log, dt)
+        return q, k, v, g, beta
+
+    def loss(x, w, a, b, A_log, dt, S0):
+        q, k, v, g, beta = fwd(x, w, a, b, A_log, dt, S0)
+        o, S = orc.recurrent(q, k, v, g, beta, S0, cu, scale=0.8)
+        return (o * Wo).sum() + (S * WS).sum()
+
+    q, k, v, g, beta = fwd(x, w, a, b, A_log, dt, S0)
+    dq, dk, dv, dg, db, dS0 = orc.recurrent_backward(q, k, v, g, beta, Wo, S0, WS, cu, scale=0.8)
+    dx, dw = orc.prelude_backward(x, w, dq, dk, dv, cu, H_qk=H_qk, H_v=H_v, eps=1e-3)
+    da, dbr, dA, ddt = orc.gates_backward(a, b, A_log, dt, dg, db)
+    args = [x, w, a, b, A_log, dt, S0]
+    for got, ai in zip((dx, dw, da, dbr, dA, ddt, dS0), range(7)):
+        fd = _fd(loss, args, ai)
+        np.testing.assert_allclose(got, fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
+
+
 # ------------------------------------------------------------- size pins
 def test_sizes_printed_on_pages():
     """The layer shape and the fp32 state dtype reproduce the state and KV-cache
