@@ -206,6 +206,52 @@ int gdn_prefill_backward(const void *q, const void *k, const void *v, const floa
                          size_t ws_bytes, void *stream);
 
 /*
+ * gdn_layer_prefill_backward_workspace_size -- bytes of device workspace
+ * gdn_layer_prefill_backward needs (host-only; 0 for invalid sizes):
+ * gdn_prefill_backward_workspace_size plus the recomputed gates, q, k, v, their
+ * gradients and per-run partial sums of the conv-weight gradient.
+ */
+size_t gdn_layer_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
+                                                 int d_v);
+
+/*
+ * gdn_layer_prefill_backward -- gradients of the layer's prefill from raw
+ * projections (gdn_layer_prefill: gates, conv prelude, recurrence) with respect
+ * to all its inputs.  [Local sec. 2.1] names a fused forward and backward GDN
+ * kernel; [Dissect sec. 2.1] the conv1d.weight, A_log and dt_bias weights
+ * trained with it.  The gates and the prelude are recomputed (as gdn_gates and
+ * gdn_conv_prelude form them), gdn_prefill_backward gives the gradients of q,
+ * k, v, g and beta, and these are carried back through the L2 norm, SiLU and
+ * conv, and through the gates:
+ *     da = -dg exp(A_log) sigmoid(a + dt_bias), ddt_bias = sum over tokens of da,
+ *     dA_log = sum over tokens of dg g,         db = dbeta beta (1 - beta).
+ * Sums over tokens are reduced in a fixed order (results are reproducible).
+ *
+ *   x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state, cu_seqlens,
+ *   N, T, H_qk, H_v, d_k, d_v, scale   the forward's inputs, as for gdn_layer_prefill
+ *   d_o             device bf16 [T][H_v][d_v]: gradient with respect to o
+ *   d_final_state   device fp32 [N][H_v][d_v][d_k], or NULL (zero)
+ *   dx_raw          device bf16 [T][C_raw] output
+ *   dconv_w         device fp32 [C_raw][4] output (tap order as conv_w)
+ *   da, db          device fp32 [T][H_v] outputs
+ *   dA_log, ddt_bias  device fp32 [H_v] outputs
+ *   d_initial_state device fp32 [N][H_v][d_v][d_k] output, or NULL to skip it
+ *   workspace       at least gdn_layer_prefill_backward_workspace_size(...) bytes
+ * Outputs and workspace must not overlap each other or any input.  T = 0
+ * writes zero dconv_w, dA_log, ddt_bias and d_initial_state = d_final_state
+ * (or zero).
+ */
+int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const float *a,
+                               const float *b, const float *A_log, const float *dt_bias,
+                               float l2_eps, const float *initial_state,
+                               const int32_t *cu_seqlens, const void *d_o,
+                               const float *d_final_state, int N, int T, int H_qk, int H_v,
+                               int d_k, int d_v, float scale, void *dx_raw, float *dconv_w,
+                               float *da, float *db, float *dA_log, float *ddt_bias,
+                               float *d_initial_state, void *workspace, size_t ws_bytes,
+                               void *stream);
+
+/*
  * gdn_gates -- the layer's gates from its raw per-token projections a, b:
  *     g    = -softplus(a + dt_bias[h]) * exp(A_log[h])   (log decay, a_t = exp(g))
  *     beta = sigmoid(b)

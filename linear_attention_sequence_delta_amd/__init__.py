@@ -30,6 +30,7 @@ GDN_BF16 = 1
 EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_workspace_size", "gdn_prefill", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_raw", "gdn_prefill_backward_workspace_size", "gdn_prefill_backward",
+           "gdn_layer_prefill_backward_workspace_size", "gdn_layer_prefill_backward",
            "gdn_gates", "gdn_layer_prefill_workspace_size",
            "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_multi_step",
            "gdn_state_rollback", "gdn_gated_norm", "gdn_decode_step")
@@ -72,6 +73,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P,
                                        P, P, P, Z, P]
     L.gdn_prefill_backward.restype = I
+    L.gdn_layer_prefill_backward_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_layer_prefill_backward_workspace_size.restype = Z
+    L.gdn_layer_prefill_backward.argtypes = [P, P, P, P, P, P, F, P, P, P, P, I, I, I, I, I, I, F,
+                                             P, P, P, P, P, P, P, P, Z, P]
+    L.gdn_layer_prefill_backward.restype = I
     L.gdn_gates.argtypes = [P, P, P, P, I, I, P, P, P]
     L.gdn_gates.restype = I
     L.gdn_layer_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -298,6 +304,75 @@ def gdn_prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_stat
                                     _ptr(workspace), ws_bytes, _stream(dev))
     _check(rc, "gdn_prefill_backward")
     return dq, dk, dv, dg, db, dS0
+
+
+def gdn_layer_prefill_backward_workspace_size(N: int, T: int, H_qk: int, H_v: int,
+                                              d_k: int = 128, d_v: int = 128) -> int:
+    return int(lib().gdn_layer_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+
+
+def gdn_layer_prefill_backward(x, conv_w, a, b, A_log, dt_bias, d_o, initial_state=None,
+                               d_final_state=None, cu_seqlens=None, *, H_qk: int = 16,
+                               H_v: int = 48, d_k: int = 128, d_v: int = 128,
+                               l2_eps: float = 1e-6, scale: float = 1.0, d_initial_state=True,
+                               workspace=None):
+    """Gradients of gdn_layer_prefill.  x: bf16 [T, C_raw]; conv_w: bf16
+    [C_raw, 4]; a, b: fp32 [T, H_v]; A_log, dt_bias: fp32 [H_v]; d_o: bf16
+    [T, H_v, d_v]; initial_state, d_final_state: fp32 [N, H_v, 128, 128] or None.
+    Returns (dx bf16, dconv_w fp32 [C_raw, 4], da, db, dA_log, ddt_bias,
+    d_initial_state or None)."""
+    torch = _torch()
+    dev = _device_of(x)
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, dev, 2)
+    _need(d_o, "d_o", torch.bfloat16, dev, 3)
+    T, C = x.shape
+    if C != (2 * H_qk + H_v) * d_k or tuple(conv_w.shape) != (C, 4):
+        raise ValueError("x / conv_w shapes do not match H_qk, H_v")
+    if tuple(d_o.shape) != (T, H_v, d_v):
+        raise ValueError("d_o must be [T, H_v, d_v]")
+    for t, name in ((a, "a"), (b, "b")):
+        _need(t, name, torch.float32, dev, 2)
+        if tuple(t.shape) != (T, H_v):
+            raise ValueError(f"{name} must be [T, H_v]")
+    for t, name in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _need(t, name, torch.float32, dev, 1)
+        if tuple(t.shape) != (H_v,):
+            raise ValueError(f"{name} must be [H_v]")
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    sshape = (N, H_v, d_v, d_k)
+    for t, name in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None:
+            _need(t, name, torch.float32, dev, 4)
+            if tuple(t.shape) != sshape:
+                raise ValueError(f"{name} must be {sshape}")
+    if d_initial_state is True:
+        dS0 = torch.empty(sshape, dtype=torch.float32, device=dev)
+    elif d_initial_state is None or d_initial_state is False:
+        dS0 = None
+    else:
+        dS0 = d_initial_state
+        _need(dS0, "d_initial_state", torch.float32, dev, 4)
+        if tuple(dS0.shape) != sshape:
+            raise ValueError(f"d_initial_state must be {sshape}")
+    dx = torch.empty_like(x)
+    dw = torch.empty((C, 4), dtype=torch.float32, device=dev)
+    da, db = torch.empty_like(a), torch.empty_like(b)
+    dA, ddt = torch.empty_like(A_log), torch.empty_like(dt_bias)
+    need = gdn_layer_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().gdn_layer_prefill_backward(
+        _ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), float(l2_eps),
+        _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), N, T, H_qk, H_v,
+        d_k, d_v, float(scale), _ptr(dx), _ptr(dw), _ptr(da), _ptr(db), _ptr(dA), _ptr(ddt),
+        _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
+    _check(rc, "gdn_layer_prefill_backward")
+    return dx, dw, da, db, dA, ddt, dS0
 
 
 def gdn_prefill_raw_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
@@ -604,6 +679,7 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_backward", "gdn_prefill_backward_workspace_size",
+           "gdn_layer_prefill_backward", "gdn_layer_prefill_backward_workspace_size",
            "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
            "gdn_layer_decode_step", "gdn_decode_multi_step", "gdn_state_rollback",
            "gdn_gated_norm", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_abi.cpp", "gdn_prelude.hip", "gdn_recurrent.hip", "gdn_chunked.hip",
-           "gdn_layer.hip", "gdn_checks.hip", "gdn_backward.hip"]
+           "gdn_layer.hip", "gdn_checks.hip", "gdn_backward.hip",
+           "gdn_layer_bwd.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -229,6 +229,27 @@ int check_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const
 
 }  // namespace
 
+namespace {
+// Backward of the layer: the workspace holds g, b, dg, dbeta, q, k, dq, dk,
+// v, dv, the dw partial sums and the gate-sum partials (each 256-byte
+// aligned), then the chunked backward's workspace.
+struct LayerBwdWs {
+    size_t g, q, v, part, gpart, total;
+};
+LayerBwdWs layer_bwd_ws(int N, int T, int H_qk, int H_v) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    LayerBwdWs w;
+    w.g = al((size_t)T * H_v * 4);
+    w.q = al((size_t)T * H_qk * gdn::kD * 2);
+    w.v = al((size_t)T * H_v * gdn::kD * 2);
+    w.part = al(gdn::prelude_bwd_partial_bytes(T, H_qk, H_v));
+    w.gpart = al(gdn::gates_bwd_partial_bytes(H_v));
+    w.total = 4 * w.g + 4 * w.q + 2 * w.v + w.part + w.gpart +
+              gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v);
+    return w;
+}
+}  // namespace
+
 extern "C" {
 
 int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
@@ -300,6 +321,89 @@ int gdn_prefill_backward(const void *q, const void *k, const void *v, const floa
                                                 H_qk, H_v, scale, d_o, d_final_state, dq, dk, dv,
                                                 dg, dbeta, d_initial_state, workspace, s);
     return finish(e, s, "gdn_prefill_backward launch");
+}
+
+size_t gdn_layer_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
+                                                 int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (N < 1 || T < 0 || H_qk < 1 || H_v < 1) return 0;
+    return layer_bwd_ws(N, T, H_qk, H_v).total;
+}
+
+int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const float *a,
+                               const float *b, const float *A_log, const float *dt_bias,
+                               float l2_eps, const float *initial_state,
+                               const int32_t *cu_seqlens, const void *d_o,
+                               const float *d_final_state, int N, int T, int H_qk, int H_v,
+                               int d_k, int d_v, float scale, void *dx_raw, float *dconv_w,
+                               float *da, float *db, float *dA_log, float *ddt_bias,
+                               float *d_initial_state, void *workspace, size_t ws_bytes,
+                               void *stream) {
+    int rc;
+    if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
+    if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
+    if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps))
+        return fail(GDN_ERR_INVALID_ARG, "l2_eps must be finite and >= 0");
+    if (H_v / H_qk > gdn::kMaxPrepGroup)
+        return fail(GDN_ERR_UNSUPPORTED, "bf16 prefill supports at most %d V-heads per QK head (got %d)",
+                    gdn::kMaxPrepGroup, H_v / H_qk);
+    if (!conv_w || !A_log || !dt_bias || !dconv_w || !dA_log || !ddt_bias)
+        return fail(GDN_ERR_INVALID_ARG,
+                    "conv_w, A_log, dt_bias, dconv_w, dA_log and ddt_bias must be non-NULL");
+    if (T > 0 && (!x_raw || !a || !b || !d_o || !dx_raw || !da || !db))
+        return fail(GDN_ERR_INVALID_ARG, "x_raw, a, b, d_o, dx_raw, da and db must be non-NULL");
+    const LayerBwdWs L = layer_bwd_ws(N, T, H_qk, H_v);
+    if (ws_bytes < L.total || !workspace)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, L.total);
+    const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
+    const size_t nx = (size_t)T * craw * 2, nw = craw * 4 * 2, nwf = craw * 4 * 4;
+    const size_t ng = (size_t)T * H_v * 4, nh = (size_t)H_v * 4, nv = (size_t)T * H_v * gdn::kD * 2;
+    const size_t ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
+    const struct { const void *p; size_t n; } in[] = {
+        {x_raw, nx}, {conv_w, nw}, {a, ng}, {b, ng}, {A_log, nh}, {dt_bias, nh},
+        {initial_state, ns}, {d_o, nv}, {d_final_state, ns}, {cu_seqlens, (size_t)(N + 1) * 4}};
+    const struct { const void *p; size_t n; } out[] = {
+        {dx_raw, nx}, {dconv_w, nwf}, {da, ng}, {db, ng}, {dA_log, nh}, {ddt_bias, nh},
+        {d_initial_state, ns}, {workspace, L.total}};
+    for (const auto &o : out) {
+        for (const auto &i : in)
+            if (overlaps(o.p, o.n, i.p, i.n))
+                return fail(GDN_ERR_INVALID_ARG, "gradients and workspace must not overlap any input");
+        for (const auto &o2 : out)
+            if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n))
+                return fail(GDN_ERR_INVALID_ARG, "gradients and workspace must not overlap each other");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
+    char *p = static_cast<char *>(workspace);
+    float *g = reinterpret_cast<float *>(p), *beta = reinterpret_cast<float *>(p + L.g);
+    float *dg = reinterpret_cast<float *>(p + 2 * L.g), *dbeta = reinterpret_cast<float *>(p + 3 * L.g);
+    p += 4 * L.g;
+    void *q = p, *k = p + L.q, *dq = p + 2 * L.q, *dk = p + 3 * L.q;
+    p += 4 * L.q;
+    void *v = p, *dv = p + L.v;
+    p += 2 * L.v;
+    float *part = reinterpret_cast<float *>(p);
+    float *gpart = reinterpret_cast<float *>(p + L.part);
+    void *rest = p + L.part + L.gpart;
+    hipError_t e = hipSuccess;
+    if (T > 0) {
+        if ((e = gdn::launch_gates(a, b, A_log, dt_bias, T, H_v, g, beta, s)) == hipSuccess)
+            e = gdn::launch_conv_prelude(x_raw, conv_w, cu_seqlens, N, T, H_qk, H_v, l2_eps, q, k, v, s);
+    }
+    if (e == hipSuccess)
+        e = gdn::launch_chunked_backward(q, k, v, g, beta, initial_state, cu_seqlens, N, T, H_qk, H_v,
+                                         scale, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                                         d_initial_state, rest, s);
+    if (e == hipSuccess)
+        e = gdn::launch_prelude_bwd(x_raw, conv_w, cu_seqlens, N, T, H_qk, H_v, l2_eps, dq, dk, dv,
+                                    dx_raw, dconv_w, part, s);
+    if (e == hipSuccess)
+        e = gdn::launch_gates_bwd(a, b, A_log, dt_bias, dg, dbeta, T, H_v, da, db, dA_log, ddt_bias,
+                                  gpart, s);
+    return finish(e, s, "gdn_layer_prefill_backward launch");
 }
 
 int gdn_gates(const float *a, const float *b, const float *A_log, const float *dt_bias, int T,

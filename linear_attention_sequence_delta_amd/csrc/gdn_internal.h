@@ -57,6 +57,20 @@ hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const vo
                            const void *dsw, const void *duw, void *dq, void *dk, float *dg,
                            float *dbeta, hipStream_t stream);
 
+// Gradients of the prelude (dx bf16, dw fp32 [C_raw][4]; `partial` holds
+// prelude_bwd_partial_bytes) and of the gates (da, db fp32 [T][H_v]; dA_log,
+// ddt_bias fp32 [H_v]; `partial` holds gates_bwd_partial_bytes).
+size_t prelude_bwd_partial_bytes(int T, int H_qk, int H_v);
+size_t gates_bwd_partial_bytes(int H_v);
+hipError_t launch_prelude_bwd(const void *x, const void *w, const int32_t *cu_seqlens, int N, int T,
+                              int H_qk, int H_v, float eps, const void *dq, const void *dk,
+                              const void *dv, void *dx, float *dw, float *partial,
+                              hipStream_t stream);
+hipError_t launch_gates_bwd(const float *a, const float *b, const float *A_log,
+                            const float *dt_bias, const float *dg, const float *dbeta, int T,
+                            int H_v, float *da, float *db, float *dA_log, float *ddt_bias,
+                            float *partial, hipStream_t stream);
+
 // The layer's forward from raw projections: gates, conv history, decode.
 hipError_t launch_gates(const float *a, const float *b, const float *A_log, const float *dt_bias,
                         int T, int H_v, float *g, float *beta, hipStream_t stream);

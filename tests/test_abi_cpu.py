@@ -243,3 +243,73 @@ def test_gated_norm_rejects_bad_arguments():
     assert L.gdn_gated_norm(big, 2 * big, 3 * big, 10, 128, 1e-6, big + 64, None) == gdn.GDN_ERR_INVALID_ARG
     assert L.gdn_gated_norm(big, 2 * big, 3 * big, 10, 128, 1e-6, 2 * big, None) == gdn.GDN_ERR_INVALID_ARG
     assert L.gdn_gated_norm(None, None, None, 0, 128, 1e-6, None, None) == gdn.GDN_OK
+
+
+def _backward(L, **kw):
+    """gdn_prefill_backward with fake (never dereferenced) device pointers that
+    do not overlap; the host checks reject before any device call."""
+    a = dict(q=0x10000000, k=0x20000000, v=0x30000000, g=0x40000000, beta=0x50000000, S0=None,
+             cu=None, d_o=0x60000000, dSf=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128,
+             scale=1.0, dq=0x70000000, dk=0x80000000, dv=0x90000000, dg=0xA0000000,
+             db=0xB0000000, dS0=None, ws=0xC0000000, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.gdn_prefill_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"],
+                                  a["d_o"], a["dSf"], a["N"], a["T"], a["H_qk"], a["H_v"],
+                                  a["d_k"], a["d_v"], a["scale"], a["dq"], a["dk"], a["dv"],
+                                  a["dg"], a["db"], a["dS0"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_k=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(H_v=47), gdn.GDN_ERR_INVALID_ARG),
+    (dict(H_qk=1, H_v=16), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dq=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(d_o=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), gdn.GDN_ERR_WORKSPACE),
+    (dict(ws=None), gdn.GDN_ERR_WORKSPACE),
+    (dict(dq=0x10000000), gdn.GDN_ERR_INVALID_ARG),            # dq overlaps q
+    (dict(dv=0x80000000), gdn.GDN_ERR_INVALID_ARG),            # dv overlaps dk
+    (dict(ws=0x60000000), gdn.GDN_ERR_INVALID_ARG),            # workspace overlaps d_o
+    (dict(N=2), gdn.GDN_ERR_INVALID_ARG),                      # N > 1 needs cu_seqlens
+])
+def test_prefill_backward_rejects_bad_arguments(kw, code):
+    assert _backward(gdn.lib(), **kw) == code
+
+
+def test_backward_workspace_sizes():
+    L = gdn.lib()
+    assert gdn.gdn_prefill_backward_workspace_size(1, 0, 16, 48) > 0
+    assert gdn.gdn_prefill_backward_workspace_size(0, 64, 16, 48) == 0
+    a = gdn.gdn_prefill_backward_workspace_size(1, 32768, 16, 48)
+    assert a > gdn.gdn_prefill_backward_workspace_size(1, 4096, 16, 48)
+    assert gdn.gdn_layer_prefill_backward_workspace_size(1, 32768, 16, 48) > a
+    assert L.gdn_layer_prefill_backward_workspace_size(1, -1, 16, 48, 128, 128) == 0
+
+
+def _layer_backward(L, **kw):
+    a = dict(x=0x10000000, w=0x18000000, a=0x20000000, b=0x28000000, A=0x30000000,
+             dt=0x30100000, eps=1e-6, S0=None, cu=None, d_o=0x40000000, dSf=None, N=1, T=64,
+             H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0, dx=0x50000000, dw=0x58000000,
+             da=0x60000000, db=0x68000000, dA=0x70000000, ddt=0x70100000, dS0=None,
+             ws=0x80000000, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.gdn_layer_prefill_backward(
+        a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"], a["S0"], a["cu"], a["d_o"],
+        a["dSf"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"], a["scale"], a["dx"],
+        a["dw"], a["da"], a["db"], a["dA"], a["ddt"], a["dS0"], a["ws"], a["ws_bytes"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_v=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(w=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dA=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dx=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), gdn.GDN_ERR_WORKSPACE),
+    (dict(dx=0x10000000), gdn.GDN_ERR_INVALID_ARG),            # dx overlaps x
+    (dict(db=0x60000000), gdn.GDN_ERR_INVALID_ARG),            # db overlaps da
+])
+def test_layer_backward_rejects_bad_arguments(kw, code):
+    assert _layer_backward(gdn.lib(), **kw) == code
