@@ -209,7 +209,27 @@ def run_gpu(steps, warmup, path="both"):
         b1.record()
         torch.cuda.synchronize()
         res["bwd_us"] = b0.elapsed_time(b1) / bsteps * 1e3
-        del q, k, v, d_o, wsb
+        del q, k, v, wsb
+        # the whole layer's backward from the raw projections
+        A_log = to_dev(p.meta["A_log"].astype(np.float32))
+        dtb = to_dev(p.meta["dt_bias"].astype(np.float32))
+        ra, rb = to_dev(p.meta["a"]), to_dev(p.meta["b"])
+        wsl = torch.empty(gdn.gdn_layer_prefill_backward_workspace_size(1, p.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
+
+        def layer_backward():
+            gdn.gdn_layer_prefill_backward(x, w, ra, rb, A_log, dtb, d_o, H_qk=H_QK, H_v=H_V,
+                                           workspace=wsl)
+
+        layer_backward()
+        torch.cuda.synchronize()
+        b0.record()
+        for _ in range(bsteps):
+            layer_backward()
+        b1.record()
+        torch.cuda.synchronize()
+        res["layer_bwd_us"] = b0.elapsed_time(b1) / bsteps * 1e3
+        del d_o, wsl
 
     # the output gate on the prefill's o (z ~ N(0, 1), norm weight ~ U(0.5, 1.5))
     gen = torch.Generator(device=dev)
@@ -540,7 +560,13 @@ def main():
                            "roofline": {"bound": "mfma", "achieved": btf,
                                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                         "frac": btf / PEAK_BF16_TFLOPS,
-                                        "algorithmic_flop_per_launch": bflops}}
+                                        "algorithmic_flop_per_launch": bflops},
+                           "layer": {"us": r["layer_bwd_us"],
+                                     "tokens_per_s": T / (r["layer_bwd_us"] * 1e-6),
+                                     "what": "gdn_layer_prefill_backward from the raw projections "
+                                             "(gates and prelude recomputed, the recurrence's "
+                                             "gradients, then through the prelude and gates): "
+                                             "dx, dconv_w, da, db, dA_log, ddt_bias"}}
     if "pre_us" in r:
         out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",
                                    "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
