@@ -58,9 +58,10 @@ def _load():
                                            P, P, P, P, I, I]
     lib.orc_prelude_backward.argtypes = [P, P, P, I, I, I, I, I, I, D, P, P, P, P, P]
     lib.orc_gates_backward.argtypes = [P, P, P, P, I, I, P, P, P, P, P, P]
+    lib.orc_gated_norm_backward.argtypes = [P, P, P, I, I, D, P, P, P, P]
     for f in (lib.orc_prelude, lib.orc_recurrent, lib.orc_chunked, lib.orc_decode_step,
               lib.orc_gates, lib.orc_gated_norm, lib.orc_recurrent_backward,
-              lib.orc_prelude_backward, lib.orc_gates_backward):
+              lib.orc_prelude_backward, lib.orc_gates_backward, lib.orc_gated_norm_backward):
         f.restype = I
     _lib = lib
     return lib
@@ -343,3 +344,18 @@ def gated_norm(o, z, w, eps=1e-6):
     _check(_load().orc_gated_norm(_ptr(np.ascontiguousarray(o)), _ptr(np.ascontiguousarray(z)),
                                   _ptr(w), R, dv, float(eps), _ptr(y)), "gated_norm")
     return y
+
+
+def gated_norm_backward(o, z, w, dy, eps=1e-6):
+    """Gradients of ``gated_norm`` with respect to o, z (shape of o) and w [d_v],
+    given dy (shape of o).  Returns fp64 (d_o, dz, dw)."""
+    o, z, w, dy = f64(o), f64(z), f64(w), f64(dy)
+    if o.shape != z.shape or dy.shape != o.shape or w.shape != (o.shape[-1],):
+        raise ValueError("gated_norm_backward shape mismatch")
+    dv = o.shape[-1]
+    R = o.size // dv
+    d_o, dz, dw = np.zeros(o.shape), np.zeros(o.shape), np.zeros(dv)
+    _check(_load().orc_gated_norm_backward(
+        _ptr(np.ascontiguousarray(o)), _ptr(np.ascontiguousarray(z)), _ptr(w), R, dv, float(eps),
+        _ptr(np.ascontiguousarray(dy)), _ptr(d_o), _ptr(dz), _ptr(dw)), "gated_norm_backward")
+    return d_o, dz, dw

@@ -745,4 +745,40 @@ int orc_gates_backward(const double *a, const double *b, const double *A_log,
     return ORC_OK;
 }
 
+/*
+ * Gradients of orc_gated_norm: given dy [R][dv], the gradients with respect
+ * to o, z [R][dv] and w [dv] (all overwritten).  Per row, with
+ * r = (mean(o^2) + eps)^(-1/2), n = o r, s = SiLU(z) and u = dy w s:
+ *     do = r (u - n mean(u n)),   dz = dy n w SiLU'(z),   dw += dy n s.
+ */
+int orc_gated_norm_backward(const double *o, const double *z, const double *w, int R, int dv,
+                            double eps, const double *dy, double *d_o, double *dz, double *dw)
+{
+    if (R < 0 || dv < 1)
+        return ORC_EINVAL;
+    for (int c = 0; c < dv; ++c)
+        dw[c] = 0.0;
+    for (int r = 0; r < R; ++r) {
+        const double *orow = o + (size_t)r * dv, *zrow = z + (size_t)r * dv;
+        const double *dyr = dy + (size_t)r * dv;
+        double ss = 0.0;
+        for (int c = 0; c < dv; ++c)
+            ss += orow[c] * orow[c];
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        double un = 0.0;
+        for (int c = 0; c < dv; ++c) {
+            const double sg = 1.0 / (1.0 + exp(-zrow[c]));
+            un += dyr[c] * w[c] * zrow[c] * sg * orow[c] * inv;
+        }
+        for (int c = 0; c < dv; ++c) {
+            const double sg = 1.0 / (1.0 + exp(-zrow[c]));
+            const double n = orow[c] * inv, s = zrow[c] * sg;
+            d_o[(size_t)r * dv + c] = inv * (dyr[c] * w[c] * s - n * un / dv);
+            dz[(size_t)r * dv + c] = dyr[c] * n * w[c] * sg * (1.0 + zrow[c] * (1.0 - sg));
+            dw[c] += dyr[c] * n * s;
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_version(void) { return 1; }

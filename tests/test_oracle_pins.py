@@ -642,6 +642,21 @@ def test_layer_backward_composition_equals_finite_differences(orc):
         np.testing.assert_allclose(got, fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
 
 
+def test_gated_norm_backward_equals_finite_differences(orc):
+    rng = np.random.default_rng(93)
+    o, z = rng.normal(0, 2, (4, 6)), rng.normal(0, 2, (4, 6))
+    w = rng.uniform(0.5, 1.5, 6)
+    Wy = rng.standard_normal((4, 6))
+
+    def loss(o, z, w):
+        return (orc.gated_norm(o, z, w, eps=1e-3) * Wy).sum()
+
+    got = orc.gated_norm_backward(o, z, w, Wy, eps=1e-3)
+    for ai in range(3):
+        fd = _fd(loss, [o, z, w], ai)
+        np.testing.assert_allclose(got[ai], fd, rtol=0, atol=1e-7 * max(1.0, np.abs(fd).max()))
+
+
 # ------------------------------------------------------------- size pins
 def test_sizes_printed_on_pages():
     """The layer shape and the fp32 state dtype reproduce the state and KV-cache
