@@ -247,7 +247,20 @@ def run_gpu(steps, warmup, path="both"):
     g1.record()
     torch.cuda.synchronize()
     res["gate_us"] = g0.elapsed_time(g1) / steps * 1e3
-    del z, y
+    # its backward (dy ~ N(0, 1))
+    gy = torch.randn(o.shape, generator=gen, device=dev).to(torch.bfloat16)
+    gws = torch.empty(max(int(gdn.lib().gdn_gated_norm_backward_workspace_size(o.numel() // D, D)), 1),
+                      dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        gdn.gdn_gated_norm_backward(o, z, wn, gy, workspace=gws)
+    torch.cuda.synchronize()
+    g0.record()
+    for _ in range(steps):
+        gdn.gdn_gated_norm_backward(o, z, wn, gy, workspace=gws)
+    g1.record()
+    torch.cuda.synchronize()
+    res["gate_bwd_us"] = g0.elapsed_time(g1) / steps * 1e3
+    del z, y, gy, gws
 
     # ---------------- decode workload: B = 256 over rotating 256-slot pools
     d = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
@@ -545,11 +558,18 @@ def main():
                                "new raw row, gates from raw a, b, the update, history shift"}},
     }
     gate_bytes = 3 * T * H_V * D * 2
+    gate_bwd_bytes = 5 * T * H_V * D * 2     # o, z, dy in; d_o, dz out
     out["output_gate"] = {"us": r["gate_us"], "what": "gdn_gated_norm on the prefill's o "
                           "(RMS norm per head, norm weight, SiLU(z)); not part of the step",
                           "roofline": {"bound": "hbm", "achieved": gate_bytes / (r["gate_us"] * 1e-6) / 1e9,
                                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                       "frac": gate_bytes / (r["gate_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}}
+                                       "frac": gate_bytes / (r["gate_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+                          "backward": {"us": r["gate_bwd_us"],
+                                       "what": "gdn_gated_norm_backward (d_o, dz, dw)",
+                                       "roofline": {"bound": "hbm",
+                                                    "achieved": gate_bwd_bytes / (r["gate_bwd_us"] * 1e-6) / 1e9,
+                                                    "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                                    "frac": gate_bwd_bytes / (r["gate_bwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}}}
     if "bwd_us" in r:
         bflops = BACKWARD_FLOP_PER_TOKEN * T
         btf = bflops / (r["bwd_us"] * 1e-6) / 1e12

@@ -366,6 +366,34 @@ int gdn_gated_norm(const void *o, const void *z, const float *w, int rows, int d
                    void *out, void *stream);
 
 /*
+ * gdn_gated_norm_backward_workspace_size -- bytes of device workspace
+ * gdn_gated_norm_backward needs (host-only; 0 for invalid sizes): the per-
+ * workgroup partial sums of dw, at most 512 KiB.
+ */
+size_t gdn_gated_norm_backward_workspace_size(int rows, int d_v);
+
+/*
+ * gdn_gated_norm_backward -- gradients of gdn_gated_norm with respect to o, z
+ * and w, given dy (the gradient with respect to its output).  Per row, with
+ * r = (mean(o^2) + eps)^(-1/2), n = o r, s = SiLU(z), u = dy w s:
+ *     d_o = r (u - n mean(u n)),  dz = dy n w SiLU'(z),  dw = sum over rows dy n s
+ * (dw reduced in a fixed order: results are reproducible).  The form of the
+ * gate is the reading of [Dissect sec. 2.1]'s norm and in_proj_z weights that
+ * gdn_gated_norm documents.
+ *
+ *   o, z, dy    device bf16 [rows][d_v]
+ *   w           device fp32 [d_v]
+ *   d_o, dz     device bf16 [rows][d_v] outputs
+ *   dw          device fp32 [d_v] output
+ *   workspace   at least gdn_gated_norm_backward_workspace_size(rows, d_v) bytes
+ * Outputs and workspace must not overlap each other or any input.  rows = 0
+ * writes dw = 0.
+ */
+int gdn_gated_norm_backward(const void *o, const void *z, const float *w, const void *dy,
+                            int rows, int d_v, float eps, void *d_o, void *dz, float *dw,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * gdn_decode_step -- one token for each of B sequences whose states live in a
  * slot pool; each addressed state is read once and overwritten in place.
  * [OOM sec. 1.2] per-token step (q, k, v, S_prev, gates) -> (o, S); the update

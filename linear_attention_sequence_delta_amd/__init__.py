@@ -33,7 +33,8 @@ EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_layer_prefill_backward_workspace_size", "gdn_layer_prefill_backward",
            "gdn_gates", "gdn_layer_prefill_workspace_size",
            "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_multi_step",
-           "gdn_state_rollback", "gdn_gated_norm", "gdn_decode_step")
+           "gdn_state_rollback", "gdn_gated_norm", "gdn_gated_norm_backward_workspace_size",
+           "gdn_gated_norm_backward", "gdn_decode_step")
 
 _lib = None
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
     L.gdn_state_rollback.restype = I
     L.gdn_gated_norm.argtypes = [P, P, P, I, I, F, P, P]
     L.gdn_gated_norm.restype = I
+    L.gdn_gated_norm_backward_workspace_size.argtypes = [I, I]
+    L.gdn_gated_norm_backward_workspace_size.restype = Z
+    L.gdn_gated_norm_backward.argtypes = [P, P, P, P, I, I, F, P, P, P, P, Z, P]
+    L.gdn_gated_norm_backward.restype = I
     L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_decode_step.restype = I
     _lib = L
@@ -676,10 +681,35 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, slot_idx, *, scale: float = 1.
     return o
 
 
+def gdn_gated_norm_backward(o, z, w, dy, *, eps: float = 1e-6, workspace=None):
+    """Gradients of gdn_gated_norm: o, z, dy bf16 [..., 128]; w fp32 [128].
+    Returns (d_o bf16, dz bf16, dw fp32 [128])."""
+    torch = _torch()
+    dev = _device_of(o)
+    for t, name in ((o, "o"), (z, "z"), (dy, "dy")):
+        if t.dtype != torch.bfloat16 or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor on {dev}")
+    if tuple(z.shape) != tuple(o.shape) or tuple(dy.shape) != tuple(o.shape) or o.shape[-1] != 128:
+        raise ValueError("o, z and dy must share a shape [..., 128]")
+    _need(w, "w", torch.float32, dev, 1)
+    rows = o.numel() // 128
+    d_o, dz = torch.empty_like(o), torch.empty_like(z)
+    dw = torch.empty((128,), dtype=torch.float32, device=dev)
+    need = int(lib().gdn_gated_norm_backward_workspace_size(rows, 128))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_gated_norm_backward(_ptr(o), _ptr(z), _ptr(w), _ptr(dy), rows, 128, float(eps),
+                                       _ptr(d_o), _ptr(dz), _ptr(dw), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, "gdn_gated_norm_backward")
+    return d_o, dz, dw
+
+
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_backward", "gdn_prefill_backward_workspace_size",
            "gdn_layer_prefill_backward", "gdn_layer_prefill_backward_workspace_size",
            "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
            "gdn_layer_decode_step", "gdn_decode_multi_step", "gdn_state_rollback",
-           "gdn_gated_norm", "gdn_decode_step", "GDN_F32", "GDN_BF16", "EXPORTS"]
+           "gdn_gated_norm", "gdn_gated_norm_backward", "gdn_decode_step", "GDN_F32", "GDN_BF16",
+           "EXPORTS"]

@@ -606,6 +606,40 @@ int gdn_gated_norm(const void *o, const void *z, const float *w, int rows, int d
     return finish(gdn::launch_gated_norm(o, z, w, rows, eps, out, s), s, "gdn_gated_norm launch");
 }
 
+size_t gdn_gated_norm_backward_workspace_size(int rows, int d_v) {
+    if (rows < 0 || d_v != gdn::kD) return 0;
+    return gdn::gated_norm_bwd_partial_bytes(rows);
+}
+
+int gdn_gated_norm_backward(const void *o, const void *z, const float *w, const void *dy,
+                            int rows, int d_v, float eps, void *d_o, void *dz, float *dw,
+                            void *workspace, size_t ws_bytes, void *stream) {
+    if (d_v != gdn::kD) return fail(GDN_ERR_UNSUPPORTED, "only d_v = 128 is built (got %d)", d_v);
+    if (rows < 0) return fail(GDN_ERR_INVALID_ARG, "rows must be >= 0 (got %d)", rows);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!w || !dw) return fail(GDN_ERR_INVALID_ARG, "w and dw must be non-NULL");
+    if (rows > 0 && (!o || !z || !dy || !d_o || !dz))
+        return fail(GDN_ERR_INVALID_ARG, "o, z, dy, d_o and dz must be non-NULL");
+    const size_t need = gdn_gated_norm_backward_workspace_size(rows, d_v);
+    if (ws_bytes < need || !workspace)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    const size_t n = (size_t)rows * gdn::kD * 2, nw = (size_t)gdn::kD * 4;
+    const struct { const void *p; size_t n; } in[] = {{o, n}, {z, n}, {w, nw}, {dy, n}};
+    const struct { const void *p; size_t n; } out[] = {{d_o, n}, {dz, n}, {dw, nw}, {workspace, need}};
+    for (const auto &x : out) {
+        for (const auto &i : in)
+            if (overlaps(x.p, x.n, i.p, i.n))
+                return fail(GDN_ERR_INVALID_ARG, "gradients and workspace must not overlap any input");
+        for (const auto &x2 : out)
+            if (&x2 != &x && overlaps(x.p, x.n, x2.p, x2.n))
+                return fail(GDN_ERR_INVALID_ARG, "gradients and workspace must not overlap each other");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(gdn::launch_gated_norm_bwd(o, z, w, dy, rows, eps, d_o, dz, dw,
+                                             static_cast<float *>(workspace), s),
+                  s, "gdn_gated_norm_backward launch");
+}
+
 int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                     const float *beta, float *state_pool, const int32_t *slot_idx, int B, int P,
                     int H_qk, int H_v, int d_k, int d_v, float scale, void *o, void *stream) {

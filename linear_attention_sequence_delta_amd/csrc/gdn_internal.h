@@ -62,6 +62,12 @@ hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const vo
 // ddt_bias fp32 [H_v]; `partial` holds gates_bwd_partial_bytes).
 size_t prelude_bwd_partial_bytes(int T, int H_qk, int H_v);
 size_t gates_bwd_partial_bytes(int H_v);
+// Gradients of the output gate (d_o, dz bf16; dw fp32 [128]; `partial` holds
+// gated_norm_bwd_partial_bytes).
+size_t gated_norm_bwd_partial_bytes(int rows);
+hipError_t launch_gated_norm_bwd(const void *o, const void *z, const float *w, const void *dy,
+                                 int rows, float eps, void *d_o, void *dz, float *dw,
+                                 float *partial, hipStream_t stream);
 hipError_t launch_prelude_bwd(const void *x, const void *w, const int32_t *cu_seqlens, int N, int T,
                               int H_qk, int H_v, float eps, const void *dq, const void *dk,
                               const void *dv, void *dx, float *dw, float *partial,

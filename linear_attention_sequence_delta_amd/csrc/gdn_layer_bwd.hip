@@ -15,6 +15,10 @@
 // and for the gates g = -softplus(a + dt_bias) exp(A_log), beta = sigmoid(b):
 //   da = -dg exp(A_log) sigmoid(a + dt_bias),  ddt_bias = sum_t da,
 //   dA_log = sum_t dg g,  db = dbeta beta (1 - beta).
+// The output gate after the recurrence (y = o r w SiLU(z) per (token, V-head)
+// row, r = (mean o^2 + eps)^(-1/2), the reading taken of the norm and in_proj_z
+// weights the first page lists) has, with n = o r, s = SiLU(z), u = dy w s:
+//   do = r (u - n mean(u n)),  dz = dy n w SiLU'(z),  dw = sum over rows dy n s.
 // All HBM-bound elementwise work; the sums over tokens go through per-run
 // partials reduced in a fixed order (no atomics: results are reproducible).
 #include "gdn_device.h"
@@ -280,7 +284,86 @@ __global__ __launch_bounds__(64) void gates_sum_splits_kernel(const float *__res
     ddt_bias[h] = s2;
 }
 
+// Output gate: 16 lanes per 128-channel row (8 channels each, the forward's
+// layout), 16 rows per pass of a 256-thread workgroup, the grid striding over
+// the rows; each workgroup's share of dw goes to partial [block][128].
+constexpr int kGateNormBlocks = 1024;
+__global__ __launch_bounds__(256) void gated_norm_bwd_kernel(
+    const uint16_t *__restrict__ o, const uint16_t *__restrict__ z, const float *__restrict__ w,
+    const uint16_t *__restrict__ dy, int rows, float eps, uint16_t *__restrict__ d_o,
+    uint16_t *__restrict__ dz, float *__restrict__ partial) {
+    __shared__ float part[16][kD];
+    const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
+    const float4 w0 = *reinterpret_cast<const float4 *>(w + 8 * cg);
+    const float4 w1 = *reinterpret_cast<const float4 *>(w + 8 * cg + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int base = blockIdx.x * 16; base < rows; base += gridDim.x * 16) {
+        const int row = base + rg;
+        const bool ok = row < rows;
+        const size_t off = (size_t)min(row, rows - 1) * kD + 8 * cg;   // whole DPP rows stay active
+        float ov[8], zv[8], gv[8];
+        unpack8(*reinterpret_cast<const uint4 *>(o + off), ov);
+        unpack8(*reinterpret_cast<const uint4 *>(z + off), zv);
+        unpack8(*reinterpret_cast<const uint4 *>(dy + off), gv);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(ov[e], ov[e], ss);
+        const float inv = rsqrtf(row16_sum(ss) * (1.f / kD) + eps);
+        float n[8], sg[8], u[8], un = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            n[e] = ov[e] * inv;
+            sg[e] = 1.f / (1.f + __expf(-zv[e]));
+            u[e] = gv[e] * wv[e] * (zv[e] * sg[e]);
+            un = __builtin_fmaf(u[e], n[e], un);
+        }
+        const float m = row16_sum(un) * (1.f / kD);
+        float go[8], gz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            go[e] = inv * (u[e] - n[e] * m);
+            gz[e] = gv[e] * n[e] * wv[e] * sg[e] * (1.f + zv[e] * (1.f - sg[e]));
+            if (ok) acc[e] = __builtin_fmaf(gv[e] * n[e], zv[e] * sg[e], acc[e]);
+        }
+        if (ok) {
+            *reinterpret_cast<uint4 *>(d_o + off) = pack_bf8(go);
+            *reinterpret_cast<uint4 *>(dz + off) = pack_bf8(gz);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg][8 * cg + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < kD) {
+        float s = 0.f;
+        for (int r = 0; r < 16; ++r) s += part[r][threadIdx.x];
+        partial[(size_t)blockIdx.x * kD + threadIdx.x] = s;
+    }
+}
+
 }  // namespace
+
+size_t gated_norm_bwd_partial_bytes(int rows) {
+    const int blocks = max(1, min(kGateNormBlocks, (rows + 15) / 16));
+    return (size_t)blocks * kD * sizeof(float);
+}
+
+hipError_t launch_gated_norm_bwd(const void *o, const void *z, const float *w, const void *dy,
+                                 int rows, float eps, void *d_o, void *dz, float *dw,
+                                 float *partial, hipStream_t stream) {
+    const int blocks = max(1, min(kGateNormBlocks, (rows + 15) / 16));
+    if (rows > 0) {
+        hipLaunchKernelGGL(gated_norm_bwd_kernel, dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(z), w,
+                           static_cast<const uint16_t *>(dy), rows, eps, static_cast<uint16_t *>(d_o),
+                           static_cast<uint16_t *>(dz), partial);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(sum_runs_kernel, dim3((kD + 63) / 64), dim3(256), 0, stream, partial,
+                       rows > 0 ? blocks : 0, kD, dw);
+    return hipGetLastError();
+}
 
 size_t gates_bwd_partial_bytes(int H_v) { return (size_t)kGateSplits * H_v * 2 * sizeof(float); }
 

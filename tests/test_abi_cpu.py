@@ -313,3 +313,28 @@ def _layer_backward(L, **kw):
 ])
 def test_layer_backward_rejects_bad_arguments(kw, code):
     assert _layer_backward(gdn.lib(), **kw) == code
+
+
+def test_gated_norm_backward_rejects_bad_arguments():
+    L = gdn.lib()
+    o, z, w, dy, d_o, dz, dw, ws = (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000,
+                                    0x60000000, 0x70000000, 0x80000000)
+
+    def call(**kw):
+        a = dict(o=o, z=z, w=w, dy=dy, rows=64, d_v=128, eps=1e-6, d_o=d_o, dz=dz, dw=dw, ws=ws,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return L.gdn_gated_norm_backward(a["o"], a["z"], a["w"], a["dy"], a["rows"], a["d_v"],
+                                         a["eps"], a["d_o"], a["dz"], a["dw"], a["ws"],
+                                         a["ws_bytes"], None)
+
+    assert call(d_v=64) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(rows=-1) == gdn.GDN_ERR_INVALID_ARG
+    assert call(eps=float("inf")) == gdn.GDN_ERR_INVALID_ARG
+    assert call(dw=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(dy=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(ws_bytes=8) == gdn.GDN_ERR_WORKSPACE
+    assert call(d_o=o) == gdn.GDN_ERR_INVALID_ARG              # d_o overlaps o
+    assert call(dz=d_o) == gdn.GDN_ERR_INVALID_ARG             # dz overlaps d_o
+    assert L.gdn_gated_norm_backward_workspace_size(64, 128) > 0
+    assert L.gdn_gated_norm_backward_workspace_size(64, 64) == 0

@@ -81,3 +81,22 @@ def test_layer_backward_zero_length():
     torch.cuda.synchronize()
     assert not out[1].any() and not out[4].any() and not out[5].any()
     assert np.array_equal(out[6].cpu().numpy(), dSf)
+
+
+@pytest.mark.parametrize("rows", [1, 17, 48 * 700, 48 * 4000])
+def test_gated_norm_backward_against_oracle(rows):
+    """The output gate's gradients on bf16 rows of 128 (48 * 4000 rows take the
+    grid-stride loop several times)."""
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    rng = np.random.default_rng(rows + 5)
+    o = synth.bf16_bits(rng.normal(0, 2, (rows, 128)).astype(np.float32))
+    z = synth.bf16_bits(rng.normal(0, 2, (rows, 128)).astype(np.float32))
+    dy = synth.bf16_bits(rng.normal(0, 1, (rows, 128)).astype(np.float32))
+    w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    d_o, dz, dw = gdn.gdn_gated_norm_backward(dev(o), dev(z), dev(w), dev(dy))
+    torch.cuda.synchronize()
+    r_o, r_z, r_w = oracle.gated_norm_backward(o, z, w, dy)
+    assert_close(host(d_o), r_o, TOL_BF16, "d_o")
+    assert_close(host(dz), r_z, TOL_BF16, "dz")
+    assert_close(host(dw), r_w, TOL_BF16, "dw")
