@@ -64,13 +64,30 @@ __device__ __forceinline__ void unpack4(uint2 u, float *f) {
     f[2] = __uint_as_float(u.y << 16);
     f[3] = __uint_as_float(u.y & 0xFFFF0000u);
 }
-__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
-    float x[8], y[8], s = 0.f;
-    unpack8(a, x);
-    unpack8(b, y);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(x[e], y[e], s);
-    return s;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// sum of the 8 products of two 8-wide bf16 pieces, plus acc (packed dot products)
+__device__ __forceinline__ float dot8_acc(uint4 a, uint4 b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
+    return acc;
+}
+// Column sums of a 16-row tile held in the MFMA result layout: x[j] is row
+// c, column 4 g4 + j of the lane (c, g4).  After the exchange, lanes with
+// c % 4 == 0 hold the sum over the 16 rows for column 4 g4 + c / 4 (the
+// lanes exchange half of what they hold with row_mirror, then half again
+// with row_half_mirror, then sum each group of four).
+__device__ __forceinline__ float col16_sums(f32x4 x, int c) {
+    const bool h8 = c & 8, h4 = c & 4;
+#define GDN_DPP(v, ctl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctl, 0xF, 0xF, false))
+    const float y0 = (h8 ? x[2] : x[0]) + GDN_DPP(h8 ? x[0] : x[2], 0x140);
+    const float y1 = (h8 ? x[3] : x[1]) + GDN_DPP(h8 ? x[1] : x[3], 0x140);
+    float z = (h4 ? y1 : y0) + GDN_DPP(h4 ? y0 : y1, 0x141);
+    z += GDN_DPP(z, 0xB1);
+    z += GDN_DPP(z, 0x4E);
+#undef GDN_DPP
+    return z;
 }
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -388,7 +405,10 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
 // Every row-wise result is held with lane (c, g4) on the row 16 (w % 4) + c,
 // columns 16 t + 4 g4 .. +3 of each tile t, which an MFMA gives when the left
 // factor's rows are its B operand and the right factor's columns its A
-// operand.
+// operand.  A V-head's inputs are read in whole rows (every load instruction
+// covers whole cache lines) and staged in LDS, each once for both halves; the
+// column sums of the dG and db terms stay in registers until the end of the
+// step and are reduced across the 16 rows of a tile by one exchange pass.
 __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ d_o, const uint16_t *__restrict__ dv, const float *__restrict__ beta,
@@ -400,7 +420,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sSt[kD * kKP];      // S, then dS' ([v][k])
     __shared__ __attribute__((aligned(16))) uint16_t sR[kChunk * kKP];   // R [r][v]
-    __shared__ __attribute__((aligned(16))) uint16_t sU[kChunk * kKP];   // U [r][v]
+    __shared__ __attribute__((aligned(16))) uint16_t sU[kChunk * kKP];   // dR, then U [r][v]
+    __shared__ __attribute__((aligned(16))) uint16_t sDO[kChunk * kKP];  // dO [r][v]
     __shared__ __attribute__((aligned(16))) uint16_t sT[kChunk * kRP];   // T
     __shared__ __attribute__((aligned(16))) uint16_t sM[kChunk * kRP];   // M_P, then M_A'
     __shared__ __attribute__((aligned(16))) uint16_t sM2[kChunk * kRP];  // dT
@@ -424,7 +445,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const int lane = tid & 63, g4 = lane >> 4, c = lane & 15;
     const int row = 16 * w + c;                        // this lane's row
     const bool row_ok = row < L;
-    const int rr = min(row, L - 1);
     const int wb = w >> 1;                             // 32-row block of this wave's rows
 
 #pragma unroll
@@ -445,14 +465,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         for (int s = 0; s < 4; ++s) a = mfma32(frag_rows(sK, kKP, 16 * t, 32 * s, ol), frag_rows(M, kKP, 16 * w, 32 * s, ol), a);
         return a;
     };
-    // the 16-lane column sums of x (one per column 16 t + 4 g4 + j) into dst
-    auto col_sums = [&](f32x4 x, float *dst, int t, bool add) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float y = row16_sum(x[j]);
-            if (c == 0) dst[16 * t + 4 * g4 + j] = add ? dst[16 * t + 4 * g4 + j] + y : y;
-        }
-    };
     f32x4 dQa[4], dKa[4];                              // columns 16 (4 hf + i) + 4 g4 + j
 #pragma unroll
     for (int i = 0; i < 4; ++i) dQa[i] = dKa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -468,63 +480,60 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         asm volatile("" : "+v"(ol));
         const int c = ol & 15, g4 = ol >> 4, tid = 64 * wave + ol;
         const int row = 16 * w + c;
-        const bool row_ok = row < L;
-        const int rr = min(row, L - 1);
         const uint16_t *brec = bws + ((size_t)gc * H_v + h) * kBwdRecElems;
         const uint16_t *Sg = states + ((size_t)gc * H_v + h) * (kD * kD);
         const uint16_t *dSg = dsw + ((size_t)gc * H_v + h) * (kD * kD);
-        // this V-head's inputs in flight together: T, S (into LDS) and dS' (for
-        // <dS', S>), G, b; V at this lane's result positions; the rows `row` of
-        // dO and dR as MFMA operands (columns 32 s + 8 g4 .. +7)
-        uint4 dOf[4], dVf[4];
-        uint2 vr[4];
+        // this V-head's inputs in flight together, all in whole rows: T, S,
+        // G, b, and the rows of dO, dR and V (rows past the chunk's end read
+        // as zero), written into LDS after the previous V-head's reads
         float e1 = 0.f;                                // this thread's share of <dS', S>
         {
             const u32x4 tv = *reinterpret_cast<const u32x4 *>(brec + kBwdTOff + (tid >> 3) * kChunk + 8 * (tid & 7));
-            u32x4 sv[4], dsv[4];
+            u32x4 sv[4], ov[2], rv[2], xv[2];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int e = tid + 512 * m;
                 sv[m] = *reinterpret_cast<const u32x4 *>(Sg + (e >> 4) * kD + 8 * (e & 15));
-                dsv[m] = *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int e = tid + 512 * m;
+                const size_t off = ((size_t)(c0 + min(e >> 4, L - 1)) * H_v + h) * kD + 8 * (e & 15);
+                ov[m] = *reinterpret_cast<const u32x4 *>(d_o + off);
+                rv[m] = *reinterpret_cast<const u32x4 *>(dv + off);
+                xv[m] = *reinterpret_cast<const u32x4 *>(v + off);
             }
             float gl = 0.f, bl = 0.f;
             if (tid < kChunk) {
                 gl = reinterpret_cast<const float *>(brec + kBwdGOff)[tid];
                 bl = tid < L ? beta[(size_t)(c0 + tid) * H_v + h] : 0.f;
             }
-            const size_t ro = ((size_t)(c0 + rr) * H_v + h) * kD;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                dOf[s] = *reinterpret_cast<const uint4 *>(d_o + ro + 32 * s + 8 * g4);
-                dVf[s] = *reinterpret_cast<const uint4 *>(dv + ro + 32 * s + 8 * g4);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const uint2 *>(v + ro + 16 * (4 * hf + i) + 4 * g4);
             __syncthreads();                           // the previous V-head's LDS reads are done
             *reinterpret_cast<u32x4 *>(sT + (tid >> 3) * kRP + 8 * (tid & 7)) = tv;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int e = tid + 512 * m;
                 *reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15)) = sv[m];
-                e1 += dot8(__builtin_bit_cast(uint4, sv[m]), __builtin_bit_cast(uint4, dsv[m]));
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int e = tid + 512 * m, r = e >> 4, o = r * kKP + 8 * (e & 15);
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(sDO + o) = r < L ? ov[m] : z;
+                *reinterpret_cast<u32x4 *>(sU + o) = r < L ? rv[m] : z;
+                *reinterpret_cast<u32x4 *>(sR + o) = r < L ? xv[m] : z;
             }
             if (tid < kChunk) {
                 sG[tid] = gl;
                 sB[tid] = bl;
             }
         }
-        if (!row_ok) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dOf[s] = dVf[s] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = make_uint2(0, 0);
-        }
         __syncthreads();
 
         const float Gr = sG[row], GLast = sG[kChunk - 1];
         const float gam = __expf(Gr), lam = __expf(GLast - Gr), br = sB[row];
         float rowG = 0.f, rowB = 0.f, e2 = 0.f;
+        f32x4 colG[2], colB[2];                        // column-sum terms of the wave's two tiles
 
         // X = K S^T -> R = V - diag(gamma) X
 #pragma unroll
@@ -534,7 +543,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) x = mfma32(frag_rows(sSt, kKP, 16 * nt, 32 * s, ol), frag_rows(sK, kKP, 16 * w, 32 * s, ol), x);
             float vf[4];
-            unpack4(vr[i], vf);
+            unpack4(*reinterpret_cast<const uint2 *>(sR + row * kKP + 16 * nt + 4 * g4), vf);
             *reinterpret_cast<uint2 *>(sR + row * kKP + 16 * nt + 4 * g4) =
                 pk4(vf[0] - gam * x[0], vf[1] - gam * x[1], vf[2] - gam * x[2], vf[3] - gam * x[3]);
         }
@@ -547,8 +556,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const uint4 sf = frag_cols(sSt, kKP, 32 * s, 16 * kt, ol);
-                a1 = mfma32(sf, dOf[s], a1);
-                a2 = mfma32(sf, dVf[s], a2);
+                a1 = mfma32(sf, frag_rows(sDO, kKP, 16 * w, 32 * s, ol), a1);
+                a2 = mfma32(sf, frag_rows(sU, kKP, 16 * w, 32 * s, ol), a2);
             }
             float qf[4], kf[4];
             unpack4(*reinterpret_cast<const uint2 *>(sQ + row * kKP + 16 * kt + 4 * g4), qf);
@@ -563,17 +572,30 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 rowG -= u * kf[j];
             }
         }
+        // the row-dot terms are finished here: left to the compiler they sink
+        // to the end of the step and hold the products in registers until then
+        asm volatile("" : "+v"(rowG));
         __syncthreads();                               // R complete; S no longer read
         uint4 dUf[4];                                  // row `row` of dU, columns 32 s + 8 g4 .. +7
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             dUf[s] = *reinterpret_cast<const uint4 *>(duw + (((size_t)gc * kChunk + row) * H_v + h) * kD + 32 * s + 8 * g4);
+        {
+            u32x4 dsv[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = tid + 512 * m;
-            *reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15)) =
-                *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
+            for (int m = 0; m < 4; ++m) {
+                const int e = tid + 512 * m;
+                dsv[m] = *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = tid + 512 * m;
+                u32x4 *p = reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15));
+                e1 = dot8_acc(__builtin_bit_cast(uint4, *p), __builtin_bit_cast(uint4, dsv[m]), e1);
+                *p = dsv[m];
+            }
         }
+        asm volatile("" : "+v"(e1));
         // U = T' R (T'[row][i] = T[row][i] b_i)
         {
             uint4 tB[2];
@@ -622,7 +644,11 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 }
             }
         }
+        asm volatile("" : "+v"(rowG), "+v"(e2));
         // dP = dO U^T -> M_P; dT' = dU R^T -> dT; row and column sums
+        uint4 dOf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dOf[s] = frag_rows(sDO, kKP, 16 * w, 32 * s, ol);
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             const int t = 2 * ti + hf;
@@ -641,21 +667,18 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
             float tf[4];
             unpack4(*reinterpret_cast<const uint2 *>(sT + row * kRP + 16 * t + 4 * g4), tf);
             float mp[4], dt[4];
-            f32x4 cg, cb;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool lo = 16 * t + 4 * g4 + j <= row;
                 mp[j] = lo ? dp[j] * scale * __expf(Gr - gi[j]) : 0.f;
                 const float wp = lo ? mp[j] * qk[j] : 0.f;
                 rowG += wp;
-                cg[j] = -wp;
+                colG[ti][j] = -wp;
                 dt[j] = lo ? dtp[j] * bi[j] : 0.f;
-                cb[j] = lo ? dtp[j] * tf[j] : 0.f;
+                colB[ti][j] = lo ? dtp[j] * tf[j] : 0.f;
             }
             *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(mp[0], mp[1], mp[2], mp[3]);
             *reinterpret_cast<uint2 *>(sM2 + row * kRP + 16 * t + 4 * g4) = pk4(dt[0], dt[1], dt[2], dt[3]);
-            col_sums(cg, sColG[w], t, false);
-            col_sums(cb, sColB[w], t, false);
         }
         __syncthreads();                               // M_P, dT complete
 
@@ -711,7 +734,6 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                 const float4 Gj = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
                 const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
                 float ma[4];
-                f32x4 cg;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const bool lo = 16 * t + 4 * g4 + j < row;
@@ -720,11 +742,10 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
                     rowB += m * kkv;
                     const float wa = m * br * kkv;
                     rowG += wa;
-                    cg[j] = -wa;
+                    colG[ti][j] -= wa;
                     ma[j] = m * br;
                 }
                 *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(ma[0], ma[1], ma[2], ma[3]);
-                col_sums(cg, sColG[w], t, true);
             }
         }
         rowG += __shfl_xor(rowG, 16, 64);
@@ -734,6 +755,14 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         if (g4 == 0) {
             sRowG[hf][row] = rowG;
             sRowB[hf][row] = rowB;
+        }
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            const float zg = col16_sums(colG[ti], c), zb = col16_sums(colB[ti], c);
+            if ((c & 3) == 0) {
+                sColG[w][16 * (2 * ti + hf) + 4 * g4 + (c >> 2)] = zg;
+                sColB[w][16 * (2 * ti + hf) + 4 * g4 + (c >> 2)] = zb;
+            }
         }
         {
             const float ew = wave_sum(__expf(GLast) * e1 + e2);
