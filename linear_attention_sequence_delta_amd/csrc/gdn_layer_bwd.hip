@@ -200,18 +200,26 @@ __global__ __launch_bounds__(256) void prelude_bwd_kernel(
     for (int e = 0; e < 8; ++e) pp[e] = make_float4(dwacc[0][e], dwacc[1][e], dwacc[2][e], dwacc[3][e]);
 }
 
-// dw[i] = sum over runs of partial[run][i], i over C_raw * 4: wave j of a
-// workgroup sums the runs r = j mod 4 for 64 consecutive i (in run order),
-// then the four sums are added in wave order.
+// dw[i] = sum over runs of partial[run][i]: wave j of a workgroup takes the
+// runs r = j mod 4 for 64 consecutive i, spread over eight running sums (run
+// r + 4 k of each group of 32 into sum k, the leftover runs into sum 0) so
+// that eight loads are in flight; the sums and then the four waves are added
+// in a fixed order.
 __global__ __launch_bounds__(256) void sum_runs_kernel(const float *__restrict__ partial, int runs,
                                                        int n, float *__restrict__ out) {
     __shared__ float part[4][64];
     const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
     const int i = blockIdx.x * 64 + lane;
-    float acc = 0.f;
-    if (i < n)
-        for (int r = j; r < runs; r += 4) acc += partial[(size_t)r * n + i];
-    part[j][lane] = acc;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (i < n) {
+        int r = j;
+        for (; r + 28 < runs; r += 32) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] += partial[(size_t)(r + 4 * k) * n + i];
+        }
+        for (; r < runs; r += 4) a[0] += partial[(size_t)r * n + i];
+    }
+    part[j][lane] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     __syncthreads();
     if (j == 0 && i < n) out[i] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
@@ -285,50 +293,72 @@ __global__ __launch_bounds__(64) void gates_sum_splits_kernel(const float *__res
 }
 
 // Output gate: 16 lanes per 128-channel row (8 channels each, the forward's
-// layout), 16 rows per pass of a 256-thread workgroup, the grid striding over
-// the rows; each workgroup's share of dw goes to partial [block][128].
-constexpr int kGateNormBlocks = 1024;
+// layout), 16 rows per step of a 256-thread workgroup, two steps' rows loaded
+// before either is computed, the grid striding over the rows; each
+// workgroup's share of dw goes to partial [block][128].  The rows are read
+// and written once, with non-temporal loads and stores.
+constexpr int kGateNormBlocks = 512;
+constexpr int kGateNormSteps = 2;
 __global__ __launch_bounds__(256) void gated_norm_bwd_kernel(
     const uint16_t *__restrict__ o, const uint16_t *__restrict__ z, const float *__restrict__ w,
     const uint16_t *__restrict__ dy, int rows, float eps, uint16_t *__restrict__ d_o,
     uint16_t *__restrict__ dz, float *__restrict__ partial) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     __shared__ float part[16][kD];
     const int cg = threadIdx.x & 15, rg = threadIdx.x >> 4;
     const float4 w0 = *reinterpret_cast<const float4 *>(w + 8 * cg);
     const float4 w1 = *reinterpret_cast<const float4 *>(w + 8 * cg + 4);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int base = blockIdx.x * 16; base < rows; base += gridDim.x * 16) {
-        const int row = base + rg;
-        const bool ok = row < rows;
-        const size_t off = (size_t)min(row, rows - 1) * kD + 8 * cg;   // whole DPP rows stay active
-        float ov[8], zv[8], gv[8];
-        unpack8(*reinterpret_cast<const uint4 *>(o + off), ov);
-        unpack8(*reinterpret_cast<const uint4 *>(z + off), zv);
-        unpack8(*reinterpret_cast<const uint4 *>(dy + off), gv);
-        float ss = 0.f;
+    auto ld = [](const uint16_t *p) {
+        const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+        return make_uint4(x.x, x.y, x.z, x.w);
+    };
+    auto st = [](uint16_t *p, uint4 x) {
+        __builtin_nontemporal_store(v4u{x.x, x.y, x.z, x.w}, reinterpret_cast<v4u *>(p));
+    };
+    for (int base = blockIdx.x * 16 * kGateNormSteps; base < rows; base += gridDim.x * 16 * kGateNormSteps) {
+        uint4 ou[kGateNormSteps], zu[kGateNormSteps], gu[kGateNormSteps];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(ov[e], ov[e], ss);
-        const float inv = rsqrtf(row16_sum(ss) * (1.f / kD) + eps);
-        float n[8], sg[8], u[8], un = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            n[e] = ov[e] * inv;
-            sg[e] = 1.f / (1.f + __expf(-zv[e]));
-            u[e] = gv[e] * wv[e] * (zv[e] * sg[e]);
-            un = __builtin_fmaf(u[e], n[e], un);
+        for (int u = 0; u < kGateNormSteps; ++u) {
+            const size_t off = (size_t)min(base + 16 * u + rg, rows - 1) * kD + 8 * cg;   // whole DPP rows stay active
+            ou[u] = ld(o + off);
+            zu[u] = ld(z + off);
+            gu[u] = ld(dy + off);
         }
-        const float m = row16_sum(un) * (1.f / kD);
-        float go[8], gz[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            go[e] = inv * (u[e] - n[e] * m);
-            gz[e] = gv[e] * n[e] * wv[e] * sg[e] * (1.f + zv[e] * (1.f - sg[e]));
-            if (ok) acc[e] = __builtin_fmaf(gv[e] * n[e], zv[e] * sg[e], acc[e]);
-        }
-        if (ok) {
-            *reinterpret_cast<uint4 *>(d_o + off) = pack_bf8(go);
-            *reinterpret_cast<uint4 *>(dz + off) = pack_bf8(gz);
+        for (int u = 0; u < kGateNormSteps; ++u) {
+            const int row = base + 16 * u + rg;
+            const bool ok = row < rows;
+            const size_t off = (size_t)min(row, rows - 1) * kD + 8 * cg;
+            float ov[8], zv[8], gv[8];
+            unpack8(ou[u], ov);
+            unpack8(zu[u], zv);
+            unpack8(gu[u], gv);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(ov[e], ov[e], ss);
+            const float inv = rsqrtf(row16_sum(ss) * (1.f / kD) + eps);
+            float n[8], sg[8], uu[8], un = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                n[e] = ov[e] * inv;
+                sg[e] = 1.f / (1.f + __expf(-zv[e]));
+                uu[e] = gv[e] * wv[e] * (zv[e] * sg[e]);
+                un = __builtin_fmaf(uu[e], n[e], un);
+            }
+            const float m = row16_sum(un) * (1.f / kD);
+            float go[8], gz[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                go[e] = inv * (uu[e] - n[e] * m);
+                gz[e] = gv[e] * n[e] * wv[e] * sg[e] * (1.f + zv[e] * (1.f - sg[e]));
+                if (ok) acc[e] = __builtin_fmaf(gv[e] * n[e], zv[e] * sg[e], acc[e]);
+            }
+            if (ok) {
+                st(d_o + off, pack_bf8(go));
+                st(dz + off, pack_bf8(gz));
+            }
         }
     }
 #pragma unroll
@@ -344,14 +374,14 @@ __global__ __launch_bounds__(256) void gated_norm_bwd_kernel(
 }  // namespace
 
 size_t gated_norm_bwd_partial_bytes(int rows) {
-    const int blocks = max(1, min(kGateNormBlocks, (rows + 15) / 16));
+    const int blocks = max(1, min(kGateNormBlocks, (rows + 16 * kGateNormSteps - 1) / (16 * kGateNormSteps)));
     return (size_t)blocks * kD * sizeof(float);
 }
 
 hipError_t launch_gated_norm_bwd(const void *o, const void *z, const float *w, const void *dy,
                                  int rows, float eps, void *d_o, void *dz, float *dw,
                                  float *partial, hipStream_t stream) {
-    const int blocks = max(1, min(kGateNormBlocks, (rows + 15) / 16));
+    const int blocks = max(1, min(kGateNormBlocks, (rows + 16 * kGateNormSteps - 1) / (16 * kGateNormSteps)));
     if (rows > 0) {
         hipLaunchKernelGGL(gated_norm_bwd_kernel, dim3(blocks), dim3(256), 0, stream,
                            static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(z), w,
