@@ -148,7 +148,9 @@ __global__ __launch_bounds__(256) void prelude_bwd_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float sg = 1.f / (1.f + __expf(-yc[e]));
+                // the same reciprocal as silu(), so the exponential and the
+                // reciprocal are shared with the recomputed forward
+                const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-yc[e]));
                 dy[e] = da[e] * sg * (1.f + yc[e] * (1.f - sg));
             }
             if (t < t1) {
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(256) void gated_norm_bwd_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 n[e] = ov[e] * inv;
-                sg[e] = 1.f / (1.f + __expf(-zv[e]));
+                sg[e] = __builtin_amdgcn_rcpf(1.f + __expf(-zv[e]));
                 uu[e] = gv[e] * wv[e] * (zv[e] * sg[e]);
                 un = __builtin_fmaf(uu[e], n[e], un);
             }
