@@ -41,6 +41,32 @@ __device__ __forceinline__ void load_vec8(const T *base, const RowMap &m, float 
     load4(base + m.col(1), d + 4);
 }
 
+// The 8 state rows this thread owns (s[j][0..7] = row m.row(j), columns
+// m.col(0)+0..3 and m.col(1)+0..3), read and written with non-temporal
+// accesses: a decode call touches each state once, and cached fills and
+// write-backs of the 805 MB of states per B = 256 step only cost bandwidth.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load_state_rows(const float *S, const RowMap &m, float (&s)[8][8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(S + m.row(j) * kD + m.col(hh)));
+            s[j][4 * hh] = x.x;
+            s[j][4 * hh + 1] = x.y;
+            s[j][4 * hh + 2] = x.z;
+            s[j][4 * hh + 3] = x.w;
+        }
+}
+__device__ __forceinline__ void store_state_rows(float *S, const RowMap &m, const float (&s)[8][8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            __builtin_nontemporal_store(f32x4v{s[j][4 * hh], s[j][4 * hh + 1], s[j][4 * hh + 2], s[j][4 * hh + 3]},
+                                        reinterpret_cast<f32x4v *>(S + m.row(j) * kD + m.col(hh)));
+}
+
 // One token applied to the 8 rows this thread owns.  s[j][0..7] holds row
 // m.row(j), columns (m.col(0)+0..3, m.col(1)+0..3).  vr[j] = v[m.row(j)].
 // Returns, in lanes with c16 < 8, o of row m.row(c16).
@@ -103,11 +129,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     float *S = pool + ((size_t)slot * H_v + h) * (kD * kD);
 
     float s[8][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        load4(S + m.row(j) * kD + m.col(0), s[j]);
-        load4(S + m.row(j) * kD + m.col(1), s[j] + 4);
-    }
+    load_state_rows(S, m, s);
     float kk[8], qq[8], vr[8];
     float alpha, bt;
     if constexpr (kRaw) {
@@ -154,13 +176,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
     const float mine = delta_rows(s, kk, qq, vr, alpha, bt, m);
 
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(0)) =
-            make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
-        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(1)) =
-            make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
-    }
+    store_state_rows(S, m, s);
     if (m.c16 < 8) o[((size_t)b * H_v + h) * kD + m.wave * 32 + m.c16 * 4 + m.r4] = f2bf(mine);
 }
 
@@ -182,11 +198,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     float *S = pool + ((size_t)slot_idx[b] * H_v + h) * (kD * kD);
 
     float s[8][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        load4(S + m.row(j) * kD + m.col(0), s[j]);
-        load4(S + m.row(j) * kD + m.col(1), s[j] + 4);
-    }
+    load_state_rows(S, m, s);
     float kk[8], qq[8], vr[8], gt, bt;
     auto fetch = [&](int t, float *kd, float *qd, float *vd, float &gd, float &bd) {
         const size_t bt_ = (size_t)b * n + t;
@@ -201,14 +213,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     fetch(0, kk, qq, vr, gt, bt);
     for (int t = 0; t < n; ++t) {
         if (snapshots) {
-            float *snap = snapshots + (((size_t)b * n + t) * H_v + h) * (kD * kD);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                *reinterpret_cast<float4 *>(snap + m.row(j) * kD + m.col(0)) =
-                    make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
-                *reinterpret_cast<float4 *>(snap + m.row(j) * kD + m.col(1)) =
-                    make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
-            }
+            store_state_rows(snapshots + (((size_t)b * n + t) * H_v + h) * (kD * kD), m, s);
         }
         float kn[8], qn[8], vn[8], gn, bn;
         fetch(min(t + 1, n - 1), kn, qn, vn, gn, bn);   // clamped: the last fetch is unused
@@ -226,13 +231,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
         gt = gn;
         bt = bn;
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(0)) =
-            make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
-        *reinterpret_cast<float4 *>(S + m.row(j) * kD + m.col(1)) =
-            make_float4(s[j][4], s[j][5], s[j][6], s[j][7]);
-    }
+    store_state_rows(S, m, s);
 }
 
 // Return slot_idx[b] to the state after its first n_keep[b] tokens:
