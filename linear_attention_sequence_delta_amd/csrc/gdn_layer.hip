@@ -71,9 +71,13 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const uint16_t *o,
     const int cg = threadIdx.x & 15;
     const int rr = min(row, rows - 1);              // a whole DPP row stays active
     const size_t off = (size_t)rr * kD + 8 * cg;
+    // o and z are read once and out written once: non-temporal accesses
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u oa = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(o + off));
+    const v4u za = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(z + off));
     float ov[8], zv[8];
-    unpack8(*reinterpret_cast<const uint4 *>(o + off), ov);
-    unpack8(*reinterpret_cast<const uint4 *>(z + off), zv);
+    unpack8(make_uint4(oa.x, oa.y, oa.z, oa.w), ov);
+    unpack8(make_uint4(za.x, za.y, za.z, za.w), zv);
     const float4 w0 = *reinterpret_cast<const float4 *>(w + 8 * cg);
     const float4 w1 = *reinterpret_cast<const float4 *>(w + 8 * cg + 4);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -84,7 +88,10 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const uint16_t *o,
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = ov[e] * inv * wv[e] * silu(zv[e]);
-    if (row < rows) *reinterpret_cast<uint4 *>(out + off) = pack_bf8(y);
+    if (row < rows) {
+        const uint4 pv = pack_bf8(y);
+        __builtin_nontemporal_store(v4u{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<v4u *>(out + off));
+    }
 }
 
 }  // namespace

@@ -81,12 +81,18 @@ __global__ __launch_bounds__(256) void conv_prelude_kernel(
     }
     const bool normalise = cb < 2 * H_qk;
 
+    // the run's rows of x are read once and q, k, v written once: non-temporal
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    auto ldx = [&](int t) {
+        const v4u a = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(x + (size_t)t * C + ch0));
+        return make_uint4(a.x, a.y, a.z, a.w);
+    };
     uint4 nxt = make_uint4(0, 0, 0, 0);
-    if (t0 < t1) nxt = *reinterpret_cast<const uint4 *>(x + (size_t)t0 * C + ch0);
+    if (t0 < t1) nxt = ldx(t0);
     for (int t = t0; t < t1; ++t) {
         float cur[8];
         unpack8(nxt, cur);
-        if (t + 1 < t1) nxt = *reinterpret_cast<const uint4 *>(x + (size_t)(t + 1) * C + ch0);
+        if (t + 1 < t1) nxt = ldx(t + 1);
         if (cu_seqlens && t >= s1) {                   // a new sequence starts at t
             while (n + 1 < N && cu_seqlens[n + 1] <= t) ++n;
             s1 = cu_seqlens[n + 1];
@@ -103,7 +109,8 @@ __global__ __launch_bounds__(256) void conv_prelude_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] *= r;
         }
-        *reinterpret_cast<uint4 *>(dst + (size_t)t * dst_stride) = pack_bf8(y);
+        const uint4 pv = pack_bf8(y);
+        __builtin_nontemporal_store(v4u{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<v4u *>(dst + (size_t)t * dst_stride));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             win[0][e] = win[1][e];
