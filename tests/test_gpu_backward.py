@@ -1,8 +1,9 @@
 """Gradients of the bf16 chunked prefill (gdn_prefill_backward) on the GPU
 against the fp64 oracle's reverse-mode gradients of the token recurrence:
 ragged lengths, packed varlen, initial state and final-state gradient present
-or not, an odd head grid, T = 0, and the 32768-token workload (one QK group
-against the oracle, every head through the adjoint identities)."""
+or not, an odd head grid, T = 0, and the 32768-token and packed 8-sequence
+workloads (one QK group against the oracle, every head through the adjoint
+identities)."""
 import numpy as np
 import pytest
 
@@ -112,6 +113,34 @@ def test_backward_full_size_one_group_and_adjoint():
     dq, dk, dv, dg, db, dS0 = gdn.gdn_prefill_backward(dev(p.q), dev(p.k), dev(p.v), dev(p.g),
                                                        dev(p.beta), dev(d_o), dev(p.S0), dev(dSf))
     o, S = gdn.gdn_prefill(dev(p.q), dev(p.k), dev(p.v), dev(p.g), dev(p.beta), dev(p.S0))
+    f64 = lambda t: t.double()
+    lhs = (f64(dv) * f64(dev(p.v))).sum() + (f64(dS0) * f64(dev(p.S0))).sum()
+    rhs = (f64(dev(d_o)) * f64(o)).sum() + (f64(dev(dSf)) * f64(S)).sum()
+    scale = (f64(dev(d_o)) * f64(o)).abs().sum()
+    assert abs(float(lhs - rhs)) <= 2e-2 * float(scale), (float(lhs), float(rhs), float(scale))
+    qq = (f64(dq) * f64(dev(p.q))).sum()
+    oo = (f64(dev(d_o)) * f64(o)).sum()
+    assert abs(float(qq - oo)) <= 2e-2 * float(scale), (float(qq), float(oo))
+    for t in (dq, dk, dv, dg, db, dS0):
+        assert torch.isfinite(t.float()).all()
+
+
+def test_backward_varlen_8seq_one_group_and_adjoint():
+    """The packed varlen workload (8 sequences, lengths U{512..16384}, each
+    with its own initial state and final-state gradient): QK head 11 and its
+    V-heads against the oracle, every head through the adjoint identities of
+    the test above (summed over the sequences)."""
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    lengths = synth.varlen_lengths(1004)
+    p = synth.direct_prefill(7600, lengths=lengths, init_state=True)
+    d_o, dSf = synth.output_grads(7600, p.T, p.N)
+    print("backward varlen", list(lengths), flush=True)
+    _check(p, d_o, dSf, 1.0, qk_heads=(11, 12))
+    cu = dev(p.cu_seqlens)
+    dq, dk, dv, dg, db, dS0 = gdn.gdn_prefill_backward(dev(p.q), dev(p.k), dev(p.v), dev(p.g),
+                                                       dev(p.beta), dev(d_o), dev(p.S0), dev(dSf), cu)
+    o, S = gdn.gdn_prefill(dev(p.q), dev(p.k), dev(p.v), dev(p.g), dev(p.beta), dev(p.S0), cu)
     f64 = lambda t: t.double()
     lhs = (f64(dv) * f64(dev(p.v))).sum() + (f64(dS0) * f64(dev(p.S0))).sum()
     rhs = (f64(dev(d_o)) * f64(o)).sum() + (f64(dev(dSf)) * f64(S)).sum()
