@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -162,6 +162,55 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
                     float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * gdn_chunk_states_size -- bytes of the chunk-states buffer that
+ * gdn_prefill_save_states and gdn_prefill_raw_save_states fill and
+ * gdn_prefill_backward_saved reads (host-only; 0 for invalid sizes): one bf16
+ * [d_v][d_k] state per (64-token chunk, V-head), for (T + 63) / 64 + N chunks
+ * (an upper bound on the chunks of N packed sequences; 32 KiB per chunk and
+ * V-head, 805 MB for one 32768-token sequence with 48 V-heads).
+ */
+size_t gdn_chunk_states_size(int N, int T, int H_v, int d_k, int d_v);
+
+/*
+ * gdn_prefill_save_states -- gdn_prefill (io_dtype GDN_BF16) that also keeps,
+ * for a later gdn_prefill_backward_saved, the state each 64-token chunk starts
+ * from, rounded to bf16 as the chunk's products use it.  A forward pass of a
+ * training step calls it so that the backward need not recompute the forward
+ * states ([Local sec. 2.1] names a fused forward and backward kernel for the
+ * trained GDN layer).  o and final_state are bit-identical to gdn_prefill's.
+ *
+ *   q ... o, workspace, ws_bytes, stream   as for gdn_prefill (bf16)
+ *   chunk_states   device bf16 [chunks][H_v][d_v][d_k] output, chunks counted
+ *                  over the packed sequences in order (sequence n's chunks
+ *                  follow those of sequences 0 .. n - 1); at least
+ *                  gdn_chunk_states_size(N, T, H_v, d_k, d_v) = cs_bytes bytes;
+ *                  must not overlap any other argument.  Owned by the caller;
+ *                  entries past the sequences' chunk count are not written.
+ * Returns as gdn_prefill; GDN_ERR_INVALID_ARG for a NULL or short chunk_states.
+ */
+int gdn_prefill_save_states(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, float *final_state,
+                            const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
+                            int d_v, float scale, void *o, void *chunk_states, size_t cs_bytes,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_prefill_raw_save_states -- gdn_prefill_raw that also keeps the chunk
+ * states, as gdn_prefill_save_states does.  The states are those of the
+ * equivalent gdn_conv_prelude + gdn_prefill_save_states (bit for bit), so a
+ * backward on the prelude's q, k, v may use them.
+ *
+ *   x_raw ... o, workspace, ws_bytes, stream   as for gdn_prefill_raw
+ *   chunk_states, cs_bytes                     as for gdn_prefill_save_states
+ */
+int gdn_prefill_raw_save_states(const void *x_raw, const void *conv_w, float l2_eps,
+                                const float *g, const float *beta, const float *initial_state,
+                                float *final_state, const int32_t *cu_seqlens, int N, int T,
+                                int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                                void *chunk_states, size_t cs_bytes, void *workspace,
+                                size_t ws_bytes, void *stream);
+
+/*
  * gdn_prefill_backward_workspace_size -- bytes of device workspace
  * gdn_prefill_backward needs (host-only; 0 for invalid sizes, > 0 for any
  * valid N >= 1, T >= 0).  It holds, per (64-token chunk, V-head), the
@@ -204,6 +253,40 @@ int gdn_prefill_backward(const void *q, const void *k, const void *v, const floa
                          int H_v, int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
                          float *dg, float *dbeta, float *d_initial_state, void *workspace,
                          size_t ws_bytes, void *stream);
+
+/*
+ * gdn_prefill_backward_saved_workspace_size -- bytes of device workspace
+ * gdn_prefill_backward_saved needs (host-only; 0 for invalid sizes): the
+ * backward chunk records, the state gradients at chunk ends and dU, without
+ * the forward records and states (about 70 KB per chunk and V-head).
+ */
+size_t gdn_prefill_backward_saved_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
+                                                 int d_v);
+
+/*
+ * gdn_prefill_backward_saved -- gdn_prefill_backward given the chunk states
+ * kept by gdn_prefill_save_states (or gdn_prefill_raw_save_states) on the same
+ * q, k, v, g, beta, initial_state and cu_seqlens: the forward pass over the
+ * chunks is not repeated.  The gradients are bit-identical to
+ * gdn_prefill_backward's on the same inputs.
+ *
+ *   q, k, v, g, beta, cu_seqlens, d_o, d_final_state, N ... scale, dq ...
+ *   d_initial_state            as for gdn_prefill_backward (the initial state
+ *                              itself is carried by chunk_states)
+ *   chunk_states, cs_bytes     device bf16, as filled by the forward pass;
+ *                              at least gdn_chunk_states_size(...) bytes; read only
+ *   workspace, ws_bytes        device scratch of at least
+ *                              gdn_prefill_backward_saved_workspace_size bytes
+ * Outputs and workspace must not overlap each other or any input (chunk_states
+ * included).  GDN_ERR_INVALID_ARG for a NULL or short chunk_states.
+ */
+int gdn_prefill_backward_saved(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const void *chunk_states, size_t cs_bytes,
+                               const int32_t *cu_seqlens, const void *d_o,
+                               const float *d_final_state, int N, int T, int H_qk, int H_v,
+                               int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
+                               float *dg, float *dbeta, float *d_initial_state, void *workspace,
+                               size_t ws_bytes, void *stream);
 
 /*
  * gdn_layer_prefill_backward_workspace_size -- bytes of device workspace

@@ -34,7 +34,9 @@ EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_gates", "gdn_layer_prefill_workspace_size",
            "gdn_layer_prefill", "gdn_layer_decode_step", "gdn_decode_multi_step",
            "gdn_state_rollback", "gdn_gated_norm", "gdn_gated_norm_backward_workspace_size",
-           "gdn_gated_norm_backward", "gdn_decode_step")
+           "gdn_gated_norm_backward", "gdn_decode_step", "gdn_chunk_states_size",
+           "gdn_prefill_save_states", "gdn_prefill_raw_save_states",
+           "gdn_prefill_backward_saved_workspace_size", "gdn_prefill_backward_saved")
 
 _lib = None
 
@@ -100,6 +102,19 @@ def lib() -> ctypes.CDLL:
     L.gdn_gated_norm_backward.restype = I
     L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_decode_step.restype = I
+    L.gdn_chunk_states_size.argtypes = [I, I, I, I, I]
+    L.gdn_chunk_states_size.restype = Z
+    L.gdn_prefill_save_states.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P,
+                                          Z, P]
+    L.gdn_prefill_save_states.restype = I
+    L.gdn_prefill_raw_save_states.argtypes = [P, P, F, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z,
+                                              P, Z, P]
+    L.gdn_prefill_raw_save_states.restype = I
+    L.gdn_prefill_backward_saved_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_prefill_backward_saved_workspace_size.restype = Z
+    L.gdn_prefill_backward_saved.argtypes = [P, P, P, P, P, P, Z, P, P, P, I, I, I, I, I, I, F, P,
+                                             P, P, P, P, P, P, Z, P]
+    L.gdn_prefill_backward_saved.restype = I
     _lib = L
     return L
 
@@ -185,15 +200,35 @@ def gdn_prefill_workspace_size(io_dtype: int, N: int, T: int, H_qk: int, H_v: in
     return int(lib().gdn_prefill_workspace_size(io_dtype, N, T, H_qk, H_v, d_k, d_v))
 
 
+def gdn_chunk_states_size(N: int, T: int, H_v: int, d_k: int = 128, d_v: int = 128) -> int:
+    """Bytes of the chunk-states buffer a training forward pass keeps."""
+    return int(lib().gdn_chunk_states_size(N, T, H_v, d_k, d_v))
+
+
+def _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev):
+    torch = _torch()
+    need = gdn_chunk_states_size(N, T, H_v, d_k, d_v)
+    if chunk_states is True:
+        chunk_states = torch.empty(max(need, 2) // 2, dtype=torch.bfloat16, device=dev)
+    _need(chunk_states, "chunk_states", torch.bfloat16, dev)
+    nbytes = chunk_states.numel() * chunk_states.element_size()
+    if nbytes < need:
+        raise ValueError(f"chunk_states holds {nbytes} bytes, {need} needed")
+    return chunk_states, nbytes
+
+
 def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale: float = 1.0,
-                final_state=True, o=None, workspace=None):
+                final_state=True, o=None, workspace=None, chunk_states=None):
     """Prefill over packed sequences.  q, k: [T, H_qk, 128]; v: [T, H_v, 128], all
     bf16 (chunked matrix-core path) or all fp32 (token-by-token fp32 path); g,
     beta: fp32 [T, H_v]; initial_state: fp32 [N, H_v, 128, 128] or None.
 
     final_state: True (allocate and return it), False/None (skip it), or an fp32
     tensor to write (may be ``initial_state`` itself for an in-place hand-off).
-    Returns (o, final_state or None)."""
+    chunk_states (bf16 only): None, True (allocate) or a bf16 tensor of at least
+    gdn_chunk_states_size bytes: the states at chunk starts are kept there for
+    gdn_prefill_backward.  Returns (o, final_state or None), plus chunk_states
+    when it is given."""
     torch = _torch()
     dev = _device_of(q)
     if q.dtype == torch.bfloat16:
@@ -241,6 +276,16 @@ def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale:
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if chunk_states is not None:
+        if io != GDN_BF16:
+            raise ValueError("chunk_states are kept by the bf16 prefill only")
+        cs, cs_bytes = _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev)
+        rc = lib().gdn_prefill_save_states(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(initial_state), _ptr(fs), _ptr(cu_seqlens), N, T,
+                                           H_qk, H_v, d_k, d_v, float(scale), _ptr(o), _ptr(cs),
+                                           cs_bytes, _ptr(workspace), ws_bytes, _stream(dev))
+        _check(rc, "gdn_prefill_save_states")
+        return o, fs, cs
     rc = lib().gdn_prefill(io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(initial_state), _ptr(fs), _ptr(cu_seqlens), N, T, H_qk, H_v,
                            d_k, d_v, float(scale), _ptr(o), _ptr(workspace), ws_bytes,
@@ -254,14 +299,22 @@ def gdn_prefill_backward_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k
     return int(lib().gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v))
 
 
+def gdn_prefill_backward_saved_workspace_size(N: int, T: int, H_qk: int, H_v: int,
+                                              d_k: int = 128, d_v: int = 128) -> int:
+    return int(lib().gdn_prefill_backward_saved_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+
+
 def gdn_prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
                          cu_seqlens=None, *, scale: float = 1.0, d_initial_state=True,
-                         workspace=None):
+                         workspace=None, chunk_states=None):
     """Gradients of the bf16 gdn_prefill.  q, k: bf16 [T, H_qk, 128]; v, d_o:
     bf16 [T, H_v, 128]; g, beta: fp32 [T, H_v]; initial_state, d_final_state:
     fp32 [N, H_v, 128, 128] or None.  d_initial_state: True (allocate and
-    return it), False/None (skip it) or an fp32 tensor to write.  Returns
-    (dq, dk, dv, dg, dbeta, d_initial_state or None)."""
+    return it), False/None (skip it) or an fp32 tensor to write.
+    chunk_states: the bf16 buffer a gdn_prefill / gdn_prefill_raw with
+    chunk_states filled on the same inputs (then initial_state is not read and
+    the forward states are not recomputed).  Returns (dq, dk, dv, dg, dbeta,
+    d_initial_state or None)."""
     torch = _torch()
     dev = _device_of(q)
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
@@ -298,6 +351,21 @@ def gdn_prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_stat
     dv = torch.empty_like(v)
     dg = torch.empty_like(g)
     db = torch.empty_like(beta)
+    if chunk_states is not None:
+        if chunk_states is True:
+            raise ValueError("chunk_states must be the buffer the forward pass filled")
+        cs, cs_bytes = _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev)
+        ws_need = gdn_prefill_backward_saved_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+        if workspace is None:
+            workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc = lib().gdn_prefill_backward_saved(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cs), cs_bytes, _ptr(cu_seqlens),
+            _ptr(d_o), _ptr(d_final_state), N, T, H_qk, H_v, d_k, d_v, float(scale), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace), ws_bytes,
+            _stream(dev))
+        _check(rc, "gdn_prefill_backward_saved")
+        return dq, dk, dv, dg, db, dS0
     ws_need = gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
@@ -387,11 +455,13 @@ def gdn_prefill_raw_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int
 
 def gdn_prefill_raw(x, conv_w, g, beta, initial_state=None, cu_seqlens=None, *, H_qk: int = 16,
                     H_v: int = 48, d_k: int = 128, d_v: int = 128, l2_eps: float = 1e-6,
-                    scale: float = 1.0, final_state=True, o=None, workspace=None):
+                    scale: float = 1.0, final_state=True, o=None, workspace=None,
+                    chunk_states=None):
     """Prefill from the raw projections, conv prelude fused.  x: bf16 [T, C_raw];
     conv_w: bf16 [C_raw, 4]; g, beta: fp32 [T, H_v]; initial_state: fp32
-    [N, H_v, 128, 128] or None; final_state as for gdn_prefill.  Returns
-    (o bf16 [T, H_v, d_v], final_state or None)."""
+    [N, H_v, 128, 128] or None; final_state and chunk_states as for gdn_prefill.
+    Returns (o bf16 [T, H_v, d_v], final_state or None), plus chunk_states when
+    it is given."""
     torch = _torch()
     dev = _device_of(x)
     _need(x, "x", torch.bfloat16, dev, 2)
@@ -431,6 +501,14 @@ def gdn_prefill_raw(x, conv_w, g, beta, initial_state=None, cu_seqlens=None, *, 
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if chunk_states is not None:
+        cs, cs_bytes = _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev)
+        rc = lib().gdn_prefill_raw_save_states(
+            _ptr(x), _ptr(conv_w), float(l2_eps), _ptr(g), _ptr(beta), _ptr(initial_state),
+            _ptr(fs), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v, float(scale), _ptr(o), _ptr(cs),
+            cs_bytes, _ptr(workspace), ws_bytes, _stream(dev))
+        _check(rc, "gdn_prefill_raw_save_states")
+        return o, fs, cs
     rc = lib().gdn_prefill_raw(_ptr(x), _ptr(conv_w), float(l2_eps), _ptr(g), _ptr(beta),
                                _ptr(initial_state), _ptr(fs), _ptr(cu_seqlens), N, T, H_qk, H_v,
                                d_k, d_v, float(scale), _ptr(o), _ptr(workspace), ws_bytes,
@@ -706,6 +784,7 @@ def gdn_gated_norm_backward(o, z, w, dy, *, eps: float = 1e-6, workspace=None):
 
 
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
+           "gdn_chunk_states_size", "gdn_prefill_backward_saved_workspace_size",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_backward", "gdn_prefill_backward_workspace_size",
            "gdn_layer_prefill_backward", "gdn_layer_prefill_backward_workspace_size",

@@ -125,10 +125,16 @@ size_t gdn_prefill_workspace_size(int io_dtype, int N, int T, int H_qk, int H_v,
     return gdn::chunked_workspace_bytes(N, T, H_qk, H_v, false);
 }
 
-int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const float *g,
-                const float *beta, const float *initial_state, float *final_state,
-                const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill, and with chunk_states (bf16 only) gdn_prefill_save_states.
+int prefill_impl(int io_dtype, const void *q, const void *k, const void *v, const float *g,
+                 const float *beta, const float *initial_state, float *final_state,
+                 const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                 float scale, void *o, void *chunk_states, size_t cs_bytes, void *workspace,
+                 size_t ws_bytes, void *stream) {
     int rc;
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
         return fail(GDN_ERR_UNSUPPORTED, "io_dtype must be GDN_F32 or GDN_BF16 (got %d)", io_dtype);
@@ -162,6 +168,17 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
                      overlaps(workspace, need, final_state, ns) ||
                      overlaps(workspace, need, initial_state, ns)))
         return fail(GDN_ERR_INVALID_ARG, "workspace must not overlap inputs or outputs");
+    if (chunk_states) {
+        const size_t ncs = gdn_chunk_states_size(N, T, H_v, d_k, d_v);
+        if (cs_bytes < ncs)
+            return fail(GDN_ERR_INVALID_ARG, "chunk_states of %zu bytes given, %zu needed", cs_bytes, ncs);
+        const struct { const void *p; size_t n; } other[] = {
+            {q, nqk}, {k, nqk}, {v, nv}, {g, ng}, {beta, ng}, {initial_state, ns}, {final_state, ns},
+            {o, nv}, {workspace, need}, {cu_seqlens, (size_t)(N + 1) * 4}};
+        for (const auto &x : other)
+            if (overlaps(chunk_states, ncs, x.p, x.n))
+                return fail(GDN_ERR_INVALID_ARG, "chunk_states must not overlap any other argument");
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
     hipError_t e;
@@ -171,9 +188,38 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
                                           T, H_qk, H_v, scale, o, s);
     else
         e = gdn::launch_chunked_prefill(q, k, v, g, beta, initial_state, final_state, cu_seqlens,
-                                        N, T, H_qk, H_v, scale, o, workspace, s);
+                                        N, T, H_qk, H_v, scale, o, chunk_states, workspace, s);
     return finish(e, s, "gdn_prefill launch");
 }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const float *g,
+                const float *beta, const float *initial_state, float *final_state,
+                const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    return prefill_impl(io_dtype, q, k, v, g, beta, initial_state, final_state, cu_seqlens, N, T,
+                        H_qk, H_v, d_k, d_v, scale, o, nullptr, 0, workspace, ws_bytes, stream);
+}
+
+size_t gdn_chunk_states_size(int N, int T, int H_v, int d_k, int d_v) {
+    if (N < 1 || T < 0 || H_v < 1 || d_k != gdn::kD || d_v != gdn::kD) return 0;
+    return gdn::chunk_states_bytes(N, T, H_v);
+}
+
+int gdn_prefill_save_states(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, float *final_state,
+                            const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
+                            int d_v, float scale, void *o, void *chunk_states, size_t cs_bytes,
+                            void *workspace, size_t ws_bytes, void *stream) {
+    if (!chunk_states) return fail(GDN_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+    return prefill_impl(GDN_BF16, q, k, v, g, beta, initial_state, final_state, cu_seqlens, N, T,
+                        H_qk, H_v, d_k, d_v, scale, o, chunk_states, cs_bytes, workspace, ws_bytes,
+                        stream);
+}
+
 
 size_t gdn_prefill_raw_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v) {
     (void)d_k;
@@ -245,20 +291,41 @@ LayerBwdWs layer_bwd_ws(int N, int T, int H_qk, int H_v) {
     w.part = al(gdn::prelude_bwd_partial_bytes(T, H_qk, H_v));
     w.gpart = al(gdn::gates_bwd_partial_bytes(H_v));
     w.total = 4 * w.g + 4 * w.q + 2 * w.v + w.part + w.gpart +
-              gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v);
+              gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v, false);
     return w;
 }
 }  // namespace
 
 extern "C" {
 
-int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
-                    const float *beta, const float *initial_state, float *final_state,
-                    const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                    float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill_raw, and with chunk_states gdn_prefill_raw_save_states.
+int prefill_raw_impl(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
+                     const float *beta, const float *initial_state, float *final_state,
+                     const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                     float scale, void *o, void *chunk_states, size_t cs_bytes, void *workspace,
+                     size_t ws_bytes, void *stream) {
     int rc = check_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state, final_state,
                                cu_seqlens, N, T, H_qk, H_v, d_k, d_v, scale, o, workspace, ws_bytes);
     if (rc) return rc;
+    if (chunk_states) {
+        const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
+        const size_t nx = (size_t)T * craw * 2, nw = craw * 4 * 2, nv = (size_t)T * H_v * gdn::kD * 2;
+        const size_t ng = (size_t)T * H_v * 4, ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
+        const size_t need = gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+        const size_t ncs = gdn_chunk_states_size(N, T, H_v, d_k, d_v);
+        if (cs_bytes < ncs)
+            return fail(GDN_ERR_INVALID_ARG, "chunk_states of %zu bytes given, %zu needed", cs_bytes, ncs);
+        const struct { const void *p; size_t n; } other[] = {
+            {x_raw, nx}, {conv_w, nw}, {g, ng}, {beta, ng}, {initial_state, ns}, {final_state, ns},
+            {o, nv}, {workspace, need}, {cu_seqlens, (size_t)(N + 1) * 4}};
+        for (const auto &x : other)
+            if (overlaps(chunk_states, ncs, x.p, x.n))
+                return fail(GDN_ERR_INVALID_ARG, "chunk_states must not overlap any other argument");
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
     hipError_t e;
@@ -269,23 +336,62 @@ int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const f
     else
         e = gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
                                             final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
-                                            workspace, s);
+                                            chunk_states, workspace, s);
     return finish(e, s, "gdn_prefill_raw launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
+                    const float *beta, const float *initial_state, float *final_state,
+                    const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                    float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    return prefill_raw_impl(x_raw, conv_w, l2_eps, g, beta, initial_state, final_state, cu_seqlens,
+                            N, T, H_qk, H_v, d_k, d_v, scale, o, nullptr, 0, workspace, ws_bytes,
+                            stream);
+}
+
+int gdn_prefill_raw_save_states(const void *x_raw, const void *conv_w, float l2_eps,
+                                const float *g, const float *beta, const float *initial_state,
+                                float *final_state, const int32_t *cu_seqlens, int N, int T,
+                                int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                                void *chunk_states, size_t cs_bytes, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    if (!chunk_states) return fail(GDN_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+    return prefill_raw_impl(x_raw, conv_w, l2_eps, g, beta, initial_state, final_state, cu_seqlens,
+                            N, T, H_qk, H_v, d_k, d_v, scale, o, chunk_states, cs_bytes, workspace,
+                            ws_bytes, stream);
 }
 
 size_t gdn_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v) {
     (void)d_k;
     (void)d_v;
     if (N < 1 || T < 0 || H_qk < 1 || H_v < 1) return 0;
-    return gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v);
+    return gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v, false);
 }
 
-int gdn_prefill_backward(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                         const void *d_o, const float *d_final_state, int N, int T, int H_qk,
-                         int H_v, int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
-                         float *dg, float *dbeta, float *d_initial_state, void *workspace,
-                         size_t ws_bytes, void *stream) {
+size_t gdn_prefill_backward_saved_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
+                                                 int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (N < 1 || T < 0 || H_qk < 1 || H_v < 1) return 0;
+    return gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill_backward (the states recomputed: chunk_states NULL, initial_state
+// read) and gdn_prefill_backward_saved (the states of an earlier forward pass).
+int backward_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const float *initial_state, const void *chunk_states, size_t cs_bytes,
+                  const int32_t *cu_seqlens, const void *d_o, const float *d_final_state, int N,
+                  int T, int H_qk, int H_v, int d_k, int d_v, float scale, void *dq, void *dk,
+                  void *dv, float *dg, float *dbeta, float *d_initial_state, void *workspace,
+                  size_t ws_bytes, void *stream) {
     int rc;
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
@@ -298,12 +404,17 @@ int gdn_prefill_backward(const void *q, const void *k, const void *v, const floa
                     "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
     const size_t nqk = (size_t)T * H_qk * gdn::kD * 2, nv = (size_t)T * H_v * gdn::kD * 2;
     const size_t ng = (size_t)T * H_v * 4, ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
-    const size_t need = gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+    const bool saved = chunk_states != nullptr;
+    const size_t ncs = saved ? gdn_chunk_states_size(N, T, H_v, d_k, d_v) : 0;
+    if (saved && cs_bytes < ncs)
+        return fail(GDN_ERR_INVALID_ARG, "chunk_states of %zu bytes given, %zu needed", cs_bytes, ncs);
+    const size_t need = saved ? gdn_prefill_backward_saved_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+                              : gdn_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v);
     if (ws_bytes < need || !workspace)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
     const struct { const void *p; size_t n; } in[] = {
         {q, nqk}, {k, nqk}, {v, nv}, {g, ng}, {beta, ng}, {initial_state, ns}, {d_o, nv},
-        {d_final_state, ns}, {cu_seqlens, (size_t)(N + 1) * 4}};
+        {d_final_state, ns}, {cu_seqlens, (size_t)(N + 1) * 4}, {chunk_states, ncs}};
     const struct { const void *p; size_t n; } out[] = {
         {dq, nqk}, {dk, nqk}, {dv, nv}, {dg, ng}, {dbeta, ng}, {d_initial_state, ns},
         {workspace, need}};
@@ -317,10 +428,39 @@ int gdn_prefill_backward(const void *q, const void *k, const void *v, const floa
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
-    hipError_t e = gdn::launch_chunked_backward(q, k, v, g, beta, initial_state, cu_seqlens, N, T,
-                                                H_qk, H_v, scale, d_o, d_final_state, dq, dk, dv,
-                                                dg, dbeta, d_initial_state, workspace, s);
+    hipError_t e = gdn::launch_chunked_backward(q, k, v, g, beta, saved ? nullptr : initial_state,
+                                                cu_seqlens, N, T, H_qk, H_v, scale, d_o,
+                                                d_final_state, dq, dk, dv, dg, dbeta,
+                                                d_initial_state, chunk_states, workspace, s);
     return finish(e, s, "gdn_prefill_backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_backward(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                         const void *d_o, const float *d_final_state, int N, int T, int H_qk,
+                         int H_v, int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
+                         float *dg, float *dbeta, float *d_initial_state, void *workspace,
+                         size_t ws_bytes, void *stream) {
+    return backward_impl(q, k, v, g, beta, initial_state, nullptr, 0, cu_seqlens, d_o,
+                         d_final_state, N, T, H_qk, H_v, d_k, d_v, scale, dq, dk, dv, dg, dbeta,
+                         d_initial_state, workspace, ws_bytes, stream);
+}
+
+int gdn_prefill_backward_saved(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const void *chunk_states, size_t cs_bytes,
+                               const int32_t *cu_seqlens, const void *d_o,
+                               const float *d_final_state, int N, int T, int H_qk, int H_v,
+                               int d_k, int d_v, float scale, void *dq, void *dk, void *dv,
+                               float *dg, float *dbeta, float *d_initial_state, void *workspace,
+                               size_t ws_bytes, void *stream) {
+    if (!chunk_states) return fail(GDN_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+    return backward_impl(q, k, v, g, beta, nullptr, chunk_states, cs_bytes, cu_seqlens, d_o,
+                         d_final_state, N, T, H_qk, H_v, d_k, d_v, scale, dq, dk, dv, dg, dbeta,
+                         d_initial_state, workspace, ws_bytes, stream);
 }
 
 size_t gdn_layer_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
@@ -396,7 +536,7 @@ int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const floa
     if (e == hipSuccess)
         e = gdn::launch_chunked_backward(q, k, v, g, beta, initial_state, cu_seqlens, N, T, H_qk, H_v,
                                          scale, d_o, d_final_state, dq, dk, dv, dg, dbeta,
-                                         d_initial_state, rest, s);
+                                         d_initial_state, nullptr, rest, s);
     if (e == hipSuccess)
         e = gdn::launch_prelude_bwd(x_raw, conv_w, cu_seqlens, N, T, H_qk, H_v, l2_eps, dq, dk, dv,
                                     dx_raw, dconv_w, part, s);
@@ -476,7 +616,7 @@ int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, con
     else if ((e = gdn::launch_gates(a, b, A_log, dt_bias, T, H_v, g, beta, s)) == hipSuccess)
         e = gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
                                             final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
-                                            rest, s);
+                                            nullptr, rest, s);
     if (e == hipSuccess && conv_state_out)
         e = gdn::launch_conv_hist(x_raw, cu_seqlens, N, T, (int)craw, conv_state_out, s);
     return finish(e, s, "gdn_layer_prefill launch");

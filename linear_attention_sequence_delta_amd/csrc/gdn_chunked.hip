@@ -94,9 +94,12 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 // in registers.  The normalised rows go to the workspace, where the scan reads
 // them, and through LDS into the MFMA fragments.
 //
-// For the backward pass (kBwd) each (chunk, V-head) also gets a backward
-// record (gdn_chunk.h): the fragments of T'^T and P^T, T row-major and G.
+// kRecs selects the records written per (chunk, V-head): the forward record
+// (kRecFwd: T', P, G, read by the scan) and/or, for the backward pass, the
+// backward record (kRecBwd, gdn_chunk.h: the fragments of T'^T and P^T, T
+// row-major and G).
 constexpr int kPrepWaves = 4;
+constexpr int kRecFwd = 1, kRecBwd = 2;
 static_assert(kChunk * kKP * sizeof(uint16_t) <= kChunk * kAP * sizeof(float),
               "a chunk's bf16 K or Q rows fit in a wave's A area");
 
@@ -107,7 +110,7 @@ struct RawIn {             // fused prelude inputs
     uint16_t *kws, *qws;   // [chunks * 64][H_qk][128] bf16 normalised K and Q rows
 };
 
-template <bool kRaw, bool kBwd = false>
+template <bool kRaw, int kRecs = kRecFwd>
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const RawIn raw,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
@@ -254,9 +257,10 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
             const float G = wave_scan(gl);
             sG[lane] = G;
             sBt[lane] = bl;
-            uint16_t *rec = ws + ((size_t)gc * H_v + h) * kRecElems;
+            constexpr bool kFwd = kRecs & kRecFwd, kBwd = kRecs & kRecBwd;
+            uint16_t *rec = kFwd ? ws + ((size_t)gc * H_v + h) * kRecElems : nullptr;
             uint16_t *brec = kBwd ? bws + ((size_t)gc * H_v + h) * kBwdRecElems : nullptr;
-            __builtin_nontemporal_store(G, reinterpret_cast<float *>(rec + 2 * kTileElems) + lane);
+            if constexpr (kFwd) __builtin_nontemporal_store(G, reinterpret_cast<float *>(rec + 2 * kTileElems) + lane);
             if constexpr (kBwd) reinterpret_cast<float *>(brec + kBwdGOff)[lane] = G;
             wave_lds_sync();
 
@@ -288,11 +292,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
             }
             wave_lds_sync();
             // P out as fragment blocks
+            if constexpr (kFwd) {
 #pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
-                const int a = qq >> 1, s = qq & 1;
-                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(sP + (16 * a + c) * kRP + 32 * s + 8 * g4),
-                                            reinterpret_cast<u32x4 *>(rec + kTileElems + frag_off(a, s, lane)));
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int a = qq >> 1, s = qq & 1;
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(sP + (16 * a + c) * kRP + 32 * s + 8 * g4),
+                                                reinterpret_cast<u32x4 *>(rec + kTileElems + frag_off(a, s, lane)));
+                }
             }
             if constexpr (kBwd) {
                 // P^T block (a, s): lane (c, g4) holds P[32 s + 8 g4 + j][16 a + c], j = 0..7
@@ -386,19 +392,21 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
             wave_lds_sync();
 
             // T' = T diag(b) (zero above the diagonal blocks) out as fragment blocks
+            if constexpr (kFwd) {
 #pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
-                const int a = qq >> 1, s = qq & 1;
-                const int row = 16 * a + c, ca = 32 * s + 8 * g4, cb = ca + 4;
-                const float4 t0 = *reinterpret_cast<const float4 *>(A + row * kAP + ca);
-                const float4 t1 = *reinterpret_cast<const float4 *>(A + row * kAP + cb);
-                const float4 b0 = *reinterpret_cast<const float4 *>(sBt + ca);
-                const float4 b1 = *reinterpret_cast<const float4 *>(sBt + cb);
-                const bool la = (ca >> 4) <= a, lb = la;   // 8 columns in one 16-column block
-                const uint2 u0 = la ? pk4(t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w) : make_uint2(0, 0);
-                const uint2 u1 = lb ? pk4(t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w) : make_uint2(0, 0);
-                __builtin_nontemporal_store(u32x4{u0.x, u0.y, u1.x, u1.y},
-                                            reinterpret_cast<u32x4 *>(rec + frag_off(a, s, lane)));
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int a = qq >> 1, s = qq & 1;
+                    const int row = 16 * a + c, ca = 32 * s + 8 * g4, cb = ca + 4;
+                    const float4 t0 = *reinterpret_cast<const float4 *>(A + row * kAP + ca);
+                    const float4 t1 = *reinterpret_cast<const float4 *>(A + row * kAP + cb);
+                    const float4 b0 = *reinterpret_cast<const float4 *>(sBt + ca);
+                    const float4 b1 = *reinterpret_cast<const float4 *>(sBt + cb);
+                    const bool la = (ca >> 4) <= a, lb = la;   // 8 columns in one 16-column block
+                    const uint2 u0 = la ? pk4(t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w) : make_uint2(0, 0);
+                    const uint2 u1 = lb ? pk4(t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w) : make_uint2(0, 0);
+                    __builtin_nontemporal_store(u32x4{u0.x, u0.y, u1.x, u1.y},
+                                                reinterpret_cast<u32x4 *>(rec + frag_off(a, s, lane)));
+                }
             }
             if constexpr (kBwd) {
                 // T'^T block (a, s): lane (c, g4) holds T'[r][16 a + c] for the rows
@@ -473,12 +481,15 @@ struct OutRegs {          // waves 4-7
 // apply conv and SiLU (the prelude's arithmetic) to the raw v rows of chunk
 // ci + 1 and write them into the other half of a double-buffered v tile.
 //
-// For the backward pass (kSave) the output waves compute no outputs: they
-// copy the bf16 state each chunk starts from (the values the chunk's products
-// use) out of LDS into states [chunk][H_v][d_v][d_k].  (Stores issued by the
-// state waves would lengthen their chain: the waits for their own prefetched
-// loads would also cover the stores.)
-template <bool kRaw, bool kSave = false>
+// kOut selects what the output waves write: kOutO the outputs o; kOutStates
+// (the backward's own forward pass) no outputs but the bf16 state each chunk
+// starts from (the values the chunk's products use), copied out of LDS into
+// states [chunk][H_v][d_v][d_k]; kOutBoth both (a forward pass that keeps the
+// states for a later backward).  (Stores issued by the state waves would
+// lengthen their chain: the waits for their own prefetched loads would also
+// cover the stores.)
+constexpr int kOutO = 0, kOutStates = 1, kOutBoth = 2;
+template <bool kRaw, int kOut = kOutO>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const RawIn raw, const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
@@ -682,7 +693,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     *reinterpret_cast<float4 *>(final_state + st_off + (size_t)(e0 + 16 * nt + c) * kD + 32 * w + 16 * t + 4 * g4) =
                         make_float4(st[t][nt][0], st[t][nt][1], st[t][nt][2], st[t][nt][3]);
         }
-    } else if constexpr (kSave) {
+    } else if constexpr (kOut == kOutStates) {
         // ---------------- output waves, backward pass: the start states out
         const int ol = threadIdx.x - 256;
         __syncthreads();                                       // matches the state waves' first barrier
@@ -761,6 +772,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 for (int nt = 0; nt < 2; ++nt)
                     ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), qA[s], ao[nt]);
             const float gq = scale * __expf(cur.Gown);
+            if constexpr (kOut == kOutBoth) {
+                // sS holds the state chunk ci starts from until barrier (2)
+                uint16_t *sp = states + ((size_t)(cbase + ci) * H_v + h) * (kD * kD) + (size_t)e0 * kD;
+                const int ol = threadIdx.x - 256;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int e = ol + 256 * m, r = e >> 4, pcs = 8 * (e & 15);
+                    *reinterpret_cast<u32x4 *>(sp + r * kD + pcs) = *reinterpret_cast<const u32x4 *>(sS + r * kKP + pcs);
+                }
+            }
             __syncthreads();                                   // (1)
             // next loads issued while the state waves form U: the vector
             // memory pipe is then quiet while they form X and R
@@ -775,7 +796,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 8 * g4), cur.pA[0], a);
                 if (w >= 2)
                     a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 32 + 8 * g4), cur.pA[1], a);
-                if (row_ok && !kSave)
+                if (row_ok)
                     *reinterpret_cast<uint2 *>(o + ((size_t)(c0 + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
                         pk4(a[0], a[1], a[2], a[3]);
             }
@@ -899,7 +920,7 @@ template <bool kRaw>
 hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, RawIn raw,
                        const float *g, const float *beta, const float *S0, float *S_final,
                        const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, float scale,
-                       uint16_t *o16, void *workspace, hipStream_t stream) {
+                       uint16_t *o16, uint16_t *states, void *workspace, hipStream_t stream) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
     Workspace W;
     workspace_layout(N, T, H_qk, H_v, kRaw, workspace, &W);
@@ -917,9 +938,14 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
         return hipGetLastError();
     };
     auto scan = [&](int c_lo, int c_hi, const float *init, float *fin) {
-        hipLaunchKernelGGL(scan_kernel<kRaw>, dim3(scan_grid), dim3(512), 0, stream, q16, k16, v16,
-                           raw, init, fin, cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo,
-                           c_hi, ws, o16);
+        if (states)
+            hipLaunchKernelGGL((scan_kernel<kRaw, kOutBoth>), dim3(scan_grid), dim3(512), 0, stream,
+                               q16, k16, v16, raw, init, fin, cu_seqlens, chunk_base, N, T, H_qk,
+                               H_v, scale, c_lo, c_hi, ws, o16, states);
+        else
+            hipLaunchKernelGGL((scan_kernel<kRaw, kOutO>), dim3(scan_grid), dim3(512), 0, stream,
+                               q16, k16, v16, raw, init, fin, cu_seqlens, chunk_base, N, T, H_qk,
+                               H_v, scale, c_lo, c_hi, ws, o16, nullptr);
         return hipGetLastError();
     };
 
@@ -967,30 +993,37 @@ struct BwdWorkspace {
     int32_t *chunk_base;
     uint16_t *rec, *brec, *states, *dsw, *duw;
 };
-size_t bwd_workspace_layout(int N, int T, int H_v, void *base, BwdWorkspace *wsp) {
+// Given the chunk states of an earlier forward pass, the workspace has no
+// states region and the forward records are not kept.
+size_t bwd_workspace_layout(int N, int T, int H_v, bool saved, void *base, BwdWorkspace *wsp) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
     const size_t head = align256((size_t)(N + 1) * sizeof(int32_t));
-    const size_t rec = max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);
+    const size_t rec = saved ? 0 : max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);
     const size_t brec = max_chunks * (size_t)H_v * kBwdRecElems * sizeof(uint16_t);
     const size_t st = max_chunks * (size_t)H_v * kD * kD * sizeof(uint16_t);
+    const size_t own = saved ? 0 : st;
     const size_t du = max_chunks * kChunk * (size_t)H_v * kD * sizeof(uint16_t);
     if (wsp) {
         char *p = static_cast<char *>(base);
         wsp->chunk_base = reinterpret_cast<int32_t *>(p);
-        wsp->rec = reinterpret_cast<uint16_t *>(p + head);
+        wsp->rec = saved ? nullptr : reinterpret_cast<uint16_t *>(p + head);
         wsp->brec = reinterpret_cast<uint16_t *>(p + head + rec);
-        wsp->states = reinterpret_cast<uint16_t *>(p + head + rec + brec);
-        wsp->dsw = reinterpret_cast<uint16_t *>(p + head + rec + brec + st);
-        wsp->duw = reinterpret_cast<uint16_t *>(p + head + rec + brec + 2 * st);
+        wsp->states = saved ? nullptr : reinterpret_cast<uint16_t *>(p + head + rec + brec);
+        wsp->dsw = reinterpret_cast<uint16_t *>(p + head + rec + brec + own);
+        wsp->duw = reinterpret_cast<uint16_t *>(p + head + rec + brec + own + st);
     }
-    return head + rec + brec + 2 * st + du;
+    return head + rec + brec + own + st + du;
 }
 
 }  // namespace
 
-size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v) {
+size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v, bool saved) {
     (void)H_qk;
-    return bwd_workspace_layout(N, T, H_v, nullptr, nullptr);
+    return bwd_workspace_layout(N, T, H_v, saved, nullptr, nullptr);
+}
+
+size_t chunk_states_bytes(int N, int T, int H_v) {
+    return ((size_t)(T + kChunk - 1) / kChunk + (size_t)N) * (size_t)H_v * kD * kD * sizeof(uint16_t);
 }
 
 // plan -> prep (forward and backward records) -> forward scan storing each
@@ -998,33 +1031,47 @@ size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v) {
 // dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta), all on `stream`.
 // (The two scans need only prep's records, but 512-thread workgroups of both
 // do not fit one CU together, so running them side by side gains nothing.)
+// With chunk_states from an earlier forward pass (gdn_prefill with states
+// kept), prep writes only the backward records and the forward scan is
+// skipped.
 hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *S0, const int32_t *cu_seqlens,
                                    int N, int T, int H_qk, int H_v, float scale, const void *d_o,
                                    const float *dS_final, void *dq, void *dk, void *dv, float *dg,
-                                   float *dbeta, float *dS0, void *workspace, hipStream_t stream) {
+                                   float *dbeta, float *dS0, const void *chunk_states,
+                                   void *workspace, hipStream_t stream) {
     const int max_chunks = (T + kChunk - 1) / kChunk + N;
     BwdWorkspace W;
-    bwd_workspace_layout(N, T, H_v, workspace, &W);
+    const bool saved = chunk_states != nullptr;
+    bwd_workspace_layout(N, T, H_v, saved, workspace, &W);
     const uint16_t *q16 = static_cast<const uint16_t *>(q), *k16 = static_cast<const uint16_t *>(k);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, W.chunk_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int items = max_chunks * H_qk;
-    hipLaunchKernelGGL((prep_kernel<false, true>), dim3((items + kPrepWaves - 1) / kPrepWaves),
-                       dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
-                       W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
+    if (saved)
+        hipLaunchKernelGGL((prep_kernel<false, kRecBwd>), dim3((items + kPrepWaves - 1) / kPrepWaves),
+                           dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
+                           W.chunk_base, N, T, H_qk, H_v, scale, 0, items, nullptr, W.brec);
+    else
+        hipLaunchKernelGGL((prep_kernel<false, kRecFwd | kRecBwd>), dim3((items + kPrepWaves - 1) / kPrepWaves),
+                           dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
+                           W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_kernel<false, true>), dim3(N * H_v * kSlabsW), dim3(512), 0, stream,
-                       q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
-                       cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
-                       nullptr, W.states);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const void *states = chunk_states;
+    if (!saved) {
+        hipLaunchKernelGGL((scan_kernel<false, kOutStates>), dim3(N * H_v * kSlabsW), dim3(512), 0,
+                           stream, q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
+                           cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
+                           nullptr, W.states);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        states = W.states;
+    }
     if ((e = launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
                              W.brec, W.dsw, W.duw, dv, dS0, stream)) != hipSuccess)
         return e;
     return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
-                           max_chunks, scale, W.brec, W.states, W.dsw, W.duw, dq, dk, dg, dbeta,
+                           max_chunks, scale, W.brec, states, W.dsw, W.duw, dq, dk, dg, dbeta,
                            stream);
 }
 
@@ -1035,20 +1082,23 @@ size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw) {
 hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, const float *S0, float *S_final,
                                   const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
-                                  float scale, void *o, void *workspace, hipStream_t stream) {
+                                  float scale, void *o, void *chunk_states, void *workspace,
+                                  hipStream_t stream) {
     return launch_impl<false>(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                               static_cast<const uint16_t *>(v), RawIn{}, g, beta, S0, S_final,
                               cu_seqlens, N, T, H_qk, H_v, scale, static_cast<uint16_t *>(o),
-                              workspace, stream);
+                              static_cast<uint16_t *>(chunk_states), workspace, stream);
 }
 
 hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, const float *g,
                                       const float *beta, const float *S0, float *S_final,
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
-                                      float scale, void *o, void *workspace, hipStream_t stream) {
+                                      float scale, void *o, void *chunk_states, void *workspace,
+                                      hipStream_t stream) {
     RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr};
     return launch_impl<true>(nullptr, nullptr, nullptr, raw, g, beta, S0, S_final, cu_seqlens, N, T,
-                             H_qk, H_v, scale, static_cast<uint16_t *>(o), workspace, stream);
+                             H_qk, H_v, scale, static_cast<uint16_t *>(o),
+                             static_cast<uint16_t *>(chunk_states), workspace, stream);
 }
 
 }  // namespace gdn

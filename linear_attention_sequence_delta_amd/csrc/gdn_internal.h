@@ -28,24 +28,31 @@ hipError_t launch_recurrent_prefill(int io_dtype, const void *q, const void *k, 
                                     int H_qk, int H_v, float scale, void *o, hipStream_t stream);
 
 // Chunked bf16 prefill (64-token chunks, bf16 matrix-core products); `raw`:
-// from the raw projections, with the conv prelude fused.
+// from the raw projections, with the conv prelude fused.  chunk_states (or
+// NULL): bf16 [chunks][H_v][d_v][d_k], the state each chunk starts from, kept
+// for a later backward (chunk_states_bytes of them).
 size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw);
+size_t chunk_states_bytes(int N, int T, int H_v);
 hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, const float *S0, float *S_final,
                                   const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
-                                  float scale, void *o, void *workspace, hipStream_t stream);
+                                  float scale, void *o, void *chunk_states, void *workspace,
+                                  hipStream_t stream);
 hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, const float *g,
                                       const float *beta, const float *S0, float *S_final,
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
-                                      float scale, void *o, void *workspace, hipStream_t stream);
+                                      float scale, void *o, void *chunk_states, void *workspace,
+                                      hipStream_t stream);
 
-// Gradients of the chunked bf16 prefill (dq, dk, dv bf16; dg, dbeta, dS0 fp32).
-size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v);
+// Gradients of the chunked bf16 prefill (dq, dk, dv bf16; dg, dbeta, dS0 fp32);
+// `saved` / chunk_states: with the chunk states of an earlier forward pass.
+size_t chunked_backward_workspace_bytes(int N, int T, int H_qk, int H_v, bool saved);
 hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *S0, const int32_t *cu_seqlens,
                                    int N, int T, int H_qk, int H_v, float scale, const void *d_o,
                                    const float *dS_final, void *dq, void *dk, void *dv, float *dg,
-                                   float *dbeta, float *dS0, void *workspace, hipStream_t stream);
+                                   float *dbeta, float *dS0, const void *chunk_states,
+                                   void *workspace, hipStream_t stream);
 hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const float *dS_final,
                            const int32_t *cu_seqlens, const int32_t *chunk_base, int N, int T,
                            int H_qk, int H_v, float scale, const void *bws, void *dsw, void *duw,

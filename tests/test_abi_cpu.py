@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert decl == sorted(gdn.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == 2
 
 
 def _prefill(L, **kw):
@@ -338,3 +338,93 @@ def test_gated_norm_backward_rejects_bad_arguments():
     assert call(dz=d_o) == gdn.GDN_ERR_INVALID_ARG             # dz overlaps d_o
     assert L.gdn_gated_norm_backward_workspace_size(64, 128) > 0
     assert L.gdn_gated_norm_backward_workspace_size(64, 64) == 0
+
+
+def _prefill_save(L, **kw):
+    """gdn_prefill_save_states with far-apart fake device addresses (rejected
+    on the host before any device call)."""
+    a = dict(q=0x10000000, k=0x20000000, v=0x30000000, g=0x40000000, beta=0x50000000, S0=None,
+             Sf=None, cu=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0,
+             o=0x60000000, cs=0x1000000000, cs_bytes=1 << 40, ws=0x70000000, ws_bytes=1 << 28,
+             stream=None)
+    a.update(kw)
+    return L.gdn_prefill_save_states(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["Sf"],
+                                     a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"],
+                                     a["d_v"], a["scale"], a["o"], a["cs"], a["cs_bytes"], a["ws"],
+                                     a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs_bytes=1024), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs=0x10000000), gdn.GDN_ERR_INVALID_ARG),            # chunk_states overlaps q
+    (dict(cs=0x70000000), gdn.GDN_ERR_INVALID_ARG),            # chunk_states overlaps the workspace
+    (dict(d_k=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), gdn.GDN_ERR_WORKSPACE),
+])
+def test_prefill_save_states_rejects_bad_arguments(kw, code):
+    L = gdn.lib()
+    assert _prefill_save(L, **kw) == code
+    assert L.gdn_last_error().decode()
+
+
+def _prefill_raw_save(L, **kw):
+    a = dict(x=0x10000000, w=0x20000000, eps=1e-6, g=0x40000000, beta=0x50000000, S0=None,
+             Sf=None, cu=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0,
+             o=0x60000000, cs=0x1000000000, cs_bytes=1 << 40, ws=0x70000000, ws_bytes=1 << 28,
+             stream=None)
+    a.update(kw)
+    return L.gdn_prefill_raw_save_states(a["x"], a["w"], a["eps"], a["g"], a["beta"], a["S0"],
+                                         a["Sf"], a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"],
+                                         a["d_k"], a["d_v"], a["scale"], a["o"], a["cs"],
+                                         a["cs_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs_bytes=1024), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs=0x10000000), gdn.GDN_ERR_INVALID_ARG),            # chunk_states overlaps x
+    (dict(eps=-1.0), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_prefill_raw_save_states_rejects_bad_arguments(kw, code):
+    assert _prefill_raw_save(gdn.lib(), **kw) == code
+
+
+def _backward_saved(L, **kw):
+    a = dict(q=0x10000000, k=0x20000000, v=0x30000000, g=0x40000000, beta=0x50000000,
+             cs=0x1000000000, cs_bytes=1 << 40, cu=None, d_o=0x60000000, dSf=None, N=1, T=64,
+             H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0, dq=0x70000000, dk=0x80000000,
+             dv=0x90000000, dg=0xA0000000, db=0xB0000000, dS0=None, ws=0xC0000000,
+             ws_bytes=1 << 34, stream=None)
+    a.update(kw)
+    return L.gdn_prefill_backward_saved(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cs"],
+                                        a["cs_bytes"], a["cu"], a["d_o"], a["dSf"], a["N"], a["T"],
+                                        a["H_qk"], a["H_v"], a["d_k"], a["d_v"], a["scale"],
+                                        a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dS0"],
+                                        a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs_bytes=1024), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dq=0x1000000000), gdn.GDN_ERR_INVALID_ARG),          # dq overlaps chunk_states
+    (dict(ws=0x1000000000), gdn.GDN_ERR_INVALID_ARG),          # workspace overlaps chunk_states
+    (dict(ws_bytes=1024), gdn.GDN_ERR_WORKSPACE),
+    (dict(dq=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(H_v=47), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_prefill_backward_saved_rejects_bad_arguments(kw, code):
+    assert _backward_saved(gdn.lib(), **kw) == code
+
+
+def test_chunk_states_and_saved_workspace_sizes():
+    assert gdn.gdn_chunk_states_size(1, 32768, 48) == (512 + 1) * 48 * 128 * 128 * 2
+    assert gdn.gdn_chunk_states_size(3, 100, 48) == (2 + 3) * 48 * 128 * 128 * 2
+    assert gdn.gdn_chunk_states_size(1, 0, 48) == 48 * 128 * 128 * 2
+    assert gdn.gdn_chunk_states_size(0, 64, 48) == 0
+    assert gdn.gdn_chunk_states_size(1, 64, 48, 64, 128) == 0
+    full = gdn.gdn_prefill_backward_workspace_size(1, 32768, 16, 48)
+    saved = gdn.gdn_prefill_backward_saved_workspace_size(1, 32768, 16, 48)
+    # the saved form drops the states and the forward records
+    assert 0 < saved < full - gdn.gdn_chunk_states_size(1, 32768, 48)
+    assert gdn.gdn_prefill_backward_saved_workspace_size(0, 64, 16, 48) == 0
