@@ -209,7 +209,38 @@ def run_gpu(steps, warmup, path="both"):
         b1.record()
         torch.cuda.synchronize()
         res["bwd_us"] = b0.elapsed_time(b1) / bsteps * 1e3
-        del q, k, v, wsb
+        # a training pair: the forward keeps the chunk states (from the raw
+        # projections, prelude fused), the backward reads them
+        del wsb
+        cs = torch.empty(gdn.gdn_chunk_states_size(1, p.T, H_V) // 2, dtype=torch.bfloat16, device=dev)
+        wsf = torch.empty(gdn.gdn_prefill_raw_workspace_size(1, p.T, H_QK, H_V), dtype=torch.uint8,
+                          device=dev)
+        wss = torch.empty(gdn.gdn_prefill_backward_saved_workspace_size(1, p.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
+
+        def fwd_keep():
+            gdn.gdn_prefill_raw(x, w, g, beta, None, None, H_qk=H_QK, H_v=H_V, final_state=fs, o=o,
+                                workspace=wsf, chunk_states=cs)
+
+        def bwd_saved():
+            gdn.gdn_prefill_backward(q, k, v, g, beta, d_o, workspace=wss, chunk_states=cs)
+
+        for _ in range(max(warmup, 1)):
+            fwd_keep()
+            bwd_saved()
+        torch.cuda.synchronize()
+        ev = [(_events(torch), _events(torch)) for _ in range(bsteps)]
+        for (a0, a1), (c0, c1) in ev:
+            a0.record()
+            fwd_keep()
+            a1.record()
+            c0.record()
+            bwd_saved()
+            c1.record()
+        torch.cuda.synchronize()
+        res["fwd_keep_us"] = sum(a0.elapsed_time(a1) for (a0, a1), _ in ev) / bsteps * 1e3
+        res["bwd_saved_us"] = sum(c0.elapsed_time(c1) for _, (c0, c1) in ev) / bsteps * 1e3
+        del q, k, v, cs, wsf, wss
         # the whole layer's backward from the raw projections
         A_log = to_dev(p.meta["A_log"].astype(np.float32))
         dtb = to_dev(p.meta["dt_bias"].astype(np.float32))
@@ -586,7 +617,14 @@ def main():
                                      "what": "gdn_layer_prefill_backward from the raw projections "
                                              "(gates and prelude recomputed, the recurrence's "
                                              "gradients, then through the prelude and gates): "
-                                             "dx, dconv_w, da, db, dA_log, ddt_bias"}}
+                                             "dx, dconv_w, da, db, dA_log, ddt_bias"},
+                           "from_kept_states": {
+                               "forward_us": r["fwd_keep_us"], "backward_us": r["bwd_saved_us"],
+                               "pair_us": r["fwd_keep_us"] + r["bwd_saved_us"],
+                               "pair_tokens_per_s": T / ((r["fwd_keep_us"] + r["bwd_saved_us"]) * 1e-6),
+                               "what": "a training pair: gdn_prefill_raw keeping the chunk states, "
+                                       "then gdn_prefill_backward reading them (the forward scan "
+                                       "is not repeated)"}}
     if "pre_us" in r:
         out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",
                                    "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,
