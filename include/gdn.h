@@ -335,6 +335,31 @@ int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const floa
                                void *stream);
 
 /*
+ * gdn_layer_prefill_backward_saved_workspace_size,
+ * gdn_layer_prefill_backward_saved -- gdn_layer_prefill_backward given the
+ * chunk states that gdn_layer_prefill_save_states kept on the same inputs
+ * (initial_state is then not an argument: the states carry it).  The forward
+ * pass over the chunks is not repeated; the gradients are bit-identical.
+ *
+ *   chunk_states, cs_bytes   device bf16, at least gdn_chunk_states_size(...)
+ *                            bytes, read only; other arguments as for
+ *                            gdn_layer_prefill_backward
+ * GDN_ERR_INVALID_ARG for a NULL or short chunk_states; the overlap rules of
+ * gdn_layer_prefill_backward apply with chunk_states among the inputs.
+ */
+size_t gdn_layer_prefill_backward_saved_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
+                                                       int d_v);
+int gdn_layer_prefill_backward_saved(const void *x_raw, const void *conv_w, const float *a,
+                                     const float *b, const float *A_log, const float *dt_bias,
+                                     float l2_eps, const void *chunk_states, size_t cs_bytes,
+                                     const int32_t *cu_seqlens, const void *d_o,
+                                     const float *d_final_state, int N, int T, int H_qk, int H_v,
+                                     int d_k, int d_v, float scale, void *dx_raw, float *dconv_w,
+                                     float *da, float *db, float *dA_log, float *ddt_bias,
+                                     float *d_initial_state, void *workspace, size_t ws_bytes,
+                                     void *stream);
+
+/*
  * gdn_gates -- the layer's gates from its raw per-token projections a, b:
  *     g    = -softplus(a + dt_bias[h]) * exp(A_log[h])   (log decay, a_t = exp(g))
  *     beta = sigmoid(b)
@@ -374,6 +399,23 @@ int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, con
                       const float *initial_state, float *final_state, void *conv_state_out,
                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
                       float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_layer_prefill_save_states -- gdn_layer_prefill that also keeps the
+ * chunk states for gdn_layer_prefill_backward_saved (as
+ * gdn_prefill_raw_save_states does; outputs bit-identical to gdn_layer_prefill).
+ *
+ *   chunk_states, cs_bytes   device bf16 output of at least
+ *                            gdn_chunk_states_size(N, T, H_v, d_k, d_v) bytes,
+ *                            overlapping no other argument
+ */
+int gdn_layer_prefill_save_states(const void *x_raw, const void *conv_w, const float *a,
+                                  const float *b, const float *A_log, const float *dt_bias,
+                                  float l2_eps, const float *initial_state, float *final_state,
+                                  void *conv_state_out, const int32_t *cu_seqlens, int N, int T,
+                                  int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                                  void *chunk_states, size_t cs_bytes, void *workspace,
+                                  size_t ws_bytes, void *stream);
 
 /*
  * gdn_layer_decode_step -- one token for each of B sequences from its raw

@@ -36,7 +36,9 @@ EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_state_rollback", "gdn_gated_norm", "gdn_gated_norm_backward_workspace_size",
            "gdn_gated_norm_backward", "gdn_decode_step", "gdn_chunk_states_size",
            "gdn_prefill_save_states", "gdn_prefill_raw_save_states",
-           "gdn_prefill_backward_saved_workspace_size", "gdn_prefill_backward_saved")
+           "gdn_prefill_backward_saved_workspace_size", "gdn_prefill_backward_saved",
+           "gdn_layer_prefill_save_states", "gdn_layer_prefill_backward_saved_workspace_size",
+           "gdn_layer_prefill_backward_saved")
 
 _lib = None
 
@@ -115,6 +117,14 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_backward_saved.argtypes = [P, P, P, P, P, P, Z, P, P, P, I, I, I, I, I, I, F, P,
                                              P, P, P, P, P, P, Z, P]
     L.gdn_prefill_backward_saved.restype = I
+    L.gdn_layer_prefill_save_states.argtypes = [P, P, P, P, P, P, F, P, P, P, P, I, I, I, I, I, I,
+                                                F, P, P, Z, P, Z, P]
+    L.gdn_layer_prefill_save_states.restype = I
+    L.gdn_layer_prefill_backward_saved_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_layer_prefill_backward_saved_workspace_size.restype = Z
+    L.gdn_layer_prefill_backward_saved.argtypes = [P, P, P, P, P, P, F, P, Z, P, P, P, I, I, I, I,
+                                                   I, I, F, P, P, P, P, P, P, P, P, Z, P]
+    L.gdn_layer_prefill_backward_saved.restype = I
     _lib = L
     return L
 
@@ -388,8 +398,10 @@ def gdn_layer_prefill_backward(x, conv_w, a, b, A_log, dt_bias, d_o, initial_sta
                                d_final_state=None, cu_seqlens=None, *, H_qk: int = 16,
                                H_v: int = 48, d_k: int = 128, d_v: int = 128,
                                l2_eps: float = 1e-6, scale: float = 1.0, d_initial_state=True,
-                               workspace=None):
-    """Gradients of gdn_layer_prefill.  x: bf16 [T, C_raw]; conv_w: bf16
+                               workspace=None, chunk_states=None):
+    """Gradients of gdn_layer_prefill (chunk_states: the buffer a
+    gdn_layer_prefill with chunk_states filled on the same inputs; then
+    initial_state is not read).  x: bf16 [T, C_raw]; conv_w: bf16
     [C_raw, 4]; a, b: fp32 [T, H_v]; A_log, dt_bias: fp32 [H_v]; d_o: bf16
     [T, H_v, d_v]; initial_state, d_final_state: fp32 [N, H_v, 128, 128] or None.
     Returns (dx bf16, dconv_w fp32 [C_raw, 4], da, db, dA_log, ddt_bias,
@@ -435,6 +447,21 @@ def gdn_layer_prefill_backward(x, conv_w, a, b, A_log, dt_bias, d_o, initial_sta
     dw = torch.empty((C, 4), dtype=torch.float32, device=dev)
     da, db = torch.empty_like(a), torch.empty_like(b)
     dA, ddt = torch.empty_like(A_log), torch.empty_like(dt_bias)
+    if chunk_states is not None:
+        if chunk_states is True:
+            raise ValueError("chunk_states must be the buffer the forward pass filled")
+        kst, k_bytes = _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev)
+        need = int(lib().gdn_layer_prefill_backward_saved_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc = lib().gdn_layer_prefill_backward_saved(
+            _ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), float(l2_eps),
+            _ptr(kst), k_bytes, _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), N, T, H_qk, H_v,
+            d_k, d_v, float(scale), _ptr(dx), _ptr(dw), _ptr(da), _ptr(db), _ptr(dA), _ptr(ddt),
+            _ptr(dS0), _ptr(workspace), ws_bytes, _stream(dev))
+        _check(rc, "gdn_layer_prefill_backward_saved")
+        return dx, dw, da, db, dA, ddt, dS0
     need = gdn_layer_prefill_backward_workspace_size(N, T, H_qk, H_v, d_k, d_v)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -552,12 +579,13 @@ def gdn_layer_prefill_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: i
 def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_seqlens=None, *,
                       H_qk: int = 16, H_v: int = 48, d_k: int = 128, d_v: int = 128,
                       l2_eps: float = 1e-6, scale: float = 1.0, final_state=True,
-                      conv_state=True, o=None, workspace=None):
+                      conv_state=True, o=None, workspace=None, chunk_states=None):
     """The layer's prefill from raw projections: gates from a, b, then the fused
     prelude + chunked prefill, then each sequence's conv history.  x: bf16
     [T, C_raw]; a, b: fp32 [T, H_v]; A_log, dt_bias: fp32 [H_v].  final_state /
     conv_state: True (allocate), False/None (skip) or a tensor to write
-    (conv_state: bf16 [N, 3, C_raw]).  Returns (o, final_state, conv_state)."""
+    (conv_state: bf16 [N, 3, C_raw]); chunk_states as for gdn_prefill.  Returns
+    (o, final_state, conv_state), plus chunk_states when it is given."""
     torch = _torch()
     dev = _device_of(x)
     _need(x, "x", torch.bfloat16, dev, 2)
@@ -600,6 +628,14 @@ def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_se
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if chunk_states is not None:
+        kst, k_bytes = _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev)
+        rc = lib().gdn_layer_prefill_save_states(
+            _ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), float(l2_eps),
+            _ptr(initial_state), _ptr(fs), _ptr(cs), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v,
+            float(scale), _ptr(o), _ptr(kst), k_bytes, _ptr(workspace), ws_bytes, _stream(dev))
+        _check(rc, "gdn_layer_prefill_save_states")
+        return o, fs, cs, kst
     rc = lib().gdn_layer_prefill(_ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log),
                                  _ptr(dt_bias), float(l2_eps), _ptr(initial_state), _ptr(fs),
                                  _ptr(cs), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v,

@@ -282,7 +282,7 @@ namespace {
 struct LayerBwdWs {
     size_t g, q, v, part, gpart, total;
 };
-LayerBwdWs layer_bwd_ws(int N, int T, int H_qk, int H_v) {
+LayerBwdWs layer_bwd_ws(int N, int T, int H_qk, int H_v, bool saved) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     LayerBwdWs w;
     w.g = al((size_t)T * H_v * 4);
@@ -291,7 +291,7 @@ LayerBwdWs layer_bwd_ws(int N, int T, int H_qk, int H_v) {
     w.part = al(gdn::prelude_bwd_partial_bytes(T, H_qk, H_v));
     w.gpart = al(gdn::gates_bwd_partial_bytes(H_v));
     w.total = 4 * w.g + 4 * w.q + 2 * w.v + w.part + w.gpart +
-              gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v, false);
+              gdn::chunked_backward_workspace_bytes(N, T, H_qk, H_v, saved);
     return w;
 }
 }  // namespace
@@ -468,18 +468,22 @@ size_t gdn_layer_prefill_backward_workspace_size(int N, int T, int H_qk, int H_v
     (void)d_k;
     (void)d_v;
     if (N < 1 || T < 0 || H_qk < 1 || H_v < 1) return 0;
-    return layer_bwd_ws(N, T, H_qk, H_v).total;
+    return layer_bwd_ws(N, T, H_qk, H_v, false).total;
 }
 
-int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const float *a,
-                               const float *b, const float *A_log, const float *dt_bias,
-                               float l2_eps, const float *initial_state,
-                               const int32_t *cu_seqlens, const void *d_o,
-                               const float *d_final_state, int N, int T, int H_qk, int H_v,
-                               int d_k, int d_v, float scale, void *dx_raw, float *dconv_w,
-                               float *da, float *db, float *dA_log, float *ddt_bias,
-                               float *d_initial_state, void *workspace, size_t ws_bytes,
-                               void *stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_layer_prefill_backward, and with chunk_states gdn_layer_prefill_backward_saved.
+int layer_backward_impl(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                        const float *A_log, const float *dt_bias, float l2_eps,
+                        const float *initial_state, const void *chunk_states, size_t cs_bytes,
+                        const int32_t *cu_seqlens, const void *d_o, const float *d_final_state,
+                        int N, int T, int H_qk, int H_v, int d_k, int d_v, float scale,
+                        void *dx_raw, float *dconv_w, float *da, float *db, float *dA_log,
+                        float *ddt_bias, float *d_initial_state, void *workspace, size_t ws_bytes,
+                        void *stream) {
     int rc;
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
@@ -494,7 +498,11 @@ int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const floa
                     "conv_w, A_log, dt_bias, dconv_w, dA_log and ddt_bias must be non-NULL");
     if (T > 0 && (!x_raw || !a || !b || !d_o || !dx_raw || !da || !db))
         return fail(GDN_ERR_INVALID_ARG, "x_raw, a, b, d_o, dx_raw, da and db must be non-NULL");
-    const LayerBwdWs L = layer_bwd_ws(N, T, H_qk, H_v);
+    const bool saved = chunk_states != nullptr;
+    const size_t ncs = saved ? gdn_chunk_states_size(N, T, H_v, d_k, d_v) : 0;
+    if (saved && cs_bytes < ncs)
+        return fail(GDN_ERR_INVALID_ARG, "chunk_states of %zu bytes given, %zu needed", cs_bytes, ncs);
+    const LayerBwdWs L = layer_bwd_ws(N, T, H_qk, H_v, saved);
     if (ws_bytes < L.total || !workspace)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, L.total);
     const size_t craw = (size_t)(2 * H_qk + H_v) * gdn::kD;
@@ -503,7 +511,8 @@ int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const floa
     const size_t ns = (size_t)N * H_v * gdn::kD * gdn::kD * 4;
     const struct { const void *p; size_t n; } in[] = {
         {x_raw, nx}, {conv_w, nw}, {a, ng}, {b, ng}, {A_log, nh}, {dt_bias, nh},
-        {initial_state, ns}, {d_o, nv}, {d_final_state, ns}, {cu_seqlens, (size_t)(N + 1) * 4}};
+        {initial_state, ns}, {d_o, nv}, {d_final_state, ns}, {cu_seqlens, (size_t)(N + 1) * 4},
+        {chunk_states, ncs}};
     const struct { const void *p; size_t n; } out[] = {
         {dx_raw, nx}, {dconv_w, nwf}, {da, ng}, {db, ng}, {dA_log, nh}, {ddt_bias, nh},
         {d_initial_state, ns}, {workspace, L.total}};
@@ -534,9 +543,10 @@ int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const floa
             e = gdn::launch_conv_prelude(x_raw, conv_w, cu_seqlens, N, T, H_qk, H_v, l2_eps, q, k, v, s);
     }
     if (e == hipSuccess)
-        e = gdn::launch_chunked_backward(q, k, v, g, beta, initial_state, cu_seqlens, N, T, H_qk, H_v,
-                                         scale, d_o, d_final_state, dq, dk, dv, dg, dbeta,
-                                         d_initial_state, nullptr, rest, s);
+        e = gdn::launch_chunked_backward(q, k, v, g, beta, saved ? nullptr : initial_state,
+                                         cu_seqlens, N, T, H_qk, H_v, scale, d_o, d_final_state,
+                                         dq, dk, dv, dg, dbeta, d_initial_state, chunk_states,
+                                         rest, s);
     if (e == hipSuccess)
         e = gdn::launch_prelude_bwd(x_raw, conv_w, cu_seqlens, N, T, H_qk, H_v, l2_eps, dq, dk, dv,
                                     dx_raw, dconv_w, part, s);
@@ -544,6 +554,49 @@ int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const floa
         e = gdn::launch_gates_bwd(a, b, A_log, dt_bias, dg, dbeta, T, H_v, da, db, dA_log, ddt_bias,
                                   gpart, s);
     return finish(e, s, "gdn_layer_prefill_backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_layer_prefill_backward(const void *x_raw, const void *conv_w, const float *a,
+                               const float *b, const float *A_log, const float *dt_bias,
+                               float l2_eps, const float *initial_state,
+                               const int32_t *cu_seqlens, const void *d_o,
+                               const float *d_final_state, int N, int T, int H_qk, int H_v,
+                               int d_k, int d_v, float scale, void *dx_raw, float *dconv_w,
+                               float *da, float *db, float *dA_log, float *ddt_bias,
+                               float *d_initial_state, void *workspace, size_t ws_bytes,
+                               void *stream) {
+    return layer_backward_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state, nullptr,
+                               0, cu_seqlens, d_o, d_final_state, N, T, H_qk, H_v, d_k, d_v, scale,
+                               dx_raw, dconv_w, da, db, dA_log, ddt_bias, d_initial_state,
+                               workspace, ws_bytes, stream);
+}
+
+size_t gdn_layer_prefill_backward_saved_workspace_size(int N, int T, int H_qk, int H_v, int d_k,
+                                                       int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (N < 1 || T < 0 || H_qk < 1 || H_v < 1) return 0;
+    return layer_bwd_ws(N, T, H_qk, H_v, true).total;
+}
+
+int gdn_layer_prefill_backward_saved(const void *x_raw, const void *conv_w, const float *a,
+                                     const float *b, const float *A_log, const float *dt_bias,
+                                     float l2_eps, const void *chunk_states, size_t cs_bytes,
+                                     const int32_t *cu_seqlens, const void *d_o,
+                                     const float *d_final_state, int N, int T, int H_qk, int H_v,
+                                     int d_k, int d_v, float scale, void *dx_raw, float *dconv_w,
+                                     float *da, float *db, float *dA_log, float *ddt_bias,
+                                     float *d_initial_state, void *workspace, size_t ws_bytes,
+                                     void *stream) {
+    if (!chunk_states) return fail(GDN_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+    return layer_backward_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, nullptr, chunk_states,
+                               cs_bytes, cu_seqlens, d_o, d_final_state, N, T, H_qk, H_v, d_k,
+                               d_v, scale, dx_raw, dconv_w, da, db, dA_log, ddt_bias,
+                               d_initial_state, workspace, ws_bytes, stream);
 }
 
 int gdn_gates(const float *a, const float *b, const float *A_log, const float *dt_bias, int T,
@@ -567,11 +620,17 @@ size_t gdn_layer_prefill_workspace_size(int N, int T, int H_qk, int H_v, int d_k
     return 2 * gate + gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v);
 }
 
-int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, const float *b,
-                      const float *A_log, const float *dt_bias, float l2_eps,
-                      const float *initial_state, float *final_state, void *conv_state_out,
-                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                      float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_layer_prefill, and with chunk_states gdn_layer_prefill_save_states.
+int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                       const float *A_log, const float *dt_bias, float l2_eps,
+                       const float *initial_state, float *final_state, void *conv_state_out,
+                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
+                       int d_v, float scale, void *o, void *chunk_states, size_t cs_bytes,
+                       void *workspace, size_t ws_bytes, void *stream) {
     int rc;
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
@@ -606,6 +665,18 @@ int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, con
                            initial_state, final_state, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
                            scale, o, rest, rest_bytes);
     if (rc) return rc;
+    if (chunk_states) {
+        const size_t ncs = gdn_chunk_states_size(N, T, H_v, d_k, d_v);
+        if (cs_bytes < ncs)
+            return fail(GDN_ERR_INVALID_ARG, "chunk_states of %zu bytes given, %zu needed", cs_bytes, ncs);
+        const struct { const void *p; size_t n; } other[] = {
+            {x_raw, nx}, {conv_w, craw * 4 * 2}, {a, ng}, {b, ng}, {A_log, nh}, {dt_bias, nh},
+            {initial_state, ns}, {final_state, ns}, {conv_state_out, nc}, {o, nv},
+            {workspace, need}, {cu_seqlens, (size_t)(N + 1) * 4}};
+        for (const auto &x : other)
+            if (overlaps(chunk_states, ncs, x.p, x.n))
+                return fail(GDN_ERR_INVALID_ARG, "chunk_states must not overlap any other argument");
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = device_check_cu(cu_seqlens, N, T, s))) return rc;
     hipError_t e = hipSuccess;
@@ -616,10 +687,37 @@ int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, con
     else if ((e = gdn::launch_gates(a, b, A_log, dt_bias, T, H_v, g, beta, s)) == hipSuccess)
         e = gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
                                             final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
-                                            nullptr, rest, s);
+                                            chunk_states, rest, s);
     if (e == hipSuccess && conv_state_out)
         e = gdn::launch_conv_hist(x_raw, cu_seqlens, N, T, (int)craw, conv_state_out, s);
     return finish(e, s, "gdn_layer_prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                      const float *A_log, const float *dt_bias, float l2_eps,
+                      const float *initial_state, float *final_state, void *conv_state_out,
+                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
+                      float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+    return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
+                              final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
+                              scale, o, nullptr, 0, workspace, ws_bytes, stream);
+}
+
+int gdn_layer_prefill_save_states(const void *x_raw, const void *conv_w, const float *a,
+                                  const float *b, const float *A_log, const float *dt_bias,
+                                  float l2_eps, const float *initial_state, float *final_state,
+                                  void *conv_state_out, const int32_t *cu_seqlens, int N, int T,
+                                  int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                                  void *chunk_states, size_t cs_bytes, void *workspace,
+                                  size_t ws_bytes, void *stream) {
+    if (!chunk_states) return fail(GDN_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+    return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
+                              final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
+                              scale, o, chunk_states, cs_bytes, workspace, ws_bytes, stream);
 }
 
 int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a, const float *b,

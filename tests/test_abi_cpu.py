@@ -428,3 +428,58 @@ def test_chunk_states_and_saved_workspace_sizes():
     # the saved form drops the states and the forward records
     assert 0 < saved < full - gdn.gdn_chunk_states_size(1, 32768, 48)
     assert gdn.gdn_prefill_backward_saved_workspace_size(0, 64, 16, 48) == 0
+
+
+def _layer_prefill_save(L, **kw):
+    a = dict(x=0x10000000, w=0x18000000, a=0x20000000, b=0x28000000, A=0x30000000,
+             dt=0x30100000, eps=1e-6, S0=None, Sf=None, conv=None, cu=None, N=1, T=64, H_qk=16,
+             H_v=48, d_k=128, d_v=128, scale=1.0, o=0x40000000, cs=0x1000000000,
+             cs_bytes=1 << 40, ws=0x80000000, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.gdn_layer_prefill_save_states(
+        a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"], a["S0"], a["Sf"], a["conv"],
+        a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"], a["scale"], a["o"],
+        a["cs"], a["cs_bytes"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs_bytes=1024), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs=0x20000000), gdn.GDN_ERR_INVALID_ARG),            # chunk_states overlaps a
+    (dict(ws_bytes=16), gdn.GDN_ERR_WORKSPACE),
+])
+def test_layer_prefill_save_states_rejects_bad_arguments(kw, code):
+    assert _layer_prefill_save(gdn.lib(), **kw) == code
+
+
+def _layer_backward_saved(L, **kw):
+    a = dict(x=0x10000000, w=0x18000000, a=0x20000000, b=0x28000000, A=0x30000000,
+             dt=0x30100000, eps=1e-6, cs=0x1000000000, cs_bytes=1 << 40, cu=None,
+             d_o=0x40000000, dSf=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0,
+             dx=0x50000000, dw=0x58000000, da=0x60000000, db=0x68000000, dA=0x70000000,
+             ddt=0x70100000, dS0=None, ws=0x80000000, ws_bytes=1 << 36, stream=None)
+    a.update(kw)
+    return L.gdn_layer_prefill_backward_saved(
+        a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"], a["cs"], a["cs_bytes"], a["cu"],
+        a["d_o"], a["dSf"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"], a["scale"],
+        a["dx"], a["dw"], a["da"], a["db"], a["dA"], a["ddt"], a["dS0"], a["ws"], a["ws_bytes"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cs_bytes=1024), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dx=0x1000000000), gdn.GDN_ERR_INVALID_ARG),          # dx overlaps chunk_states
+    (dict(ws_bytes=1024), gdn.GDN_ERR_WORKSPACE),
+    (dict(eps=-1.0), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_layer_backward_saved_rejects_bad_arguments(kw, code):
+    assert _layer_backward_saved(gdn.lib(), **kw) == code
+
+
+def test_layer_saved_workspace_size():
+    L = gdn.lib()
+    full = gdn.gdn_layer_prefill_backward_workspace_size(1, 32768, 16, 48)
+    saved = L.gdn_layer_prefill_backward_saved_workspace_size(1, 32768, 16, 48, 128, 128)
+    assert 0 < saved < full
+    assert L.gdn_layer_prefill_backward_saved_workspace_size(0, 64, 16, 48, 128, 128) == 0

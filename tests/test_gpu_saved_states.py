@@ -11,6 +11,7 @@ gdn_prefill_raw_save_states) and the backward that reads them
 * the backward from the kept states is bit-identical to the backward that
   recomputes them (ragged, packed varlen, and a sequence long enough for the
   forward to run in segments)."""
+import numpy as np
 import pytest
 
 import oracle
@@ -137,3 +138,30 @@ def test_backward_from_kept_states_against_oracle():
     ref = oracle.recurrent_backward(p.q, p.k, p.v, p.g, p.beta, d_o, p.S0, dSf, None)
     for nm, x, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), got, ref):
         assert_close(host(x), r, TOL_BF16, nm)
+
+
+@pytest.mark.parametrize("name", ["T300", "varlen", "T8192"])
+def test_layer_pair_from_kept_states_is_bit_identical(name):
+    """gdn_layer_prefill keeping the chunk states, then
+    gdn_layer_prefill_backward from them: outputs and gradients bit-identical
+    to the plain layer calls."""
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    p = synth.raw_prefill(8500, init_state=True, **CASES[name])
+    d_o, dSf = synth.output_grads(8500, p.T, p.N)
+    cu = None if p.cu_seqlens is None else dev(p.cu_seqlens)
+    x, w, S0 = dev(p.x), dev(p.w), dev(p.S0)
+    a, b = dev(p.meta["a"]), dev(p.meta["b"])
+    A_log = dev(p.meta["A_log"].astype(np.float32))
+    dtb = dev(p.meta["dt_bias"].astype(np.float32))
+    print("layer pair", name, flush=True)
+    o0, S0f, c0 = gdn.gdn_layer_prefill(x, w, a, b, A_log, dtb, S0, cu)
+    o1, S1f, c1, cs = gdn.gdn_layer_prefill(x, w, a, b, A_log, dtb, S0, cu, chunk_states=True)
+    ref = gdn.gdn_layer_prefill_backward(x, w, a, b, A_log, dtb, dev(d_o), S0, dev(dSf), cu)
+    got = gdn.gdn_layer_prefill_backward(x, w, a, b, A_log, dtb, dev(d_o), None, dev(dSf), cu,
+                                         chunk_states=cs)
+    torch.cuda.synchronize()
+    for nm, u, t in (("o", o0, o1), ("final state", S0f, S1f), ("conv state", c0, c1)):
+        _same(u, t, nm)
+    for nm, u, t in zip(("dx", "dconv_w", "da", "db", "dA_log", "ddt_bias", "dS0"), got, ref):
+        _same(u, t, nm)
