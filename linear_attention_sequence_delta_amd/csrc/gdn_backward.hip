@@ -126,10 +126,10 @@ struct RevHelp {      // waves 4-7
 // state waves write the gradient with respect to the initial state.
 __global__ __launch_bounds__(512) void bwd_scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ d_o,
-    const float *__restrict__ dS_final, const int32_t *__restrict__ cu,
+    const float *dS_final, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
     const uint16_t *__restrict__ bws, uint16_t *__restrict__ dsw, uint16_t *__restrict__ duw,
-    uint16_t *__restrict__ dv, float *__restrict__ dS0) {
+    uint16_t *__restrict__ dv, float *dS0, int c_lo, int c_hi) {
     __shared__ __attribute__((aligned(16))) uint16_t sS[kBSlab * kKP];       // dS' (bf16), [v][k]
     __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];      // K rows of the chunk
     __shared__ __attribute__((aligned(16))) uint16_t sQr[kChunk * kKP];      // Q rows (helpers)
@@ -150,7 +150,9 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
     const int w = wave & 3;
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c = lane & 15;
     const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
-    const int nch = (s1 - s0 + kChunk - 1) / kChunk;
+    // chunks [c_lo, nch) of the sequence, last to first: the gradient enters as
+    // dS_final and leaves as dS0, so a sequence can be walked in segments
+    const int nch = min((s1 - s0 + kChunk - 1) / kChunk, c_hi);
     const int cbase = chunk_base[n];
     const int e0 = kBSlab * slab;
     const size_t st_off = ((size_t)n * H_v + h) * (kD * kD);
@@ -260,18 +262,18 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
         };
 
         RevState r0, r1, r2;
-        if (nch > 0) {
+        if (nch > c_lo) {
             fetch(nch - 1, r0);
             fetch(nch - 2, r1);
         }
         write_state_lds();
         __syncthreads();                                        // helpers' first staging
         __syncthreads();                                        // helpers' first P^T dO
-        for (int ci = nch - 1; ci >= 0; ci -= 3) {
+        for (int ci = nch - 1; ci >= c_lo; ci -= 3) {
             body(ci, r0, r2);
-            if (ci == 0) break;
+            if (ci == c_lo) break;
             body(ci - 1, r1, r0);
-            if (ci == 1) break;
+            if (ci - 1 == c_lo) break;
             body(ci - 2, r2, r1);
         }
         if (dS0) {
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
                     *reinterpret_cast<u32x4 *>(dsp + r * kD + pcs) = *reinterpret_cast<const u32x4 *>(sS + r * kKP + pcs);
                 }
             }
-            if (ci > 0) stage_do(ci - 1, nxt);
+            if (ci > c_lo) stage_do(ci - 1, nxt);
             fetch(ci - 2, pf);
             // W = scale dO^T diag(gamma) Q of chunk ci, in the state layout
             uint4 zq[2][2], qa[2][2];
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
                     *reinterpret_cast<float4 *>(sW + ((w * 4 + t * 2 + nt) * 64 + lane) * 4) = make_float4(a[0], a[1], a[2], a[3]);
                 }
             __syncthreads();                                    // (1)
-            if (ci > 0) {
+            if (ci > c_lo) {
                 pdo(nxt);
                 stage_qz(ci - 1, nxt);
             }
@@ -377,20 +379,20 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
         };
 
         RevHelp r0, r1, r2;
-        if (nch > 0) {
+        if (nch > c_lo) {
             fetch(nch - 1, r0);
             fetch(nch - 2, r1);
             stage_do(nch - 1, r0);
             stage_qz(nch - 1, r0);
         }
         __syncthreads();
-        if (nch > 0) pdo(r0);
+        if (nch > c_lo) pdo(r0);
         __syncthreads();
-        for (int ci = nch - 1; ci >= 0; ci -= 3) {
+        for (int ci = nch - 1; ci >= c_lo; ci -= 3) {
             body(ci, r1, r2);
-            if (ci == 0) break;
+            if (ci == c_lo) break;
             body(ci - 1, r2, r0);
-            if (ci == 1) break;
+            if (ci - 1 == c_lo) break;
             body(ci - 2, r0, r1);
         }
     }
@@ -829,13 +831,13 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
 hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const float *dS_final,
                            const int32_t *cu_seqlens, const int32_t *chunk_base, int N, int T,
                            int H_qk, int H_v, float scale, const void *bws, void *dsw, void *duw,
-                           void *dv, float *dS0, hipStream_t stream) {
+                           void *dv, float *dS0, int c_lo, int c_hi, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(N * H_v * kBSlabs), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(d_o), dS_final, cu_seqlens, chunk_base, N, T,
                        H_qk, H_v, scale, static_cast<const uint16_t *>(bws),
                        static_cast<uint16_t *>(dsw), static_cast<uint16_t *>(duw),
-                       static_cast<uint16_t *>(dv), dS0);
+                       static_cast<uint16_t *>(dv), dS0, c_lo, c_hi);
     return hipGetLastError();
 }
 

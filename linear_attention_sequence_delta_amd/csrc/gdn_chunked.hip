@@ -841,6 +841,10 @@ constexpr int kMaxSegments = 12;
 #endif
 constexpr double kSegGrowth = 1.1;
 constexpr double kSegGrowthRaw = GDN_SEG_GROWTH_RAW;
+#ifndef GDN_SEG_GROWTH_REV
+#define GDN_SEG_GROWTH_REV 1.0
+#endif
+constexpr double kSegGrowthRev = GDN_SEG_GROWTH_REV;   // the backward's reverse scan (walked last to first)
 constexpr int kFirstSegChunks = 128;
 constexpr int kSegMinChunks = 64;     // shorter sequences are not split
 constexpr int kMinIdleCUs = 32;       // fewer idle CUs: not split
@@ -996,6 +1000,7 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
 struct BwdWorkspace {
     int32_t *chunk_base;
     uint16_t *rec, *brec, *states, *dsw, *duw;
+    float *carry;     // the state gradient between segments of the reverse scan (one sequence)
 };
 // Given the chunk states of an earlier forward pass, the workspace has no
 // states region and the forward records are not kept.
@@ -1007,6 +1012,7 @@ size_t bwd_workspace_layout(int N, int T, int H_v, bool saved, void *base, BwdWo
     const size_t st = max_chunks * (size_t)H_v * kD * kD * sizeof(uint16_t);
     const size_t own = saved ? 0 : st;
     const size_t du = max_chunks * kChunk * (size_t)H_v * kD * sizeof(uint16_t);
+    const size_t carry = saved && N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0;
     if (wsp) {
         char *p = static_cast<char *>(base);
         wsp->chunk_base = reinterpret_cast<int32_t *>(p);
@@ -1015,8 +1021,9 @@ size_t bwd_workspace_layout(int N, int T, int H_v, bool saved, void *base, BwdWo
         wsp->states = saved ? nullptr : reinterpret_cast<uint16_t *>(p + head + rec + brec);
         wsp->dsw = reinterpret_cast<uint16_t *>(p + head + rec + brec + own);
         wsp->duw = reinterpret_cast<uint16_t *>(p + head + rec + brec + own + st);
+        wsp->carry = carry ? reinterpret_cast<float *>(p + head + rec + brec + own + st + du) : nullptr;
     }
-    return head + rec + brec + own + st + du;
+    return head + rec + brec + own + st + du + carry;
 }
 
 }  // namespace
@@ -1053,14 +1060,57 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int items = max_chunks * H_qk;
-    if (saved)
-        hipLaunchKernelGGL((prep_kernel<false, kRecBwd>), dim3((items + kPrepWaves - 1) / kPrepWaves),
-                           dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
-                           W.chunk_base, N, T, H_qk, H_v, scale, 0, items, nullptr, W.brec);
-    else
-        hipLaunchKernelGGL((prep_kernel<false, kRecFwd | kRecBwd>), dim3((items + kPrepWaves - 1) / kPrepWaves),
-                           dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
-                           W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
+    if (saved) {
+        // prep (backward records only) and the reverse scan, in segments walked
+        // last to first: the prep of the last segment alone, the prep of the
+        // earlier ones on the auxiliary stream, on the CUs the reverse scan
+        // leaves idle, while the caller's stream scans the later segments
+        auto prep = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
+            const int it = (c_hi - c_lo) * H_qk;
+            const int grid = min((it + kPrepWaves - 1) / kPrepWaves, max_grid);
+            hipLaunchKernelGGL((prep_kernel<false, kRecBwd>), dim3(grid), dim3(64 * kPrepWaves), 0, s,
+                               q16, k16, RawIn{}, g, beta, cu_seqlens, W.chunk_base, N, T, H_qk,
+                               H_v, scale, c_lo * H_qk, c_hi * H_qk, nullptr, W.brec);
+            return hipGetLastError();
+        };
+        auto rscan = [&](int c_lo, int c_hi, const float *in, float *out) {
+            return launch_bwd_scan(q, k, d_o, in, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
+                                   W.brec, W.dsw, W.duw, dv, out, c_lo, c_hi, stream);
+        };
+        const int nch = (T + kChunk - 1) / kChunk;
+        const int scan_grid = N * H_v * kSlabsW;      // the reverse scan's grid: 32-column slabs too
+        std::unique_lock<std::mutex> lock(g_aux_mu);
+        DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux() : nullptr;
+        const int idle = aux ? aux->cus - scan_grid : 0;
+        if (idle < kMinIdleCUs) {
+            lock.unlock();
+            if ((e = prep(0, max_chunks, INT32_MAX, stream)) != hipSuccess) return e;
+            if ((e = rscan(0, max_chunks, dS_final, dS0)) != hipSuccess) return e;
+        } else {
+            int b[kMaxSegments + 1];
+            const int nseg = segment_bounds(nch, kSegGrowthRev, b);
+            const int last = nseg - 1;
+            if ((e = prep(b[last], b[last + 1], INT32_MAX, stream)) != hipSuccess) return e;
+            if ((e = hipEventRecord(aux->ev[last], stream)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(aux->stream, aux->ev[last], 0)) != hipSuccess) return e;
+            for (int i = last - 1; i >= 0; --i) {
+                if ((e = prep(b[i], b[i + 1], idle, aux->stream)) != hipSuccess) return e;
+                if ((e = hipEventRecord(aux->ev[i], aux->stream)) != hipSuccess) return e;
+            }
+            for (int i = last; i >= 0; --i) {
+                if (i < last && (e = hipStreamWaitEvent(stream, aux->ev[i], 0)) != hipSuccess) return e;
+                if ((e = rscan(b[i], b[i + 1], i == last ? dS_final : W.carry, i == 0 ? dS0 : W.carry)) !=
+                    hipSuccess)
+                    return e;
+            }
+        }
+        return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
+                               max_chunks, scale, W.brec, chunk_states, W.dsw, W.duw, dq, dk, dg,
+                               dbeta, stream);
+    }
+    hipLaunchKernelGGL((prep_kernel<false, kRecFwd | kRecBwd>), dim3((items + kPrepWaves - 1) / kPrepWaves),
+                       dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
+                       W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const void *states = chunk_states;
     if (!saved) {
@@ -1072,7 +1122,7 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
         states = W.states;
     }
     if ((e = launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
-                             W.brec, W.dsw, W.duw, dv, dS0, stream)) != hipSuccess)
+                             W.brec, W.dsw, W.duw, dv, dS0, 0, max_chunks, stream)) != hipSuccess)
         return e;
     return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
                            max_chunks, scale, W.brec, states, W.dsw, W.duw, dq, dk, dg, dbeta,

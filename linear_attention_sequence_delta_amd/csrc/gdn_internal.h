@@ -56,7 +56,7 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
 hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const float *dS_final,
                            const int32_t *cu_seqlens, const int32_t *chunk_base, int N, int T,
                            int H_qk, int H_v, float scale, const void *bws, void *dsw, void *duw,
-                           void *dv, float *dS0, hipStream_t stream);
+                           void *dv, float *dS0, int c_lo, int c_hi, hipStream_t stream);
 hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const void *d_o,
                            const void *dv, const float *beta, const int32_t *cu_seqlens,
                            const int32_t *chunk_base, int N, int T, int H_qk, int H_v,
