@@ -43,6 +43,14 @@ constexpr int kBSlab = 32;             // d_v columns per reverse-scan workgroup
 constexpr int kBSlabs = kD / kBSlab;   // 4
 constexpr int kSP = kBSlab + 8;        // LDS row stride (bf16) of slab-wide rows
 
+// dU of a (chunk, V-head) is kept as 16 MFMA fragment blocks of 1 KiB: block
+// (a, s) holds, for lane (c, g4) at 8 (16 g4 + c), row 16 a + c, columns
+// 32 s + 8 g4 .. +7 -- the B operand the chunk-gradient kernel loads, one whole
+// contiguous block per load instruction.  Offset (bf16 elements) of block (a, s):
+__device__ __forceinline__ size_t dU_block(int chunk, int h, int H_v, int a, int s) {
+    return (((size_t)chunk * H_v + h) * 16 + 4 * a + s) * 512;
+}
+
 // MFMA operands from row-major bf16 LDS matrices, for lane (c = lane % 16,
 // g4 = lane / 16): frag_rows gives M[r0 + c][k0 + 8 g4 .. +7] (a row piece),
 // frag_cols gives M[k0 + 8 g4 + j][c0 + c], j = 0..7 (a column piece, two
@@ -119,7 +127,7 @@ struct RevHelp {      // waves 4-7
 // they form P^T dO of the next chunk and the update's Q term
 // W = scale dO^T diag(gamma) Q (handed over in fp32 through LDS), and they
 // write the results out of LDS: per chunk the bf16 dS' it starts from
-// (dsw [chunk][H_v][d_v][d_k]), dU (duw [chunk row][H_v][d_v]) and the dv
+// (dsw [chunk][H_v][d_v][d_k]), dU (duw, MFMA fragment blocks: see dU_block) and the dv
 // rows.  (Global stores issued by the state waves lengthen their chain: the
 // waits for their own prefetched loads would also cover the stores.)  Three
 // barriers per chunk: (1) dU complete, (2) dR complete, (3) dS complete.  The
@@ -364,9 +372,11 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
                 stage_qz(ci - 1, nxt);
             }
             {
-                const int r = hl >> 2, pcs = 8 * (hl & 3);
-                *reinterpret_cast<u32x4 *>(duw + (((size_t)(cbase + ci) * kChunk + r) * H_v + h) * kD + e0 + pcs) =
-                    *reinterpret_cast<const u32x4 *>(sDU + r * kSP + pcs);
+                // block (a = hl / 64, s = slab); lane hl % 64 = (c, g4): row 16 a + c,
+                // slab columns 8 g4 .. +7
+                const int a = hl >> 6, fl = hl & 63;
+                *reinterpret_cast<u32x4 *>(duw + dU_block(cbase + ci, h, H_v, a, slab) + 8 * fl) =
+                    *reinterpret_cast<const u32x4 *>(sDU + (16 * a + (fl & 15)) * kSP + 8 * (fl >> 4));
             }
             __syncthreads();                                    // (2)
             {
@@ -581,7 +591,7 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
         uint4 dUf[4];                                  // row `row` of dU, columns 32 s + 8 g4 .. +7
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            dUf[s] = *reinterpret_cast<const uint4 *>(duw + (((size_t)gc * kChunk + row) * H_v + h) * kD + 32 * s + 8 * g4);
+            dUf[s] = *reinterpret_cast<const uint4 *>(duw + dU_block(gc, h, H_v, w, s) + 8 * ol);
         {
             u32x4 dsv[4];
 #pragma unroll

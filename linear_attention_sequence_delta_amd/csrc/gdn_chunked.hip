@@ -996,7 +996,7 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
 
 // Backward workspace: chunk offsets | forward records | backward records |
 // bf16 state at each chunk start | bf16 state gradient at each chunk end |
-// bf16 dU rows (chunk-aligned).
+// bf16 dU per (chunk, V-head) as MFMA fragment blocks.
 struct BwdWorkspace {
     int32_t *chunk_base;
     uint16_t *rec, *brec, *states, *dsw, *duw;
