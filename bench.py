@@ -293,6 +293,34 @@ def run_gpu(steps, warmup, path="both"):
     res["gate_bwd_us"] = g0.elapsed_time(g1) / steps * 1e3
     del z, y, gy, gws
 
+    # the packed varlen workload (8 sequences, lengths U{512..16384}, initial
+    # states): the same fused call over several independent sequences
+    if path == "both":
+        pv = synth.workload_varlen()
+        xv, wv = to_dev(pv.x), to_dev(pv.w)
+        gv, bv, S0v, cuv = to_dev(pv.g), to_dev(pv.beta), to_dev(pv.S0), to_dev(pv.cu_seqlens)
+        ov = torch.empty((pv.T, H_V, D), dtype=torch.bfloat16, device=dev)
+        fsv = torch.empty((pv.N, H_V, D, D), dtype=torch.float32, device=dev)
+        wsv = torch.empty(gdn.gdn_prefill_raw_workspace_size(pv.N, pv.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
+
+        def varlen():
+            gdn.gdn_prefill_raw(xv, wv, gv, bv, S0v, cuv, H_qk=H_QK, H_v=H_V, final_state=fsv,
+                                o=ov, workspace=wsv)
+
+        for _ in range(max(warmup, 1)):
+            varlen()
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(steps):
+            varlen()
+        g1.record()
+        torch.cuda.synchronize()
+        res["varlen_us"] = g0.elapsed_time(g1) / steps * 1e3
+        res["varlen_T"] = pv.T
+        res["varlen_lengths"] = [int(x) for x in np.diff(pv.cu_seqlens)]
+        del xv, wv, gv, bv, S0v, cuv, ov, fsv, wsv
+
     # ---------------- decode workload: B = 256 over rotating 256-slot pools
     d = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
     pools = [to_dev(d.pool) for _ in range(2)]     # 768 MiB each, larger than the on-die cache
@@ -625,6 +653,14 @@ def main():
                                "what": "a training pair: gdn_prefill_raw keeping the chunk states, "
                                        "then gdn_prefill_backward reading them (the forward scan "
                                        "is not repeated)"}}
+    if "varlen_us" in r:
+        vf = PREFILL_FLOP_PER_TOKEN * r["varlen_T"]
+        out["varlen_8seq"] = {"us": r["varlen_us"], "tokens": r["varlen_T"],
+                              "lengths": r["varlen_lengths"],
+                              "tokens_per_s": r["varlen_T"] / (r["varlen_us"] * 1e-6),
+                              "mfma_frac": vf / (r["varlen_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                              "what": "gdn_prefill_raw on the packed 8-sequence workload (initial "
+                                      "states); not part of the step"}
     if "pre_us" in r:
         out["prelude_roofline"] = {"bound": "hbm", "kernel": "gdn_conv_prelude (two-call path)",
                                    "achieved": pre_bytes / (r["pre_us"] * 1e-6) / 1e9,

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(512) void bwd_scan_kernel(
     __shared__ __attribute__((aligned(16))) float sW[4 * 4 * 64 * 4];        // W, in the state layout
     __shared__ __attribute__((aligned(16))) float sPd[4 * 2 * 64 * 4];      // P^T dO, in dU's layout
 
-    const int u = xcd_unit();
+    const int u = xcd_group_unit((H_v / H_qk) * kBSlabs);
     const int slab = u % kBSlabs;
     const int nh = u / kBSlabs;
     const int h = nh % H_v, n = nh / H_v;

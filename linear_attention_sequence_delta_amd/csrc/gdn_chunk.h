@@ -112,4 +112,24 @@ __device__ __forceinline__ int xcd_unit() {
     return xcd * ((int)gridDim.x >> 3) + min(xcd, (int)gridDim.x & 7) + (int)(blockIdx.x >> 3);
 }
 
+// xcd_unit() for a grid of whole groups of gsz units (the workgroups of one QK
+// group of one sequence): each XCD's contiguous share of positions is filled
+// with the groups g = x, x + 8, x + 16, ... (x the share's first residue), so a
+// group stays on one XCD while the groups of every sequence are spread over all
+// eight.  (Positions are dealt out by residue of g mod 8, then by g / 8, then by
+// unit within the group; a bijection on [0, gridDim.x) when gridDim.x is a
+// multiple of gsz.)
+__device__ __forceinline__ int xcd_group_unit(int gsz) {
+    const int p = xcd_unit();
+    const int ngroups = (int)gridDim.x / gsz;
+    const int q = p / gsz, j = p - q * gsz;
+    const int base = ngroups >> 3, rem = ngroups & 7;
+    int r = 0;
+#pragma unroll
+    for (int k = 1; k < 8; ++k)
+        if (q >= k * base + min(k, rem)) r = k;
+    const int g = r + 8 * (q - (r * base + min(r, rem)));
+    return g * gsz + j;
+}
+
 }  // namespace gdn

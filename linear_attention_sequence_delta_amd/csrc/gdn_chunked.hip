@@ -506,9 +506,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sQ[4][16 * kKP];     // each output wave's Q rows
     __shared__ __attribute__((aligned(16))) uint16_t sXv[kRaw ? 4 : 1][20 * kVP];   // raw v rows per output wave
 
-    // Workgroup -> (sequence, V-head, slab); consecutive units (all slabs of a
-    // head, neighbouring heads of one QK group) share an XCD's L2.
-    const int u = xcd_unit();
+    // Workgroup -> (sequence, V-head, slab): the workgroups of one QK group of
+    // one sequence share an XCD's L2 (they read the same K and Q rows), and the
+    // groups of every sequence are spread over the eight XCDs.
+    const int u = xcd_group_unit((H_v / H_qk) * kSlabsW);
     const int slab = u % kSlabsW;
     const int nh = u / kSlabsW;
     const int h = nh % H_v, n = nh / H_v;
