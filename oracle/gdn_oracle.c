@@ -81,47 +81,59 @@ int orc_prelude(const double *x, const double *w, const int32_t *cu, int N, int 
     const int Craw = 2 * Cq + H_v * dv;
     if (T < 0 || N < 1 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1)
         return ORC_EINVAL;
-    double *y = (double *)malloc(sizeof(double) * (size_t)(Craw > 0 ? Craw : 1));
-    if (!y)
-        return ORC_ENOMEM;
     for (int n = 0; n < N; ++n) {
         int s0 = 0, s1 = 0;
-        if (seq_bounds(cu, N, T, n, &s0, &s1)) {
-            free(y);
+        if (seq_bounds(cu, N, T, n, &s0, &s1))
             return ORC_EINVAL;
-        }
-        for (int t = s0; t < s1; ++t) {
-            /* conv + SiLU on every channel */
-            for (int c = 0; c < Craw; ++c) {
-                double acc = 0.0;
-                for (int j = 0; j < 4; ++j) {
-                    int src = t - 3 + j;
-                    if (src >= s0)
-                        acc += w[(size_t)c * 4 + j] * x[(size_t)src * Craw + c];
-                }
-                y[c] = acc / (1.0 + exp(-acc));
-            }
-            /* L2 normalisation of each q head and each k head */
-            for (int h = 0; h < H_qk; ++h) {
-                const double *yq = y + (size_t)h * dk;
-                const double *yk = y + Cq + (size_t)h * dk;
-                double sq = 0.0, sk = 0.0;
-                for (int i = 0; i < dk; ++i) {
-                    sq += yq[i] * yq[i];
-                    sk += yk[i] * yk[i];
-                }
-                double rq = 1.0 / sqrt(sq + eps), rk = 1.0 / sqrt(sk + eps);
-                for (int i = 0; i < dk; ++i) {
-                    q[((size_t)t * H_qk + h) * dk + i] = yq[i] * rq;
-                    k[((size_t)t * H_qk + h) * dk + i] = yk[i] * rk;
-                }
-            }
-            for (int c = 0; c < H_v * dv; ++c)
-                v[(size_t)t * H_v * dv + c] = y[2 * Cq + c];
-        }
     }
-    free(y);
-    return ORC_OK;
+    int status = ORC_OK;
+    /* tokens are independent: threads take tokens, each with its own row y */
+#pragma omp parallel
+    {
+        double *y = (double *)malloc(sizeof(double) * (size_t)(Craw > 0 ? Craw : 1));
+        if (!y) {
+#pragma omp atomic write
+            status = ORC_ENOMEM;
+        }
+        for (int n = 0; n < N; ++n) {
+            int s0 = 0, s1 = 0;
+            seq_bounds(cu, N, T, n, &s0, &s1);
+#pragma omp for schedule(static)
+            for (int t = s0; t < s1; ++t) {
+                if (!y)
+                    continue;
+                /* conv + SiLU on every channel */
+                for (int c = 0; c < Craw; ++c) {
+                    double acc = 0.0;
+                    for (int j = 0; j < 4; ++j) {
+                        int src = t - 3 + j;
+                        if (src >= s0)
+                            acc += w[(size_t)c * 4 + j] * x[(size_t)src * Craw + c];
+                    }
+                    y[c] = acc / (1.0 + exp(-acc));
+                }
+                /* L2 normalisation of each q head and each k head */
+                for (int h = 0; h < H_qk; ++h) {
+                    const double *yq = y + (size_t)h * dk;
+                    const double *yk = y + Cq + (size_t)h * dk;
+                    double sq = 0.0, sk = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        sq += yq[i] * yq[i];
+                        sk += yk[i] * yk[i];
+                    }
+                    double rq = 1.0 / sqrt(sq + eps), rk = 1.0 / sqrt(sk + eps);
+                    for (int i = 0; i < dk; ++i) {
+                        q[((size_t)t * H_qk + h) * dk + i] = yq[i] * rq;
+                        k[((size_t)t * H_qk + h) * dk + i] = yk[i] * rk;
+                    }
+                }
+                for (int c = 0; c < H_v * dv; ++c)
+                    v[(size_t)t * H_v * dv + c] = y[2 * Cq + c];
+            }
+        }
+        free(y);
+    }
+    return status;
 }
 
 /*
