@@ -31,8 +31,12 @@
  *   - The decay gate is passed as its logarithm g (a = exp(g)), fp32.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on that stream and returns; nothing synchronises unless the
- *     environment variable GDN_DEBUG=1 is set, in which case each call waits for
- *     its kernels and reports device-side failures.
+ *     environment variable GDN_DEBUG=1 is set (read at every call), in which
+ *     case each call waits for its kernels and reports device-side failures.
+ *   - Graph capture: every entry point may be captured into a HIP graph.  On a
+ *     stream under capture the calls enqueue all their work on `stream` itself
+ *     (no auxiliary stream, same results), and GDN_DEBUG checks are skipped
+ *     (they would have to synchronise).
  *   - Return value: GDN_OK (0) or a negative gdn_status.  On failure nothing has
  *     been enqueued (argument errors are detected on the host before any launch)
  *     except for GDN_ERR_HIP, which reports a failing launch.  The text of the

@@ -29,13 +29,21 @@ int ok() {
     return GDN_OK;
 }
 
-bool debug_mode() {
-    static const bool on = [] {
-        const char *e = std::getenv("GDN_DEBUG");
-        return e && e[0] && std::strcmp(e, "0") != 0;
-    }();
-    return on;
+// GDN_DEBUG=1: device-side precondition checks and a synchronisation after
+// every call.  Read at every call, so a process can switch it on and off.
+bool debug_env() {
+    const char *e = std::getenv("GDN_DEBUG");
+    return e && e[0] && std::strcmp(e, "0") != 0;
 }
+
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
+// The checks synchronise the stream, which a stream under graph capture must
+// not do: on a capturing stream debug mode checks nothing.
+bool debug_mode(hipStream_t s) { return debug_env() && !capturing(s); }
 
 int hip_fail(hipError_t e, const char *what) {
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -45,7 +53,7 @@ int hip_fail(hipError_t e, const char *what) {
 // asynchronous faults too.
 int finish(hipError_t e, hipStream_t s, const char *what) {
     if (e != hipSuccess) return hip_fail(e, what);
-    if (debug_mode()) {
+    if (debug_mode(s)) {
         e = hipStreamSynchronize(s);
         if (e != hipSuccess) return hip_fail(e, what);
     }
@@ -77,7 +85,7 @@ int check_seqs(const int32_t *cu_seqlens, int N, int T) {
 }
 
 int device_check_cu(const int32_t *cu_seqlens, int N, int T, hipStream_t s) {
-    if (!debug_mode() || !cu_seqlens) return GDN_OK;
+    if (!debug_mode(s) || !cu_seqlens) return GDN_OK;
     int bad = 0;
     hipError_t e = gdn::debug_check_cu_seqlens(cu_seqlens, N, T, s, &bad);
     if (e != hipSuccess) return hip_fail(e, "cu_seqlens check");
@@ -750,7 +758,7 @@ int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a,
         overlaps(state_pool, npool, conv_w, nw))
         return fail(GDN_ERR_INVALID_ARG, "the pools must not overlap each other or the inputs");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (debug_mode()) {
+    if (debug_mode(s)) {
         int bad = 0;
         hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
         if (e != hipSuccess) return hip_fail(e, "slot_idx check");
@@ -793,7 +801,7 @@ int gdn_decode_multi_step(const void *q, const void *k, const void *v, const flo
                       overlaps(snapshots, nsnap, g, ng) || overlaps(snapshots, nsnap, beta, ng)))
         return fail(GDN_ERR_INVALID_ARG, "snapshots must not overlap the pool or the inputs");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (debug_mode()) {
+    if (debug_mode(s)) {
         int bad = 0;
         hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
         if (e != hipSuccess) return hip_fail(e, "slot_idx check");
@@ -819,7 +827,7 @@ int gdn_state_rollback(const float *snapshots, const int32_t *n_keep, int n_tok,
     if (overlaps(snapshots, (size_t)B * n_tok * H_v * st, state_pool, (size_t)P * H_v * st))
         return fail(GDN_ERR_INVALID_ARG, "snapshots must not overlap the pool");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (debug_mode()) {
+    if (debug_mode(s)) {
         int bad = 0;
         hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
         if (e != hipSuccess) return hip_fail(e, "slot_idx check");
@@ -896,7 +904,7 @@ int gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
         overlaps(o, no, k, (size_t)B * H_qk * gdn::kD * 2) || overlaps(o, no, v, no))
         return fail(GDN_ERR_INVALID_ARG, "o must not overlap inputs or the state pool");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (debug_mode()) {
+    if (debug_mode(s)) {
         int bad = 0;
         hipError_t e = gdn::debug_check_slots(slot_idx, B, P, s, &bad);
         if (e != hipSuccess) return hip_fail(e, "slot_idx check");

@@ -880,8 +880,13 @@ std::mutex g_aux_mu;         // guards g_aux and every enqueue on an auxiliary s
 DeviceAux g_aux[kMaxDevices];
 
 // The current device's auxiliary stream (default priority) and events, or
-// nullptr if they cannot be made.  Caller holds g_aux_mu.
-DeviceAux *device_aux() {
+// nullptr if they cannot be made or `s` is under graph capture (a captured
+// call stays on the caller's stream: it runs unsegmented, with the same
+// results, since segments hand the fp32 state over unchanged).  Caller holds
+// g_aux_mu.
+DeviceAux *device_aux(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     DeviceAux &a = g_aux[dev];
@@ -965,7 +970,7 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
     // one sequence (cu_seqlens, if given, is {0, T}): nch chunks known on the host
     const int nch = (T + kChunk - 1) / kChunk;
     std::unique_lock<std::mutex> lock(g_aux_mu);
-    DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux() : nullptr;
+    DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux(stream) : nullptr;
     const int idle = aux ? aux->cus - scan_grid : 0;
     if (idle < kMinIdleCUs) {
         lock.unlock();
@@ -1081,7 +1086,7 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
         const int nch = (T + kChunk - 1) / kChunk;
         const int scan_grid = N * H_v * kSlabsW;      // the reverse scan's grid: 32-column slabs too
         std::unique_lock<std::mutex> lock(g_aux_mu);
-        DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux() : nullptr;
+        DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux(stream) : nullptr;
         const int idle = aux ? aux->cus - scan_grid : 0;
         if (idle < kMinIdleCUs) {
             lock.unlock();
