@@ -2,8 +2,8 @@
 against the fp64 oracle's reverse-mode gradients of the token recurrence:
 ragged lengths, packed varlen, initial state and final-state gradient present
 or not, an odd head grid, T = 0, and the 32768-token and packed 8-sequence
-workloads (one QK group against the oracle, every head through the adjoint
-identities)."""
+workloads (four QK groups against the oracle element by element, every head
+through the adjoint identities)."""
 import numpy as np
 import pytest
 
@@ -100,7 +100,8 @@ def test_backward_zero_length():
 
 def test_backward_full_size_one_group_and_adjoint():
     """The 32768-token workload (16 QK / 48 V heads, initial state, final-state
-    gradient): QK head 5 and its three V-heads against the oracle; every head
+    gradient): QK heads 6-9 and their twelve V-heads (workgroup placements on
+    four different XCDs) against the oracle element by element; every head
     through <dv, v> + <dS0, S0> = <d_o, o> + <dS_T, S_T> and <dq, q> = <d_o, o>,
     which hold because (o, S_T) is linear in (v, S0) and o is linear in q."""
     import torch
@@ -109,7 +110,7 @@ def test_backward_full_size_one_group_and_adjoint():
     p = synth.direct_prefill(7500, T=T, init_state=True)
     d_o, dSf = synth.output_grads(7500, T, 1)
     print("backward T", T, flush=True)
-    _check(p, d_o, dSf, 1.0, qk_heads=(5, 6))
+    _check(p, d_o, dSf, 1.0, qk_heads=(6, 10))
     dq, dk, dv, dg, db, dS0 = gdn.gdn_prefill_backward(dev(p.q), dev(p.k), dev(p.v), dev(p.g),
                                                        dev(p.beta), dev(d_o), dev(p.S0), dev(dSf))
     o, S = gdn.gdn_prefill(dev(p.q), dev(p.k), dev(p.v), dev(p.g), dev(p.beta), dev(p.S0))
@@ -127,8 +128,8 @@ def test_backward_full_size_one_group_and_adjoint():
 
 def test_backward_varlen_8seq_one_group_and_adjoint():
     """The packed varlen workload (8 sequences, lengths U{512..16384}, each
-    with its own initial state and final-state gradient): QK head 11 and its
-    V-heads against the oracle, every head through the adjoint identities of
+    with its own initial state and final-state gradient): QK heads 10-13 and
+    their V-heads against the oracle, every head through the adjoint identities of
     the test above (summed over the sequences)."""
     import torch
     import linear_attention_sequence_delta_amd as gdn
@@ -136,7 +137,7 @@ def test_backward_varlen_8seq_one_group_and_adjoint():
     p = synth.direct_prefill(7600, lengths=lengths, init_state=True)
     d_o, dSf = synth.output_grads(7600, p.T, p.N)
     print("backward varlen", list(lengths), flush=True)
-    _check(p, d_o, dSf, 1.0, qk_heads=(11, 12))
+    _check(p, d_o, dSf, 1.0, qk_heads=(10, 14))
     cu = dev(p.cu_seqlens)
     dq, dk, dv, dg, db, dS0 = gdn.gdn_prefill_backward(dev(p.q), dev(p.k), dev(p.v), dev(p.g),
                                                        dev(p.beta), dev(d_o), dev(p.S0), dev(dSf), cu)
