@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -135,6 +135,25 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
                 const float *beta, const float *initial_state, float *final_state,
                 const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
                 float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_prefill_no_alloc -- gdn_prefill for callers that cannot allocate device
+ * memory or pass a workspace (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and rules as
+ * gdn_prefill without workspace / ws_bytes: the bf16 path keeps its workspace
+ * in a scratch array the library holds on each device it runs on (64 MiB,
+ * kept until the process ends), so the call allocates nothing.  The limit:
+ * gdn_prefill_workspace_size(GDN_BF16, N, T, ...) must not exceed 64 MiB --
+ * about 80 chunks of 64 tokens at 48 V-heads, e.g. one sequence of 4096
+ * tokens -- else GDN_ERR_WORKSPACE and nothing is enqueued.  All work runs on
+ * `stream` (no auxiliary stream).  Calls on the same device share the scratch:
+ * calls that overlap in time on one device (two streams, or two threads) race
+ * and give wrong results; order them on one stream.  GDN_F32 needs no scratch.
+ */
+int gdn_prefill_no_alloc(int io_dtype, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *initial_state,
+                         float *final_state, const int32_t *cu_seqlens, int N, int T, int H_qk,
+                         int H_v, int d_k, int d_v, float scale, void *o, void *stream);
 
 /*
  * gdn_prefill_raw_workspace_size -- bytes of device workspace gdn_prefill_raw

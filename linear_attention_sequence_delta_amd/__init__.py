@@ -38,7 +38,7 @@ EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_save_states", "gdn_prefill_raw_save_states",
            "gdn_prefill_backward_saved_workspace_size", "gdn_prefill_backward_saved",
            "gdn_layer_prefill_save_states", "gdn_layer_prefill_backward_saved_workspace_size",
-           "gdn_layer_prefill_backward_saved")
+           "gdn_layer_prefill_backward_saved", "gdn_prefill_no_alloc")
 
 _lib = None
 
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_prefill_workspace_size.restype = Z
     L.gdn_prefill.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
     L.gdn_prefill.restype = I
+    L.gdn_prefill_no_alloc.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, P, P]
+    L.gdn_prefill_no_alloc.restype = I
     L.gdn_prefill_raw_workspace_size.argtypes = [I, I, I, I, I, I]
     L.gdn_prefill_raw_workspace_size.restype = Z
     L.gdn_prefill_raw.argtypes = [P, P, F, P, P, P, P, P, I, I, I, I, I, I, F, P, P, Z, P]
@@ -302,6 +304,32 @@ def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale:
                            _stream(dev))
     _check(rc, "gdn_prefill")
     return o, fs
+
+
+def gdn_prefill_no_alloc(q, k, v, g, beta, o, initial_state=None, final_state=None,
+                         cu_seqlens=None, *, scale: float = 1.0):
+    """gdn_prefill with the workspace in the library's own scratch: allocates
+    nothing (the caller passes o and, if wanted, final_state).  Same tensors as
+    gdn_prefill; the bf16 path is limited to a workspace of 64 MiB."""
+    torch = _torch()
+    dev = _device_of(q)
+    io = GDN_BF16 if q.dtype == torch.bfloat16 else GDN_F32
+    io_t = torch.bfloat16 if io == GDN_BF16 else torch.float32
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, name, io_t, dev, 3)
+    _need(g, "g", torch.float32, dev, 2)
+    _need(beta, "beta", torch.float32, dev, 2)
+    T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    for t, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None:
+            _need(t, name, torch.float32, dev, 4)
+    rc = lib().gdn_prefill_no_alloc(io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
+                                    T, H_qk, H_v, d_k, d_v, float(scale), _ptr(o), _stream(dev))
+    _check(rc, "gdn_prefill_no_alloc")
+    return o, final_state
 
 
 def gdn_prefill_backward_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
@@ -820,6 +848,7 @@ def gdn_gated_norm_backward(o, z, w, dy, *, eps: float = 1e-6, workspace=None):
 
 
 __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefill",
+           "gdn_prefill_no_alloc",
            "gdn_chunk_states_size", "gdn_prefill_backward_saved_workspace_size",
            "gdn_prefill_workspace_size", "gdn_prefill_raw", "gdn_prefill_raw_workspace_size",
            "gdn_prefill_backward", "gdn_prefill_backward_workspace_size",

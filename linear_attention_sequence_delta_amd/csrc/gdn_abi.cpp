@@ -137,12 +137,13 @@ size_t gdn_prefill_workspace_size(int io_dtype, int N, int T, int H_qk, int H_v,
 
 namespace {
 
-// gdn_prefill, and with chunk_states (bf16 only) gdn_prefill_save_states.
+// gdn_prefill, with chunk_states (bf16 only) gdn_prefill_save_states, and with
+// no_alloc gdn_prefill_no_alloc (the workspace in the library's fixed scratch).
 int prefill_impl(int io_dtype, const void *q, const void *k, const void *v, const float *g,
                  const float *beta, const float *initial_state, float *final_state,
                  const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
                  float scale, void *o, void *chunk_states, size_t cs_bytes, void *workspace,
-                 size_t ws_bytes, void *stream) {
+                 size_t ws_bytes, void *stream, bool no_alloc = false) {
     int rc;
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
         return fail(GDN_ERR_UNSUPPORTED, "io_dtype must be GDN_F32 or GDN_BF16 (got %d)", io_dtype);
@@ -169,7 +170,10 @@ int prefill_impl(int io_dtype, const void *q, const void *k, const void *v, cons
                         overlaps(final_state, ns, beta, ng)))
         return fail(GDN_ERR_INVALID_ARG, "final_state must not overlap q, k, v, g or beta");
     const size_t need = gdn_prefill_workspace_size(io_dtype, N, T, H_qk, H_v, d_k, d_v);
-    if (ws_bytes < need || (need > 0 && !workspace))
+    if (no_alloc && need > gdn::chunked_scratch_bytes())
+        return fail(GDN_ERR_WORKSPACE, "the prefill needs %zu bytes of scratch, the library holds %zu",
+                    need, gdn::chunked_scratch_bytes());
+    if (!no_alloc && (ws_bytes < need || (need > 0 && !workspace)))
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
     if (need > 0 && (overlaps(workspace, need, o, nv) || overlaps(workspace, need, q, nqk) ||
                      overlaps(workspace, need, k, nqk) || overlaps(workspace, need, v, nv) ||
@@ -194,10 +198,13 @@ int prefill_impl(int io_dtype, const void *q, const void *k, const void *v, cons
         e = gdn::launch_recurrent_prefill(io_dtype == GDN_F32 ? gdn::kIoF32 : gdn::kIoBF16, q, k,
                                           v, g, beta, initial_state, final_state, cu_seqlens, N,
                                           T, H_qk, H_v, scale, o, s);
+    else if (no_alloc)
+        e = gdn::launch_chunked_prefill_no_alloc(q, k, v, g, beta, initial_state, final_state,
+                                                 cu_seqlens, N, T, H_qk, H_v, scale, o, s);
     else
         e = gdn::launch_chunked_prefill(q, k, v, g, beta, initial_state, final_state, cu_seqlens,
                                         N, T, H_qk, H_v, scale, o, chunk_states, workspace, s);
-    return finish(e, s, "gdn_prefill launch");
+    return finish(e, s, no_alloc ? "gdn_prefill_no_alloc launch" : "gdn_prefill launch");
 }
 
 }  // namespace
@@ -210,6 +217,14 @@ int gdn_prefill(int io_dtype, const void *q, const void *k, const void *v, const
                 float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
     return prefill_impl(io_dtype, q, k, v, g, beta, initial_state, final_state, cu_seqlens, N, T,
                         H_qk, H_v, d_k, d_v, scale, o, nullptr, 0, workspace, ws_bytes, stream);
+}
+
+int gdn_prefill_no_alloc(int io_dtype, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, const float *initial_state,
+                         float *final_state, const int32_t *cu_seqlens, int N, int T, int H_qk,
+                         int H_v, int d_k, int d_v, float scale, void *o, void *stream) {
+    return prefill_impl(io_dtype, q, k, v, g, beta, initial_state, final_state, cu_seqlens, N, T,
+                        H_qk, H_v, d_k, d_v, scale, o, nullptr, 0, nullptr, 0, stream, true);
 }
 
 size_t gdn_chunk_states_size(int N, int T, int H_v, int d_k, int d_v) {

@@ -930,11 +930,14 @@ size_t workspace_layout(int N, int T, int H_qk, int H_v, bool raw, void *base, W
     return head + rec + 2 * rows + carry;
 }
 
+// may_fork: a single long sequence may run in segments with part of the work
+// on the device's auxiliary stream (created on first use).
 template <bool kRaw>
 hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, RawIn raw,
                        const float *g, const float *beta, const float *S0, float *S_final,
                        const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, float scale,
-                       uint16_t *o16, uint16_t *states, void *workspace, hipStream_t stream) {
+                       uint16_t *o16, uint16_t *states, void *workspace, hipStream_t stream,
+                       bool may_fork = true) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
     Workspace W;
     workspace_layout(N, T, H_qk, H_v, kRaw, workspace, &W);
@@ -970,7 +973,7 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
     // one sequence (cu_seqlens, if given, is {0, T}): nch chunks known on the host
     const int nch = (T + kChunk - 1) / kChunk;
     std::unique_lock<std::mutex> lock(g_aux_mu);
-    DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux(stream) : nullptr;
+    DeviceAux *aux = (may_fork && N == 1 && nch >= kSegMinChunks) ? device_aux(stream) : nullptr;
     const int idle = aux ? aux->cus - scan_grid : 0;
     if (idle < kMinIdleCUs) {
         lock.unlock();
@@ -1148,6 +1151,53 @@ hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, c
                               static_cast<const uint16_t *>(v), RawIn{}, g, beta, S0, S_final,
                               cu_seqlens, N, T, H_qk, H_v, scale, static_cast<uint16_t *>(o),
                               static_cast<uint16_t *>(chunk_states), workspace, stream);
+}
+
+// Scratch for callers that cannot allocate (gdn_prefill_no_alloc): one array
+// per device, holding the prefill workspace of one call.  Its device address
+// is looked up once per device, with that device current; host code uses only
+// that address.  Calls that overlap on one device share the array and race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+struct ScratchAddr {
+    bool tried = false;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+std::mutex g_scratch_mu;
+ScratchAddr g_scratch[kMaxDevices];
+}  // namespace
+
+size_t chunked_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_chunked_prefill_no_alloc(const void *q, const void *k, const void *v,
+                                           const float *g, const float *beta, const float *S0,
+                                           float *S_final, const int32_t *cu_seqlens, int N, int T,
+                                           int H_qk, int H_v, float scale, void *o,
+                                           hipStream_t stream) {
+    if (chunked_workspace_bytes(N, T, H_qk, H_v, false) > kScratchBytes) return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ScratchAddr &a = g_scratch[dev];
+        if (!a.tried) {
+            a.tried = true;
+            a.err = hipGetSymbolAddress(&a.ptr, HIP_SYMBOL(scratch));
+        }
+        if (a.err != hipSuccess) return a.err;
+        ws = a.ptr;
+    }
+    // everything on the caller's stream (no auxiliary stream, no events)
+    return launch_impl<false>(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                              static_cast<const uint16_t *>(v), RawIn{}, g, beta, S0, S_final,
+                              cu_seqlens, N, T, H_qk, H_v, scale, static_cast<uint16_t *>(o),
+                              nullptr, ws, stream, false);
 }
 
 hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, const float *g,

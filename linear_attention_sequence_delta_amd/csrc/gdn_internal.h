@@ -38,6 +38,15 @@ hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, c
                                   const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                   float scale, void *o, void *chunk_states, void *workspace,
                                   hipStream_t stream);
+// The bf16 chunked prefill with its workspace in a fixed device array of
+// chunked_scratch_bytes() (for callers that cannot allocate); everything on
+// `stream`.  hipErrorInvalidValue if the workspace would not fit.
+size_t chunked_scratch_bytes();
+hipError_t launch_chunked_prefill_no_alloc(const void *q, const void *k, const void *v,
+                                           const float *g, const float *beta, const float *S0,
+                                           float *S_final, const int32_t *cu_seqlens, int N, int T,
+                                           int H_qk, int H_v, float scale, void *o,
+                                           hipStream_t stream);
 hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, const float *g,
                                       const float *beta, const float *S0, float *S_final,
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,

@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert decl == sorted(gdn.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert gdn.gdn_abi_version() == 2
+    assert gdn.gdn_abi_version() == 3
 
 
 def _prefill(L, **kw):
