@@ -69,15 +69,18 @@ T_LONG, LONG_STEPS, STACK_LAYERS = 262144, 64, 48
 MULTI_TOKENS = 4
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_T32768.txt")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_B256.txt")
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_prefill_T32768.txt")
-CHUNKED_SRC = os.path.join(ROOT, "linear_attention_sequence_delta_amd", "csrc", "gdn_chunked.hip")
+CSRC = os.path.join(ROOT, "linear_attention_sequence_delta_amd", "csrc")
+CHUNKED_SRC = os.path.join(CSRC, "gdn_chunked.hip")
+RECURRENT_SRC = os.path.join(CSRC, "gdn_recurrent.hip")
 
 
 def _sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def _profile_value(path, key):
+def _profile_value(path, key, src=CHUNKED_SRC):
     """A per-launch figure from a committed counter summary, or None when it is
     missing or the kernels changed since the counters were taken."""
     try:
@@ -86,7 +89,7 @@ def _profile_value(path, key):
             if "=" in line and not line.startswith("#"):
                 k, val = line.split("=", 1)
                 kv[k.strip()] = val.strip()
-        if kv.get("source_sha256_16") != _sha(CHUNKED_SRC):
+        if kv.get("source_sha256_16") != _sha(src):
             return None
         return float(kv[key])
     except (OSError, KeyError, ValueError):
@@ -97,8 +100,19 @@ def _traffic_bytes():
     return _profile_value(TRAFFIC_FILE, "hbm_bytes_per_prefill")
 
 
+def _decode_traffic_bytes():
+    return _profile_value(DECODE_TRAFFIC_FILE, "hbm_bytes_per_decode_step", RECURRENT_SRC)
+
+
 def _issued_mfma_flops():
     return _profile_value(MFMA_FILE, "bf16_mfma_flop_per_prefill")
+
+
+def _digests(**arrays):
+    """SHA-256 (first 16 hex digits) of each host input array's bytes."""
+    import numpy as np
+    return {k: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+            for k, a in arrays.items()}
 
 
 def _events(torch):
@@ -127,7 +141,8 @@ def run_gpu(steps, warmup, path="both"):
     g, beta = to_dev(p.g), to_dev(p.beta)
     o = torch.empty((p.T, H_V, D), dtype=torch.bfloat16, device=dev)
     fs = torch.empty((1, H_V, D, D), dtype=torch.float32, device=dev)
-    res = {}
+    res = {"numpy": np.__version__,
+           "digests": {"prefill_T32768": _digests(x=p.x, w=p.w, g=p.g, beta=p.beta)}}
 
     if path in ("both", "fused"):
         wsr = torch.empty(gdn.gdn_prefill_raw_workspace_size(1, p.T, H_QK, H_V),
@@ -319,10 +334,14 @@ def run_gpu(steps, warmup, path="both"):
         res["varlen_us"] = g0.elapsed_time(g1) / steps * 1e3
         res["varlen_T"] = pv.T
         res["varlen_lengths"] = [int(x) for x in np.diff(pv.cu_seqlens)]
+        res["digests"]["prefill_varlen_8seq"] = _digests(x=pv.x, w=pv.w, g=pv.g, beta=pv.beta,
+                                                         S0=pv.S0, cu_seqlens=pv.cu_seqlens)
         del xv, wv, gv, bv, S0v, cuv, ov, fsv, wsv
 
     # ---------------- decode workload: B = 256 over rotating 256-slot pools
     d = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
+    res["digests"]["decode_B256"] = _digests(q=d.q, k=d.k, v=d.v, g=d.g, beta=d.beta,
+                                             pool=d.pool, slot_idx=d.slot_idx)
     pools = [to_dev(d.pool) for _ in range(2)]     # 768 MiB each, larger than the on-die cache
     dq, dk, dv_, dg, db = (to_dev(a) for a in (d.q, d.k, d.v, d.g, d.beta))
     slots = to_dev(d.slot_idx)
@@ -490,26 +509,76 @@ def run_longctx():
                        "what": "256 sequences continuing from the prefill's final state"},
             "stack48": {"layers": STACK_LAYERS, "ms_per_token": stack_ms,
                         "tokens_per_s": B_DECODE / (stack_ms * 1e-3),
-                        "what": "48 independently seeded layers, one B = 256 decode step each"}}
+                        "what": "48 independently seeded layers, one B = 256 decode step each",
+                        "inputs": "timing only: each layer's pool, q, k, v and gates drawn on the "
+                                  "GPU by torch.Generator (seed 1005000 + layer), outside the "
+                                  "host-side seeded recipe; results are not compared"}}
 
 
-def cpu_baseline(T_sample=T_PREFILL):
-    """The fp64 oracle (prelude + token recurrence) on the first T_sample tokens
-    (by default all of them) of the same prefill workload, all 48 V-heads."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline():
+    """The fp64 oracle on the host's cores, on the same synthetic workloads:
+    the 32768-token prefill (prelude + token recurrence, all 48 V-heads), the
+    packed 8-sequence prefill, and one decode step at B = 64 (128-slot pool)
+    and at B = 256 (256-slot pool).  The headline value is the first; every
+    figure is whole-workload (no sampling beyond what "sample" says)."""
+    import numpy as np
     import oracle
     import synth
     oracle._load()
-    p = synth.workload_prefill_32k(T_PREFILL)
-    x = p.x[:T_sample]
-    t0 = time.perf_counter()
-    qo, ko, vo = oracle.prelude(x, p.w, None, H_qk=H_QK, H_v=H_V, dk=D, dv=D)
-    oracle.recurrent(qo, ko, vo, p.g[:T_sample], p.beta[:T_sample])
-    dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    return {"value": T_sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 prelude + token-by-token recurrence over {T_sample} of the "
-                      f"{T_PREFILL} prefill tokens, all {H_V} V-heads ({dt:.1f} s; the prelude "
-                      f"loop is single-threaded, the recurrence uses OpenMP over heads)"}
+
+    def prefill_rate(p):
+        t0 = time.perf_counter()
+        qo, ko, vo = oracle.prelude(p.x, p.w, p.cu_seqlens, H_qk=H_QK, H_v=H_V, dk=D, dv=D)
+        oracle.recurrent(qo, ko, vo, p.g, p.beta, p.S0, p.cu_seqlens)
+        dt = time.perf_counter() - t0
+        return p.T / dt, dt
+
+    def decode_rate(d):
+        t0 = time.perf_counter()
+        oracle.decode_step(d.q, d.k, d.v, d.g, d.beta, d.pool, d.slot_idx)
+        dt = time.perf_counter() - t0
+        return d.B / dt, dt
+
+    p3 = synth.workload_prefill_32k(T_PREFILL)
+    v3, t3 = prefill_rate(p3)
+    del p3
+    p4 = synth.workload_varlen()
+    v4, t4 = prefill_rate(p4)
+    T4 = p4.T
+    del p4
+    d2 = synth.workload_decode_b64()
+    v2, t2 = decode_rate(d2)
+    del d2
+    d5 = synth.decode_inputs(1005, B=B_DECODE, P=B_DECODE)
+    v5, t5 = decode_rate(d5)
+    del d5
+    return {"value": v3, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"fp64 oracle, whole workloads: prelude + token-by-token recurrence over "
+                      f"all {T_PREFILL} prefill tokens and all {H_V} V-heads ({t3:.1f} s; "
+                      f"prelude OpenMP over tokens, recurrence OpenMP over heads)",
+            "configs": {
+                "prefill_T32768": {"tokens_per_s": v3, "s": t3},
+                "prefill_varlen_8seq": {"tokens_per_s": v4, "s": t4, "tokens": T4,
+                                        "what": "packed 8-sequence prefill with initial states"},
+                "decode_B64": {"tokens_per_s": v2, "s": t2,
+                               "what": "one decode step, 64 sequences, 128-slot pool"},
+                "decode_B256": {"tokens_per_s": v5, "s": t5,
+                                "what": "one decode step, 256 sequences, 256-slot pool (the "
+                                        "long-context hand-off's decode shape; its 262144-token "
+                                        "prefill runs at the 32768-token prefill's per-token "
+                                        "rate, the oracle's cost being linear in tokens)"}}}
 
 
 def copy_calibration(nbytes):
@@ -558,6 +627,7 @@ def main():
     issued = _issued_mfma_flops() if fused else None
     pre_bytes = PRELUDE_BYTES_PER_TOKEN * T
     dec_bytes = DECODE_BYTES_PER_SEQ * B_DECODE
+    dec_traffic = _decode_traffic_bytes()
     phases = {}
     if fused:
         phases["fused_call"] = r["fused_us"]
@@ -579,6 +649,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic, seeded: raw projections N(0,1) bf16, conv weights N(0,0.5) bf16, "
                 "gates from A_log, dt_bias ~ U(-1,1) and a, b ~ N(0,1)",
+        "data_digests": r["digests"],
+        "numpy": r["numpy"],
         "config": {"workload": "prefill of one 32768-token sequence from raw bf16 projections "
                                "(conv prelude + chunked prefill), 16 QK / 48 V heads, d=128, "
                                "chunk 64, fp32 state",
@@ -601,7 +673,11 @@ def main():
                    "roofline": {"bound": "hbm",
                                 "achieved": dec_bytes / (r["dec_us"] * 1e-6) / 1e9,
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS},
+                                "frac": dec_bytes / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                                "algorithmic_bytes_per_step": dec_bytes,
+                                "traffic": dec_traffic,
+                                "traffic_frac": (None if dec_traffic is None else
+                                                 dec_traffic / (r["dec_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS)},
                    "multi_token": {
                        "tokens_per_call": MULTI_TOKENS,
                        "us_per_call": r["multi_us"],

@@ -11,7 +11,9 @@ Recipe (the same for every workload):
   * ``N(0, s)`` means a normal with standard deviation ``s``;
   * bf16 tensors are float32 draws rounded to nearest-even and returned as
     ``numpy.uint16`` bit patterns; float32 tensors are returned as float32;
-  * raw projections are drawn in 4096-token blocks in token order.
+  * raw projections [T, C] are drawn one stream per 128-channel block: block b
+    (channels 128 b .. 128 b + 127) takes child b of the tensor's seed and is
+    filled with float32 normals in row-major order (blocks drawn in parallel).
 
 Gate recipe of the gated workloads (the decay gate is handed to the layer as
 its logarithm g, the write strength as beta):
