@@ -85,13 +85,16 @@ __device__ __forceinline__ int seq_of_chunk(const int32_t *chunk_base, int N, in
 }
 
 // Workspace record of one (chunk, V-head) of the forward prefill: T', then P,
-// then the chunk's cumulative log decay G as 64 fp32.  T' and P (bf16 64 x 64)
+// then the decays gamma_r = exp(G_r) and lambda_r = exp(G_L - G_r) as 64 fp32
+// each (G the chunk's cumulative log decay, G_L its last row's; rows past a
+// sequence's end repeat G_L).  T' and P (bf16 64 x 64)
 // are stored as MFMA operand fragments: block (a, s) = 2 a + s holds, for lane
 // (c, g4), the 16 bytes of row 16 a + c, columns 32 s + 8 g4 .. +7, lanes in
 // order -- so a kernel loads each fragment as one contiguous 1 KiB block.  (A
 // fragment read from a row-major tile would touch half of 16 cache lines,
 // which halves the rate the vector memory pipe delivers.)
-constexpr int kRecElems = 2 * kTileElems + 2 * kChunk;   // in bf16 units (16640 bytes)
+constexpr int kRecElems = 2 * kTileElems + 4 * kChunk;   // in bf16 units (16896 bytes)
+constexpr int kRecGam = 2 * kTileElems;                  // gamma (fp32), then lambda
 __device__ __forceinline__ int frag_off(int a, int s, int lane) { return ((2 * a + s) * 64 + lane) * 8; }
 
 // Record of one (chunk, V-head) for the backward pass: the fragments of T'^T

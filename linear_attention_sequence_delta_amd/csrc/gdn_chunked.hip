@@ -260,7 +260,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
             constexpr bool kFwd = kRecs & kRecFwd, kBwd = kRecs & kRecBwd;
             uint16_t *rec = kFwd ? ws + ((size_t)gc * H_v + h) * kRecElems : nullptr;
             uint16_t *brec = kBwd ? bws + ((size_t)gc * H_v + h) * kBwdRecElems : nullptr;
-            if constexpr (kFwd) __builtin_nontemporal_store(G, reinterpret_cast<float *>(rec + 2 * kTileElems) + lane);
+            if constexpr (kFwd) {
+                // the decays the scan applies, exponentiated once here
+                const float GL = __shfl(G, kChunk - 1, 64);
+                float *dec = reinterpret_cast<float *>(rec + kRecGam);
+                __builtin_nontemporal_store(__expf(G), dec + lane);
+                __builtin_nontemporal_store(__expf(GL - G), dec + kChunk + lane);
+            }
             if constexpr (kBwd) reinterpret_cast<float *>(brec + kBwdGOff)[lane] = G;
             wave_lds_sync();
 
@@ -458,13 +464,13 @@ struct StateRegs {        // waves 0-3
     u32x4 kr[4];          // K row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
     u32x4 tA[2];          // T' row 16 w + c, columns 32 s + 8 g4 .. +7
     u32x4 vrow;           // v row 16 w + lane/4, slab columns 8 (lane%4) .. +7
-    float4 G4;            // G of rows 16 w + 4 g4 + j
-    float GL;             // G of the chunk's last row
+    float4 gam4, lam4;    // gamma and lambda of rows 16 w + 4 g4 + j
+    float gamL;           // gamma of the chunk's last row
 };
 struct OutRegs {          // waves 4-7
     u32x4 qr[4];          // Q row 16 w + 4 i + lane / 16, d_k 8 (lane % 16) .. +7
     u32x4 pA[2];          // P row 16 w + c, columns 32 s + 8 g4 .. +7
-    float Gown;           // G of row 16 w + c
+    float gown;           // gamma of row 16 w + c
     u32x4 xv, xvh;        // prelude fused: raw v row 16 w + lane / 4 and (lanes < 12)
                           // row 16 w - 3 + lane / 4, slab columns 8 (lane % 4) .. +7
 };
@@ -528,13 +534,18 @@ __global__ __launch_bounds__(512) void scan_kernel(
     auto chunk_len = [&](int ci) { return min(kChunk, s1 - (s0 + kChunk * ci)); };
     // K and Q rows are loaded whole (16 lanes x 16 B per row, 4 rows per
     // instruction: every cache line fully used) and regrouped into MFMA
-    // fragments through LDS.  Offset of row 16 w + 4 i + lane / 16 (clamped),
-    // 16-byte piece lane % 16, of chunk ci (rows of the q, k inputs, or of
-    // prep's chunk-aligned rows in the workspace):
-    auto krow_off = [&](int ci, int i) {
+    // fragments through LDS.  Row 16 w + 4 i + lane / 16, 16-byte piece
+    // lane % 16, of chunk ci: a chunk base common to the wave plus a 32-bit
+    // lane offset.  Prep's chunk-aligned rows in the workspace are read as
+    // they are (rows past a sequence's end hold finite values that meet only
+    // zero columns of T' and P); rows of the caller's q, k are clamped into
+    // the sequence.
+    auto krow_ptr = [&](const uint16_t *base, int ci, int i) {
+        const int r = 16 * w + 4 * i + (lane >> 4);
         const size_t row0 = kRaw ? (size_t)(cbase + ci) * kChunk : (size_t)(s0 + kChunk * ci);
-        return row0 * H_qk * kD +
-               (size_t)((min(16 * w + 4 * i + (lane >> 4), chunk_len(ci) - 1) * H_qk + hq) * kD + 8 * (lane & 15));
+        const int rc = kRaw ? r : min(r, chunk_len(ci) - 1);
+        return reinterpret_cast<const u32x4 *>(base + row0 * H_qk * kD +
+                                               (uint32_t)(__umul24(rc, H_qk * kD) + hq * kD + 8 * (lane & 15)));
     };
     const uint16_t *kin = kRaw ? raw.kws : k;
     const uint16_t *qin = kRaw ? raw.qws : q;
@@ -566,7 +577,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
         auto fetch_a = [&](int ci, StateRegs &R) {
             ci = min(ci, c_end - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R.kr[i] = *reinterpret_cast<const u32x4 *>(kin + krow_off(ci, i));
+            for (int i = 0; i < 4; ++i) R.kr[i] = *krow_ptr(kin, ci, i);
             const uint16_t *rec = rec_of(ci);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -574,12 +585,14 @@ __global__ __launch_bounds__(512) void scan_kernel(
         };
         auto fetch_b = [&](int ci, StateRegs &R) {
             ci = min(ci, c_end - 1);
-            const float *Gp = reinterpret_cast<const float *>(rec_of(ci) + 2 * kTileElems);
-            R.G4 = *reinterpret_cast<const float4 *>(Gp + 16 * w + 4 * g4);
-            R.GL = Gp[kChunk - 1];
+            const float *dp = reinterpret_cast<const float *>(rec_of(ci) + kRecGam);
+            R.gam4 = *reinterpret_cast<const float4 *>(dp + 16 * w + 4 * g4);
+            R.lam4 = *reinterpret_cast<const float4 *>(dp + kChunk + 16 * w + 4 * g4);
+            R.gamL = dp[kChunk - 1];
             if constexpr (!kRaw) {
                 const int vr = min(16 * w + (lane >> 2), chunk_len(ci) - 1);
-                R.vrow = *reinterpret_cast<const u32x4 *>(v + ((size_t)(s0 + kChunk * ci + vr) * H_v + h) * kD + e0 + 8 * (lane & 3));
+                const uint16_t *vb = v + ((size_t)(s0 + kChunk * ci) * H_v + h) * kD + e0;
+                R.vrow = *reinterpret_cast<const u32x4 *>(vb + (uint32_t)(__umul24(vr, H_v * kD) + 8 * (lane & 3)));
             }
         };
 
@@ -598,14 +611,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) kA[s] = *reinterpret_cast<const uint4 *>(sKr + (16 * w + c) * kKP + 32 * s + 8 * g4);
             fetch_a(ci + 2, pf);
-            float gam[4], dec[4];
-            const float Gr4[4] = {cur.G4.x, cur.G4.y, cur.G4.z, cur.G4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                gam[j] = __expf(Gr4[j]);
-                dec[j] = __expf(cur.GL - Gr4[j]);
-            }
-            const float gamL = __expf(cur.GL);
+            const float gam[4] = {cur.gam4.x, cur.gam4.y, cur.gam4.z, cur.gam4.w};
+            const float dec[4] = {cur.lam4.x, cur.lam4.y, cur.lam4.z, cur.lam4.w};
+            const float gamL = cur.gamL;
 
             // X = K S^T for chunk rows 16 w .. +15, both d_v tiles
             f32x4 ax[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -713,26 +721,27 @@ __global__ __launch_bounds__(512) void scan_kernel(
     } else {
         // ---------------- output waves
         // prelude fused: raw v rows of the slab, rows x row stride C
-        const size_t C = (size_t)(2 * H_qk + H_v) * kD;
+        const int C = (2 * H_qk + H_v) * kD;
         const size_t vch = (size_t)(2 * H_qk + h) * kD + e0 + 8 * (lane & 3);
         const int pr = lane >> 2;                  // this lane's row within the wave's 16
         auto fetch = [&](int ci, OutRegs &R) {
             ci = min(ci, c_end - 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R.qr[i] = *reinterpret_cast<const u32x4 *>(qin + krow_off(ci, i));
+            for (int i = 0; i < 4; ++i) R.qr[i] = *krow_ptr(qin, ci, i);
             const uint16_t *rec = rec_of(ci);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 R.pA[s] = *reinterpret_cast<const u32x4 *>(rec + kTileElems + frag_off(w, s, lane));
-            R.Gown = reinterpret_cast<const float *>(rec + 2 * kTileElems)[16 * w + c];
+            R.gown = reinterpret_cast<const float *>(rec + kRecGam)[16 * w + c];
             if constexpr (kRaw) {
                 // rows clamped into the sequence; halo rows before its start
                 // are replaced by zero when used
                 const int Lc = chunk_len(ci), c0 = s0 + kChunk * ci;
                 const int r = min(16 * w + pr, Lc - 1);
                 const int rh = max(min(16 * w - 3 + min(pr, 2), Lc - 1), -kChunk * ci);
-                R.xv = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + r) * C + vch);
-                R.xvh = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + rh) * C + vch);
+                const uint16_t *xb = raw.x + (size_t)c0 * C + (2 * H_qk + h) * kD + e0;
+                R.xv = *reinterpret_cast<const u32x4 *>(xb + (__mul24(r, C) + 8 * (lane & 3)));
+                R.xvh = *reinterpret_cast<const u32x4 *>(xb + (__mul24(rh, C) + 8 * (lane & 3)));
             }
         };
         // v of chunk cj (raw rows in R) -> conv, SiLU -> sV[cj & 1], rows 16 w .. +15
@@ -772,12 +781,16 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), qA[s], ao[nt]);
-            const float gq = scale * __expf(cur.Gown);
+            const float gq = scale * cur.gown;
+            // the next chunk's v slab (its buffer was last read before this
+            // chunk began), before barrier (1): the state waves form X and R
+            // meanwhile, and the VALU work then stays off the U phase, which
+            // barrier (2) ends
+            if constexpr (kRaw) v_conv(ci + 1, nxt);   // past the last chunk: written, never read
             __syncthreads();                                   // (1)
             // next loads issued while the state waves form U: the vector
             // memory pipe is then quiet while they form X and R
             fetch(ci + 2, pf);
-            if constexpr (kRaw) v_conv(ci + 1, nxt);   // past the last chunk: written, never read
             if constexpr (kOut == kOutBoth) {
                 // sS holds the state chunk ci starts from until barrier (2); the
                 // copy is read only by a later backward: non-temporal stores,
@@ -795,6 +808,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
             __syncthreads();                                   // (2) U complete
             // O^T += U^T P^T  (P is lower triangular: k-steps up to this row block)
             const bool row_ok = 16 * w + c < L;
+            uint16_t *ob = o + ((size_t)c0 * H_v + h) * kD + e0;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 f32x4 a = gq * ao[nt];
@@ -802,7 +816,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 if (w >= 2)
                     a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 32 + 8 * g4), cur.pA[1], a);
                 if (row_ok)
-                    *reinterpret_cast<uint2 *>(o + ((size_t)(c0 + 16 * w + c) * H_v + h) * kD + e0 + 16 * nt + 4 * g4) =
+                    *reinterpret_cast<uint2 *>(ob + (uint32_t)(__umul24(16 * w + c, H_v * kD) + 16 * nt + 4 * g4)) =
                         pk4(a[0], a[1], a[2], a[3]);
             }
             __syncthreads();                                   // (3)
