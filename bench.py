@@ -306,7 +306,43 @@ def run_gpu(steps, warmup, path="both"):
     g1.record()
     torch.cuda.synchronize()
     res["gate_bwd_us"] = g0.elapsed_time(g1) / steps * 1e3
-    del z, y, gy, gws
+    del y, gy, gws
+
+    # the layer's prefill with the output gate: one gdn_layer_prefill_gated
+    # call (gates, fused prelude + prefill, gate applied in the scan's
+    # stores) against gdn_layer_prefill followed by gdn_gated_norm
+    if path in ("both", "fused"):
+        la, lb = to_dev(p.meta["a"]), to_dev(p.meta["b"])
+        lA = to_dev(p.meta["A_log"].astype(np.float32))
+        ldt = to_dev(p.meta["dt_bias"].astype(np.float32))
+        yg = torch.empty_like(o)
+        wsg = torch.empty(gdn.gdn_layer_prefill_gated_workspace_size(1, p.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
+        wsl = torch.empty(gdn.gdn_layer_prefill_workspace_size(1, p.T, H_QK, H_V),
+                          dtype=torch.uint8, device=dev)
+
+        def gated():
+            gdn.gdn_layer_prefill_gated(x, w, la, lb, lA, ldt, z, wn, None, None, H_qk=H_QK,
+                                        H_v=H_V, final_state=fs, conv_state=False, o=o, y=yg,
+                                        workspace=wsg)
+
+        def separate():
+            gdn.gdn_layer_prefill(x, w, la, lb, lA, ldt, None, None, H_qk=H_QK, H_v=H_V,
+                                  final_state=fs, conv_state=False, o=o, workspace=wsl)
+            gdn.gdn_gated_norm(o, z, wn, out=yg)
+
+        for key, fn in (("layer_gated_us", gated), ("layer_separate_us", separate)):
+            for _ in range(max(warmup // 4, 2)):
+                fn()
+            torch.cuda.synchronize()
+            g0.record()
+            for _ in range(steps):
+                fn()
+            g1.record()
+            torch.cuda.synchronize()
+            res[key] = g0.elapsed_time(g1) / steps * 1e3
+        del yg, wsg, wsl
+    del z
 
     # the packed varlen workload (8 sequences, lengths U{512..16384}, initial
     # states): the same fused call over several independent sequences
@@ -705,6 +741,15 @@ def main():
                                                     "achieved": gate_bwd_bytes / (r["gate_bwd_us"] * 1e-6) / 1e9,
                                                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                                     "frac": gate_bwd_bytes / (r["gate_bwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS}}}
+    if "layer_gated_us" in r:
+        out["layer_step_gated"] = {
+            "us": r["layer_gated_us"], "tokens_per_s": T / (r["layer_gated_us"] * 1e-6),
+            "separate_us": r["layer_separate_us"],
+            "mfma_frac": PREFILL_FLOP_PER_TOKEN * T / (r["layer_gated_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+            "what": "gdn_layer_prefill_gated: gates from raw a, b, the prelude fused into the chunked "
+                    "prefill, and the output gate (RMS norm x weight x SiLU(z)) applied inside the "
+                    "scan as rows of o complete, one call; separate_us: gdn_layer_prefill then "
+                    "gdn_gated_norm"}
     if "bwd_us" in r:
         bflops = BACKWARD_FLOP_PER_TOKEN * T
         btf = bflops / (r["bwd_us"] * 1e-6) / 1e12

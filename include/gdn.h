@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -422,6 +422,41 @@ int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, con
                       const float *initial_state, float *final_state, void *conv_state_out,
                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
                       float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn_layer_prefill_gated_workspace_size -- bytes of device workspace
+ * gdn_layer_prefill_gated needs (host-only; 0 when T = 0): that of
+ * gdn_layer_prefill plus 2 KiB per chunk and V-head.
+ */
+size_t gdn_layer_prefill_gated_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v);
+
+/*
+ * gdn_layer_prefill_gated -- gdn_layer_prefill with the layer's output gate
+ * applied in the same call: besides o it writes
+ *     y = o / sqrt(mean(o^2) + norm_eps) * norm_w * SiLU(z)
+ * per (token, V-head) row of 128 outputs, the gate of gdn_gated_norm
+ * ([Dissect sec. 2.1] names the layer's norm and in_proj_z weights; the gate's
+ * form is the reading gdn_gated_norm documents).  When the chunked prefill's
+ * grid fits on the device at once (one sequence: 4 * H_v workgroups, at most
+ * the number of CUs), the gate is applied inside it, as each chunk's rows of
+ * o are completed, not as a pass of its own; otherwise it runs as a pass
+ * after the prefill.  Either way o and y are bit-identical to
+ * gdn_layer_prefill followed by gdn_gated_norm(o, z, norm_w, norm_eps).
+ *
+ *   x_raw ... scale, o   as for gdn_layer_prefill (o is written as there)
+ *   z               device bf16 [T][H_v][d_v], the gate projections
+ *   norm_w          device fp32 [d_v];  norm_eps >= 0
+ *   y               device bf16 [T][H_v][d_v] output, overlapping no other
+ *                   argument
+ *   workspace       at least gdn_layer_prefill_gated_workspace_size(...) bytes
+ * T = 0 leaves y untouched (final_state as for gdn_layer_prefill).
+ */
+int gdn_layer_prefill_gated(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                            const float *A_log, const float *dt_bias, float l2_eps, const void *z,
+                            const float *norm_w, float norm_eps, const float *initial_state,
+                            float *final_state, void *conv_state_out, const int32_t *cu_seqlens,
+                            int N, int T, int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                            void *y, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * gdn_layer_prefill_save_states -- gdn_layer_prefill that also keeps the

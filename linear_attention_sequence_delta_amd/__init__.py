@@ -38,7 +38,8 @@ EXPORTS = ("gdn_abi_version", "gdn_last_error", "gdn_conv_prelude",
            "gdn_prefill_save_states", "gdn_prefill_raw_save_states",
            "gdn_prefill_backward_saved_workspace_size", "gdn_prefill_backward_saved",
            "gdn_layer_prefill_save_states", "gdn_layer_prefill_backward_saved_workspace_size",
-           "gdn_layer_prefill_backward_saved", "gdn_prefill_no_alloc")
+           "gdn_layer_prefill_backward_saved", "gdn_prefill_no_alloc",
+           "gdn_layer_prefill_gated_workspace_size", "gdn_layer_prefill_gated")
 
 _lib = None
 
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is not built; run `python -m linear_attention_sequence_delta_amd.build`")
+    # torch first: its HIP runtime is then the one the process has loaded when
+    # libgdn.so's dependencies are resolved (loading the library first would
+    # bring in the system runtime ahead of torch's)
+    _torch()
     L = ctypes.CDLL(LIB_PATH)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.gdn_abi_version.argtypes = []
@@ -92,6 +97,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_layer_prefill.argtypes = [P, P, P, P, P, P, F, P, P, P, P, I, I, I, I, I, I, F, P, P,
                                     Z, P]
     L.gdn_layer_prefill.restype = I
+    L.gdn_layer_prefill_gated_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.gdn_layer_prefill_gated_workspace_size.restype = Z
+    L.gdn_layer_prefill_gated.argtypes = [P, P, P, P, P, P, F, P, P, F, P, P, P, P, I, I, I, I, I, I,
+                                          F, P, P, P, Z, P]
+    L.gdn_layer_prefill_gated.restype = I
     L.gdn_layer_decode_step.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_layer_decode_step.restype = I
     L.gdn_decode_multi_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P]
@@ -672,6 +682,76 @@ def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_se
     return o, fs, cs
 
 
+def gdn_layer_prefill_gated_workspace_size(N, T, H_qk=16, H_v=48, d_k=128, d_v=128):
+    return int(lib().gdn_layer_prefill_gated_workspace_size(N, T, H_qk, H_v, d_k, d_v))
+
+
+def gdn_layer_prefill_gated(x, conv_w, a, b, A_log, dt_bias, z, norm_w, initial_state=None,
+                            cu_seqlens=None, *, H_qk: int = 16, H_v: int = 48, d_k: int = 128,
+                            d_v: int = 128, l2_eps: float = 1e-6, norm_eps: float = 1e-6,
+                            scale: float = 1.0, final_state=True, conv_state=True, o=None, y=None,
+                            workspace=None):
+    """gdn_layer_prefill with the output gate applied in the same call: z bf16
+    [T, H_v, d_v], norm_w fp32 [d_v].  Returns (y, o, final_state, conv_state),
+    y the gated outputs."""
+    torch = _torch()
+    dev = _device_of(x)
+    _need(x, "x", torch.bfloat16, dev, 2)
+    _need(conv_w, "conv_w", torch.bfloat16, dev, 2)
+    T, C = x.shape
+    if C != 2 * H_qk * d_k + H_v * d_v or tuple(conv_w.shape) != (C, 4):
+        raise ValueError("x / conv_w shapes do not match the head configuration")
+    for name, t in (("a", a), ("b", b)):
+        _need(t, name, torch.float32, dev, 2)
+        if tuple(t.shape) != (T, H_v):
+            raise ValueError(f"{name} must be [T, H_v]")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev, 1)
+        if t.numel() != H_v:
+            raise ValueError(f"{name} must have H_v = {H_v} entries")
+    _need(z, "z", torch.bfloat16, dev, 3)
+    if tuple(z.shape) != (T, H_v, d_v):
+        raise ValueError("z must be [T, H_v, d_v]")
+    _need(norm_w, "norm_w", torch.float32, dev, 1)
+    if norm_w.numel() != d_v:
+        raise ValueError("norm_w must have d_v entries")
+    N = 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.numel() - 1
+    sshape = (N, H_v, d_v, d_k)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev, 4)
+        if tuple(initial_state.shape) != sshape:
+            raise ValueError(f"initial_state must be {sshape}")
+
+    def out_arg(val, shape, dtype, name):
+        if val is True:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        if val is None or val is False:
+            return None
+        _need(val, name, dtype, dev, len(shape))
+        if tuple(val.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+        return val
+
+    fs = out_arg(final_state, sshape, torch.float32, "final_state")
+    cs = out_arg(conv_state, (N, 3, C), torch.bfloat16, "conv_state")
+    o = out_arg(True if o is None else o, (T, H_v, d_v), torch.bfloat16, "o")
+    y = out_arg(True if y is None else y, (T, H_v, d_v), torch.bfloat16, "y")
+    ws_need = gdn_layer_prefill_gated_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_layer_prefill_gated(
+        _ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), float(l2_eps),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(initial_state), _ptr(fs), _ptr(cs),
+        _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v, float(scale), _ptr(o), _ptr(y),
+        _ptr(workspace), ws_bytes, _stream(dev))
+    _check(rc, "gdn_layer_prefill_gated")
+    return y, o, fs, cs
+
+
 def gdn_layer_decode_step(x, conv_w, a, b, A_log, dt_bias, conv_state_pool, state_pool,
                           slot_idx, *, H_qk: int = 16, H_v: int = 48, d_k: int = 128,
                           d_v: int = 128, l2_eps: float = 1e-6, scale: float = 1.0, o=None):
@@ -854,6 +934,7 @@ __all__ = ["lib", "GDNError", "gdn_abi_version", "gdn_conv_prelude", "gdn_prefil
            "gdn_prefill_backward", "gdn_prefill_backward_workspace_size",
            "gdn_layer_prefill_backward", "gdn_layer_prefill_backward_workspace_size",
            "gdn_gates", "gdn_layer_prefill", "gdn_layer_prefill_workspace_size",
+           "gdn_layer_prefill_gated", "gdn_layer_prefill_gated_workspace_size",
            "gdn_layer_decode_step", "gdn_decode_multi_step", "gdn_state_rollback",
            "gdn_gated_norm", "gdn_gated_norm_backward", "gdn_decode_step", "GDN_F32", "GDN_BF16",
            "EXPORTS"]

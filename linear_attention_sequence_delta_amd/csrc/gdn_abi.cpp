@@ -259,7 +259,8 @@ namespace {
 int check_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const float *g,
                       const float *beta, const float *initial_state, const float *final_state,
                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                      float scale, const void *o, const void *workspace, size_t ws_bytes) {
+                      float scale, const void *o, const void *workspace, size_t ws_bytes,
+                      bool gated = false) {
     int rc;
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
@@ -284,7 +285,9 @@ int check_prefill_raw(const void *x_raw, const void *conv_w, float l2_eps, const
     if (final_state && (overlaps(final_state, ns, x_raw, nx) || overlaps(final_state, ns, conv_w, nw) ||
                         overlaps(final_state, ns, g, ng) || overlaps(final_state, ns, beta, ng)))
         return fail(GDN_ERR_INVALID_ARG, "final_state must not overlap x_raw, conv_w, g or beta");
-    const size_t need = gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+    const size_t need = !gated ? gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+                        : T > 0    ? gdn::chunked_gated_workspace_bytes(N, T, H_qk, H_v)
+                                   : 0;
     if (ws_bytes < need || (need > 0 && !workspace))
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
     if (need > 0 && (overlaps(workspace, need, o, nv) || overlaps(workspace, need, x_raw, nx) ||
@@ -643,21 +646,38 @@ size_t gdn_layer_prefill_workspace_size(int N, int T, int H_qk, int H_v, int d_k
     return 2 * gate + gdn_prefill_raw_workspace_size(N, T, H_qk, H_v, d_k, d_v);
 }
 
+size_t gdn_layer_prefill_gated_workspace_size(int N, int T, int H_qk, int H_v, int d_k, int d_v) {
+    (void)d_k;
+    (void)d_v;
+    if (N < 1 || T < 1 || H_qk < 1 || H_v < 1) return 0;
+    const size_t gate = ((size_t)T * H_v * 4 + 255) & ~size_t(255);
+    return 2 * gate + gdn::chunked_gated_workspace_bytes(N, T, H_qk, H_v);
+}
+
 }  // extern "C"
 
 namespace {
 
 // gdn_layer_prefill, and with chunk_states gdn_layer_prefill_save_states.
+struct GateArgs {        // gdn_layer_prefill_gated's output gate
+    const void *z;
+    const float *norm_w;
+    float norm_eps;
+    void *y;
+};
+
 int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, const float *b,
                        const float *A_log, const float *dt_bias, float l2_eps,
                        const float *initial_state, float *final_state, void *conv_state_out,
                        const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
                        int d_v, float scale, void *o, void *chunk_states, size_t cs_bytes,
-                       void *workspace, size_t ws_bytes, void *stream) {
+                       void *workspace, size_t ws_bytes, void *stream,
+                       const GateArgs *gt = nullptr) {
     int rc;
     if ((rc = check_heads(H_qk, H_v, d_k, d_v))) return rc;
     if ((rc = check_seqs(cu_seqlens, N, T))) return rc;
-    const size_t need = gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v);
+    const size_t need = gt ? gdn_layer_prefill_gated_workspace_size(N, T, H_qk, H_v, d_k, d_v)
+                             : gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v);
     if (ws_bytes < need || (need > 0 && !workspace))
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
     if (T > 0 && (!a || !b || !A_log || !dt_bias))
@@ -686,8 +706,25 @@ int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, co
     const size_t rest_bytes = need > 0 ? ws_bytes - 2 * gate : 0;
     rc = check_prefill_raw(x_raw, conv_w, l2_eps, T > 0 ? g : nullptr, T > 0 ? beta : nullptr,
                            initial_state, final_state, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
-                           scale, o, rest, rest_bytes);
+                           scale, o, rest, rest_bytes, gt != nullptr);
     if (rc) return rc;
+    if (gt) {
+        if (!(gt->norm_eps >= 0.f) || !std::isfinite(gt->norm_eps))
+            return fail(GDN_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
+        if (T > 0 && (!gt->z || !gt->norm_w || !gt->y))
+            return fail(GDN_ERR_INVALID_ARG, "z, norm_w and y must be non-NULL");
+        const size_t nw = (size_t)gdn::kD * 4;
+        const struct { const void *p; size_t n; } other[] = {
+            {x_raw, nx}, {conv_w, craw * 4 * 2}, {a, ng}, {b, ng}, {A_log, nh}, {dt_bias, nh},
+            {initial_state, ns}, {final_state, ns}, {conv_state_out, nc}, {o, nv}, {gt->z, nv},
+            {gt->norm_w, nw}, {workspace, need}, {cu_seqlens, (size_t)(N + 1) * 4}};
+        for (const auto &x : other)
+            if (overlaps(gt->y, nv, x.p, x.n))
+                return fail(GDN_ERR_INVALID_ARG, "y must not overlap any other argument");
+        if (overlaps(o, nv, gt->z, nv) || overlaps(o, nv, gt->norm_w, nw) ||
+            overlaps(workspace, need, gt->z, nv) || overlaps(workspace, need, gt->norm_w, nw))
+            return fail(GDN_ERR_INVALID_ARG, "o and workspace must not overlap z or norm_w");
+    }
     if (chunk_states) {
         const size_t ncs = gdn_chunk_states_size(N, T, H_v, d_k, d_v);
         if (cs_bytes < ncs)
@@ -708,9 +745,13 @@ int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, co
                                           initial_state, final_state, cu_seqlens, N, T, H_qk, H_v,
                                           scale, o, s);
     else if ((e = gdn::launch_gates(a, b, A_log, dt_bias, T, H_v, g, beta, s)) == hipSuccess)
-        e = gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
-                                            final_state, cu_seqlens, N, T, H_qk, H_v, scale, o,
-                                            chunk_states, rest, s);
+        e = gt ? gdn::launch_chunked_prefill_raw_gated(x_raw, conv_w, l2_eps, g, beta, initial_state,
+                                                         final_state, cu_seqlens, N, T, H_qk, H_v,
+                                                         scale, o, gt->z, gt->norm_w,
+                                                         gt->norm_eps, gt->y, rest, s)
+                 : gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
+                                                   final_state, cu_seqlens, N, T, H_qk, H_v, scale,
+                                                   o, chunk_states, rest, s);
     if (e == hipSuccess && conv_state_out)
         e = gdn::launch_conv_hist(x_raw, cu_seqlens, N, T, (int)craw, conv_state_out, s);
     return finish(e, s, "gdn_layer_prefill launch");
@@ -728,6 +769,18 @@ int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, con
     return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
                               final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
                               scale, o, nullptr, 0, workspace, ws_bytes, stream);
+}
+
+int gdn_layer_prefill_gated(const void *x_raw, const void *conv_w, const float *a, const float *b,
+                            const float *A_log, const float *dt_bias, float l2_eps, const void *z,
+                            const float *norm_w, float norm_eps, const float *initial_state,
+                            float *final_state, void *conv_state_out, const int32_t *cu_seqlens,
+                            int N, int T, int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
+                            void *y, void *workspace, size_t ws_bytes, void *stream) {
+    const GateArgs gate{z, norm_w, norm_eps, y};
+    return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
+                              final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
+                              scale, o, nullptr, 0, workspace, ws_bytes, stream, &gate);
 }
 
 int gdn_layer_prefill_save_states(const void *x_raw, const void *conv_w, const float *a,

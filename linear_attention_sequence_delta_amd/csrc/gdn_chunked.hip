@@ -110,6 +110,14 @@ struct RawIn {             // fused prelude inputs
     uint16_t *kws, *qws;   // [chunks * 64][H_qk][128] bf16 normalised K and Q rows
 };
 
+struct GateIn {            // output gate fused into the scan's stores (kOutGated)
+    const uint16_t *z;     // [T][H_v][128] bf16 gate projections
+    const float *w;        // [128] norm weight
+    float eps;             // norm epsilon
+    uint16_t *y;           // [T][H_v][128] bf16 gated outputs
+    uint64_t *part;        // [chunks][H_v][64 rows][4 slabs] tagged partial sums, zero on entry
+};
+
 template <bool kRaw, int kRecs = kRecFwd>
 __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const RawIn raw,
@@ -473,6 +481,7 @@ struct OutRegs {          // waves 4-7
     float gown;           // gamma of row 16 w + c
     u32x4 xv, xvh;        // prelude fused: raw v row 16 w + lane / 4 and (lanes < 12)
                           // row 16 w - 3 + lane / 4, slab columns 8 (lane % 4) .. +7
+    uint4 zr;             // gate fused: z of row 16 w + lane / 4, slab columns 8 (lane % 4) .. +7
 };
 
 // 512 threads: waves 0-3 carry the state through the chunks (X = K S^T, R,
@@ -491,17 +500,34 @@ struct OutRegs {          // waves 4-7
 // (the backward's own forward pass) no outputs but the bf16 state each chunk
 // starts from (the values the chunk's products use), copied out of LDS into
 // states [chunk][H_v][d_v][d_k]; kOutBoth both (a forward pass that keeps the
-// states for a later backward).  (Stores issued by the state waves would
-// lengthen their chain: the waits for their own prefetched loads would also
-// cover the stores.)
-constexpr int kOutO = 0, kOutStates = 1, kOutBoth = 2;
+// states for a later backward); kOutGated o and the gated outputs y.  (Stores
+// issued by the state waves would lengthen their chain: the waits for their
+// own prefetched loads would also cover the stores.)
+//
+// kOutGated: the gate divides each 128-wide row of o by its RMS, and the
+// four slab workgroups of a V-head each hold 32 columns.  Output wave w of
+// each publishes, per row of its 16, the sum of squares of its 32 bf16
+// outputs, summed exactly as the gated-norm kernel's 16-lane row sums them
+// (per 8 channels a chained fma, then pairs, then the pair sums), as one 64-bit
+// word (the chunk's index + 1 in the high half, the fp32 sum in the low half;
+// the words are zeroed at the start of the call) stored with a
+// relaxed device-scope atomic: each word is valid by itself, so no fence
+// orders it against other memory.  Three chunks later the wave reads the four
+// words of its rows (spinning, bounded, until all four tags are set), adds
+// them as the row sum's last two levels do, and stores its 32 columns of y.
+// A wave waits only for workgroups of the same launch; the launcher takes this
+// path only when the whole grid fits on the device at once (one workgroup per
+// CU), so every waited-for workgroup runs.
+constexpr int kOutO = 0, kOutStates = 1, kOutBoth = 2, kOutGated = 3;
+constexpr int kGateSpin = 1 << 22;    // bound on a wave's polls for the other slabs' sums
+constexpr int kGateLag = 3;           // chunks between a chunk's outputs and its gate
 template <bool kRaw, int kOut = kOutO>
 __global__ __launch_bounds__(512) void scan_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const RawIn raw, const float *initial_state, float *final_state, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
-    int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *__restrict__ o,
-    uint16_t *__restrict__ states = nullptr) {
+    int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *o,
+    uint16_t *__restrict__ states = nullptr, const GateIn gate = GateIn{}) {
     constexpr int kVBufs = kRaw ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t sS[kSlabW * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
@@ -511,6 +537,9 @@ __global__ __launch_bounds__(512) void scan_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sV[kVBufs][kChunk * kVP];   // v rows of the chunk (slab columns)
     __shared__ __attribute__((aligned(16))) uint16_t sQ[4][16 * kKP];     // each output wave's Q rows
     __shared__ __attribute__((aligned(16))) uint16_t sXv[kRaw ? 4 : 1][20 * kVP];   // raw v rows per output wave
+    constexpr int kGw = kOut == kOutGated ? 4 : 1;
+    __shared__ __attribute__((aligned(16))) uint16_t sGo[kGw][16 * kSlabW];   // kOutGated: a wave's o rows (row-major)
+    __shared__ uint4 sGz[kGw][64];                 // and its z, output to state wave
 
     // Workgroup -> (sequence, V-head, slab): the workgroups of one QK group of
     // one sequence share an XCD's L2 (they read the same K and Q rows), and the
@@ -549,6 +578,29 @@ __global__ __launch_bounds__(512) void scan_kernel(
     };
     const uint16_t *kin = kRaw ? raw.kws : k;
     const uint16_t *qin = kRaw ? raw.qws : q;
+
+    // kOutGated: rows of a wave's o tile in the gated-norm kernel's lane layout
+    const int gr = lane >> 2, gq = lane & 3;
+    // x_l + x_(l^1), then + x_(l^2): the first two levels of the 16-lane row sum
+    auto quad_sum = [](float x) {
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+        return x;
+    };
+    // publish the sum of squares of this slab's 32 columns of row 16 w + r
+    auto publish = [&](int cj, const uint4 &o8) {
+        float ov[8];
+        unpack8(o8, ov);
+        float l = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l = __builtin_fmaf(ov[e], ov[e], l);
+        const float sq = quad_sum(l);
+        if (gq == 0) {
+            uint64_t *pw = gate.part + (((size_t)(cbase + cj) * H_v + h) * kChunk + 16 * w + gr) * kSlabsW + slab;
+            __hip_atomic_store(pw, (uint64_t(cbase + cj + 1) << 32) | __float_as_uint(sq),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
 
     if (wave < 4) {
         // ---------------- state waves
@@ -596,7 +648,95 @@ __global__ __launch_bounds__(512) void scan_kernel(
             }
         };
 
+        // kOutGated, run by state wave w on the outputs of output wave w,
+        // handed over in LDS: lane (r, q) = (lane / 4, lane % 4) holds row
+        // 16 w + r, slab columns 8 q .. +7 of o (bf16 as stored) and of z --
+        // the gated-norm kernel's layout, so the row sum is its sum: each lane
+        // chains its 8 squares, quads add pairs then pair sums.  gw: the norm
+        // weight of the lane's columns.
+        float gw[8];
+        if constexpr (kOut == kOutGated) {
+            const float4 t0 = *reinterpret_cast<const float4 *>(gate.w + e0 + 8 * gq);
+            const float4 t1 = *reinterpret_cast<const float4 *>(gate.w + e0 + 8 * gq + 4);
+            gw[0] = t0.x; gw[1] = t0.y; gw[2] = t0.z; gw[3] = t0.w;
+            gw[4] = t1.x; gw[5] = t1.y; gw[6] = t1.z; gw[7] = t1.w;
+        }
+        auto part_of = [&](int cj) {   // this lane's word: row 16 w + r, slab q
+            return gate.part + (((size_t)(cbase + cj) * H_v + h) * kChunk + 16 * w + gr) * kSlabsW + gq;
+        };
+        // wd: the lane's word as read earlier (polled again until all are set)
+        auto apply_gate = [&](int cj, const uint4 &o8, const uint4 &z8, uint64_t wd) {
+            const uint64_t *pw = part_of(cj);
+            const uint32_t tag = (uint32_t)(cbase + cj + 1);
+            // the first check outside the poll loop: it waits for this word's
+            // own read only (a loop that rereads the word makes the compiler
+            // wait for every vector memory operation in flight at its head)
+            if (!__all((uint32_t)(wd >> 32) == tag)) {
+                for (int t = 0; t < kGateSpin; ++t) {
+                    __builtin_amdgcn_s_sleep(1);
+                    wd = __hip_atomic_load(pw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (__all((uint32_t)(wd >> 32) == tag)) break;
+                }
+            }
+            // slab q's sum in lane q of the quad; the row's total in every lane
+            const float inv = rsqrtf(quad_sum(__uint_as_float((uint32_t)wd)) * (1.f / 128) + gate.eps);
+            if (16 * w + gr < chunk_len(cj)) {
+                float ov[8], zv[8], y[8];
+                unpack8(o8, ov);
+                unpack8(z8, zv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = ov[e] * inv * gw[e] * silu(zv[e]);
+                const uint4 yv = pack_bf8(y);
+                uint16_t *yb = gate.y + ((size_t)(s0 + kChunk * cj) * H_v + h) * kD + e0;
+                __builtin_nontemporal_store(u32x4{yv.x, yv.y, yv.z, yv.w},
+                                            reinterpret_cast<u32x4 *>(yb + (uint32_t)(__umul24(16 * w + gr, H_v * kD) + 8 * gq)));
+            }
+        };
+        // chunks whose gate is pending (kGateLag of them, oldest first), with
+        // their o and z; a chunk is gated kGateLag chunks after its sums are
+        // published, when the other slabs have long published theirs
+        int pend[kGateLag];
+        uint4 pend_o[kGateLag], pend_z[kGateLag];
+#pragma unroll
+        for (int i = 0; i < kGateLag; ++i) {
+            pend[i] = -1;
+            pend_o[i] = pend_z[i] = make_uint4(0, 0, 0, 0);
+        }
+        // the outputs of chunk cj (in LDS; their sums are published later in
+        // the same body): gate the oldest pending chunk (gword: its words,
+        // read earlier), then queue cj
+        auto gate_step = [&](int cj, uint64_t gword) {
+            const uint4 oc = *reinterpret_cast<const uint4 *>(sGo[w] + gr * kSlabW + 8 * gq);
+            const uint4 zc = sGz[w][lane];
+            if (pend[0] >= 0) apply_gate(pend[0], pend_o[0], pend_z[0], gword);
+#pragma unroll
+            for (int i = 0; i + 1 < kGateLag; ++i) {
+                pend[i] = pend[i + 1];
+                pend_o[i] = pend_o[i + 1];
+                pend_z[i] = pend_z[i + 1];
+            }
+            pend[kGateLag - 1] = cj;
+            pend_o[kGateLag - 1] = oc;
+            pend_z[kGateLag - 1] = zc;
+        };
+        // the words of pending chunk i (device-scope reads are slow: the words
+        // of the chunk gated in the next body are read in this one)
+        auto gate_word = [&](int i) -> uint64_t {
+            return pend[i] >= 0 ? __hip_atomic_load(part_of(pend[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : uint64_t(0);
+        };
+        uint64_t gword_next = 0;
         auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
+            // the previous chunk's outputs (handed over before its barrier
+            // (3)), gated first: a wait here finds only the previous chunk's
+            // memory operations in flight (the next chunks' loads are issued
+            // after it), and the output waves reach barrier (1) long after
+            // this wave would otherwise; then the words of the chunk the next
+            // body gates
+            if constexpr (kOut == kOutGated) {
+                if (ci > c_lo) gate_step(ci - 1, gword_next);
+                gword_next = gate_word(0);
+            }
             // this wave's 16 rows of v and of K into LDS, row-major; K's MFMA
             // fragments come back out of its own rows (with the prelude
             // fused, the output waves have already written v)
@@ -635,6 +775,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 r[3] = __uint_as_float(vv.y & 0xFFFF0000u) - gam[3] * ax[nt][3];
                 *reinterpret_cast<uint2 *>(sR + (16 * nt + c) * kRP + 16 * w + 4 * g4) = pk4(r[0], r[1], r[2], r[3]);
             }
+            // the sums of the previous chunk's outputs, published while the
+            // output waves still form this chunk's O and v
+            if constexpr (kOut == kOutGated)
+                if (ci > c_lo) publish(ci - 1, pend_o[kGateLag - 1]);
             __syncthreads();                                   // (1) R complete
             // U = T' R (T' is lower triangular: k-steps up to this row block)
 #pragma unroll
@@ -694,6 +838,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
             if (ci + 2 >= c_end) break;
             body(ci + 2, r2, r1);
         }
+        if constexpr (kOut == kOutGated) {
+            if (c_lo < c_end) {                  // handed over before the last barrier
+                gate_step(c_end - 1, gword_next);
+                publish(c_end - 1, pend_o[kGateLag - 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < kGateLag; ++i)
+                if (pend[i] >= 0)
+                    apply_gate(pend[i], pend_o[i], pend_z[i],
+                               __hip_atomic_load(part_of(pend[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
         if (final_state) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -733,6 +888,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int s = 0; s < 2; ++s)
                 R.pA[s] = *reinterpret_cast<const u32x4 *>(rec + kTileElems + frag_off(w, s, lane));
             R.gown = reinterpret_cast<const float *>(rec + kRecGam)[16 * w + c];
+            if constexpr (kOut == kOutGated) {
+                const int Lz = chunk_len(ci);
+                const uint16_t *zb = gate.z + ((size_t)(s0 + kChunk * ci) * H_v + h) * kD + e0;
+                R.zr = *reinterpret_cast<const uint4 *>(zb + __umul24(min(16 * w + (lane >> 2), Lz - 1), H_v * kD) +
+                                                        8 * (lane & 3));
+            }
             if constexpr (kRaw) {
                 // rows clamped into the sequence; halo rows before its start
                 // are replaced by zero when used
@@ -781,7 +942,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
                     ao[nt] = mfma32(*reinterpret_cast<const uint4 *>(sS + (16 * nt + c) * kKP + 32 * s + 8 * g4), qA[s], ao[nt]);
-            const float gq = scale * cur.gown;
+            const float gsc = scale * cur.gown;
             // the next chunk's v slab (its buffer was last read before this
             // chunk began), before barrier (1): the state waves form X and R
             // meanwhile, and the VALU work then stays off the U phase, which
@@ -809,15 +970,23 @@ __global__ __launch_bounds__(512) void scan_kernel(
             // O^T += U^T P^T  (P is lower triangular: k-steps up to this row block)
             const bool row_ok = 16 * w + c < L;
             uint16_t *ob = o + ((size_t)c0 * H_v + h) * kD + e0;
+            uint2 opk[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                f32x4 a = gq * ao[nt];
+                f32x4 a = gsc * ao[nt];
                 a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 8 * g4), cur.pA[0], a);
                 if (w >= 2)
                     a = mfma32(*reinterpret_cast<const uint4 *>(sU + (16 * nt + c) * kRP + 32 + 8 * g4), cur.pA[1], a);
+                opk[nt] = pk4(a[0], a[1], a[2], a[3]);
                 if (row_ok)
                     *reinterpret_cast<uint2 *>(ob + (uint32_t)(__umul24(16 * w + c, H_v * kD) + 16 * nt + 4 * g4)) =
-                        pk4(a[0], a[1], a[2], a[3]);
+                        opk[nt];
+            }
+            if constexpr (kOut == kOutGated) {      // to state wave w, which gates them
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    *reinterpret_cast<uint2 *>(sGo[w] + c * kSlabW + 16 * nt + 4 * g4) = opk[nt];
+                sGz[w][lane] = cur.zr;
             }
             __syncthreads();                                   // (3)
         };
@@ -921,18 +1090,22 @@ DeviceAux *device_aux(hipStream_t s) {
 namespace {
 
 // Workspace: chunk offsets | chunk records | (prelude fused) K rows, Q rows |
-// (one sequence) the state carried between segments.
+// (one sequence) the state carried between segments | (gate fused) the
+// tagged partial sums of squares.
 struct Workspace {
     int32_t *chunk_base;
     uint16_t *rec, *kws, *qws;
     float *carry;
+    uint64_t *part;
 };
-size_t workspace_layout(int N, int T, int H_qk, int H_v, bool raw, void *base, Workspace *wsp) {
+size_t workspace_layout(int N, int T, int H_qk, int H_v, bool raw, void *base, Workspace *wsp,
+                        bool gated = false) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
     const size_t head = align256((size_t)(N + 1) * sizeof(int32_t));
     const size_t rec = max_chunks * (size_t)H_v * kRecElems * sizeof(uint16_t);   // 256-byte multiple
     const size_t rows = raw ? max_chunks * kChunk * (size_t)H_qk * kD * sizeof(uint16_t) : 0;
     const size_t carry = N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0;
+    const size_t part = gated ? max_chunks * (size_t)H_v * kChunk * kSlabsW * sizeof(uint64_t) : 0;
     if (wsp) {
         char *p = static_cast<char *>(base);
         wsp->chunk_base = reinterpret_cast<int32_t *>(p);
@@ -940,26 +1113,49 @@ size_t workspace_layout(int N, int T, int H_qk, int H_v, bool raw, void *base, W
         wsp->kws = reinterpret_cast<uint16_t *>(p + head + rec);
         wsp->qws = reinterpret_cast<uint16_t *>(p + head + rec + rows);
         wsp->carry = reinterpret_cast<float *>(p + head + rec + 2 * rows);
+        wsp->part = gated ? reinterpret_cast<uint64_t *>(p + head + rec + 2 * rows + carry) : nullptr;
     }
-    return head + rec + 2 * rows + carry;
+    return head + rec + 2 * rows + carry + part;
+}
+
+__global__ __launch_bounds__(256) void zero_u64_kernel(uint64_t *p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
 }
 
 // may_fork: a single long sequence may run in segments with part of the work
 // on the device's auxiliary stream (created on first use).
+// gate (prelude fused only): the output gate fused into the scan's stores.
 template <bool kRaw>
 hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t *v16, RawIn raw,
                        const float *g, const float *beta, const float *S0, float *S_final,
                        const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, float scale,
                        uint16_t *o16, uint16_t *states, void *workspace, hipStream_t stream,
-                       bool may_fork = true) {
+                       bool may_fork = true, const GateIn *gate = nullptr) {
     const size_t max_chunks = (size_t)(T + kChunk - 1) / kChunk + (size_t)N;
     Workspace W;
-    workspace_layout(N, T, H_qk, H_v, kRaw, workspace, &W);
+    workspace_layout(N, T, H_qk, H_v, kRaw, workspace, &W, gate != nullptr);
+    GateIn gt{};
+    if (gate) {
+        gt = *gate;
+        gt.part = W.part;
+    }
+    const int scan_grid = N * H_v * kSlabsW;
+    // The fused gate makes workgroups wait for their V-head's other slabs, so
+    // it is taken only when the whole grid is resident at once (one workgroup
+    // per CU); otherwise the scan writes o and the gate runs as its own pass.
+    bool fuse_gate = false;
+    if (gate) {
+        int dev = 0, cus = 0;
+        hipError_t ge = hipGetDevice(&dev);
+        if (ge == hipSuccess) ge = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (ge != hipSuccess) return ge;
+        fuse_gate = scan_grid <= cus;
+    }
     raw.kws = W.kws;
     raw.qws = W.qws;
     int32_t *chunk_base = W.chunk_base;
     uint16_t *ws = W.rec;
-    const int scan_grid = N * H_v * kSlabsW;
     auto prep = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
         const int items = (c_hi - c_lo) * H_qk;
         const int grid = min((items + kPrepWaves - 1) / kPrepWaves, max_grid);
@@ -969,6 +1165,14 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
         return hipGetLastError();
     };
     auto scan = [&](int c_lo, int c_hi, const float *init, float *fin) {
+        if constexpr (kRaw) {
+            if (fuse_gate) {
+                hipLaunchKernelGGL((scan_kernel<true, kOutGated>), dim3(scan_grid), dim3(512), 0, stream,
+                                   q16, k16, v16, raw, init, fin, cu_seqlens, chunk_base, N, T, H_qk,
+                                   H_v, scale, c_lo, c_hi, ws, o16, nullptr, gt);
+                return hipGetLastError();
+            }
+        }
         if (states)
             hipLaunchKernelGGL((scan_kernel<kRaw, kOutBoth>), dim3(scan_grid), dim3(512), 0, stream,
                                q16, k16, v16, raw, init, fin, cu_seqlens, chunk_base, N, T, H_qk,
@@ -983,6 +1187,17 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, chunk_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (fuse_gate) {     // tags cleared by a kernel (the call may be captured into a graph)
+        const size_t n = max_chunks * (size_t)H_v * kChunk * kSlabsW;
+        hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, W.part, n);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+
+    // the gate as its own pass when it could not be fused
+    auto gate_pass = [&]() {
+        if (!gate || fuse_gate) return hipSuccess;
+        return launch_gated_norm(o16, gate->z, gate->w, T * H_v, gate->eps, gate->y, stream);
+    };
 
     // one sequence (cu_seqlens, if given, is {0, T}): nch chunks known on the host
     const int nch = (T + kChunk - 1) / kChunk;
@@ -993,7 +1208,8 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
         lock.unlock();
         const int all = (int)max_chunks;
         if ((e = prep(0, all, (all * H_qk + kPrepWaves - 1) / kPrepWaves, stream)) != hipSuccess) return e;
-        return scan(0, all, S0, S_final);
+        if ((e = scan(0, all, S0, S_final)) != hipSuccess) return e;
+        return gate_pass();
     }
 
     // The state passes from segment to segment through final_state, or the
@@ -1014,7 +1230,7 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
         if ((e = scan(b[i], b[i + 1], i == 0 ? S0 : carry, i == nseg - 1 ? S_final : carry)) != hipSuccess)
             return e;
     }
-    return hipSuccess;
+    return gate_pass();
 }
 
 // Backward workspace: chunk offsets | forward records | backward records |
@@ -1156,6 +1372,10 @@ size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw) {
     return workspace_layout(N, T, H_qk, H_v, raw, nullptr, nullptr);
 }
 
+size_t chunked_gated_workspace_bytes(int N, int T, int H_qk, int H_v) {
+    return workspace_layout(N, T, H_qk, H_v, true, nullptr, nullptr, true);
+}
+
 hipError_t launch_chunked_prefill(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, const float *S0, float *S_final,
                                   const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
@@ -1223,6 +1443,20 @@ hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, c
     return launch_impl<true>(nullptr, nullptr, nullptr, raw, g, beta, S0, S_final, cu_seqlens, N, T,
                              H_qk, H_v, scale, static_cast<uint16_t *>(o),
                              static_cast<uint16_t *>(chunk_states), workspace, stream);
+}
+
+hipError_t launch_chunked_prefill_raw_gated(const void *x, const void *w, float eps, const float *g,
+                                            const float *beta, const float *S0, float *S_final,
+                                            const int32_t *cu_seqlens, int N, int T, int H_qk,
+                                            int H_v, float scale, void *o, const void *z,
+                                            const float *norm_w, float norm_eps, void *y,
+                                            void *workspace, hipStream_t stream) {
+    RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr};
+    const GateIn gate{static_cast<const uint16_t *>(z), norm_w, norm_eps, static_cast<uint16_t *>(y),
+                      nullptr};
+    return launch_impl<true>(nullptr, nullptr, nullptr, raw, g, beta, S0, S_final, cu_seqlens, N, T,
+                             H_qk, H_v, scale, static_cast<uint16_t *>(o), nullptr, workspace, stream,
+                             true, &gate);
 }
 
 }  // namespace gdn

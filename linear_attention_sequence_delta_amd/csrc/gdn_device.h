@@ -89,6 +89,24 @@ __device__ __forceinline__ uint4 pack_bf8(const float *y) {
     return out;
 }
 
+// The output gate on one 128-wide row held by a 16-lane DPP row (8 channels,
+// one 16-byte piece of o and of z per lane; wv the norm weight of the lane's
+// channels): y = o / sqrt(mean(o^2) + eps) * w * SiLU(z).  Every lane of the
+// row must be active.  Shared by every kernel that applies the gate.
+__device__ __forceinline__ uint4 gate_row8(uint4 o8, uint4 z8, const float (&wv)[8], float eps) {
+    float ov[8], zv[8];
+    unpack8(o8, ov);
+    unpack8(z8, zv);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(ov[e], ov[e], ss);
+    const float inv = rsqrtf(row16_sum(ss) * (1.f / 128) + eps);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = ov[e] * inv * wv[e] * silu(zv[e]);
+    return pack_bf8(y);
+}
+
 // Gates from the raw per-token projections a, b of a V-head and the layer's
 // A_log, dt_bias: log decay g = -softplus(a + dt_bias) * exp(A_log) (softplus
 // written max(x, 0) + log1p(exp(-|x|)), which cannot overflow) and write

@@ -52,6 +52,16 @@ hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, c
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                       float scale, void *o, void *chunk_states, void *workspace,
                                       hipStream_t stream);
+// The same with the output gate (o / sqrt(mean(o^2) + norm_eps) * norm_w *
+// SiLU(z) per 128-wide row) fused into the scan's stores: o and y both
+// written; the workspace holds chunked_gated_workspace_bytes.
+size_t chunked_gated_workspace_bytes(int N, int T, int H_qk, int H_v);
+hipError_t launch_chunked_prefill_raw_gated(const void *x, const void *w, float eps, const float *g,
+                                            const float *beta, const float *S0, float *S_final,
+                                            const int32_t *cu_seqlens, int N, int T, int H_qk,
+                                            int H_v, float scale, void *o, const void *z,
+                                            const float *norm_w, float norm_eps, void *y,
+                                            void *workspace, hipStream_t stream);
 
 // Gradients of the chunked bf16 prefill (dq, dk, dv bf16; dg, dbeta, dS0 fp32);
 // `saved` / chunk_states: with the chunk states of an earlier forward pass.

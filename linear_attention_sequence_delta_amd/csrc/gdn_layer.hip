@@ -75,23 +75,12 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const uint16_t *o,
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     const v4u oa = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(o + off));
     const v4u za = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(z + off));
-    float ov[8], zv[8];
-    unpack8(make_uint4(oa.x, oa.y, oa.z, oa.w), ov);
-    unpack8(make_uint4(za.x, za.y, za.z, za.w), zv);
     const float4 w0 = *reinterpret_cast<const float4 *>(w + 8 * cg);
     const float4 w1 = *reinterpret_cast<const float4 *>(w + 8 * cg + 4);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(ov[e], ov[e], ss);
-    const float inv = rsqrtf(row16_sum(ss) * (1.f / kD) + eps);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = ov[e] * inv * wv[e] * silu(zv[e]);
-    if (row < rows) {
-        const uint4 pv = pack_bf8(y);
+    const uint4 pv = gate_row8(make_uint4(oa.x, oa.y, oa.z, oa.w), make_uint4(za.x, za.y, za.z, za.w), wv, eps);
+    if (row < rows)
         __builtin_nontemporal_store(v4u{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<v4u *>(out + off));
-    }
 }
 
 }  // namespace

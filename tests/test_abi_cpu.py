@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert decl == sorted(gdn.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert gdn.gdn_abi_version() == 3
+    assert gdn.gdn_abi_version() == 4
 
 
 def _prefill(L, **kw):
@@ -191,6 +191,49 @@ def test_layer_prefill_workspace_size():
         assert (gdn.gdn_layer_prefill_workspace_size(N, T, 16, 48)
                 == 2 * gate + gdn.gdn_prefill_raw_workspace_size(N, T, 16, 48))
     assert gdn.gdn_layer_prefill_workspace_size(1, 0, 16, 48) == 0
+
+
+def _layer_prefill_gated(L, **kw):
+    big = 1 << 40
+    a = dict(x=big, w=2 * big, a=3 * big, b=4 * big, A=5 * big, dt=6 * big, eps=1e-6, z=9 * big,
+             nw=10 * big, neps=1e-6, S0=None, Sf=None, cs=None, cu=None, N=1, T=64, H_qk=16,
+             H_v=48, d_k=128, d_v=128, scale=1.0, o=7 * big, y=11 * big, ws=8 * big,
+             ws_bytes=gdn.gdn_layer_prefill_gated_workspace_size(1, 64, 16, 48), stream=None)
+    a.update(kw)
+    return L.gdn_layer_prefill_gated(a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"],
+                                     a["z"], a["nw"], a["neps"], a["S0"], a["Sf"], a["cs"], a["cu"],
+                                     a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"],
+                                     a["scale"], a["o"], a["y"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(z=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(nw=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(y=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(neps=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(neps=-1.0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(y=7 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),     # y overlaps o
+    (dict(y=9 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),     # y overlaps z
+    (dict(z=7 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),     # z overlaps o
+    (dict(ws_bytes="plain"), gdn.GDN_ERR_WORKSPACE),     # gdn_layer_prefill's size: too small
+    (dict(a=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(d_v=64), gdn.GDN_ERR_UNSUPPORTED),
+])
+def test_layer_prefill_gated_rejects_bad_arguments(kw, code):
+    L = gdn.lib()
+    if kw.get("ws_bytes") == "plain":
+        kw = dict(kw, ws_bytes=gdn.gdn_layer_prefill_workspace_size(1, 64, 16, 48))
+    assert _layer_prefill_gated(L, **kw) == code
+    assert L.gdn_last_error().decode()
+
+
+def test_layer_prefill_gated_workspace_size():
+    for N, T in ((1, 1), (1, 4133), (8, 65536)):
+        plain = gdn.gdn_layer_prefill_workspace_size(N, T, 16, 48)
+        chunks = (T + 63) // 64 + N
+        part = chunks * 48 * 64 * 4 * 8         # a tagged 8-byte sum per (chunk, V-head, row, slab)
+        assert gdn.gdn_layer_prefill_gated_workspace_size(N, T, 16, 48) == plain + part
+    assert gdn.gdn_layer_prefill_gated_workspace_size(1, 0, 16, 48) == 0
 
 
 def test_layer_decode_rejects_bad_arguments():
