@@ -22,6 +22,7 @@ namespace gdn {
 namespace {
 
 constexpr int kRun = 32;          // tokens walked by one lane group
+constexpr int kBatch = 8;         // rows loaded together
 constexpr int kGroupsPerBlock = 16;
 
 __global__ __launch_bounds__(256) void conv_prelude_kernel(
@@ -81,41 +82,56 @@ __global__ __launch_bounds__(256) void conv_prelude_kernel(
     }
     const bool normalise = cb < 2 * H_qk;
 
-    // the run's rows of x are read once and q, k, v written once: non-temporal
+    // the run's rows of x are read once and q, k, v written once: non-temporal.
+    // Rows are loaded kBatch at a time, the next batch in flight while this
+    // one is computed (rows past T are read clamped and not stored).
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     auto ldx = [&](int t) {
-        const v4u a = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(x + (size_t)t * C + ch0));
+        const v4u a = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u *>(x + (size_t)min(t, T - 1) * C + ch0));
         return make_uint4(a.x, a.y, a.z, a.w);
     };
-    uint4 nxt = make_uint4(0, 0, 0, 0);
-    if (t0 < t1) nxt = ldx(t0);
-    for (int t = t0; t < t1; ++t) {
-        float cur[8];
-        unpack8(nxt, cur);
-        if (t + 1 < t1) nxt = ldx(t + 1);
-        if (cu_seqlens && t >= s1) {                   // a new sequence starts at t
-            while (n + 1 < N && cu_seqlens[n + 1] <= t) ++n;
-            s1 = cu_seqlens[n + 1];
+    uint4 buf[2][kBatch];
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+    for (int i = 0; i < kBatch; ++i) buf[0][i] = ldx(t0 + i);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+    for (int bi = 0; bi < kRun / kBatch; ++bi) {
+        const int cur = bi & 1;
+        if (bi + 1 < kRun / kBatch) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) buf[cur ^ 1][i] = ldx(t0 + (bi + 1) * kBatch + i);
         }
-        float y[8];
-        float ss = 0.f;
-        conv_silu8(wt, win[0], win[1], win[2], cur, y, ss);
-        if (normalise) {
-            const float r = rsqrtf(row16_sum(ss) + eps);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] *= r;
-        }
-        const uint4 pv = pack_bf8(y);
-        __builtin_nontemporal_store(v4u{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<v4u *>(dst + (size_t)t * dst_stride));
+        for (int i = 0; i < kBatch; ++i) {
+            const int t = t0 + bi * kBatch + i;
+            if (t >= t1) break;
+            float cur_x[8];
+            unpack8(buf[cur][i], cur_x);
+            if (cu_seqlens && t >= s1) {               // a new sequence starts at t
+                while (n + 1 < N && cu_seqlens[n + 1] <= t) ++n;
+                s1 = cu_seqlens[n + 1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            win[0][e] = win[1][e];
-            win[1][e] = win[2][e];
-            win[2][e] = cur[e];
+                for (int j = 0; j < 3; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+            }
+            float y[8];
+            float ss = 0.f;
+            conv_silu8(wt, win[0], win[1], win[2], cur_x, y, ss);
+            if (normalise) {
+                const float r = rsqrtf(row16_sum(ss) + eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] *= r;
+            }
+            const uint4 pv = pack_bf8(y);
+            __builtin_nontemporal_store(v4u{pv.x, pv.y, pv.z, pv.w},
+                                        reinterpret_cast<v4u *>(dst + (size_t)t * dst_stride));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                win[0][e] = win[1][e];
+                win[1][e] = win[2][e];
+                win[2][e] = cur_x[e];
+            }
         }
     }
 }
