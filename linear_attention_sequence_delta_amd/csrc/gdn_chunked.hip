@@ -75,10 +75,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *__restrict__ c
 // and they would otherwise displace the K and Q rows the scan's workgroups
 // share through L2.
 
-// One wave per (chunk, QK head) item; a workgroup holds kPrepWaves independent
-// waves, each with its own LDS area, that step through the items
-// [item_lo, item_hi) (item = chunk * H_qk + QK head) with the grid's stride.
-// A workgroup fills one CU (one wave per SIMD), so a small grid stays on as
+// One wave per (chunk, QK head) item; a workgroup holds 8 (forward) or 4
+// (backward records) independent waves, each with its own LDS area, that step
+// through the items [item_lo, item_hi) (item = chunk * H_qk + QK head) with
+// the grid's stride.  A workgroup fills one CU, so a small grid stays on as
 // many CUs as it has workgroups.  The K and Q rows of the chunk are loaded
 // straight into MFMA operand registers: the A operand of a 16-row block and
 // the B operand of K^T for the same block are the same fragment (row c of the
@@ -118,26 +118,33 @@ struct GateIn {            // output gate fused into the scan's stores (kOutGate
     uint64_t *part;        // [chunks][H_v][64 rows][4 slabs] tagged partial sums, zero on entry
 };
 
+// Waves per prep workgroup.  The forward-only prep keeps within 256 VGPRs and
+// 18 KiB of LDS per wave, so a workgroup of 8 waves (two per SIMD, hiding each
+// other's latency) fills one CU -- and, needing more than half of its LDS,
+// never shares a CU with a second prep workgroup or a scan workgroup, so a
+// prep grid of as many workgroups as idle CUs stays on at most that many
+// CUs.  The backward forms need more registers: 4 waves, one per SIMD.
+template <int kRecs> constexpr int kPrepWavesOf = kRecs == kRecFwd ? 8 : kPrepWaves;
 template <bool kRaw, int kRecs = kRecFwd>
-__global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
+__global__ __launch_bounds__(64 * kPrepWavesOf<kRecs>) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const RawIn raw,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
     int item_lo, int item_hi, uint16_t *__restrict__ ws, uint16_t *__restrict__ bws = nullptr) {
-    __shared__ __attribute__((aligned(16))) float sA_w[kPrepWaves][kChunk * kAP];
-    __shared__ __attribute__((aligned(16))) uint16_t sP_w[kPrepWaves][kChunk * kRP];
-    __shared__ __attribute__((aligned(16))) float sG_w[kPrepWaves][kChunk];
-    __shared__ __attribute__((aligned(16))) float sBt_w[kPrepWaves][kChunk];
+    constexpr int kW = kPrepWavesOf<kRecs>;
+    __shared__ __attribute__((aligned(16))) float sA_w[kW][kChunk * kAP];
+    __shared__ __attribute__((aligned(16))) float sG_w[kW][kChunk];
+    __shared__ __attribute__((aligned(16))) float sBt_w[kW][kChunk];
 
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     float *sA = sA_w[wv];
-    uint16_t *sP = sP_w[wv];
+    uint16_t *sP = reinterpret_cast<uint16_t *>(sA);       // P (bf16 rows), before A is formed
     float *sG = sG_w[wv];
     float *sBt = sBt_w[wv];
     const int lane = threadIdx.x & 63, g4 = lane >> 4, c = lane & 15;
     const int group = H_v / H_qk;
     const int hi = min(item_hi, chunk_base[N] * H_qk);
-    for (int it = item_lo + (int)blockIdx.x * kPrepWaves + wv; it < hi; it += (int)gridDim.x * kPrepWaves) {
+    for (int it = item_lo + (int)blockIdx.x * kW + wv; it < hi; it += (int)gridDim.x * kW) {
         const int gc = it / H_qk, hq = it - gc * H_qk;
         const int n = seq_of_chunk(chunk_base, N, gc);
         const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
@@ -181,17 +188,19 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
                     }
                 }
                 uint16_t *dst = (m == 0 ? raw.kws : raw.qws) + ((size_t)gc * kChunk * H_qk + hq) * kD + 8 * cg;
-                // all 16 rows in flight before any arithmetic (one wave per
-                // SIMD: nothing else hides the memory latency)
-                u32x4 xr[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    xr[j] = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + min(16 * sg + j, L - 1)) * C + ch);
+                // the rows in two groups of 8, each in flight before its
+                // arithmetic (the other wave on the SIMD hides the rest)
+                u32x4 xr[8];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
+                    if (j % 8 == 0) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            xr[i] = *reinterpret_cast<const u32x4 *>(raw.x + (size_t)(c0 + min(16 * sg + j + i, L - 1)) * C + ch);
+                    }
                     const int r = 16 * sg + j;
                     float cur[8], y[8], ss = 0.f;
-                    unpack8(__builtin_bit_cast(uint4, xr[j]), cur);
+                    unpack8(__builtin_bit_cast(uint4, xr[j % 8]), cur);
                     conv_silu8(wt, win[0], win[1], win[2], cur, y, ss);
                     const float rn = rsqrtf(row16_sum(ss) + raw.eps);
 #pragma unroll
@@ -278,12 +287,13 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
             if constexpr (kBwd) reinterpret_cast<float *>(brec + kBwdGOff)[lane] = G;
             wave_lds_sync();
 
-            // gated K K^T -> A (fp32 rows in LDS, lower tiles); gated Q K^T -> P
-            // (bf16 rows in LDS, zero above the diagonal)
+            // gated Q K^T -> P (bf16 rows in the wave's LDS area, zero above the
+            // diagonal), stored out; then gated K K^T -> A (fp32 rows in the
+            // same area, lower tiles)
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const int row = 16 * I + c;
-                const float Gr = sG[row], br = sBt[row];
+                const float Gr = sG[row];
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
                     if (J > I) {
@@ -292,15 +302,12 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
                     }
                     const float4 Gv = *reinterpret_cast<const float4 *>(sG + 16 * J + 4 * g4);
                     const float gi[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
-                    float av[4], pv[4];
+                    float pv[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int col = 16 * J + 4 * g4 + j;
-                        const float e = __expf(Gr - gi[j]);
-                        av[j] = col < row ? br * e * kk[I][J][j] : 0.f;
-                        pv[j] = col <= row ? scale * e * qk[I][J][j] : 0.f;
+                        pv[j] = col <= row ? scale * __expf(Gr - gi[j]) * qk[I][J][j] : 0.f;
                     }
-                    *reinterpret_cast<float4 *>(sA + row * kAP + 16 * J + 4 * g4) = make_float4(av[0], av[1], av[2], av[3]);
                     *reinterpret_cast<uint2 *>(sP + row * kRP + 16 * J + 4 * g4) = pk4(pv[0], pv[1], pv[2], pv[3]);
                 }
             }
@@ -327,6 +334,25 @@ __global__ __launch_bounds__(64 * kPrepWaves) void prep_kernel(
                                    e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
                 }
             }
+            wave_lds_sync();                                // P read before A overwrites it
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int row = 16 * I + c;
+                const float Gr = sG[row], br = sBt[row];
+#pragma unroll
+                for (int J = 0; J <= I; ++J) {
+                    const float4 Gv = *reinterpret_cast<const float4 *>(sG + 16 * J + 4 * g4);
+                    const float gi[4] = {Gv.x, Gv.y, Gv.z, Gv.w};
+                    float av[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int col = 16 * J + 4 * g4 + j;
+                        av[j] = col < row ? br * __expf(Gr - gi[j]) * kk[I][J][j] : 0.f;
+                    }
+                    *reinterpret_cast<float4 *>(sA + row * kAP + 16 * J + 4 * g4) = make_float4(av[0], av[1], av[2], av[3]);
+                }
+            }
+            wave_lds_sync();
 
             float *A = sA;
             // Diagonal 16 x 16 blocks: lane (b, c) solves column c of block b by
@@ -1158,8 +1184,9 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
     uint16_t *ws = W.rec;
     auto prep = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
         const int items = (c_hi - c_lo) * H_qk;
-        const int grid = min((items + kPrepWaves - 1) / kPrepWaves, max_grid);
-        hipLaunchKernelGGL(prep_kernel<kRaw>, dim3(grid), dim3(64 * kPrepWaves), 0, s, q16, k16, raw,
+        constexpr int kW = kPrepWavesOf<kRecFwd>;
+        const int grid = min((items + kW - 1) / kW, max_grid);
+        hipLaunchKernelGGL(prep_kernel<kRaw>, dim3(grid), dim3(64 * kW), 0, s, q16, k16, raw,
                            g, beta, cu_seqlens, chunk_base, N, T, H_qk, H_v, scale, c_lo * H_qk,
                            c_hi * H_qk, ws);
         return hipGetLastError();
@@ -1207,7 +1234,7 @@ hipError_t launch_impl(const uint16_t *q16, const uint16_t *k16, const uint16_t 
     if (idle < kMinIdleCUs) {
         lock.unlock();
         const int all = (int)max_chunks;
-        if ((e = prep(0, all, (all * H_qk + kPrepWaves - 1) / kPrepWaves, stream)) != hipSuccess) return e;
+        if ((e = prep(0, all, INT32_MAX, stream)) != hipSuccess) return e;
         if ((e = scan(0, all, S0, S_final)) != hipSuccess) return e;
         return gate_pass();
     }
