@@ -554,12 +554,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
     const int32_t *__restrict__ chunk_base, int N, int T, int H_qk, int H_v, float scale,
     int c_lo, int c_hi, const uint16_t *__restrict__ ws, uint16_t *o,
     uint16_t *__restrict__ states = nullptr, const GateIn gate = GateIn{}) {
-    constexpr int kVBufs = kRaw ? 2 : 1;
+    constexpr int kVBufs = 2;
     __shared__ __attribute__((aligned(16))) uint16_t sS[kSlabW * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sR[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sU[kSlabW * kRP];
     __shared__ __attribute__((aligned(16))) uint16_t sUs[kSlabW * kRP];
-    __shared__ __attribute__((aligned(16))) uint16_t sKr[kChunk * kKP];   // K rows of the chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sKr[2][kChunk * kKP];   // K rows of the chunk (double-buffered)
     __shared__ __attribute__((aligned(16))) uint16_t sV[kVBufs][kChunk * kVP];   // v rows of the chunk (slab columns)
     __shared__ __attribute__((aligned(16))) uint16_t sQ[4][16 * kKP];     // each output wave's Q rows
     __shared__ __attribute__((aligned(16))) uint16_t sXv[kRaw ? 4 : 1][20 * kVP];   // raw v rows per output wave
@@ -752,7 +752,17 @@ __global__ __launch_bounds__(512) void scan_kernel(
                                 : uint64_t(0);
         };
         uint64_t gword_next = 0;
-        auto body = [&](int ci, StateRegs &cur, StateRegs &pf) {
+        // this wave's 16 rows of K (and, prelude not fused, of v) of chunk cj
+        // into LDS, row-major, written a chunk ahead (the output waves write
+        // v when the prelude is fused)
+        auto stage_rows = [&](int cj, const StateRegs &R) {
+            if constexpr (!kRaw)
+                *reinterpret_cast<u32x4 *>(sV[cj & 1] + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = R.vrow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4 *>(sKr[cj & 1] + (16 * w + 4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = R.kr[i];
+        };
+        auto body = [&](int ci, StateRegs &cur, StateRegs &nxt, StateRegs &pf) {
             // the previous chunk's outputs (handed over before its barrier
             // (3)), gated first: a wait here finds only the previous chunk's
             // memory operations in flight (the next chunks' loads are issued
@@ -763,19 +773,13 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 if (ci > c_lo) gate_step(ci - 1, gword_next);
                 gword_next = gate_word(0);
             }
-            // this wave's 16 rows of v and of K into LDS, row-major; K's MFMA
-            // fragments come back out of its own rows (with the prelude
-            // fused, the output waves have already written v)
-            const uint16_t *sVc = sV[kRaw ? (ci & 1) : 0];
-            if constexpr (!kRaw)
-                *reinterpret_cast<u32x4 *>(sV[0] + (16 * w + (lane >> 2)) * kVP + 8 * (lane & 3)) = cur.vrow;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4 *>(sKr + (16 * w + 4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = cur.kr[i];
-            wave_lds_sync();
+            // K's MFMA fragments out of this wave's own rows, staged in LDS
+            // during the previous chunk
+            const uint16_t *sVc = sV[ci & 1];
+            const uint16_t *sKc = sKr[ci & 1];
             uint4 kA[4];          // K row 16 w + c, d_k 32 s + 8 g4 .. +7
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kA[s] = *reinterpret_cast<const uint4 *>(sKr + (16 * w + c) * kKP + 32 * s + 8 * g4);
+            for (int s = 0; s < 4; ++s) kA[s] = *reinterpret_cast<const uint4 *>(sKc + (16 * w + c) * kKP + 32 * s + 8 * g4);
             fetch_a(ci + 2, pf);
             const float gam[4] = {cur.gam4.x, cur.gam4.y, cur.gam4.z, cur.gam4.w};
             const float dec[4] = {cur.lam4.x, cur.lam4.y, cur.lam4.z, cur.lam4.w};
@@ -829,7 +833,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 // K^T row 32 w + 16 t + c, chunk rows 32 s + 8 g4 .. +7: two transposing reads
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const uint16_t *base = sKr + (32 * s + 8 * g4 + (c >> 2)) * kKP + 32 * w + 16 * t + 4 * (c & 3);
+                    const uint16_t *base = sKc + (32 * s + 8 * g4 + (c >> 2)) * kKP + 32 * w + 16 * t + 4 * (c & 3);
                     const uint2 lo = lds_read_tr16(base);
                     const uint2 hi = lds_read_tr16(base + 4 * kKP);
                     ka[t][s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -844,6 +848,7 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     for (int s = 0; s < 2; ++s) as = mfma32(ka[t][s], ub[nt][s], as);
                     st[t][nt] = as;
                 }
+            stage_rows(ci + 1, nxt);       // the other buffers: last read in chunk ci - 1
             write_state_lds();
             __syncthreads();                                   // (3) S' complete
         };
@@ -855,14 +860,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
             fetch_b(c_lo, r0);
             fetch_a(c_lo + 1, r1);
             fetch_b(c_lo + 1, r1);
+            stage_rows(c_lo, r0);
         }
         __syncthreads();
         for (int ci = c_lo; ci < c_end; ci += 3) {
-            body(ci, r0, r2);
+            body(ci, r0, r1, r2);
             if (ci + 1 >= c_end) break;
-            body(ci + 1, r1, r0);
+            body(ci + 1, r1, r2, r0);
             if (ci + 2 >= c_end) break;
-            body(ci + 2, r2, r1);
+            body(ci + 2, r2, r0, r1);
         }
         if constexpr (kOut == kOutGated) {
             if (c_lo < c_end) {                  // handed over before the last barrier
