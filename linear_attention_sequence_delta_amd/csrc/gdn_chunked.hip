@@ -762,6 +762,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<u32x4 *>(sKr[cj & 1] + (16 * w + 4 * i + (lane >> 4)) * kKP + 8 * (lane & 15)) = R.kr[i];
         };
+        uint4 kA[4];              // K row 16 w + c, d_k 32 s + 8 g4 .. +7 of the chunk about to run
+        auto read_ka = [&](int cj) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                kA[s] = *reinterpret_cast<const uint4 *>(sKr[cj & 1] + (16 * w + c) * kKP + 32 * s + 8 * g4);
+        };
         auto body = [&](int ci, StateRegs &cur, StateRegs &nxt, StateRegs &pf) {
             // the previous chunk's outputs (handed over before its barrier
             // (3)), gated first: a wait here finds only the previous chunk's
@@ -773,13 +779,10 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 if (ci > c_lo) gate_step(ci - 1, gword_next);
                 gword_next = gate_word(0);
             }
-            // K's MFMA fragments out of this wave's own rows, staged in LDS
-            // during the previous chunk
+            // K's MFMA fragments (kA) were read out of this wave's own rows,
+            // staged in LDS, at the end of the previous chunk
             const uint16_t *sVc = sV[ci & 1];
             const uint16_t *sKc = sKr[ci & 1];
-            uint4 kA[4];          // K row 16 w + c, d_k 32 s + 8 g4 .. +7
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kA[s] = *reinterpret_cast<const uint4 *>(sKc + (16 * w + c) * kKP + 32 * s + 8 * g4);
             fetch_a(ci + 2, pf);
             const float gam[4] = {cur.gam4.x, cur.gam4.y, cur.gam4.z, cur.gam4.w};
             const float dec[4] = {cur.lam4.x, cur.lam4.y, cur.lam4.z, cur.lam4.w};
@@ -822,15 +825,12 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     pk4(dec[0] * au[0], dec[1] * au[1], dec[2] * au[2], dec[3] * au[3]);
             }
             fetch_b(ci + 2, pf);
-            __syncthreads();                                   // (2) U complete
-            // S' = gamma_L S + (diag(exp(G_L - G)) U)^T K   (d_k 32 w .. +31)
+            // the state update's K^T fragments and gamma_L S, ahead of barrier
+            // (2): they do not depend on U.  K^T row 32 w + 16 t + c, chunk rows
+            // 32 s + 8 g4 .. +7: two transposing reads
             uint4 ub[2][2], ka[2][2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    ub[nt][s] = *reinterpret_cast<const uint4 *>(sUs + (16 * nt + c) * kRP + 32 * s + 8 * g4);
-                // K^T row 32 w + 16 t + c, chunk rows 32 s + 8 g4 .. +7: two transposing reads
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const uint16_t *base = sKc + (32 * s + 8 * g4 + (c >> 2)) * kKP + 32 * w + 16 * t + 4 * (c & 3);
@@ -838,18 +838,30 @@ __global__ __launch_bounds__(512) void scan_kernel(
                     const uint2 hi = lds_read_tr16(base + 4 * kKP);
                     ka[t][s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 }
-            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) st[t][nt] = gamL * st[t][nt];
+            __syncthreads();                                   // (2) U complete
+            // S' = gamma_L S + (diag(exp(G_L - G)) U)^T K   (d_k 32 w .. +31)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    ub[nt][s] = *reinterpret_cast<const uint4 *>(sUs + (16 * nt + c) * kRP + 32 * s + 8 * g4);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    f32x4 as = gamL * st[t][nt];
+                    f32x4 as = st[t][nt];
 #pragma unroll
                     for (int s = 0; s < 2; ++s) as = mfma32(ka[t][s], ub[nt][s], as);
                     st[t][nt] = as;
                 }
             stage_rows(ci + 1, nxt);       // the other buffers: last read in chunk ci - 1
             write_state_lds();
+            wave_lds_sync();
+            read_ka(ci + 1);
             __syncthreads();                                   // (3) S' complete
         };
 
@@ -861,6 +873,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
             fetch_a(c_lo + 1, r1);
             fetch_b(c_lo + 1, r1);
             stage_rows(c_lo, r0);
+            wave_lds_sync();
+            read_ka(c_lo);
         }
         __syncthreads();
         for (int ci = c_lo; ci < c_end; ci += 3) {
