@@ -617,6 +617,27 @@ def cpu_baseline():
                                         "rate, the oracle's cost being linear in tokens)"}}}
 
 
+def copy_rate_gbps(nbytes=1 << 30, reps=20):
+    """HBM rate of a plain device copy (torch copy_, nbytes read and nbytes
+    written per copy), timed with HIP events after warm-up copies."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / t / 1e9
+
+
 def copy_calibration(nbytes):
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
@@ -728,6 +749,11 @@ def main():
                        "what": "gdn_layer_decode_step: conv from each slot's 3-row history + the "
                                "new raw row, gates from raw a, b, the update, history shift"}},
     }
+    cps = copy_rate_gbps()
+    out["hbm_copy"] = {"GB/s": cps, "frac": cps / PEAK_HBM_GBPS,
+                       "what": "torch copy_ of a 1 GiB device buffer (reads and writes in equal "
+                               "parts, the mix of the decode step and the prelude): context for "
+                               "their HBM fractions, not a step"}
     gate_bytes = 3 * T * H_V * D * 2
     gate_bwd_bytes = 5 * T * H_V * D * 2     # o, z, dy in; d_o, dz out
     out["output_gate"] = {"us": r["gate_us"], "what": "gdn_gated_norm on the prefill's o "
