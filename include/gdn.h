@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -409,19 +409,35 @@ size_t gdn_layer_prefill_workspace_size(int N, int T, int H_qk, int H_v, int d_k
  * gdn_prefill_raw (conv prelude fused into the bf16 chunked prefill), then,
  * if conv_state_out is given, each sequence's conv history for decoding on:
  * its last three raw rows, oldest first, zero where the sequence is shorter.
- * Bit-identical to those calls made one after the other.
+ * Without conv_state_in, bit-identical to those calls made one after the
+ * other.
+ *
+ * A prefill that resumes sequences (a prompt fed in several calls, or a
+ * prefill after decode steps) passes their conv history as conv_state_in:
+ * the conv window before each sequence's first token reads those three raw
+ * rows instead of zeros, and a sequence shorter than three tokens takes the
+ * rest of its conv_state_out from them.  With initial_state and
+ * conv_state_in carried from a prefill of a sequence's first tokens, the
+ * outputs of its remaining tokens are those of one prefill of the whole
+ * sequence (bit for bit when the first part is a whole number of 64-token
+ * chunks: the chunks then coincide).
  *
  *   x_raw, conv_w, l2_eps, initial_state, final_state, cu_seqlens, scale, o
  *                   as for gdn_prefill_raw
  *   a, b            device fp32 [T][H_v];  A_log, dt_bias  device fp32 [H_v]
+ *   conv_state_in   device bf16 [N][3][C_raw], each sequence's three raw rows
+ *                   before its first token, oldest first; or NULL (zeros).
+ *                   May be conv_state_out itself (updated in place), but no
+ *                   other output or the workspace.
  *   conv_state_out  device bf16 [N][3][C_raw] output, or NULL
  *   workspace       at least gdn_layer_prefill_workspace_size(...) bytes
  */
 int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, const float *b,
                       const float *A_log, const float *dt_bias, float l2_eps,
-                      const float *initial_state, float *final_state, void *conv_state_out,
-                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                      float scale, void *o, void *workspace, size_t ws_bytes, void *stream);
+                      const float *initial_state, float *final_state, const void *conv_state_in,
+                      void *conv_state_out, const int32_t *cu_seqlens, int N, int T, int H_qk,
+                      int H_v, int d_k, int d_v, float scale, void *o, void *workspace,
+                      size_t ws_bytes, void *stream);
 
 /*
  * gdn_layer_prefill_gated_workspace_size -- bytes of device workspace
@@ -454,14 +470,17 @@ size_t gdn_layer_prefill_gated_workspace_size(int N, int T, int H_qk, int H_v, i
 int gdn_layer_prefill_gated(const void *x_raw, const void *conv_w, const float *a, const float *b,
                             const float *A_log, const float *dt_bias, float l2_eps, const void *z,
                             const float *norm_w, float norm_eps, const float *initial_state,
-                            float *final_state, void *conv_state_out, const int32_t *cu_seqlens,
-                            int N, int T, int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
-                            void *y, void *workspace, size_t ws_bytes, void *stream);
+                            float *final_state, const void *conv_state_in, void *conv_state_out,
+                            const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
+                            int d_v, float scale, void *o, void *y, void *workspace, size_t ws_bytes,
+                            void *stream);
 
 /*
  * gdn_layer_prefill_save_states -- gdn_layer_prefill that also keeps the
  * chunk states for gdn_layer_prefill_backward_saved (as
- * gdn_prefill_raw_save_states does; outputs bit-identical to gdn_layer_prefill).
+ * gdn_prefill_raw_save_states does; outputs bit-identical to gdn_layer_prefill
+ * with no conv_state_in: the backward differentiates sequences that start
+ * with zero conv history).
  *
  *   chunk_states, cs_bytes   device bf16 output of at least
  *                            gdn_chunk_states_size(N, T, H_v, d_k, d_v) bytes,

@@ -94,13 +94,13 @@ def lib() -> ctypes.CDLL:
     L.gdn_gates.restype = I
     L.gdn_layer_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     L.gdn_layer_prefill_workspace_size.restype = Z
-    L.gdn_layer_prefill.argtypes = [P, P, P, P, P, P, F, P, P, P, P, I, I, I, I, I, I, F, P, P,
-                                    Z, P]
+    L.gdn_layer_prefill.argtypes = [P, P, P, P, P, P, F, P, P, P, P, P, I, I, I, I, I, I, F, P,
+                                    P, Z, P]
     L.gdn_layer_prefill.restype = I
     L.gdn_layer_prefill_gated_workspace_size.argtypes = [I, I, I, I, I, I]
     L.gdn_layer_prefill_gated_workspace_size.restype = Z
-    L.gdn_layer_prefill_gated.argtypes = [P, P, P, P, P, P, F, P, P, F, P, P, P, P, I, I, I, I, I, I,
-                                          F, P, P, P, Z, P]
+    L.gdn_layer_prefill_gated.argtypes = [P, P, P, P, P, P, F, P, P, F, P, P, P, P, P, I, I, I, I, I,
+                                          I, F, P, P, P, Z, P]
     L.gdn_layer_prefill_gated.restype = I
     L.gdn_layer_decode_step.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, F, P, P]
     L.gdn_layer_decode_step.restype = I
@@ -609,6 +609,16 @@ def gdn_gates(a, b, A_log, dt_bias, *, out=None):
     return g, beta
 
 
+def _conv_state_in_arg(t, N, C, dev):
+    if t is None:
+        return None
+    torch = _torch()
+    _need(t, "conv_state_in", torch.bfloat16, dev, 3)
+    if tuple(t.shape) != (N, 3, C):
+        raise ValueError(f"conv_state_in must be {(N, 3, C)}")
+    return t
+
+
 def gdn_layer_prefill_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: int = 128,
                                      d_v: int = 128) -> int:
     return int(lib().gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v))
@@ -617,13 +627,17 @@ def gdn_layer_prefill_workspace_size(N: int, T: int, H_qk: int, H_v: int, d_k: i
 def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_seqlens=None, *,
                       H_qk: int = 16, H_v: int = 48, d_k: int = 128, d_v: int = 128,
                       l2_eps: float = 1e-6, scale: float = 1.0, final_state=True,
-                      conv_state=True, o=None, workspace=None, chunk_states=None):
+                      conv_state=True, o=None, workspace=None, chunk_states=None,
+                      conv_state_in=None):
     """The layer's prefill from raw projections: gates from a, b, then the fused
     prelude + chunked prefill, then each sequence's conv history.  x: bf16
     [T, C_raw]; a, b: fp32 [T, H_v]; A_log, dt_bias: fp32 [H_v].  final_state /
     conv_state: True (allocate), False/None (skip) or a tensor to write
-    (conv_state: bf16 [N, 3, C_raw]); chunk_states as for gdn_prefill.  Returns
-    (o, final_state, conv_state), plus chunk_states when it is given."""
+    (conv_state: bf16 [N, 3, C_raw]); chunk_states as for gdn_prefill (not
+    with conv_state_in).  conv_state_in: bf16 [N, 3, C_raw], the conv history
+    each sequence resumes from (a previous call's conv_state; may be the
+    conv_state tensor itself), or None for zeros.  Returns (o, final_state,
+    conv_state), plus chunk_states when it is given."""
     torch = _torch()
     dev = _device_of(x)
     _need(x, "x", torch.bfloat16, dev, 2)
@@ -661,12 +675,15 @@ def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_se
 
     fs = out_arg(final_state, sshape, torch.float32, "final_state")
     cs = out_arg(conv_state, (N, 3, C), torch.bfloat16, "conv_state")
+    ci = _conv_state_in_arg(conv_state_in, N, C, dev)
     o = out_arg(True if o is None else o, (T, H_v, d_v), torch.bfloat16, "o")
     ws_need = gdn_layer_prefill_workspace_size(N, T, H_qk, H_v, d_k, d_v)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if chunk_states is not None:
+        if ci is not None:
+            raise ValueError("chunk_states (training) takes no conv_state_in")
         kst, k_bytes = _chunk_states_arg(chunk_states, N, T, H_v, d_k, d_v, dev)
         rc = lib().gdn_layer_prefill_save_states(
             _ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), float(l2_eps),
@@ -676,7 +693,7 @@ def gdn_layer_prefill(x, conv_w, a, b, A_log, dt_bias, initial_state=None, cu_se
         return o, fs, cs, kst
     rc = lib().gdn_layer_prefill(_ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log),
                                  _ptr(dt_bias), float(l2_eps), _ptr(initial_state), _ptr(fs),
-                                 _ptr(cs), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v,
+                                 _ptr(ci), _ptr(cs), _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v,
                                  float(scale), _ptr(o), _ptr(workspace), ws_bytes, _stream(dev))
     _check(rc, "gdn_layer_prefill")
     return o, fs, cs
@@ -690,10 +707,10 @@ def gdn_layer_prefill_gated(x, conv_w, a, b, A_log, dt_bias, z, norm_w, initial_
                             cu_seqlens=None, *, H_qk: int = 16, H_v: int = 48, d_k: int = 128,
                             d_v: int = 128, l2_eps: float = 1e-6, norm_eps: float = 1e-6,
                             scale: float = 1.0, final_state=True, conv_state=True, o=None, y=None,
-                            workspace=None):
+                            workspace=None, conv_state_in=None):
     """gdn_layer_prefill with the output gate applied in the same call: z bf16
-    [T, H_v, d_v], norm_w fp32 [d_v].  Returns (y, o, final_state, conv_state),
-    y the gated outputs."""
+    [T, H_v, d_v], norm_w fp32 [d_v]; conv_state_in as for gdn_layer_prefill.
+    Returns (y, o, final_state, conv_state), y the gated outputs."""
     torch = _torch()
     dev = _device_of(x)
     _need(x, "x", torch.bfloat16, dev, 2)
@@ -739,13 +756,14 @@ def gdn_layer_prefill_gated(x, conv_w, a, b, A_log, dt_bias, z, norm_w, initial_
     cs = out_arg(conv_state, (N, 3, C), torch.bfloat16, "conv_state")
     o = out_arg(True if o is None else o, (T, H_v, d_v), torch.bfloat16, "o")
     y = out_arg(True if y is None else y, (T, H_v, d_v), torch.bfloat16, "y")
+    ci = _conv_state_in_arg(conv_state_in, N, C, dev)
     ws_need = gdn_layer_prefill_gated_workspace_size(N, T, H_qk, H_v, d_k, d_v)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().gdn_layer_prefill_gated(
         _ptr(x), _ptr(conv_w), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), float(l2_eps),
-        _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(initial_state), _ptr(fs), _ptr(cs),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(initial_state), _ptr(fs), _ptr(ci), _ptr(cs),
         _ptr(cu_seqlens), N, T, H_qk, H_v, d_k, d_v, float(scale), _ptr(o), _ptr(y),
         _ptr(workspace), ws_bytes, _stream(dev))
     _check(rc, "gdn_layer_prefill_gated")

@@ -668,7 +668,8 @@ struct GateArgs {        // gdn_layer_prefill_gated's output gate
 
 int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, const float *b,
                        const float *A_log, const float *dt_bias, float l2_eps,
-                       const float *initial_state, float *final_state, void *conv_state_out,
+                       const float *initial_state, float *final_state, const void *conv_state_in,
+                       void *conv_state_out,
                        const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
                        int d_v, float scale, void *o, void *chunk_states, size_t cs_bytes,
                        void *workspace, size_t ws_bytes, void *stream,
@@ -698,6 +699,17 @@ int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, co
     if (overlaps(o, nv, a, ng) || overlaps(o, nv, b, ng) ||
         (final_state && (overlaps(final_state, ns, a, ng) || overlaps(final_state, ns, b, ng))))
         return fail(GDN_ERR_INVALID_ARG, "o and final_state must not overlap a or b");
+    if (conv_state_in) {
+        // read through the whole call; conv_state_out may be the same buffer
+        // (it is written last), but not a shifted view of it
+        if (conv_state_out && conv_state_out != conv_state_in && overlaps(conv_state_out, nc, conv_state_in, nc))
+            return fail(GDN_ERR_INVALID_ARG, "conv_state_in must be conv_state_out or not overlap it");
+        if (overlaps(conv_state_in, nc, o, nv) || overlaps(conv_state_in, nc, final_state, ns) ||
+            (need > 0 && overlaps(conv_state_in, nc, workspace, need)) ||
+            (gt && overlaps(conv_state_in, nc, gt->y, nv)) ||
+            (chunk_states && overlaps(conv_state_in, nc, chunk_states, cs_bytes)))
+            return fail(GDN_ERR_INVALID_ARG, "conv_state_in must not overlap any output or the workspace");
+    }
     // the gates go to the front of the workspace, the prefill's workspace follows
     const size_t gate = need > 0 ? ((size_t)T * H_v * 4 + 255) & ~size_t(255) : 0;
     float *g = need > 0 ? static_cast<float *>(workspace) : nullptr;
@@ -748,12 +760,12 @@ int layer_prefill_impl(const void *x_raw, const void *conv_w, const float *a, co
         e = gt ? gdn::launch_chunked_prefill_raw_gated(x_raw, conv_w, l2_eps, g, beta, initial_state,
                                                          final_state, cu_seqlens, N, T, H_qk, H_v,
                                                          scale, o, gt->z, gt->norm_w,
-                                                         gt->norm_eps, gt->y, rest, s)
+                                                         gt->norm_eps, gt->y, rest, s, conv_state_in)
                  : gdn::launch_chunked_prefill_raw(x_raw, conv_w, l2_eps, g, beta, initial_state,
                                                    final_state, cu_seqlens, N, T, H_qk, H_v, scale,
-                                                   o, chunk_states, rest, s);
+                                                   o, chunk_states, rest, s, conv_state_in);
     if (e == hipSuccess && conv_state_out)
-        e = gdn::launch_conv_hist(x_raw, cu_seqlens, N, T, (int)craw, conv_state_out, s);
+        e = gdn::launch_conv_hist(x_raw, cu_seqlens, N, T, (int)craw, conv_state_in, conv_state_out, s);
     return finish(e, s, "gdn_layer_prefill launch");
 }
 
@@ -763,23 +775,27 @@ extern "C" {
 
 int gdn_layer_prefill(const void *x_raw, const void *conv_w, const float *a, const float *b,
                       const float *A_log, const float *dt_bias, float l2_eps,
-                      const float *initial_state, float *final_state, void *conv_state_out,
-                      const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k, int d_v,
-                      float scale, void *o, void *workspace, size_t ws_bytes, void *stream) {
+                      const float *initial_state, float *final_state, const void *conv_state_in,
+                      void *conv_state_out, const int32_t *cu_seqlens, int N, int T, int H_qk,
+                      int H_v, int d_k, int d_v, float scale, void *o, void *workspace,
+                      size_t ws_bytes, void *stream) {
     return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
-                              final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
+                              final_state, conv_state_in, conv_state_out, cu_seqlens, N, T, H_qk,
+                              H_v, d_k, d_v,
                               scale, o, nullptr, 0, workspace, ws_bytes, stream);
 }
 
 int gdn_layer_prefill_gated(const void *x_raw, const void *conv_w, const float *a, const float *b,
                             const float *A_log, const float *dt_bias, float l2_eps, const void *z,
                             const float *norm_w, float norm_eps, const float *initial_state,
-                            float *final_state, void *conv_state_out, const int32_t *cu_seqlens,
-                            int N, int T, int H_qk, int H_v, int d_k, int d_v, float scale, void *o,
-                            void *y, void *workspace, size_t ws_bytes, void *stream) {
+                            float *final_state, const void *conv_state_in, void *conv_state_out,
+                            const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v, int d_k,
+                            int d_v, float scale, void *o, void *y, void *workspace, size_t ws_bytes,
+                            void *stream) {
     const GateArgs gate{z, norm_w, norm_eps, y};
     return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
-                              final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
+                              final_state, conv_state_in, conv_state_out, cu_seqlens, N, T, H_qk,
+                              H_v, d_k, d_v,
                               scale, o, nullptr, 0, workspace, ws_bytes, stream, &gate);
 }
 
@@ -792,8 +808,9 @@ int gdn_layer_prefill_save_states(const void *x_raw, const void *conv_w, const f
                                   size_t ws_bytes, void *stream) {
     if (!chunk_states) return fail(GDN_ERR_INVALID_ARG, "chunk_states must be non-NULL");
     return layer_prefill_impl(x_raw, conv_w, a, b, A_log, dt_bias, l2_eps, initial_state,
-                              final_state, conv_state_out, cu_seqlens, N, T, H_qk, H_v, d_k, d_v,
-                              scale, o, chunk_states, cs_bytes, workspace, ws_bytes, stream);
+                              final_state, nullptr, conv_state_out, cu_seqlens, N, T, H_qk, H_v,
+                              d_k, d_v, scale, o, chunk_states, cs_bytes, workspace, ws_bytes,
+                              stream);
 }
 
 int gdn_layer_decode_step(const void *x_raw, const void *conv_w, const float *a, const float *b,

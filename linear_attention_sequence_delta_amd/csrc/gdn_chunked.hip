@@ -108,6 +108,8 @@ struct RawIn {             // fused prelude inputs
     const uint16_t *w;     // [C_raw][4] bf16 conv taps
     float eps;             // L2-norm epsilon
     uint16_t *kws, *qws;   // [chunks * 64][H_qk][128] bf16 normalised K and Q rows
+    const uint16_t *hist;  // [N][3][C_raw] bf16: each sequence's three raw rows before its
+                           // first token, oldest first (a resumed prefill), or null: zeros
 };
 
 struct GateIn {            // output gate fused into the scan's stores (kOutGated)
@@ -175,16 +177,20 @@ __global__ __launch_bounds__(64 * kPrepWavesOf<kRecs>) void prep_kernel(
                 float wt[4][8];
                 load_taps8(raw.w, ch, wt);
                 // window x[r-3], x[r-2], x[r-1] for r = 16 sg; taps before the
-                // sequence start read zero
+                // sequence start read its history rows (zero without one)
                 float win[3][8];
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
                     const int r = 16 * sg - 3 + j;
                     const int rc = max(min(r, L - 1), s0 - c0);
-                    unpack8(*reinterpret_cast<const uint4 *>(raw.x + (size_t)(c0 + rc) * C + ch), win[j]);
-                    if (c0 + r < s0) {
+                    const bool pre = c0 + r < s0;          // c0 + r - s0 in [-3, -1]
+                    if (pre && !raw.hist) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) win[j][e] = 0.f;
+                    } else {
+                        const uint16_t *src = pre ? raw.hist + ((size_t)n * 3 + 3 + (c0 + r - s0)) * C + ch
+                                                  : raw.x + (size_t)(c0 + rc) * C + ch;
+                        unpack8(*reinterpret_cast<const uint4 *>(src), win[j]);
                     }
                 }
                 uint16_t *dst = (m == 0 ? raw.kws : raw.qws) + ((size_t)gc * kChunk * H_qk + hq) * kD + 8 * cg;
@@ -945,10 +951,15 @@ __global__ __launch_bounds__(512) void scan_kernel(
                 // are replaced by zero when used
                 const int Lc = chunk_len(ci), c0 = s0 + kChunk * ci;
                 const int r = min(16 * w + pr, Lc - 1);
+                const int rel = kChunk * ci + 16 * w - 3 + min(pr, 2);      // halo row, from the sequence start
                 const int rh = max(min(16 * w - 3 + min(pr, 2), Lc - 1), -kChunk * ci);
                 const uint16_t *xb = raw.x + (size_t)c0 * C + (2 * H_qk + h) * kD + e0;
                 R.xv = *reinterpret_cast<const u32x4 *>(xb + (__mul24(r, C) + 8 * (lane & 3)));
-                R.xvh = *reinterpret_cast<const u32x4 *>(xb + (__mul24(rh, C) + 8 * (lane & 3)));
+                // a halo row before the sequence start comes from its history (rel in [-3, -1])
+                const uint16_t *hsrc = rel < 0 && raw.hist
+                                           ? raw.hist + ((size_t)n * 3 + 3 + max(rel, -3)) * C + (2 * H_qk + h) * kD + e0
+                                           : xb + __mul24(rh, C);
+                R.xvh = *reinterpret_cast<const u32x4 *>(hsrc + 8 * (lane & 3));
             }
         };
         // v of chunk cj (raw rows in R) -> conv, SiLU -> sV[cj & 1], rows 16 w .. +15
@@ -958,7 +969,8 @@ __global__ __launch_bounds__(512) void scan_kernel(
             uint16_t *xs = sXv[w];                 // rows 0-2: halo, 3-18: the wave's rows, 19: unused
             const int pc = 8 * (lane & 3);
             *reinterpret_cast<u32x4 *>(xs + (3 + pr) * kVP + pc) = R.xv;
-            const bool before = kChunk * cj + 16 * w - 3 + pr < 0;       // ahead of the sequence start
+            // ahead of the sequence start: its history row, or zero without one
+            const bool before = kChunk * cj + 16 * w - 3 + pr < 0 && !raw.hist;
             *reinterpret_cast<u32x4 *>(xs + (lane < 12 ? pr : 19) * kVP + pc) =
                 before ? u32x4{0u, 0u, 0u, 0u} : R.xvh;
             wave_lds_sync();
@@ -1485,8 +1497,9 @@ hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, c
                                       const float *beta, const float *S0, float *S_final,
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                       float scale, void *o, void *chunk_states, void *workspace,
-                                      hipStream_t stream) {
-    RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr};
+                                      hipStream_t stream, const void *conv_hist_in) {
+    RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr,
+              static_cast<const uint16_t *>(conv_hist_in)};
     return launch_impl<true>(nullptr, nullptr, nullptr, raw, g, beta, S0, S_final, cu_seqlens, N, T,
                              H_qk, H_v, scale, static_cast<uint16_t *>(o),
                              static_cast<uint16_t *>(chunk_states), workspace, stream);
@@ -1497,8 +1510,10 @@ hipError_t launch_chunked_prefill_raw_gated(const void *x, const void *w, float 
                                             const int32_t *cu_seqlens, int N, int T, int H_qk,
                                             int H_v, float scale, void *o, const void *z,
                                             const float *norm_w, float norm_eps, void *y,
-                                            void *workspace, hipStream_t stream) {
-    RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr};
+                                            void *workspace, hipStream_t stream,
+                                            const void *conv_hist_in) {
+    RawIn raw{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w), eps, nullptr, nullptr,
+              static_cast<const uint16_t *>(conv_hist_in)};
     const GateIn gate{static_cast<const uint16_t *>(z), norm_w, norm_eps, static_cast<uint16_t *>(y),
                       nullptr};
     return launch_impl<true>(nullptr, nullptr, nullptr, raw, g, beta, S0, S_final, cu_seqlens, N, T,

@@ -51,7 +51,7 @@ hipError_t launch_chunked_prefill_raw(const void *x, const void *w, float eps, c
                                       const float *beta, const float *S0, float *S_final,
                                       const int32_t *cu_seqlens, int N, int T, int H_qk, int H_v,
                                       float scale, void *o, void *chunk_states, void *workspace,
-                                      hipStream_t stream);
+                                      hipStream_t stream, const void *conv_hist_in = nullptr);
 // The same with the output gate (o / sqrt(mean(o^2) + norm_eps) * norm_w *
 // SiLU(z) per 128-wide row) fused into the scan's stores: o and y both
 // written; the workspace holds chunked_gated_workspace_bytes.
@@ -61,7 +61,8 @@ hipError_t launch_chunked_prefill_raw_gated(const void *x, const void *w, float 
                                             const int32_t *cu_seqlens, int N, int T, int H_qk,
                                             int H_v, float scale, void *o, const void *z,
                                             const float *norm_w, float norm_eps, void *y,
-                                            void *workspace, hipStream_t stream);
+                                            void *workspace, hipStream_t stream,
+                                            const void *conv_hist_in = nullptr);
 
 // Gradients of the chunked bf16 prefill (dq, dk, dv bf16; dg, dbeta, dS0 fp32);
 // `saved` / chunk_states: with the chunk states of an earlier forward pass.
@@ -106,8 +107,11 @@ hipError_t launch_gates_bwd(const float *a, const float *b, const float *A_log,
 // The layer's forward from raw projections: gates, conv history, decode.
 hipError_t launch_gates(const float *a, const float *b, const float *A_log, const float *dt_bias,
                         int T, int H_v, float *g, float *beta, hipStream_t stream);
+// Each sequence's last three raw rows into hist_out ([N][3][C_raw]); rows
+// before a sequence's start come from hist_in (or are zero without it).
+// hist_out may be hist_in.
 hipError_t launch_conv_hist(const void *x, const int32_t *cu_seqlens, int N, int T, int C_raw,
-                            void *hist, hipStream_t stream);
+                            const void *hist_in, void *hist_out, hipStream_t stream);
 hipError_t launch_conv_shift(const void *x, const int32_t *slot_idx, int B, int C_raw, void *hist,
                              hipStream_t stream);
 hipError_t launch_gated_norm(const void *o, const void *z, const float *w, int rows, float eps,

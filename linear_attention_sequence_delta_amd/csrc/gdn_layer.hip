@@ -32,18 +32,30 @@ __global__ __launch_bounds__(256) void gates_kernel(const float *__restrict__ a,
     beta[i] = gate_beta(b[i]);
 }
 
-// grid (pieces per row / 256, 3, N): row j of sequence n's history
+// grid (pieces per row / 256, N): piece p of sequence n's three history rows.
+// Row j is raw row s1 - 3 + j, or, before the sequence start, row L + j of
+// its incoming history (zero without one); each thread reads its three
+// values before writing any, so hist_out may be hist_in.
 __global__ __launch_bounds__(256) void conv_hist_kernel(const uint16_t *__restrict__ x,
                                                         const int32_t *__restrict__ cu, int T,
-                                                        int pieces, uint16_t *__restrict__ hist) {
+                                                        int pieces, const uint16_t *hist_in,
+                                                        uint16_t *hist_out) {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= pieces) return;
-    const int j = blockIdx.y, n = blockIdx.z;
+    const int n = blockIdx.y;
     const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
-    const int t = s1 - 3 + j;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (t >= s0) val = reinterpret_cast<const uint4 *>(x)[(size_t)t * pieces + p];
-    reinterpret_cast<uint4 *>(hist)[((size_t)n * 3 + j) * pieces + p] = val;
+    uint4 val[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int t = s1 - 3 + j;
+        val[j] = make_uint4(0, 0, 0, 0);
+        if (t >= s0)
+            val[j] = reinterpret_cast<const uint4 *>(x)[(size_t)t * pieces + p];
+        else if (hist_in)
+            val[j] = reinterpret_cast<const uint4 *>(hist_in)[((size_t)n * 3 + 3 + (t - s0)) * pieces + p];
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) reinterpret_cast<uint4 *>(hist_out)[((size_t)n * 3 + j) * pieces + p] = val[j];
 }
 
 // grid (pieces per row / 256, B): slot_idx[b]'s history <- rows 1, 2, x[b]
@@ -104,11 +116,11 @@ hipError_t launch_gates(const float *a, const float *b, const float *A_log, cons
 }
 
 hipError_t launch_conv_hist(const void *x, const int32_t *cu_seqlens, int N, int T, int C_raw,
-                            void *hist, hipStream_t stream) {
+                            const void *hist_in, void *hist_out, hipStream_t stream) {
     const int pieces = C_raw / 8;
-    hipLaunchKernelGGL(conv_hist_kernel, dim3((pieces + 255) / 256, 3, N), dim3(256), 0, stream,
+    hipLaunchKernelGGL(conv_hist_kernel, dim3((pieces + 255) / 256, N), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(x), cu_seqlens, T, pieces,
-                       static_cast<uint16_t *>(hist));
+                       static_cast<const uint16_t *>(hist_in), static_cast<uint16_t *>(hist_out));
     return hipGetLastError();
 }
 

@@ -93,13 +93,40 @@ def _check(rc, name):
         raise RuntimeError(f"oracle {name} failed with code {rc}")
 
 
-def prelude(x, w, cu_seqlens=None, *, H_qk, H_v, dk, dv, eps=1e-6):
-    """Causal conv (width 4) -> SiLU -> L2 norm of q, k.  Returns fp64 (q, k, v)."""
+def _with_history(x, cu_seqlens, conv_state_in):
+    """Each sequence's three history rows placed before its first row: the
+    extended rows, their sequence offsets, and the indices of the original rows
+    in the extended layout."""
+    T, C = x.shape
+    cu, N = _cu(cu_seqlens, T)
+    hist = f64(conv_state_in)
+    if hist.shape != (N, 3, C):
+        raise ValueError("conv_state_in must be [N, 3, C_raw]")
+    bounds = [(0, T)] if cu is None else [(int(cu[n]), int(cu[n + 1])) for n in range(N)]
+    rows, keep, cu_ext = [], [], [0]
+    for n, (s0, s1) in enumerate(bounds):
+        keep.append(np.arange(cu_ext[-1] + 3, cu_ext[-1] + 3 + s1 - s0))
+        rows += [hist[n], x[s0:s1]]
+        cu_ext.append(cu_ext[-1] + 3 + s1 - s0)
+    return np.concatenate(rows), np.asarray(cu_ext, dtype=np.int32), np.concatenate(keep)
+
+
+def prelude(x, w, cu_seqlens=None, *, H_qk, H_v, dk, dv, eps=1e-6, conv_state_in=None):
+    """Causal conv (width 4) -> SiLU -> L2 norm of q, k.  Returns fp64 (q, k, v).
+
+    The conv window of a sequence's first rows reaches back three rows before
+    its start: zeros, or the rows conv_state_in [N, 3, C_raw] (oldest first)
+    holds for it, as the raw rows a previous part of the same sequence ended
+    with.  Those rows are placed before the sequence and their outputs dropped."""
     x = f64(x)
     w = f64(w)
     T, Craw = x.shape
     if Craw != 2 * H_qk * dk + H_v * dv or w.shape != (Craw, 4):
         raise ValueError("prelude shape mismatch")
+    if conv_state_in is not None:
+        xe, cue, keep = _with_history(x, cu_seqlens, conv_state_in)
+        q, k, v = prelude(xe, w, cue, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, eps=eps)
+        return q[keep], k[keep], v[keep]
     cu, N = _cu(cu_seqlens, T)
     q = np.zeros((T, H_qk, dk))
     k = np.zeros((T, H_qk, dk))
@@ -257,10 +284,11 @@ def gates(a, b, A_log, dt_bias):
     return g, beta
 
 
-def conv_state(x, cu_seqlens=None):
+def conv_state(x, cu_seqlens=None, conv_state_in=None):
     """The conv history a sequence leaves for its next token: its last three raw
-    rows, oldest first ([N, 3, C_raw], same dtype as x), zero where the sequence
-    has fewer than three rows."""
+    rows, oldest first ([N, 3, C_raw], same dtype as x).  Where the sequence has
+    fewer than three rows the rest comes from the rows before its start: zeros,
+    or the end of its conv_state_in history [N, 3, C_raw]."""
     x = np.asarray(x)
     T = x.shape[0]
     cu, N = _cu(cu_seqlens, T)
@@ -271,6 +299,8 @@ def conv_state(x, cu_seqlens=None):
             t = s1 - 3 + j
             if t >= s0:
                 out[n, j] = x[t]
+            elif conv_state_in is not None:
+                out[n, j] = np.asarray(conv_state_in)[n, 3 + t - s0]
     return out
 
 

@@ -23,7 +23,7 @@ def test_exports_match_header():
     assert decl == sorted(gdn.EXPORTS)
     for name in decl:
         assert hasattr(L, name), name
-    assert gdn.gdn_abi_version() == 4
+    assert gdn.gdn_abi_version() == 5
 
 
 def _prefill(L, **kw):
@@ -160,14 +160,14 @@ def test_gates_rejects_bad_arguments():
 def _layer_prefill(L, **kw):
     big = 1 << 40
     a = dict(x=big, w=2 * big, a=3 * big, b=4 * big, A=5 * big, dt=6 * big, eps=1e-6, S0=None,
-             Sf=None, cs=None, cu=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0,
-             o=7 * big, ws=8 * big, ws_bytes=gdn.gdn_layer_prefill_workspace_size(1, 64, 16, 48),
-             stream=None)
+             Sf=None, ci=None, cs=None, cu=None, N=1, T=64, H_qk=16, H_v=48, d_k=128, d_v=128,
+             scale=1.0, o=7 * big, ws=8 * big,
+             ws_bytes=gdn.gdn_layer_prefill_workspace_size(1, 64, 16, 48), stream=None)
     a.update(kw)
     return L.gdn_layer_prefill(a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"], a["S0"],
-                               a["Sf"], a["cs"], a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"],
-                               a["d_k"], a["d_v"], a["scale"], a["o"], a["ws"], a["ws_bytes"],
-                               a["stream"])
+                               a["Sf"], a["ci"], a["cs"], a["cu"], a["N"], a["T"], a["H_qk"],
+                               a["H_v"], a["d_k"], a["d_v"], a["scale"], a["o"], a["ws"],
+                               a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -178,6 +178,9 @@ def _layer_prefill(L, **kw):
     (dict(o=3 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),    # o overlaps a
     (dict(eps=float("nan")), gdn.GDN_ERR_INVALID_ARG),
     (dict(d_v=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ci=7 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),   # conv history in overlaps o
+    (dict(ci=8 * (1 << 40)), gdn.GDN_ERR_INVALID_ARG),   # ... or the workspace
+    (dict(cs=12 << 40, ci=(12 << 40) + 64), gdn.GDN_ERR_INVALID_ARG),   # a shifted view of the history out
 ])
 def test_layer_prefill_rejects_bad_arguments(kw, code):
     L = gdn.lib()
@@ -196,14 +199,15 @@ def test_layer_prefill_workspace_size():
 def _layer_prefill_gated(L, **kw):
     big = 1 << 40
     a = dict(x=big, w=2 * big, a=3 * big, b=4 * big, A=5 * big, dt=6 * big, eps=1e-6, z=9 * big,
-             nw=10 * big, neps=1e-6, S0=None, Sf=None, cs=None, cu=None, N=1, T=64, H_qk=16,
-             H_v=48, d_k=128, d_v=128, scale=1.0, o=7 * big, y=11 * big, ws=8 * big,
+             nw=10 * big, neps=1e-6, S0=None, Sf=None, ci=None, cs=None, cu=None, N=1, T=64,
+             H_qk=16, H_v=48, d_k=128, d_v=128, scale=1.0, o=7 * big, y=11 * big, ws=8 * big,
              ws_bytes=gdn.gdn_layer_prefill_gated_workspace_size(1, 64, 16, 48), stream=None)
     a.update(kw)
     return L.gdn_layer_prefill_gated(a["x"], a["w"], a["a"], a["b"], a["A"], a["dt"], a["eps"],
-                                     a["z"], a["nw"], a["neps"], a["S0"], a["Sf"], a["cs"], a["cu"],
-                                     a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"], a["d_v"],
-                                     a["scale"], a["o"], a["y"], a["ws"], a["ws_bytes"], a["stream"])
+                                     a["z"], a["nw"], a["neps"], a["S0"], a["Sf"], a["ci"], a["cs"],
+                                     a["cu"], a["N"], a["T"], a["H_qk"], a["H_v"], a["d_k"],
+                                     a["d_v"], a["scale"], a["o"], a["y"], a["ws"], a["ws_bytes"],
+                                     a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -301,6 +301,51 @@ def test_prelude_conv_resets_at_sequence_start(orc):
     np.testing.assert_array_equal(q[6:], q2)
 
 
+def test_prelude_history_equals_conv1d_over_the_joined_sequence(orc):
+    """A prelude resumed with conv_state_in: each sequence's outputs are the
+    last rows of torch's conv1d prelude over its history rows followed by its
+    own rows (the history is the raw rows before its start)."""
+    rng = np.random.default_rng(15)
+    H_qk, H_v, dk, dv = 1, 3, 8, 4
+    lens = [7, 1, 0, 2, 12]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    C = 2 * H_qk * dk + H_v * dv
+    x = rng.standard_normal((T, C))
+    w = rng.normal(0, 0.5, (C, 4))
+    hist = rng.standard_normal((len(lens), 3, C))
+    q, k, v = orc.prelude(x, w, cu, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv, eps=0.0,
+                          conv_state_in=hist)
+    for n, (s0, s1) in enumerate(zip(cu[:-1], cu[1:])):
+        joined = np.concatenate([hist[n], x[s0:s1]])
+        qr, kr, vr = _prelude_reference_torch(joined, w, np.array([0, len(joined)], np.int32),
+                                              H_qk, H_v, dk, dv)
+        np.testing.assert_allclose(q[s0:s1], qr[3:], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(k[s0:s1], kr[3:], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(v[s0:s1], vr[3:], rtol=1e-12, atol=1e-12)
+    # zero history is no history
+    z = orc.prelude(x, w, cu, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv,
+                    conv_state_in=np.zeros_like(hist))
+    for a, b in zip(z, orc.prelude(x, w, cu, H_qk=H_qk, H_v=H_v, dk=dk, dv=dv)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_prelude_split_at_any_row_with_carried_history(orc):
+    """Cutting a sequence anywhere and passing the first part's conv_state as
+    the second part's conv_state_in reproduces the whole sequence's prelude."""
+    rng = np.random.default_rng(16)
+    dk, dv = 4, 4
+    C = 2 * dk + dv
+    x = rng.standard_normal((11, C))
+    w = rng.standard_normal((C, 4))
+    whole = orc.prelude(x, w, None, H_qk=1, H_v=1, dk=dk, dv=dv)
+    for cut in (0, 1, 2, 3, 4, 10, 11):
+        hist = orc.conv_state(x[:cut])
+        part = orc.prelude(x[cut:], w, None, H_qk=1, H_v=1, dk=dk, dv=dv, conv_state_in=hist)
+        for a, b in zip(part, whole):
+            np.testing.assert_allclose(a, b[cut:], rtol=1e-14, atol=1e-15)
+
+
 # ------------------------------------------------------------------ decode
 def test_decode_step_matches_one_token_prefill_and_spares_other_slots(orc):
     d = synth.decode_inputs(21, B=5, P=9, H_qk=2, H_v=6, dk=16, dv=8)
@@ -360,6 +405,13 @@ def test_conv_state_is_last_three_rows(orc):
     np.testing.assert_array_equal(cs[1], np.vstack([np.zeros((1, 3)), x[5:7]]))
     np.testing.assert_array_equal(cs[2], np.zeros((3, 3)))       # empty sequence
     np.testing.assert_array_equal(cs[3], x[7:10])
+    # rows missing before a short sequence's start come from the end of its history
+    hist = -np.arange(4 * 9, dtype=np.float64).reshape(4, 3, 3) - 1
+    ch = orc.conv_state(x, np.array([0, 5, 7, 7, 10], dtype=np.int32), conv_state_in=hist)
+    np.testing.assert_array_equal(ch[0], x[2:5])
+    np.testing.assert_array_equal(ch[1], np.vstack([hist[1, 2:], x[5:7]]))
+    np.testing.assert_array_equal(ch[2], hist[2])
+    np.testing.assert_array_equal(ch[3], x[7:10])
 
 
 def test_raw_decode_chain_equals_prefill(orc):
