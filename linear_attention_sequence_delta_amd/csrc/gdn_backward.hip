@@ -427,7 +427,8 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_base, int N, int T, int H_qk,
     int H_v, float scale, const uint16_t *__restrict__ bws, const uint16_t *__restrict__ states,
     const uint16_t *__restrict__ dsw, const uint16_t *__restrict__ duw, uint16_t *__restrict__ dq,
-    uint16_t *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta) {
+    uint16_t *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta, int item_lo,
+    int item_hi) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * kKP];
     __shared__ __attribute__((aligned(16))) uint16_t sSt[kD * kKP];      // S, then dS' ([v][k])
@@ -444,394 +445,398 @@ __global__ __launch_bounds__(512) void bwd_grad_kernel(
     __shared__ float sColG[4][kChunk], sColB[4][kChunk];
     __shared__ float sE[8];
 
-    const int gc = blockIdx.x / H_qk, hq = blockIdx.x - gc * H_qk;
-    if (gc >= chunk_base[N]) return;                   // same for the whole workgroup
-    const int n = seq_of_chunk(chunk_base, N, gc);
-    const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
-    const int c0 = s0 + kChunk * (gc - chunk_base[n]);
-    const int L = min(kChunk, s1 - c0);
-    const int group = H_v / H_qk;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w = wave & 3;
-    const int lane = tid & 63, g4 = lane >> 4, c = lane & 15;
-    const int row = 16 * w + c;                        // this lane's row
-    const bool row_ok = row < L;
-    const int wb = w >> 1;                             // 32-row block of this wave's rows
+    // items (chunk, QK head) item_lo + blockIdx.x, then every gridDim.x-th after it
+    for (int item = item_lo + blockIdx.x; item < item_hi; item += gridDim.x) {
+        __syncthreads();                                   // the previous item's LDS reads are done
+        const int gc = item / H_qk, hq = item - gc * H_qk;
+        if (gc >= chunk_base[N]) break;                    // so are the later items (same for the whole workgroup)
+        const int n = seq_of_chunk(chunk_base, N, gc);
+        const int s0 = cu ? cu[n] : 0, s1 = cu ? cu[n + 1] : T;
+        const int c0 = s0 + kChunk * (gc - chunk_base[n]);
+        const int L = min(kChunk, s1 - c0);
+        const int group = H_v / H_qk;
+        const int tid = threadIdx.x;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int w = wave & 3;
+        const int lane = tid & 63, g4 = lane >> 4, c = lane & 15;
+        const int row = 16 * w + c;                        // this lane's row
+        const bool row_ok = row < L;
+        const int wb = w >> 1;                             // 32-row block of this wave's rows
 
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int e = tid + 512 * m, r = e >> 4, pc = e & 15;
-        const size_t off = ((size_t)(c0 + min(r, L - 1)) * H_qk + hq) * kD + 8 * pc;
-        uint4 kv = *reinterpret_cast<const uint4 *>(k + off), qv = *reinterpret_cast<const uint4 *>(q + off);
-        if (r >= L) kv = qv = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4 *>(sK + r * kKP + 8 * pc) = kv;
-        *reinterpret_cast<uint4 *>(sQ + r * kKP + 8 * pc) = qv;
-    }
-    __syncthreads();
-    int ol = lane;
-    // x_row . k_(16 t + 4 g4 + j) for the rows x of M (K or Q), tile t
-    auto dot_k = [&](const uint16_t *M, int t) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) a = mfma32(frag_rows(sK, kKP, 16 * t, 32 * s, ol), frag_rows(M, kKP, 16 * w, 32 * s, ol), a);
-        return a;
-    };
-    f32x4 dQa[4], dKa[4];                              // columns 16 (4 hf + i) + 4 g4 + j
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dQa[i] = dKa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // the V-head step, for a compile-time half (tile offsets fold into
-    // instruction immediates); both halves pass the same barriers in order
-    auto vhead = [&](int vv, auto half) {
-        constexpr int hf = decltype(half)::value;
-        const int h = hq * group + vv;
-        // the lane index, opaque to the optimiser: LDS addresses are formed
-        // inside each step instead of being kept in registers across steps
-        ol = lane;
-        asm volatile("" : "+v"(ol));
-        const int c = ol & 15, g4 = ol >> 4, tid = 64 * wave + ol;
-        const int row = 16 * w + c;
-        const uint16_t *brec = bws + ((size_t)gc * H_v + h) * kBwdRecElems;
-        const uint16_t *Sg = states + ((size_t)gc * H_v + h) * (kD * kD);
-        const uint16_t *dSg = dsw + ((size_t)gc * H_v + h) * (kD * kD);
-        // this V-head's inputs in flight together, all in whole rows: T, S,
-        // G, b, and the rows of dO, dR and V (rows past the chunk's end read
-        // as zero), written into LDS after the previous V-head's reads
-        float e1 = 0.f;                                // this thread's share of <dS', S>
-        {
-            const u32x4 tv = *reinterpret_cast<const u32x4 *>(brec + kBwdTOff + (tid >> 3) * kChunk + 8 * (tid & 7));
-            u32x4 sv[4], ov[2], rv[2], xv[2];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int e = tid + 512 * m;
-                sv[m] = *reinterpret_cast<const u32x4 *>(Sg + (e >> 4) * kD + 8 * (e & 15));
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int e = tid + 512 * m;
-                const size_t off = ((size_t)(c0 + min(e >> 4, L - 1)) * H_v + h) * kD + 8 * (e & 15);
-                ov[m] = *reinterpret_cast<const u32x4 *>(d_o + off);
-                rv[m] = *reinterpret_cast<const u32x4 *>(dv + off);
-                xv[m] = *reinterpret_cast<const u32x4 *>(v + off);
-            }
-            float gl = 0.f, bl = 0.f;
-            if (tid < kChunk) {
-                gl = reinterpret_cast<const float *>(brec + kBwdGOff)[tid];
-                bl = tid < L ? beta[(size_t)(c0 + tid) * H_v + h] : 0.f;
-            }
-            __syncthreads();                           // the previous V-head's LDS reads are done
-            *reinterpret_cast<u32x4 *>(sT + (tid >> 3) * kRP + 8 * (tid & 7)) = tv;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int e = tid + 512 * m;
-                *reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15)) = sv[m];
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int e = tid + 512 * m, r = e >> 4, o = r * kKP + 8 * (e & 15);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(sDO + o) = r < L ? ov[m] : z;
-                *reinterpret_cast<u32x4 *>(sU + o) = r < L ? rv[m] : z;
-                *reinterpret_cast<u32x4 *>(sR + o) = r < L ? xv[m] : z;
-            }
-            if (tid < kChunk) {
-                sG[tid] = gl;
-                sB[tid] = bl;
-            }
+        for (int m = 0; m < 2; ++m) {
+            const int e = tid + 512 * m, r = e >> 4, pc = e & 15;
+            const size_t off = ((size_t)(c0 + min(r, L - 1)) * H_qk + hq) * kD + 8 * pc;
+            uint4 kv = *reinterpret_cast<const uint4 *>(k + off), qv = *reinterpret_cast<const uint4 *>(q + off);
+            if (r >= L) kv = qv = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(sK + r * kKP + 8 * pc) = kv;
+            *reinterpret_cast<uint4 *>(sQ + r * kKP + 8 * pc) = qv;
         }
         __syncthreads();
+        int ol = lane;
+        // x_row . k_(16 t + 4 g4 + j) for the rows x of M (K or Q), tile t
+        auto dot_k = [&](const uint16_t *M, int t) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) a = mfma32(frag_rows(sK, kKP, 16 * t, 32 * s, ol), frag_rows(M, kKP, 16 * w, 32 * s, ol), a);
+            return a;
+        };
+        f32x4 dQa[4], dKa[4];                              // columns 16 (4 hf + i) + 4 g4 + j
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dQa[i] = dKa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        const float Gr = sG[row], GLast = sG[kChunk - 1];
-        const float gam = __expf(Gr), lam = __expf(GLast - Gr), br = sB[row];
-        float rowG = 0.f, rowB = 0.f, e2 = 0.f;
-        f32x4 colG[2], colB[2];                        // column-sum terms of the wave's two tiles
+        // the V-head step, for a compile-time half (tile offsets fold into
+        // instruction immediates); both halves pass the same barriers in order
+        auto vhead = [&](int vv, auto half) {
+            constexpr int hf = decltype(half)::value;
+            const int h = hq * group + vv;
+            // the lane index, opaque to the optimiser: LDS addresses are formed
+            // inside each step instead of being kept in registers across steps
+            ol = lane;
+            asm volatile("" : "+v"(ol));
+            const int c = ol & 15, g4 = ol >> 4, tid = 64 * wave + ol;
+            const int row = 16 * w + c;
+            const uint16_t *brec = bws + ((size_t)gc * H_v + h) * kBwdRecElems;
+            const uint16_t *Sg = states + ((size_t)gc * H_v + h) * (kD * kD);
+            const uint16_t *dSg = dsw + ((size_t)gc * H_v + h) * (kD * kD);
+            // this V-head's inputs in flight together, all in whole rows: T, S,
+            // G, b, and the rows of dO, dR and V (rows past the chunk's end read
+            // as zero), written into LDS after the previous V-head's reads
+            float e1 = 0.f;                                // this thread's share of <dS', S>
+            {
+                const u32x4 tv = *reinterpret_cast<const u32x4 *>(brec + kBwdTOff + (tid >> 3) * kChunk + 8 * (tid & 7));
+                u32x4 sv[4], ov[2], rv[2], xv[2];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = tid + 512 * m;
+                    sv[m] = *reinterpret_cast<const u32x4 *>(Sg + (e >> 4) * kD + 8 * (e & 15));
+                }
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int e = tid + 512 * m;
+                    const size_t off = ((size_t)(c0 + min(e >> 4, L - 1)) * H_v + h) * kD + 8 * (e & 15);
+                    ov[m] = *reinterpret_cast<const u32x4 *>(d_o + off);
+                    rv[m] = *reinterpret_cast<const u32x4 *>(dv + off);
+                    xv[m] = *reinterpret_cast<const u32x4 *>(v + off);
+                }
+                float gl = 0.f, bl = 0.f;
+                if (tid < kChunk) {
+                    gl = reinterpret_cast<const float *>(brec + kBwdGOff)[tid];
+                    bl = tid < L ? beta[(size_t)(c0 + tid) * H_v + h] : 0.f;
+                }
+                __syncthreads();                           // the previous V-head's LDS reads are done
+                *reinterpret_cast<u32x4 *>(sT + (tid >> 3) * kRP + 8 * (tid & 7)) = tv;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = tid + 512 * m;
+                    *reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15)) = sv[m];
+                }
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int e = tid + 512 * m, r = e >> 4, o = r * kKP + 8 * (e & 15);
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(sDO + o) = r < L ? ov[m] : z;
+                    *reinterpret_cast<u32x4 *>(sU + o) = r < L ? rv[m] : z;
+                    *reinterpret_cast<u32x4 *>(sR + o) = r < L ? xv[m] : z;
+                }
+                if (tid < kChunk) {
+                    sG[tid] = gl;
+                    sB[tid] = bl;
+                }
+            }
+            __syncthreads();
 
-        // X = K S^T -> R = V - diag(gamma) X
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int nt = 4 * hf + i;
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) x = mfma32(frag_rows(sSt, kKP, 16 * nt, 32 * s, ol), frag_rows(sK, kKP, 16 * w, 32 * s, ol), x);
-            float vf[4];
-            unpack4(*reinterpret_cast<const uint2 *>(sR + row * kKP + 16 * nt + 4 * g4), vf);
-            *reinterpret_cast<uint2 *>(sR + row * kKP + 16 * nt + 4 * g4) =
-                pk4(vf[0] - gam * x[0], vf[1] - gam * x[1], vf[2] - gam * x[2], vf[3] - gam * x[3]);
-        }
-        // dO S and dR S: dQ += scale gamma dO S (dG: q_r . that), dK -= gamma dR S
-        // (dG: -gamma_r dR_r . X_r = -gamma_r k_r . (dR S)_r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kt = 4 * hf + i;
-            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 sf = frag_cols(sSt, kKP, 32 * s, 16 * kt, ol);
-                a1 = mfma32(sf, frag_rows(sDO, kKP, 16 * w, 32 * s, ol), a1);
-                a2 = mfma32(sf, frag_rows(sU, kKP, 16 * w, 32 * s, ol), a2);
-            }
-            float qf[4], kf[4];
-            unpack4(*reinterpret_cast<const uint2 *>(sQ + row * kKP + 16 * kt + 4 * g4), qf);
-            unpack4(*reinterpret_cast<const uint2 *>(sK + row * kKP + 16 * kt + 4 * g4), kf);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float t = scale * gam * a1[j];
-                dQa[i][j] += t;
-                rowG += t * qf[j];
-                const float u = gam * a2[j];
-                dKa[i][j] -= u;
-                rowG -= u * kf[j];
-            }
-        }
-        // the row-dot terms are finished here: left to the compiler they sink
-        // to the end of the step and hold the products in registers until then
-        asm volatile("" : "+v"(rowG));
-        __syncthreads();                               // R complete; S no longer read
-        uint4 dUf[4];                                  // row `row` of dU, columns 32 s + 8 g4 .. +7
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            dUf[s] = *reinterpret_cast<const uint4 *>(duw + dU_block(gc, h, H_v, w, s) + 8 * ol);
-        {
-            u32x4 dsv[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int e = tid + 512 * m;
-                dsv[m] = *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int e = tid + 512 * m;
-                u32x4 *p = reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15));
-                e1 = dot8_acc(__builtin_bit_cast(uint4, *p), __builtin_bit_cast(uint4, dsv[m]), e1);
-                *p = dsv[m];
-            }
-        }
-        asm volatile("" : "+v"(e1));
-        // U = T' R (T'[row][i] = T[row][i] b_i)
-        {
-            uint4 tB[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                float tf[8];
-                unpack8(*reinterpret_cast<const uint4 *>(sT + row * kRP + 32 * s + 8 * g4), tf);
-                const float4 b0 = *reinterpret_cast<const float4 *>(sB + 32 * s + 8 * g4);
-                const float4 b1 = *reinterpret_cast<const float4 *>(sB + 32 * s + 8 * g4 + 4);
-                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tf[e] *= bb[e];
-                tB[s] = pack_bf8(tf);
-            }
+            const float Gr = sG[row], GLast = sG[kChunk - 1];
+            const float gam = __expf(Gr), lam = __expf(GLast - Gr), br = sB[row];
+            float rowG = 0.f, rowB = 0.f, e2 = 0.f;
+            f32x4 colG[2], colB[2];                        // column-sum terms of the wave's two tiles
+
+            // X = K S^T -> R = V - diag(gamma) X
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int nt = 4 * hf + i;
-                f32x4 ua = {0.f, 0.f, 0.f, 0.f};
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    if (s <= wb) ua = mfma32(frag_cols(sR, kKP, 32 * s, 16 * nt, ol), tB[s], ua);
-                *reinterpret_cast<uint2 *>(sU + row * kKP + 16 * nt + 4 * g4) = pk4(ua[0], ua[1], ua[2], ua[3]);
+                for (int s = 0; s < 4; ++s) x = mfma32(frag_rows(sSt, kKP, 16 * nt, 32 * s, ol), frag_rows(sK, kKP, 16 * w, 32 * s, ol), x);
+                float vf[4];
+                unpack4(*reinterpret_cast<const uint2 *>(sR + row * kKP + 16 * nt + 4 * g4), vf);
+                *reinterpret_cast<uint2 *>(sR + row * kKP + 16 * nt + 4 * g4) =
+                    pk4(vf[0] - gam * x[0], vf[1] - gam * x[1], vf[2] - gam * x[2], vf[3] - gam * x[3]);
             }
-        }
-        __syncthreads();                               // U and dS' complete
-
-        // U dS': dK += lambda U dS'; dG: -lambda_r k_r . (U dS')_r (the last row gets the sum)
-        {
-            uint4 uB[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) uB[s] = frag_rows(sU, kKP, 16 * w, 32 * s, ol);
+            // dO S and dR S: dQ += scale gamma dO S (dG: q_r . that), dK -= gamma dR S
+            // (dG: -gamma_r dR_r . X_r = -gamma_r k_r . (dR S)_r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int kt = 4 * hf + i;
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+                f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a = mfma32(frag_cols(sSt, kKP, 32 * s, 16 * kt, ol), uB[s], a);
-                float kf[4];
+                for (int s = 0; s < 4; ++s) {
+                    const uint4 sf = frag_cols(sSt, kKP, 32 * s, 16 * kt, ol);
+                    a1 = mfma32(sf, frag_rows(sDO, kKP, 16 * w, 32 * s, ol), a1);
+                    a2 = mfma32(sf, frag_rows(sU, kKP, 16 * w, 32 * s, ol), a2);
+                }
+                float qf[4], kf[4];
+                unpack4(*reinterpret_cast<const uint2 *>(sQ + row * kKP + 16 * kt + 4 * g4), qf);
                 unpack4(*reinterpret_cast<const uint2 *>(sK + row * kKP + 16 * kt + 4 * g4), kf);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    dKa[i][j] += lam * a[j];
-                    const float t = lam * a[j] * kf[j];
-                    rowG -= t;
-                    e2 += t;
+                    const float t = scale * gam * a1[j];
+                    dQa[i][j] += t;
+                    rowG += t * qf[j];
+                    const float u = gam * a2[j];
+                    dKa[i][j] -= u;
+                    rowG -= u * kf[j];
                 }
             }
-        }
-        asm volatile("" : "+v"(rowG), "+v"(e2));
-        // dP = dO U^T -> M_P; dT' = dU R^T -> dT; row and column sums
-        uint4 dOf[4];
+            // the row-dot terms are finished here: left to the compiler they sink
+            // to the end of the step and hold the products in registers until then
+            asm volatile("" : "+v"(rowG));
+            __syncthreads();                               // R complete; S no longer read
+            uint4 dUf[4];                                  // row `row` of dU, columns 32 s + 8 g4 .. +7
 #pragma unroll
-        for (int s = 0; s < 4; ++s) dOf[s] = frag_rows(sDO, kKP, 16 * w, 32 * s, ol);
+            for (int s = 0; s < 4; ++s)
+                dUf[s] = *reinterpret_cast<const uint4 *>(duw + dU_block(gc, h, H_v, w, s) + 8 * ol);
+            {
+                u32x4 dsv[4];
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            const int t = 2 * ti + hf;
-            f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dtp = dp, qk = dp;
-            if (t <= w) {
-                qk = dot_k(sQ, t);
+                for (int m = 0; m < 4; ++m) {
+                    const int e = tid + 512 * m;
+                    dsv[m] = *reinterpret_cast<const u32x4 *>(dSg + (e >> 4) * kD + 8 * (e & 15));
+                }
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    dp = mfma32(frag_rows(sU, kKP, 16 * t, 32 * s, ol), dOf[s], dp);
-                    dtp = mfma32(frag_rows(sR, kKP, 16 * t, 32 * s, ol), dUf[s], dtp);
+                for (int m = 0; m < 4; ++m) {
+                    const int e = tid + 512 * m;
+                    u32x4 *p = reinterpret_cast<u32x4 *>(sSt + (e >> 4) * kKP + 8 * (e & 15));
+                    e1 = dot8_acc(__builtin_bit_cast(uint4, *p), __builtin_bit_cast(uint4, dsv[m]), e1);
+                    *p = dsv[m];
                 }
             }
-            const float4 Gi = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
-            const float4 Bi = *reinterpret_cast<const float4 *>(sB + 16 * t + 4 * g4);
-            const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
-            float tf[4];
-            unpack4(*reinterpret_cast<const uint2 *>(sT + row * kRP + 16 * t + 4 * g4), tf);
-            float mp[4], dt[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool lo = 16 * t + 4 * g4 + j <= row;
-                mp[j] = lo ? dp[j] * scale * __expf(Gr - gi[j]) : 0.f;
-                const float wp = lo ? mp[j] * qk[j] : 0.f;
-                rowG += wp;
-                colG[ti][j] = -wp;
-                dt[j] = lo ? dtp[j] * bi[j] : 0.f;
-                colB[ti][j] = lo ? dtp[j] * tf[j] : 0.f;
-            }
-            *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(mp[0], mp[1], mp[2], mp[3]);
-            *reinterpret_cast<uint2 *>(sM2 + row * kRP + 16 * t + 4 * g4) = pk4(dt[0], dt[1], dt[2], dt[3]);
-        }
-        __syncthreads();                               // M_P, dT complete
-
-        // dQ += M_P K; dK += M_P^T Q; F = dT T^T
-        {
-            uint4 mB[2], mtB[2], dtB[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s, ol);
-                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w, ol);
-                dtB[s] = frag_rows(sM2, kRP, 16 * w, 32 * s, ol);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kt = 4 * hf + i;
-                f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+            asm volatile("" : "+v"(e1));
+            // U = T' R (T'[row][i] = T[row][i] b_i)
+            {
+                uint4 tB[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    if (s <= wb) a = mfma32(frag_cols(sK, kKP, 32 * s, 16 * kt, ol), mB[s], a);
-                    if (s >= wb) b = mfma32(frag_cols(sQ, kKP, 32 * s, 16 * kt, ol), mtB[s], b);
+                    float tf[8];
+                    unpack8(*reinterpret_cast<const uint4 *>(sT + row * kRP + 32 * s + 8 * g4), tf);
+                    const float4 b0 = *reinterpret_cast<const float4 *>(sB + 32 * s + 8 * g4);
+                    const float4 b1 = *reinterpret_cast<const float4 *>(sB + 32 * s + 8 * g4 + 4);
+                    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tf[e] *= bb[e];
+                    tB[s] = pack_bf8(tf);
                 }
-                dQa[i] += a;
-                dKa[i] += b;
-            }
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                const int t = 2 * ti + hf;
-                f32x4 f = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    if (s <= wb) f = mfma32(frag_rows(sT, kRP, 16 * t, 32 * s, ol), dtB[s], f);
-                *reinterpret_cast<uint2 *>(sF + row * kRP + 16 * t + 4 * g4) = pk4(f[0], f[1], f[2], f[3]);
-            }
-        }
-        __syncthreads();                               // F complete; M_P no longer read
-
-        // dA = -T^T F (strictly lower) -> M_A = dA * D; db: rows of M_A * KK^T;
-        // dG: rows and columns of dA * A; M_A' = diag(b) M_A -> sM
-        {
-            uint4 ttB[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) ttB[s] = frag_cols(sT, kRP, 32 * s, 16 * w, ol);
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti) {
-                const int t = 2 * ti + hf;
-                f32x4 da = {0.f, 0.f, 0.f, 0.f}, kk = da;
-                if (t <= w) {
-                    kk = dot_k(sK, t);
+                for (int i = 0; i < 4; ++i) {
+                    const int nt = 4 * hf + i;
+                    f32x4 ua = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
-                        if (s >= wb) da = mfma32(frag_cols(sF, kRP, 32 * s, 16 * t, ol), ttB[s], da);
+                        if (s <= wb) ua = mfma32(frag_cols(sR, kKP, 32 * s, 16 * nt, ol), tB[s], ua);
+                    *reinterpret_cast<uint2 *>(sU + row * kKP + 16 * nt + 4 * g4) = pk4(ua[0], ua[1], ua[2], ua[3]);
                 }
-                const float4 Gj = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
-                const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
-                float ma[4];
+            }
+            __syncthreads();                               // U and dS' complete
+
+            // U dS': dK += lambda U dS'; dG: -lambda_r k_r . (U dS')_r (the last row gets the sum)
+            {
+                uint4 uB[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) uB[s] = frag_rows(sU, kKP, 16 * w, 32 * s, ol);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kt = 4 * hf + i;
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) a = mfma32(frag_cols(sSt, kKP, 32 * s, 16 * kt, ol), uB[s], a);
+                    float kf[4];
+                    unpack4(*reinterpret_cast<const uint2 *>(sK + row * kKP + 16 * kt + 4 * g4), kf);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        dKa[i][j] += lam * a[j];
+                        const float t = lam * a[j] * kf[j];
+                        rowG -= t;
+                        e2 += t;
+                    }
+                }
+            }
+            asm volatile("" : "+v"(rowG), "+v"(e2));
+            // dP = dO U^T -> M_P; dT' = dU R^T -> dT; row and column sums
+            uint4 dOf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dOf[s] = frag_rows(sDO, kKP, 16 * w, 32 * s, ol);
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                const int t = 2 * ti + hf;
+                f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dtp = dp, qk = dp;
+                if (t <= w) {
+                    qk = dot_k(sQ, t);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        dp = mfma32(frag_rows(sU, kKP, 16 * t, 32 * s, ol), dOf[s], dp);
+                        dtp = mfma32(frag_rows(sR, kKP, 16 * t, 32 * s, ol), dUf[s], dtp);
+                    }
+                }
+                const float4 Gi = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
+                const float4 Bi = *reinterpret_cast<const float4 *>(sB + 16 * t + 4 * g4);
+                const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w}, bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+                float tf[4];
+                unpack4(*reinterpret_cast<const uint2 *>(sT + row * kRP + 16 * t + 4 * g4), tf);
+                float mp[4], dt[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const bool lo = 16 * t + 4 * g4 + j < row;
-                    const float m = lo ? -da[j] * __expf(Gr - gj[j]) : 0.f;
-                    const float kkv = lo ? kk[j] : 0.f;
-                    rowB += m * kkv;
-                    const float wa = m * br * kkv;
-                    rowG += wa;
-                    colG[ti][j] -= wa;
-                    ma[j] = m * br;
+                    const bool lo = 16 * t + 4 * g4 + j <= row;
+                    mp[j] = lo ? dp[j] * scale * __expf(Gr - gi[j]) : 0.f;
+                    const float wp = lo ? mp[j] * qk[j] : 0.f;
+                    rowG += wp;
+                    colG[ti][j] = -wp;
+                    dt[j] = lo ? dtp[j] * bi[j] : 0.f;
+                    colB[ti][j] = lo ? dtp[j] * tf[j] : 0.f;
                 }
-                *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(ma[0], ma[1], ma[2], ma[3]);
+                *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(mp[0], mp[1], mp[2], mp[3]);
+                *reinterpret_cast<uint2 *>(sM2 + row * kRP + 16 * t + 4 * g4) = pk4(dt[0], dt[1], dt[2], dt[3]);
             }
-        }
-        rowG += __shfl_xor(rowG, 16, 64);
-        rowG += __shfl_xor(rowG, 32, 64);
-        rowB += __shfl_xor(rowB, 16, 64);
-        rowB += __shfl_xor(rowB, 32, 64);
-        if (g4 == 0) {
-            sRowG[hf][row] = rowG;
-            sRowB[hf][row] = rowB;
-        }
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            const float zg = col16_sums(colG[ti], c), zb = col16_sums(colB[ti], c);
-            if ((c & 3) == 0) {
-                sColG[w][16 * (2 * ti + hf) + 4 * g4 + (c >> 2)] = zg;
-                sColB[w][16 * (2 * ti + hf) + 4 * g4 + (c >> 2)] = zb;
-            }
-        }
-        {
-            const float ew = wave_sum(__expf(GLast) * e1 + e2);
-            if (lane == 0) sE[wave] = ew;
-        }
-        __syncthreads();                               // M_A' and the sums complete
+            __syncthreads();                               // M_P, dT complete
 
-        // dK += M_A' K + M_A'^T K
-        {
-            uint4 mB[2], mtB[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s, ol);
-                mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w, ol);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kt = 4 * hf + i;
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            // dQ += M_P K; dK += M_P^T Q; F = dT T^T
+            {
+                uint4 mB[2], mtB[2], dtB[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const uint4 kf = frag_cols(sK, kKP, 32 * s, 16 * kt, ol);
-                    if (s <= wb) a = mfma32(kf, mB[s], a);
-                    if (s >= wb) a = mfma32(kf, mtB[s], a);
+                    mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s, ol);
+                    mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w, ol);
+                    dtB[s] = frag_rows(sM2, kRP, 16 * w, 32 * s, ol);
                 }
-                dKa[i] += a;
-            }
-        }
-        // dg = suffix sums of dG inside the chunk; db
-        if (wave == 0) {
-            float dG = sRowG[0][lane] + sRowG[1][lane] + sColG[0][lane] + sColG[1][lane] +
-                       sColG[2][lane] + sColG[3][lane];
-            if (lane == kChunk - 1) {
 #pragma unroll
-                for (int x = 0; x < 8; ++x) dG += sE[x];
-            }
-            const float db = sRowB[0][lane] + sRowB[1][lane] + sColB[0][lane] + sColB[1][lane] +
-                             sColB[2][lane] + sColB[3][lane];
-            const float suf = wave_scan(__shfl(dG, 63 - lane, 64));
-            const float dgr = __shfl(suf, 63 - lane, 64);
-            if (lane < L) {
-                dg[(size_t)(c0 + lane) * H_v + h] = dgr;
-                dbeta[(size_t)(c0 + lane) * H_v + h] = db;
-            }
-        }
-    };
-    for (int vv = 0; vv < group; ++vv) {
-        if (wave < 4) vhead(vv, std::integral_constant<int, 0>{});
-        else vhead(vv, std::integral_constant<int, 1>{});
-    }
-    const int hf = wave >> 2;
-    if (row_ok) {
+                for (int i = 0; i < 4; ++i) {
+                    const int kt = 4 * hf + i;
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const size_t off = ((size_t)(c0 + row) * H_qk + hq) * kD + 16 * (4 * hf + i) + 4 * g4;
-            *reinterpret_cast<uint2 *>(dq + off) = pk4(dQa[i][0], dQa[i][1], dQa[i][2], dQa[i][3]);
-            *reinterpret_cast<uint2 *>(dk + off) = pk4(dKa[i][0], dKa[i][1], dKa[i][2], dKa[i][3]);
+                    for (int s = 0; s < 2; ++s) {
+                        if (s <= wb) a = mfma32(frag_cols(sK, kKP, 32 * s, 16 * kt, ol), mB[s], a);
+                        if (s >= wb) b = mfma32(frag_cols(sQ, kKP, 32 * s, 16 * kt, ol), mtB[s], b);
+                    }
+                    dQa[i] += a;
+                    dKa[i] += b;
+                }
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) {
+                    const int t = 2 * ti + hf;
+                    f32x4 f = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        if (s <= wb) f = mfma32(frag_rows(sT, kRP, 16 * t, 32 * s, ol), dtB[s], f);
+                    *reinterpret_cast<uint2 *>(sF + row * kRP + 16 * t + 4 * g4) = pk4(f[0], f[1], f[2], f[3]);
+                }
+            }
+            __syncthreads();                               // F complete; M_P no longer read
+
+            // dA = -T^T F (strictly lower) -> M_A = dA * D; db: rows of M_A * KK^T;
+            // dG: rows and columns of dA * A; M_A' = diag(b) M_A -> sM
+            {
+                uint4 ttB[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) ttB[s] = frag_cols(sT, kRP, 32 * s, 16 * w, ol);
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) {
+                    const int t = 2 * ti + hf;
+                    f32x4 da = {0.f, 0.f, 0.f, 0.f}, kk = da;
+                    if (t <= w) {
+                        kk = dot_k(sK, t);
+#pragma unroll
+                        for (int s = 0; s < 2; ++s)
+                            if (s >= wb) da = mfma32(frag_cols(sF, kRP, 32 * s, 16 * t, ol), ttB[s], da);
+                    }
+                    const float4 Gj = *reinterpret_cast<const float4 *>(sG + 16 * t + 4 * g4);
+                    const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
+                    float ma[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool lo = 16 * t + 4 * g4 + j < row;
+                        const float m = lo ? -da[j] * __expf(Gr - gj[j]) : 0.f;
+                        const float kkv = lo ? kk[j] : 0.f;
+                        rowB += m * kkv;
+                        const float wa = m * br * kkv;
+                        rowG += wa;
+                        colG[ti][j] -= wa;
+                        ma[j] = m * br;
+                    }
+                    *reinterpret_cast<uint2 *>(sM + row * kRP + 16 * t + 4 * g4) = pk4(ma[0], ma[1], ma[2], ma[3]);
+                }
+            }
+            rowG += __shfl_xor(rowG, 16, 64);
+            rowG += __shfl_xor(rowG, 32, 64);
+            rowB += __shfl_xor(rowB, 16, 64);
+            rowB += __shfl_xor(rowB, 32, 64);
+            if (g4 == 0) {
+                sRowG[hf][row] = rowG;
+                sRowB[hf][row] = rowB;
+            }
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti) {
+                const float zg = col16_sums(colG[ti], c), zb = col16_sums(colB[ti], c);
+                if ((c & 3) == 0) {
+                    sColG[w][16 * (2 * ti + hf) + 4 * g4 + (c >> 2)] = zg;
+                    sColB[w][16 * (2 * ti + hf) + 4 * g4 + (c >> 2)] = zb;
+                }
+            }
+            {
+                const float ew = wave_sum(__expf(GLast) * e1 + e2);
+                if (lane == 0) sE[wave] = ew;
+            }
+            __syncthreads();                               // M_A' and the sums complete
+
+            // dK += M_A' K + M_A'^T K
+            {
+                uint4 mB[2], mtB[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    mB[s] = frag_rows(sM, kRP, 16 * w, 32 * s, ol);
+                    mtB[s] = frag_cols(sM, kRP, 32 * s, 16 * w, ol);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kt = 4 * hf + i;
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const uint4 kf = frag_cols(sK, kKP, 32 * s, 16 * kt, ol);
+                        if (s <= wb) a = mfma32(kf, mB[s], a);
+                        if (s >= wb) a = mfma32(kf, mtB[s], a);
+                    }
+                    dKa[i] += a;
+                }
+            }
+            // dg = suffix sums of dG inside the chunk; db
+            if (wave == 0) {
+                float dG = sRowG[0][lane] + sRowG[1][lane] + sColG[0][lane] + sColG[1][lane] +
+                           sColG[2][lane] + sColG[3][lane];
+                if (lane == kChunk - 1) {
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) dG += sE[x];
+                }
+                const float db = sRowB[0][lane] + sRowB[1][lane] + sColB[0][lane] + sColB[1][lane] +
+                                 sColB[2][lane] + sColB[3][lane];
+                const float suf = wave_scan(__shfl(dG, 63 - lane, 64));
+                const float dgr = __shfl(suf, 63 - lane, 64);
+                if (lane < L) {
+                    dg[(size_t)(c0 + lane) * H_v + h] = dgr;
+                    dbeta[(size_t)(c0 + lane) * H_v + h] = db;
+                }
+            }
+        };
+        for (int vv = 0; vv < group; ++vv) {
+            if (wave < 4) vhead(vv, std::integral_constant<int, 0>{});
+            else vhead(vv, std::integral_constant<int, 1>{});
+        }
+        const int hf = wave >> 2;
+        if (row_ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t off = ((size_t)(c0 + row) * H_qk + hq) * kD + 16 * (4 * hf + i) + 4 * g4;
+                *reinterpret_cast<uint2 *>(dq + off) = pk4(dQa[i][0], dQa[i][1], dQa[i][2], dQa[i][3]);
+                *reinterpret_cast<uint2 *>(dk + off) = pk4(dKa[i][0], dKa[i][1], dKa[i][2], dKa[i][3]);
+            }
         }
     }
 }
@@ -854,17 +859,17 @@ hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const 
 hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const void *d_o,
                            const void *dv, const float *beta, const int32_t *cu_seqlens,
                            const int32_t *chunk_base, int N, int T, int H_qk, int H_v,
-                           int max_chunks, float scale, const void *bws, const void *states,
-                           const void *dsw, const void *duw, void *dq, void *dk, float *dg,
-                           float *dbeta, hipStream_t stream) {
-    hipLaunchKernelGGL(bwd_grad_kernel, dim3(max_chunks * H_qk), dim3(512), 0, stream,
+                           float scale, const void *bws, const void *states, const void *dsw,
+                           const void *duw, void *dq, void *dk, float *dg, float *dbeta,
+                           int item_lo, int item_hi, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3(grid), dim3(512), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                        static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(d_o),
                        static_cast<const uint16_t *>(dv), beta, cu_seqlens, chunk_base, N, T, H_qk,
                        H_v, scale, static_cast<const uint16_t *>(bws),
                        static_cast<const uint16_t *>(states), static_cast<const uint16_t *>(dsw),
                        static_cast<const uint16_t *>(duw), static_cast<uint16_t *>(dq),
-                       static_cast<uint16_t *>(dk), dg, dbeta);
+                       static_cast<uint16_t *>(dk), dg, dbeta, item_lo, item_hi);
     return hipGetLastError();
 }
 

@@ -1078,15 +1078,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // event hand-over.  With the prelude fused the prep also forms K and Q and
 // the ratio differs.
 constexpr int kMaxSegments = 12;
-#ifndef GDN_SEG_GROWTH_RAW
-#define GDN_SEG_GROWTH_RAW 1.0
-#endif
 constexpr double kSegGrowth = 1.1;
-constexpr double kSegGrowthRaw = GDN_SEG_GROWTH_RAW;
-#ifndef GDN_SEG_GROWTH_REV
-#define GDN_SEG_GROWTH_REV 1.0
-#endif
-constexpr double kSegGrowthRev = GDN_SEG_GROWTH_REV;   // the backward's reverse scan (walked last to first)
+constexpr double kSegGrowthRaw = 1.0;
+constexpr double kSegGrowthRev = 1.0;   // the backward's reverse scan (walked last to first)
 constexpr int kFirstSegChunks = 128;
 constexpr int kSegMinChunks = 64;     // shorter sequences are not split
 constexpr int kMinIdleCUs = 32;       // fewer idle CUs: not split
@@ -1110,11 +1104,14 @@ int segment_bounds(int nch, double growth, int *b) {
     return count;
 }
 
+// Events: one per segment, and two more for the backward's chunk gradients
+// beside its reverse scan.
+constexpr int kEvRscan = kMaxSegments, kEvGrad = kMaxSegments + 1, kAuxEvents = kMaxSegments + 2;
 struct DeviceAux {           // per device, created on first use, never destroyed
     bool tried = false, ok = false;
     int cus = 0;
     hipStream_t stream = nullptr;
-    hipEvent_t ev[kMaxSegments] = {};
+    hipEvent_t ev[kAuxEvents] = {};
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_aux_mu;         // guards g_aux and every enqueue on an auxiliary stream
@@ -1135,7 +1132,7 @@ DeviceAux *device_aux(hipStream_t s) {
         a.tried = true;
         bool ok = hipDeviceGetAttribute(&a.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
                   hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess;
-        for (int i = 0; ok && i < kMaxSegments; ++i)
+        for (int i = 0; ok && i < kAuxEvents; ++i)
             ok = hipEventCreateWithFlags(&a.ev[i], hipEventDisableTiming | hipEventReleaseToDevice) ==
                  hipSuccess;
         a.ok = ok;
@@ -1310,7 +1307,7 @@ size_t bwd_workspace_layout(int N, int T, int H_v, bool saved, void *base, BwdWo
     const size_t st = max_chunks * (size_t)H_v * kD * kD * sizeof(uint16_t);
     const size_t own = saved ? 0 : st;
     const size_t du = max_chunks * kChunk * (size_t)H_v * kD * sizeof(uint16_t);
-    const size_t carry = saved && N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0;
+    const size_t carry = N == 1 ? (size_t)H_v * kD * kD * sizeof(float) : 0;
     if (wsp) {
         char *p = static_cast<char *>(base);
         wsp->chunk_base = reinterpret_cast<int32_t *>(p);
@@ -1338,11 +1335,26 @@ size_t chunk_states_bytes(int N, int T, int H_v) {
 // plan -> prep (forward and backward records) -> forward scan storing each
 // chunk's start state -> reverse scan (dv, the initial-state gradient, dS' and
 // dU per chunk) -> per-chunk gradients (dq, dk, dg, dbeta), all on `stream`.
-// (The two scans need only prep's records, but 512-thread workgroups of both
-// do not fit one CU together, so running them side by side gains nothing.)
 // With chunk_states from an earlier forward pass (gdn_prefill with states
 // kept), prep writes only the backward records and the forward scan is
 // skipped.
+//
+// A single long sequence leaves CUs idle during both scans (one workgroup per
+// (V-head, slab)); the work that needs neither scan's next result runs there,
+// on the auxiliary stream, with grids no larger than the idle CUs (workgroups
+// that loop over their items):
+//   recomputing: forward records alone; then the forward scan, with the
+//     backward records beside it (the reverse scan needs only those), those
+//     of the first segment last: they are formed beside the reverse scan;
+//   from kept states: the backward records of the last segment alone; the
+//     reverse scan in segments walked last to first, with the records of the
+//     earlier segments formed beside it;
+//   both: the reverse scan in segments; once its last segment is done, that
+//     segment's chunk gradients beside the rest of it.  The other segments'
+//     gradients follow on the caller's stream, which then waits for the
+//     auxiliary stream.
+// (The two scans are independent, but 512-thread workgroups of both do not fit
+// one CU together, so running them side by side gains nothing.)
 hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *S0, const int32_t *cu_seqlens,
                                    int N, int T, int H_qk, int H_v, float scale, const void *d_o,
@@ -1357,74 +1369,98 @@ hipError_t launch_chunked_backward(const void *q, const void *k, const void *v, 
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T, W.chunk_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int items = max_chunks * H_qk;
-    if (saved) {
-        // prep (backward records only) and the reverse scan, in segments walked
-        // last to first: the prep of the last segment alone, the prep of the
-        // earlier ones on the auxiliary stream, on the CUs the reverse scan
-        // leaves idle, while the caller's stream scans the later segments
-        auto prep = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
-            const int it = (c_hi - c_lo) * H_qk;
-            const int grid = min((it + kPrepWaves - 1) / kPrepWaves, max_grid);
-            hipLaunchKernelGGL((prep_kernel<false, kRecBwd>), dim3(grid), dim3(64 * kPrepWaves), 0, s,
-                               q16, k16, RawIn{}, g, beta, cu_seqlens, W.chunk_base, N, T, H_qk,
-                               H_v, scale, c_lo * H_qk, c_hi * H_qk, nullptr, W.brec);
-            return hipGetLastError();
-        };
-        auto rscan = [&](int c_lo, int c_hi, const float *in, float *out) {
-            return launch_bwd_scan(q, k, d_o, in, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
-                                   W.brec, W.dsw, W.duw, dv, out, c_lo, c_hi, stream);
-        };
-        const int nch = (T + kChunk - 1) / kChunk;
-        const int scan_grid = N * H_v * kSlabsW;      // the reverse scan's grid: 32-column slabs too
-        std::unique_lock<std::mutex> lock(g_aux_mu);
-        DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux(stream) : nullptr;
-        const int idle = aux ? aux->cus - scan_grid : 0;
-        if (idle < kMinIdleCUs) {
-            lock.unlock();
-            if ((e = prep(0, max_chunks, INT32_MAX, stream)) != hipSuccess) return e;
-            if ((e = rscan(0, max_chunks, dS_final, dS0)) != hipSuccess) return e;
-        } else {
-            int b[kMaxSegments + 1];
-            const int nseg = segment_bounds(nch, kSegGrowthRev, b);
-            const int last = nseg - 1;
-            if ((e = prep(b[last], b[last + 1], INT32_MAX, stream)) != hipSuccess) return e;
-            if ((e = hipEventRecord(aux->ev[last], stream)) != hipSuccess) return e;
-            if ((e = hipStreamWaitEvent(aux->stream, aux->ev[last], 0)) != hipSuccess) return e;
-            for (int i = last - 1; i >= 0; --i) {
-                if ((e = prep(b[i], b[i + 1], idle, aux->stream)) != hipSuccess) return e;
-                if ((e = hipEventRecord(aux->ev[i], aux->stream)) != hipSuccess) return e;
-            }
-            for (int i = last; i >= 0; --i) {
-                if (i < last && (e = hipStreamWaitEvent(stream, aux->ev[i], 0)) != hipSuccess) return e;
-                if ((e = rscan(b[i], b[i + 1], i == last ? dS_final : W.carry, i == 0 ? dS0 : W.carry)) !=
-                    hipSuccess)
-                    return e;
-            }
-        }
-        return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
-                               max_chunks, scale, W.brec, chunk_states, W.dsw, W.duw, dq, dk, dg,
-                               dbeta, stream);
-    }
-    hipLaunchKernelGGL((prep_kernel<false, kRecFwd | kRecBwd>), dim3((items + kPrepWaves - 1) / kPrepWaves),
-                       dim3(64 * kPrepWaves), 0, stream, q16, k16, RawIn{}, g, beta, cu_seqlens,
-                       W.chunk_base, N, T, H_qk, H_v, scale, 0, items, W.rec, W.brec);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const void *states = chunk_states;
-    if (!saved) {
+
+    // records of chunks [c_lo, c_hi): forward, backward or both
+    auto prep = [&](auto recs, int c_lo, int c_hi, int max_grid, hipStream_t s) {
+        constexpr int kRecs = decltype(recs)::value, kW = kPrepWavesOf<kRecs>;
+        const int it = (c_hi - c_lo) * H_qk;
+        const int grid = min((it + kW - 1) / kW, max_grid);
+        hipLaunchKernelGGL((prep_kernel<false, kRecs>), dim3(grid), dim3(64 * kW), 0, s, q16, k16,
+                           RawIn{}, g, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
+                           c_lo * H_qk, c_hi * H_qk, W.rec, W.brec);
+        return hipGetLastError();
+    };
+    constexpr std::integral_constant<int, kRecFwd> fwd{};
+    constexpr std::integral_constant<int, kRecBwd> bwd{};
+    constexpr std::integral_constant<int, kRecFwd | kRecBwd> both{};
+    auto fscan = [&]() {      // the forward scan, storing each chunk's start state
         hipLaunchKernelGGL((scan_kernel<false, kOutStates>), dim3(N * H_v * kSlabsW), dim3(512), 0,
                            stream, q16, k16, static_cast<const uint16_t *>(v), RawIn{}, S0, nullptr,
                            cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale, 0, max_chunks, W.rec,
                            nullptr, W.states);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        states = W.states;
+        return hipGetLastError();
+    };
+    auto rscan = [&](int c_lo, int c_hi, const float *in, float *out) {
+        return launch_bwd_scan(q, k, d_o, in, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
+                               W.brec, W.dsw, W.duw, dv, out, c_lo, c_hi, stream);
+    };
+    const void *states = saved ? chunk_states : W.states;
+    auto grad = [&](int c_lo, int c_hi, int max_grid, hipStream_t s) {
+        const int lo = c_lo * H_qk, hi = c_hi * H_qk;
+        return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
+                               scale, W.brec, states, W.dsw, W.duw, dq, dk, dg, dbeta, lo, hi,
+                               min(hi - lo, max_grid), s);
+    };
+
+    const int nch = (T + kChunk - 1) / kChunk;
+    const int scan_grid = N * H_v * kSlabsW;      // both scans: one workgroup per (V-head, slab)
+    std::unique_lock<std::mutex> lock(g_aux_mu);
+    DeviceAux *aux = (N == 1 && nch >= kSegMinChunks) ? device_aux(stream) : nullptr;
+    const int idle = aux ? aux->cus - scan_grid : 0;
+    if (idle < kMinIdleCUs) {
+        lock.unlock();
+        if (saved) {
+            if ((e = prep(bwd, 0, max_chunks, INT32_MAX, stream)) != hipSuccess) return e;
+        } else {
+            if ((e = prep(both, 0, max_chunks, INT32_MAX, stream)) != hipSuccess) return e;
+            if ((e = fscan()) != hipSuccess) return e;
+        }
+        if ((e = rscan(0, max_chunks, dS_final, dS0)) != hipSuccess) return e;
+        return grad(0, max_chunks, INT32_MAX, stream);
     }
-    if ((e = launch_bwd_scan(q, k, d_o, dS_final, cu_seqlens, W.chunk_base, N, T, H_qk, H_v, scale,
-                             W.brec, W.dsw, W.duw, dv, dS0, 0, max_chunks, stream)) != hipSuccess)
-        return e;
-    return launch_bwd_grad(q, k, v, d_o, dv, beta, cu_seqlens, W.chunk_base, N, T, H_qk, H_v,
-                           max_chunks, scale, W.brec, states, W.dsw, W.duw, dq, dk, dg, dbeta,
-                           stream);
+
+    int b[kMaxSegments + 1];
+    const int nseg = segment_bounds(nch, kSegGrowthRev, b);
+    const int last = nseg - 1;
+    hipStream_t as = aux->stream;
+    if (saved) {
+        if ((e = prep(bwd, b[last], b[last + 1], INT32_MAX, stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->ev[last], stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(as, aux->ev[last], 0)) != hipSuccess) return e;
+        for (int i = last - 1; i >= 0; --i) {
+            if ((e = prep(bwd, b[i], b[i + 1], idle, as)) != hipSuccess) return e;
+            if ((e = hipEventRecord(aux->ev[i], as)) != hipSuccess) return e;
+        }
+    } else {
+        // the backward records of the sequence's first segment, which the
+        // reverse scan reaches last, come after the others on the auxiliary
+        // stream and are formed while the reverse scan starts
+        if ((e = prep(fwd, 0, nch, INT32_MAX, stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->ev[0], stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(as, aux->ev[0], 0)) != hipSuccess) return e;
+        if ((e = prep(bwd, b[1], nch, idle, as)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->ev[1], as)) != hipSuccess) return e;
+        if ((e = prep(bwd, 0, b[1], idle, as)) != hipSuccess) return e;
+        if ((e = hipEventRecord(aux->ev[2], as)) != hipSuccess) return e;
+        if ((e = fscan()) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(stream, aux->ev[1], 0)) != hipSuccess) return e;
+    }
+    for (int i = last; i >= 0; --i) {
+        // the records of segment i: from the auxiliary stream, except for the
+        // last segment from kept states (formed on this stream)
+        const int rec_ev = saved ? (i < last ? i : -1) : (i == 0 ? 2 : -1);
+        if (rec_ev >= 0 && (e = hipStreamWaitEvent(stream, aux->ev[rec_ev], 0)) != hipSuccess) return e;
+        if ((e = rscan(b[i], b[i + 1], i == last ? dS_final : W.carry, i == 0 ? dS0 : W.carry)) != hipSuccess)
+            return e;
+        if (i == last) {
+            if ((e = hipEventRecord(aux->ev[kEvRscan], stream)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(as, aux->ev[kEvRscan], 0)) != hipSuccess) return e;
+            if ((e = grad(b[last], b[last + 1], idle, as)) != hipSuccess) return e;
+            if ((e = hipEventRecord(aux->ev[kEvGrad], as)) != hipSuccess) return e;
+        }
+    }
+    if ((e = grad(b[0], b[last], INT32_MAX, stream)) != hipSuccess) return e;
+    return hipStreamWaitEvent(stream, aux->ev[kEvGrad], 0);
 }
 
 size_t chunked_workspace_bytes(int N, int T, int H_qk, int H_v, bool raw) {

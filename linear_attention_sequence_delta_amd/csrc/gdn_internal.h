@@ -80,9 +80,9 @@ hipError_t launch_bwd_scan(const void *q, const void *k, const void *d_o, const 
 hipError_t launch_bwd_grad(const void *q, const void *k, const void *v, const void *d_o,
                            const void *dv, const float *beta, const int32_t *cu_seqlens,
                            const int32_t *chunk_base, int N, int T, int H_qk, int H_v,
-                           int max_chunks, float scale, const void *bws, const void *states,
-                           const void *dsw, const void *duw, void *dq, void *dk, float *dg,
-                           float *dbeta, hipStream_t stream);
+                           float scale, const void *bws, const void *states, const void *dsw,
+                           const void *duw, void *dq, void *dk, float *dg, float *dbeta,
+                           int item_lo, int item_hi, int grid, hipStream_t stream);
 
 // Gradients of the prelude (dx bf16, dw fp32 [C_raw][4]; `partial` holds
 // prelude_bwd_partial_bytes) and of the gates (da, db fp32 [T][H_v]; dA_log,

@@ -2,8 +2,8 @@
 ("Qwen3.8-27B：27B 如何打出千亿级效果，且塞进单张消费级显卡", sec. 5: whole-graph
 capture garbling the output, a slot finder looping forever), turned into checks:
 
-* a prefill of one long sequence (which, run eagerly, forks part of its work
-  onto an auxiliary stream) and a decode step, captured into a HIP graph and
+* a prefill and a backward of one long sequence (which, run eagerly, fork part
+  of their work onto an auxiliary stream) and a decode step, captured into a HIP graph and
   replayed several times with eager work and synchronisations in between, give
   the eager results bit for bit at every replay;
 * with GDN_DEBUG=1 (read at every call) duplicate and out-of-range slot ids and
@@ -66,6 +66,44 @@ def test_graph_capture_segmented_prefill_raw():
         (o_e.float() * 2).sum()
 
     _replays_match(graph, (o_g, S_g), (o_e, S_e), other)
+
+
+@pytest.mark.parametrize("kept", [False, True])
+def test_graph_capture_segmented_backward(kept):
+    """T = 8192 backward (recomputing the forward, or from kept chunk states):
+    eagerly the reverse scan runs in segments, with the backward records and the
+    last segment's chunk gradients on the auxiliary stream; captured, everything
+    runs unsegmented on the capturing stream.  Every replay gives the eager
+    gradients bit for bit."""
+    import torch
+    import linear_attention_sequence_delta_amd as gdn
+    p = synth.direct_prefill(5150 + kept, T=8192, init_state=True)
+    d_o, dSf = synth.output_grads(5150 + kept, p.T, p.N)
+    q, k, v, g, b, S0 = dev(p.q), dev(p.k), dev(p.v), dev(p.g), dev(p.beta), dev(p.S0)
+    do, dsf = dev(d_o), dev(dSf)
+    cs = gdn.gdn_prefill(q, k, v, g, b, S0, chunk_states=True)[2] if kept else None
+    size = gdn.gdn_prefill_backward_saved_workspace_size if kept else gdn.gdn_prefill_backward_workspace_size
+    ws = torch.empty(size(1, p.T, p.H_qk, p.H_v), dtype=torch.uint8, device="cuda")
+    print("backward capture, kept states", kept, flush=True)
+    eager = gdn.gdn_prefill_backward(q, k, v, g, b, do, S0, dsf, scale=1.0, workspace=ws,
+                                     chunk_states=cs)
+    torch.cuda.synchronize()
+    ws_g = torch.empty_like(ws)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            outs = gdn.gdn_prefill_backward(q, k, v, g, b, do, S0, dsf, scale=1.0, workspace=ws_g,
+                                            chunk_states=cs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    def other():
+        gdn.gdn_prefill_backward(q, k, v, g, b, do, S0, dsf, scale=1.0, workspace=ws,
+                                 chunk_states=cs)
+
+    _replays_match(graph, outs, eager, other)
 
 
 def test_graph_capture_decode_step():
