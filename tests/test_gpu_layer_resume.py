@@ -152,17 +152,28 @@ def _gated(x, w, a, b, z, nw, S0, cu, p, **kw):
     return out
 
 
-def test_gated_with_history_equals_prefill_then_gate_and_splits():
+GATED_SPLITS = {
+    # one sequence: the gate fused into the scan (its grid fits the device);
+    # 8192 tokens also run in segments
+    "single": ([600], [192]),
+    "segmented": ([8192], [4096]),
+    # three sequences: the scan's grid is too large to fuse, the gate runs after it
+    "packed": ([300, 70, 2], [192, 64, 0]),
+}
+
+
+@pytest.mark.parametrize("name", list(GATED_SPLITS))
+def test_gated_with_history_equals_prefill_then_gate_and_splits(name):
     import torch
     import linear_attention_sequence_delta_amd as gdn
-    lengths, first = [300, 70, 2], [192, 64, 0]
-    p = synth.raw_prefill(7400, lengths=lengths, init_state=True)
+    lengths, first = GATED_SPLITS[name]
+    p = synth.raw_prefill(7400 + len(name), lengths=lengths, init_state=True)
     rng = np.random.default_rng(7401)
     z = synth.bf16_bits(rng.normal(0.0, 1.0, (p.T, p.H_v, p.dv)).astype(np.float32))
     nw = rng.uniform(0.5, 1.5, p.dv).astype(np.float32)
     hist = _history(7402, p.N, p.x.shape[1])
     a, b = p.meta["a"], p.meta["b"]
-    print("gated resumed prefill", lengths, flush=True)
+    print("gated resumed prefill", name, lengths, flush=True)
     y, o, S, cs = _gated(p.x, p.w, a, b, z, nw, p.S0, p.cu_seqlens, p, conv_state_in=dev(hist))
     o2, S2, cs2 = _call(p.x, p.w, a, b, p.S0, p.cu_seqlens, p, conv_state_in=dev(hist))
     y2 = gdn.gdn_gated_norm(o2, dev(z), dev(nw))
